@@ -1,0 +1,247 @@
+"""CPU oracle for one sparse Mixture-of-Experts FFN layer forward.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or execute this module;
+only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use it. It shares no code
+with the HIP library.
+
+Everything is computed in float64 (NumPy; BLAS dgemm is plain fp64 accumulation). Inputs arrive
+as bfloat16 bit patterns (uint16) or float32 and are widened to float64 exactly. The result is the
+plain definition of the layer; experts run in a per-expert loop, which is fine on the CPU.
+
+Sources (the pages this follows):
+  [MoE overview]  Sparse-MoE overview article, adg.csdn.net (6a31135810ee7a33f27dd6b8), §2.2 "router
+                  mechanism": Top-K routing = scoring, selection, weighting, combination; §4.1 MoE
+                  layer code (flatten, score, top-k, softmax over the k, per-expert loop).
+  [MoE kernels]   "MoE inference kernels: expert parallelism, dynamic routing gates and all-to-all
+                  overlap", blog.llmgo.top, §1.1 (always-on shared expert + fine-grained routed
+                  experts), §1.2 (W_gate, W_up, W_down per expert), §4.2 (grouped GEMM over an
+                  offsets array), §4.3 (token permutation: flatten ids, sort, bincount, offsets).
+  [Data movement] "Computation and Data Movement for Inference", §4 and §15 (sort routes by expert,
+                  run each expert once over its bucket, convert back to token order, weight, merge).
+  [Inference ch.6] "大模型推理优化基础" (LLM-from-scratch ch. 6), roofline section: a gated MLP is
+                  up, gate and down matmuls.
+
+Readings where the pages are silent or garbled (each is also listed in the design doc):
+  * combine: out = Shared(x) + sum_j w_j * Expert_{e_j}(x); the shared expert has weight 1, no
+    residual and no norm inside the layer (the [MoE kernels] §1.1 formula is lost in extraction).
+  * no learned router bias; an optional per-expert logit bias is an explicit input, added to the
+    logits before both selection and softmax.
+  * gate = softmax over the K selected raw logits, temperature 1 ([MoE overview] §2.2 step 3).
+  * expert = SwiGLU: h = SiLU(x W_gate^T) * (x W_up^T), y = h W_down^T, SiLU(z) = z * sigmoid(z)
+    (standard definition; the pages name the three matrices but never define the activation).
+  * top-K order: value descending, ties to the lower expert index.
+  * permutation: rows sorted by (expert, token), i.e. flat position t*k+j ascending inside each
+    expert; offsets are exclusive with E+1 entries.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "widen", "router_logits", "select_topk", "softmax_selected", "route", "permute", "silu",
+    "swiglu", "grouped_ffn", "combine", "layer_forward", "layer_forward_tokens", "topk_gap",
+]
+
+
+# ----------------------------------------------------------------------------- input decoding
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """bf16 bit patterns (uint16) or float32 -> float64, exactly."""
+    a = np.asarray(a)
+    if dtype == "bf16":
+        assert a.dtype == np.uint16
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return a.astype(np.float32).astype(np.float64)
+    if dtype == "f64":
+        return a.astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------- routing
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, logit_bias: np.ndarray | None = None) -> np.ndarray:
+    """Scoring: s[t, e] = x_t . W_g[e] (+ b_e).
+
+    [MoE overview] §2.2 step 1: a small linear layer scores each token against every expert;
+    W_g is stored [E, d] like a linear layer's [out, in] weight ([MoE kernels] §4.3 gate).
+    """
+    L = np.asarray(x, np.float64) @ np.asarray(w_router, np.float64).T
+    if logit_bias is not None:
+        L = L + np.asarray(logit_bias, np.float64)[None, :]
+    return L
+
+
+def select_topk(L: np.ndarray, k: int) -> np.ndarray:
+    """Selection: per token, the k experts with the highest scores.
+
+    [MoE overview] §2.2 step 2 (sort all E scores, keep the K best). Order: value descending, ties
+    to the lower expert index. A stable sort of the negated scores gives exactly that order.
+    """
+    L = np.asarray(L, np.float64)
+    T, E = L.shape
+    if not (1 <= k <= E):
+        raise ValueError("need 1 <= k <= E")
+    order = np.argsort(-L, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def softmax_selected(L: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Weighting: softmax over the k selected scores, so the k weights sum to 1.
+
+    [MoE overview] §2.2 step 3 and the §4.1 code (softmax over the top-k scores).
+    The largest selected score is subtracted first; that does not change the value.
+    """
+    v = np.take_along_axis(np.asarray(L, np.float64), idx, axis=1)
+    if v.shape[1] == 0:
+        return v
+    m = v.max(axis=1, keepdims=True)
+    e = np.exp(v - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def route(x, w_router, k, logit_bias=None):
+    """Scoring, selection and weighting for every token: (logits [T,E], idx [T,k], w [T,k])."""
+    L = router_logits(x, w_router, logit_bias)
+    idx = select_topk(L, k)
+    return L, idx, softmax_selected(L, idx)
+
+
+def topk_gap(L: np.ndarray, k: int) -> np.ndarray:
+    """Per-token margin between the k-th and (k+1)-th largest score (inf when k == E)."""
+    T, E = L.shape
+    if k >= E:
+        return np.full(T, np.inf)
+    s = -np.sort(-np.asarray(L, np.float64), axis=1)
+    return s[:, k - 1] - s[:, k]
+
+
+# ----------------------------------------------------------------------------- dispatch
+
+def permute(idx: np.ndarray, E: int):
+    """Dispatch bookkeeping: (counts [E], offsets [E+1], perm_src [T*k], inv_perm [T*k]).
+
+    [MoE kernels] §4.3: flatten the selected expert ids, bring equal ids together, count tokens per
+    expert (bincount) and turn the counts into offsets for the grouped GEMM (§4.2).
+    [Data movement] §4: route records sorted by expert id so that one weight load serves a bucket.
+
+    perm_src[r] is the flat position t*k + j of the r-th row in expert order; rows of one expert are
+    in increasing flat position (hence increasing token). inv_perm is its inverse.
+    """
+    idx = np.asarray(idx, np.int64)
+    T, k = idx.shape
+    flat = idx.reshape(-1)
+    counts = np.zeros(E, np.int64)
+    for e in flat:
+        counts[e] += 1
+    offsets = np.zeros(E + 1, np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    perm_src = np.empty(T * k, np.int64)
+    fill = offsets[:E].copy()
+    for p in range(T * k):           # flat positions in increasing order
+        e = flat[p]
+        perm_src[fill[e]] = p
+        fill[e] += 1
+    inv_perm = np.empty(T * k, np.int64)
+    inv_perm[perm_src] = np.arange(T * k)
+    return counts, offsets, perm_src, inv_perm
+
+
+# ----------------------------------------------------------------------------- experts
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU (Swish with beta = 1): z * sigmoid(z)."""
+    z = np.asarray(z, np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu(X: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """One gated expert MLP: y = (SiLU(X W_gate^T) * (X W_up^T)) W_down^T.
+
+    [MoE kernels] §1.2: each routed expert holds W_gate, W_up, W_down; [Inference ch.6] roofline
+    section: a gated MLP is the up, gate and down matmuls. Weights are [out, in].
+    """
+    X = np.asarray(X, np.float64)
+    G = X @ np.asarray(w_gate, np.float64).T
+    U = X @ np.asarray(w_up, np.float64).T
+    return (silu(G) * U) @ np.asarray(w_down, np.float64).T
+
+
+def grouped_ffn(x_rows: np.ndarray, offsets: np.ndarray, expert_fn) -> np.ndarray:
+    """Every expert over its own contiguous bucket of rows; empty buckets do no work.
+
+    [MoE kernels] §4.2: one grouped GEMM over ragged groups given by an offsets array.
+    ``x_rows`` are the dispatched rows (expert order); ``expert_fn(e)`` returns float64
+    (W_gate [H,d], W_up [H,d], W_down [d,H]).
+    """
+    x_rows = np.asarray(x_rows, np.float64)
+    y = np.zeros_like(x_rows)
+    E = len(offsets) - 1
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            g, u, dn = expert_fn(e)
+            y[a:b] = swiglu(x_rows[a:b], g, u, dn)
+    return y
+
+
+def combine(y_perm: np.ndarray, inv_perm: np.ndarray, w: np.ndarray, shared_out: np.ndarray | None = None):
+    """Combination: out_t = Shared(x_t) + sum_j w[t, j] * y[row of (t, j)].
+
+    [MoE overview] §2.2 step 4 (weighted sum of the selected experts); [MoE kernels] §1.1 (the
+    shared expert's output is added for every token); [Data movement] §4 (expert outputs go back
+    to token order, are weighted and merged).
+    """
+    w = np.asarray(w, np.float64)
+    T, k = w.shape
+    y_perm = np.asarray(y_perm, np.float64)
+    d = y_perm.shape[1] if y_perm.ndim == 2 else (shared_out.shape[1] if shared_out is not None else 0)
+    out = np.zeros((T, d)) if shared_out is None else np.array(shared_out, np.float64, copy=True)
+    for j in range(k):
+        rows = np.asarray(inv_perm, np.int64).reshape(T, k)[:, j]
+        out += w[:, j:j + 1] * y_perm[rows]
+    return out
+
+
+# ----------------------------------------------------------------------------- whole layer
+
+def layer_forward(x, w_router, k, expert_fn, shared_fn=None, logit_bias=None):
+    """The full layer on float64 inputs. Returns a dict of every intermediate.
+
+    ``expert_fn(e)`` / ``shared_fn()`` return float64 (W_gate, W_up, W_down).
+    """
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    E = np.asarray(w_router).shape[0]
+    L, idx, w = route(x, w_router, k, logit_bias)
+    counts, offsets, perm_src, inv_perm = permute(idx, E)
+    x_rows = x[perm_src // k] if T else np.zeros((0, x.shape[1]))
+    y_perm = grouped_ffn(x_rows, offsets, expert_fn)
+    shared = swiglu(x, *shared_fn()) if shared_fn is not None else None
+    out = combine(y_perm, inv_perm, w, shared)
+    return dict(logits=L, idx=idx, w=w, counts=counts, offsets=offsets, perm_src=perm_src,
+                inv_perm=inv_perm, y_perm=y_perm, shared=shared, out=out)
+
+
+def layer_forward_tokens(x_rows, w_router, k, expert_fn, shared_fn=None, logit_bias=None):
+    """Output rows for a sample of tokens, one token at a time (each token's result depends only on
+    its own row: routing is per token and the experts are applied row by row)."""
+    x_rows = np.asarray(x_rows, np.float64)
+    L, idx, w = route(x_rows, w_router, k, logit_bias)
+    out = np.zeros_like(x_rows)
+    cache = {}
+    for t in range(x_rows.shape[0]):
+        acc = np.zeros(x_rows.shape[1])
+        if shared_fn is not None:
+            if "shared" not in cache:
+                cache["shared"] = shared_fn()
+            acc += swiglu(x_rows[t:t + 1], *cache["shared"])[0]
+        for j in range(k):
+            e = int(idx[t, j])
+            if e not in cache:
+                cache[e] = expert_fn(e)
+            acc += w[t, j] * swiglu(x_rows[t:t + 1], *cache[e])[0]
+        out[t] = acc
+    return dict(logits=L, idx=idx, w=w, out=out)

@@ -1,0 +1,28 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs a real MI355X (gfx950) GPU")
+    config.addinivalue_line("markers", "slow: full-size cases (minutes)")
+
+
+def _ensure_built():
+    """Build the shared libraries in-tree if they are missing (CPU-side, e.g. a fresh checkout)."""
+    from synth import LIB_PATH as syn_lib
+    if not os.path.exists(syn_lib):
+        from synth import build as b
+        b.build()
+    lib = os.path.join(ROOT, "sparse_moe_layer_router_amd", "libmoe.so")
+    if not os.path.exists(lib) and os.path.exists(os.path.join(ROOT, "sparse_moe_layer_router_amd", "build.py")):
+        from sparse_moe_layer_router_amd import build as mb
+        mb.build()
+
+
+_ensure_built()

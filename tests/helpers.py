@@ -1,0 +1,58 @@
+"""Test helpers: gap screening of seeded inputs and oracle wiring (tests only)."""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import synth
+
+MIN_GAP = 1e-4   # tokens whose k-th and (k+1)-th router scores are closer than this are redrawn
+
+
+def screen_gaps(inp: synth.HostInputs, min_gap: float = MIN_GAP, max_rounds: int = 64) -> int:
+    """Redraw activation rows whose top-k margin (fp64 oracle logits) is below ``min_gap``.
+
+    Rejection happens per token: a near-tie row is replaced by the next draw of its own redraw
+    stream until every token clears the margin. Returns the number of rows redrawn.
+    """
+    cfg = inp.cfg
+    wg = oracle.widen(inp.w_router, cfg.dtype)
+    redrawn = 0
+    for _ in range(max_rounds):
+        L = oracle.router_logits(oracle.widen(inp.x, cfg.dtype), wg, inp.logit_bias)
+        bad = np.nonzero(oracle.topk_gap(L, cfg.k) < min_gap)[0]
+        if bad.size == 0:
+            return redrawn
+        synth.redraw_rows(inp, bad)
+        redrawn += int(bad.size)
+    raise RuntimeError("gap screening did not converge")
+
+
+def expert_fn_host(cfg: synth.LayerConfig, seed: int, stacked=None):
+    """float64 expert weights for the oracle, regenerated on the host (cached)."""
+    cache = {}
+
+    def fn(e):
+        if e not in cache:
+            if stacked is not None:
+                g, u, dn = (s[e] for s in stacked)
+            else:
+                g, u, dn = synth.expert_weights_host(cfg, seed, e)
+            cache[e] = tuple(oracle.widen(a, cfg.dtype) for a in (g, u, dn))
+        return cache[e]
+
+    return fn
+
+
+def shared_fn_host(cfg: synth.LayerConfig, seed: int):
+    if cfg.Hs == 0:
+        return None
+    box = {}
+
+    def fn():
+        if "w" not in box:
+            box["w"] = tuple(oracle.widen(a, cfg.dtype) for a in synth.expert_weights_host(cfg, seed, 0, shared=True))
+        return box["w"]
+
+    return fn

@@ -1,0 +1,364 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics (no GPU).
+
+Each test checks the oracle against something other than itself: hand-worked instances solved in
+closed form, brute force over all k-subsets, independent library routines (torch.topk, scipy's
+softmax, torch's SiLU), invariants the pages state, and the pages' own assignment counts.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import moe_oracle as om
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def sig(z):
+    return 1.0 / (1.0 + math.exp(-z))
+
+
+def rand_layer(rng, T, d, E, H, scale=1.0):
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((E, d)) * scale / math.sqrt(d)
+    ex = [(rng.standard_normal((H, d)) / math.sqrt(d), rng.standard_normal((H, d)) / math.sqrt(d),
+           rng.standard_normal((d, H)) / math.sqrt(H)) for _ in range(E)]
+    return x, wg, ex
+
+
+def screened(rng, T, d, E, k, H, min_gap=1e-3):
+    """Random layer whose tokens all have a clear top-k margin (redraw rows otherwise)."""
+    x, wg, ex = rand_layer(rng, T, d, E, H)
+    for _ in range(200):
+        bad = np.nonzero(oracle.topk_gap(oracle.router_logits(x, wg), k) < min_gap)[0]
+        if bad.size == 0:
+            return x, wg, ex
+        x[bad] = rng.standard_normal((bad.size, d))
+    raise RuntimeError
+
+
+# ------------------------------------------------------------------ hand-worked instances
+
+def w1_layer(with_shared):
+    """E=4, k=2, T=2, d=2, H=1. Router rows e0=[1,2.5], e1=[3,-1], e2=[2,2], e3=[0,1];
+    expert e: W_gate=[[1,1]], W_up=[[e+1,e+1]], W_down=[[1],[-1]]; x0=[1,0], x1=[0,1]."""
+    x = np.array([[1.0, 0.0], [0.0, 1.0]])
+    wg = np.array([[1.0, 2.5], [3.0, -1.0], [2.0, 2.0], [0.0, 1.0]])
+    ex = {e: (np.array([[1.0, 1.0]]), np.array([[e + 1.0, e + 1.0]]), np.array([[1.0], [-1.0]])) for e in range(4)}
+    sh = (np.array([[1.0, 1.0]]), np.array([[1.0, 1.0]]), np.array([[1.0], [1.0]]))
+    return oracle.layer_forward(x, wg, 2, lambda e: ex[e], (lambda: sh) if with_shared else None)
+
+
+def test_w1_routing_by_hand():
+    r = w1_layer(False)
+    # logits t0 = [1, 3, 2, 0], t1 = [2.5, -1, 2, 1]
+    np.testing.assert_array_equal(r["logits"], [[1, 3, 2, 0], [2.5, -1, 2, 1]])
+    np.testing.assert_array_equal(r["idx"], [[1, 2], [0, 2]])
+    # softmax of two scores a > b is (sigmoid(a-b), sigmoid(b-a))
+    np.testing.assert_allclose(r["w"], [[sig(1), sig(-1)], [sig(0.5), sig(-0.5)]], rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(r["counts"], [1, 1, 2, 0])           # expert 3 gets nothing
+    np.testing.assert_array_equal(r["offsets"], [0, 1, 2, 4, 4])
+    np.testing.assert_array_equal(r["perm_src"], [2, 0, 1, 3])
+    np.testing.assert_array_equal(r["inv_perm"], [1, 2, 0, 3])
+
+
+def test_w1_outputs_by_hand():
+    # every expert sees gate=1, up=e+1 for both tokens: y_e = (e+1) * SiLU(1) * [1, -1], SiLU(1) = sigmoid(1)
+    s1 = sig(1.0)
+    out0 = (2 * sig(1) + 3 * sig(-1)) * s1
+    out1 = (1 * sig(0.5) + 3 * sig(-0.5)) * s1
+    r = w1_layer(False)
+    np.testing.assert_allclose(r["out"], [[out0, -out0], [out1, -out1]], rtol=1e-14)
+    assert abs(out0 - 1.658729090501) < 1e-11 and abs(out1 - 1.283067268043) < 1e-11
+    # shared expert gate=[1,1], up=[1,1], down=[[1],[1]] adds sigmoid(1) to both features
+    r = w1_layer(True)
+    np.testing.assert_allclose(r["out"], [[out0 + s1, -out0 + s1], [out1 + s1, -out1 + s1]], rtol=1e-14)
+
+
+def test_w2_ties_go_to_lower_index():
+    L = np.array([[2.0, 2.0, 1.0, 0.0]])
+    idx = oracle.select_topk(L, 1)
+    assert idx.tolist() == [[0]]
+    assert oracle.softmax_selected(L, idx).tolist() == [[1.0]]
+    idx = oracle.select_topk(L, 2)
+    assert idx.tolist() == [[0, 1]]
+    np.testing.assert_allclose(oracle.softmax_selected(L, idx), [[0.5, 0.5]])
+    # tie at the boundary: experts 0 and 2 both score 1, the lower index wins the last slot
+    assert oracle.select_topk(np.array([[1.0, 3.0, 1.0, 0.0]]), 2).tolist() == [[1, 0]]
+    # signed zeros compare equal
+    assert oracle.select_topk(np.array([[-0.0, 0.0, -1.0]]), 1).tolist() == [[0]]
+
+
+def test_w3_k_equals_E_identical_experts_is_dense_ffn():
+    rng = np.random.default_rng(3)
+    T, d, E, H = 6, 10, 4, 7
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((E, d))
+    g, u, dn = rng.standard_normal((H, d)), rng.standard_normal((H, d)), rng.standard_normal((d, H))
+    r = oracle.layer_forward(x, wg, E, lambda e: (g, u, dn))
+    # dense FFN via torch's own SiLU in float64 (an independent routine)
+    xt = torch.from_numpy(x)
+    dense = (torch.nn.functional.silu(xt @ torch.from_numpy(g).T) * (xt @ torch.from_numpy(u).T)) @ torch.from_numpy(dn).T
+    np.testing.assert_allclose(r["out"], dense.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["w"].sum(1), 1.0, rtol=0, atol=1e-15)
+
+
+# ------------------------------------------------------------------ selection and weights
+
+@pytest.mark.parametrize("E,k", [(4, 1), (4, 2), (6, 3), (8, 2), (8, 5), (8, 8)])
+def test_topk_is_best_subset_by_brute_force(E, k):
+    rng = np.random.default_rng(E * 10 + k)
+    L = rng.standard_normal((64, E))
+    idx = oracle.select_topk(L, k)
+    for t in range(L.shape[0]):
+        best = max(itertools.combinations(range(E), k), key=lambda s: sum(L[t, list(s)]))
+        assert set(idx[t].tolist()) == set(best)
+        # in-list order: strictly decreasing scores (no ties in continuous draws)
+        assert np.all(np.diff(L[t, idx[t]]) < 0)
+
+
+def test_topk_matches_torch_topk_and_is_monotone_invariant():
+    rng = np.random.default_rng(11)
+    L = rng.standard_normal((500, 256))
+    idx = oracle.select_topk(L, 8)
+    tv, ti = torch.topk(torch.from_numpy(L), 8, dim=1)
+    np.testing.assert_array_equal(idx, ti.numpy())
+    # the selected set does not change under a monotone map of the scores
+    np.testing.assert_array_equal(idx, oracle.select_topk(scipy.special.expit(L), 8))
+    np.testing.assert_array_equal(idx, oracle.select_topk(scipy.special.softmax(L, axis=1), 8))
+
+
+def test_softmax_over_k_is_renormalised_full_softmax():
+    rng = np.random.default_rng(5)
+    L = rng.standard_normal((40, 16)) * 3
+    for k in (1, 2, 5, 16):
+        idx = oracle.select_topk(L, k)
+        w = oracle.softmax_selected(L, idx)
+        full = scipy.special.softmax(L, axis=1)
+        sel = np.take_along_axis(full, idx, 1)
+        np.testing.assert_allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-13)
+        np.testing.assert_allclose(w.sum(1), 1.0, atol=1e-15)      # weights sum to 1
+        if k == 1:
+            assert np.all(w == 1.0)
+
+
+def test_softmax_large_scores_do_not_overflow():
+    L = np.array([[1000.0, 999.0, -5.0]])
+    w = oracle.softmax_selected(L, oracle.select_topk(L, 2))
+    np.testing.assert_allclose(w, [[sig(1), sig(-1)]], rtol=1e-14)
+
+
+def test_bias_shifts_selection_and_weights():
+    # bias added to logits before both selection and softmax
+    L0 = np.zeros((1, 3))
+    b = np.array([0.0, 1.0, 2.0])
+    x = np.ones((1, 1))
+    L, idx, w = oracle.route(x, np.zeros((3, 1)), 2, b)
+    assert idx.tolist() == [[2, 1]]
+    np.testing.assert_allclose(w, [[sig(1), sig(-1)]])
+    np.testing.assert_array_equal(L, L0 + b)
+
+
+# ------------------------------------------------------------------ permutation
+
+@pytest.mark.parametrize("T,E,k", [(0, 4, 2), (1, 4, 4), (17, 8, 2), (64, 256, 8), (300, 16, 3)])
+def test_permutation_invariants_and_stable_argsort_construction(T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]) if T else np.zeros((0, k), np.int64)
+    counts, offsets, perm_src, inv_perm = oracle.permute(idx, E)
+    flat = idx.reshape(-1)
+    # counts by brute force, offsets are the exclusive running sum, total T*k
+    assert [int((flat == e).sum()) for e in range(E)] == counts.tolist()
+    assert offsets[0] == 0 and offsets[-1] == T * k and np.all(np.diff(offsets) == counts)
+    assert np.all(counts >= 0) and np.all(counts <= T)
+    # a bijection, inverse of each other
+    assert sorted(perm_src.tolist()) == list(range(T * k))
+    np.testing.assert_array_equal(inv_perm[perm_src], np.arange(T * k))
+    # the listing's construction (flatten ids, argsort, bincount, cumsum), read with a stable sort
+    np.testing.assert_array_equal(perm_src, np.argsort(flat, kind="stable"))
+    np.testing.assert_array_equal(np.bincount(flat, minlength=E), counts)
+    np.testing.assert_array_equal(np.cumsum(counts), offsets[1:])
+    # keys (expert, token) non-decreasing along the rows
+    keys = [(flat[p], p // k) for p in perm_src]
+    assert keys == sorted(keys)
+    for e in range(E):
+        assert np.all(flat[perm_src[offsets[e]:offsets[e + 1]]] == e)
+
+
+def test_assignment_counts_from_the_pages():
+    spec = json.load(open(os.path.join(GOLDEN, "assignment_counts.json")))
+    rng = np.random.default_rng(0)
+    for c in spec["cases"]:
+        T, k, E = c["tokens"], c["k"], c["E"]
+        L = rng.standard_normal((T, E))
+        idx = oracle.select_topk(L, k)
+        counts, offsets, perm_src, _ = oracle.permute(idx, E)
+        assert offsets[-1] == c["assignments"] == len(perm_src)
+        assert counts.sum() / E == pytest.approx(c["mean_per_expert"])
+
+
+def test_layer_shape_example_from_the_pages():
+    spec = json.load(open(os.path.join(GOLDEN, "layer_shape_example.json")))
+    B, S, d = spec["input_shape"]
+    rng = np.random.default_rng(1)
+    x, wg, ex = rand_layer(rng, B * S, d, spec["experts"], spec["expert_width"])
+    r = oracle.layer_forward(x, wg, spec["k"], lambda e: ex[e])
+    assert list(r["out"].reshape(B, S, d).shape) == spec["output_shape"]
+
+
+# ------------------------------------------------------------------ experts and combine
+
+def test_single_expert_is_plain_swiglu_with_torch_silu():
+    rng = np.random.default_rng(2)
+    x, wg, ex = rand_layer(rng, 9, 12, 1, 20)
+    r = oracle.layer_forward(x, wg, 1, lambda e: ex[e])
+    g, u, dn = (torch.from_numpy(a) for a in ex[0])
+    xt = torch.from_numpy(x)
+    ref = (torch.nn.functional.silu(xt @ g.T) * (xt @ u.T)) @ dn.T
+    np.testing.assert_allclose(r["out"], ref.numpy(), rtol=1e-12, atol=1e-13)
+    assert np.all(r["w"] == 1.0)
+
+
+def test_silu_known_values():
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(oracle.silu(np.array([1.0, -1.0, 20.0])), [sig(1), -sig(-1), 20 * sig(20)], rtol=1e-15)
+    np.testing.assert_allclose(oracle.silu(np.linspace(-8, 8, 33)),
+                               torch.nn.functional.silu(torch.linspace(-8, 8, 33, dtype=torch.float64)).numpy(),
+                               rtol=1e-14)
+
+
+@pytest.mark.parametrize("T,E,k", [(12, 8, 2), (20, 6, 3), (5, 4, 4)])
+def test_sparse_equals_dense_masked(T, E, k):
+    """Run every expert on every token and weight non-selected ones by zero: same output."""
+    rng = np.random.default_rng(T * E * k)
+    x, wg, ex = screened(rng, T, 16, E, k, 24)
+    sh = (rng.standard_normal((24, 16)), rng.standard_normal((24, 16)), rng.standard_normal((16, 24)))
+    r = oracle.layer_forward(x, wg, k, lambda e: ex[e], lambda: sh)
+    L = x @ wg.T
+    dense_w = np.zeros((T, E))
+    for t in range(T):
+        top = np.argsort(-L[t])[:k]
+        z = np.exp(L[t, top] - L[t, top].max())
+        dense_w[t, top] = z / z.sum()
+    xt = torch.from_numpy(x)
+
+    def ffn(g, u, dn):
+        return ((torch.nn.functional.silu(xt @ torch.from_numpy(g).T) * (xt @ torch.from_numpy(u).T))
+                @ torch.from_numpy(dn).T).numpy()
+
+    dense = ffn(*sh) + sum(dense_w[:, e:e + 1] * ffn(*ex[e]) for e in range(E))
+    np.testing.assert_allclose(r["out"], dense, rtol=1e-11, atol=1e-11)
+
+
+def test_output_linear_in_down_projection_and_shared_only():
+    rng = np.random.default_rng(9)
+    x, wg, ex = screened(rng, 10, 8, 4, 2, 6)
+    sh = (rng.standard_normal((5, 8)), rng.standard_normal((5, 8)), rng.standard_normal((8, 5)))
+    base = oracle.layer_forward(x, wg, 2, lambda e: ex[e])["out"]
+    scaled = oracle.layer_forward(x, wg, 2, lambda e: (ex[e][0], ex[e][1], 2.5 * ex[e][2]))["out"]
+    np.testing.assert_allclose(scaled, 2.5 * base, rtol=1e-12, atol=1e-14)
+    zero = oracle.layer_forward(x, wg, 2, lambda e: (ex[e][0], ex[e][1], 0 * ex[e][2]), lambda: sh)
+    np.testing.assert_allclose(zero["out"], oracle.swiglu(x, *sh), rtol=1e-14, atol=0)
+    # the shared expert adds exactly its own FFN output
+    with_sh = oracle.layer_forward(x, wg, 2, lambda e: ex[e], lambda: sh)["out"]
+    np.testing.assert_allclose(with_sh - base, oracle.swiglu(x, *sh), rtol=1e-10, atol=1e-12)
+
+
+def test_token_sampled_forward_matches_full_forward():
+    rng = np.random.default_rng(4)
+    x, wg, ex = screened(rng, 15, 12, 8, 3, 10)
+    sh = (rng.standard_normal((7, 12)), rng.standard_normal((7, 12)), rng.standard_normal((12, 7)))
+    full = oracle.layer_forward(x, wg, 3, lambda e: ex[e], lambda: sh)
+    rows = [0, 4, 14]
+    part = oracle.layer_forward_tokens(x[rows], wg, 3, lambda e: ex[e], lambda: sh)
+    np.testing.assert_allclose(part["out"], full["out"][rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(part["idx"], full["idx"][rows])
+
+
+def test_empty_batch():
+    r = oracle.layer_forward(np.zeros((0, 4)), np.ones((3, 4)), 2, lambda e: None)
+    assert r["out"].shape == (0, 4) and r["offsets"].tolist() == [0, 0, 0, 0]
+
+
+def test_widen_bf16_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x7F7F, 0x0001, 0x4049], np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.widen(bits, "bf16"), ref)
+
+
+# ------------------------------------------------------------------ planted mistakes are caught
+
+def _plant(monkeypatch, name, fn):
+    monkeypatch.setattr(om, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def _swiglu_swapped(X, g, u, dn):
+    X = np.asarray(X, np.float64)
+    return (om.silu(X @ np.asarray(u).T) * (X @ np.asarray(g).T)) @ np.asarray(dn).T
+
+
+def _combine_no_shared(y, inv, w, shared=None):
+    return _COMBINE(y, inv, w, None)
+
+
+def _combine_with_perm(y, inv, w, shared=None):
+    inv = np.asarray(inv)
+    perm = np.empty_like(inv)
+    perm[inv] = np.arange(len(inv))
+    return _COMBINE(y, perm, w, shared)
+
+
+def _softmax_unnormalised_over_k(L, idx):
+    return np.take_along_axis(scipy.special.softmax(np.asarray(L), axis=1), idx, 1)
+
+
+def _perm_reversed(idx, E):
+    c, o, p, _ = _PERMUTE(idx, E)
+    p = p.copy()
+    for e in range(E):
+        p[o[e]:o[e + 1]] = p[o[e]:o[e + 1]][::-1].copy()
+    inv = np.empty_like(p)
+    inv[p] = np.arange(len(p))
+    return c, o, p, inv
+
+
+def _route_bias_weights_only(x, w_router, k, logit_bias=None):
+    L0 = om.router_logits(x, w_router, None)
+    idx = om.select_topk(L0, k)
+    L = om.router_logits(x, w_router, logit_bias)
+    return L, idx, om.softmax_selected(L, idx)
+
+
+_COMBINE = om.combine
+_PERMUTE = om.permute
+
+MUTATIONS = {
+    "silu_as_sigmoid": ("silu", lambda z: 1.0 / (1.0 + np.exp(-np.asarray(z))),
+                        test_single_expert_is_plain_swiglu_with_torch_silu),
+    "gate_and_up_swapped": ("swiglu", _swiglu_swapped, test_single_expert_is_plain_swiglu_with_torch_silu),
+    "softmax_over_all_E": ("softmax_selected", _softmax_unnormalised_over_k,
+                           test_softmax_over_k_is_renormalised_full_softmax),
+    "topk_ascending": ("select_topk", lambda L, k: np.argsort(np.asarray(L), axis=1, kind="stable")[:, :k],
+                       lambda: test_topk_is_best_subset_by_brute_force(8, 2)),
+    "perm_reversed_within_expert": ("permute", _perm_reversed, test_w1_routing_by_hand),
+    "shared_expert_dropped": ("combine", _combine_no_shared, test_w1_outputs_by_hand),
+    "combine_gathers_with_perm_src": ("combine", _combine_with_perm, test_w1_outputs_by_hand),
+    "bias_only_in_weights": ("route", _route_bias_weights_only, test_bias_shifts_selection_and_weights),
+}
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
+    """A plausible slip planted in the oracle makes the named pin fail."""
+    name, fn, pin = MUTATIONS[mutation]
+    _plant(monkeypatch, name, fn)
+    with pytest.raises(AssertionError):
+        pin()
