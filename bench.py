@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse-MoE layer forward on one MI355X.
+
+One step = one moe_layer_forward (router, top-k + softmax, permutation, routed + shared SwiGLU
+experts, combine) over one batch of synthetic tokens already resident in HBM. W untimed warm-up
+steps, then exactly K timed steps between two device synchronizations; the step cycles through a
+few distinct token batches so consecutive steps route differently.
+
+Prints one JSON line: tokens/s for the whole step, the dominant kernel's roofline fraction (its
+average duration taken from HIP events recorded on the launch stream around that kernel during the
+timed steps, and its algorithmic bytes or flops per launch), and the CPU oracle timed on a bounded
+sample of the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; achieved HBM TB/s (decode) and MFMA util (prefill)"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+N_BATCHES = 4                   # distinct token batches cycled through the steps
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--workload", default="dsv3_decode_t8")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=None)
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------------------------ HIP events
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded (events on the library's stream)."""
+
+    def __init__(self, n):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            rc = self.lib.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.ev[i] = h
+
+    def array(self, start, count):
+        return ctypes.cast(ctypes.byref(self.ev, start * ctypes.sizeof(ctypes.c_void_p)),
+                           ctypes.POINTER(ctypes.c_void_p))
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), self.ev[a], self.ev[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for h in self.ev:
+            self.lib.hipEventDestroy(h)
+
+
+# ------------------------------------------------------------------------------- work accounting
+def alg_bytes_and_flops(cfg, counts_list, es):
+    """Per-stage algorithmic bytes and flops of one step, averaged over the cycled batches.
+
+    Bytes are what the method must move once: each active expert's weights, the shared expert's,
+    the router, x in, out out (plus, per kernel, its own inputs and outputs). Flops are
+    2*T*d*E (router) + 6*rows*d*H (gated MLP) + 6*T*d*Hs."""
+    T, d, E, k, H, Hs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.H, cfg.Hs
+    rows = T * k
+    res = []
+    for counts in counts_list:
+        n_act = int((counts > 0).sum())
+        gate_up_w = es * (n_act * 2 * H * d + 2 * Hs * d)
+        down_w = es * (n_act * d * H + d * Hs)
+        gate_up = gate_up_w + es * T * d + es * (rows * H + T * Hs)              # weights + x + hidden out
+        down = down_w + es * (rows * H + T * Hs) + es * (rows + (T if Hs else 0)) * d
+        layer = es * (n_act * 3 * H * d + 3 * Hs * d + E * d) + es * T * d + es * T * d
+        flops_gate_up = 4 * rows * d * H + 4 * T * d * Hs
+        flops_down = 2 * rows * d * H + 2 * T * d * Hs
+        res.append(dict(n_act=n_act, gate_up=gate_up, down=down, layer=layer,
+                        flops_gate_up=flops_gate_up, flops_down=flops_down,
+                        flops_layer=2 * T * d * E + 6 * rows * d * H + 6 * T * d * Hs,
+                        unit_gate_up=es * 2 * H * d, unit_down=es * d * H))
+    avg = {key: sum(r[key] for r in res) / len(res) for key in res[0]}
+    return avg
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload, kernel):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they match this source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel.split('<')[0]}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha") != source_sha(t.get("sources", [])):
+        return None
+    return t.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------------- CPU oracle
+def cpu_baseline(cfg, host, n_tokens):
+    """The fp64 oracle on a bounded sample of the same workload (input generation excluded)."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = None
+    rng = np.random.default_rng(1)
+    tokens = np.sort(rng.choice(cfg.T, size=min(n_tokens, cfg.T), replace=False))
+    x = oracle.widen(host.x[tokens], cfg.dtype)
+    wg = oracle.widen(host.w_router, cfg.dtype)
+    _, idx, _ = oracle.route(x, wg, cfg.k, host.logit_bias)
+    raw = {int(e): synth.expert_weights_host(cfg, 0, int(e)) for e in np.unique(idx)}   # untimed
+    shared_raw = synth.expert_weights_host(cfg, 0, 0, shared=True) if cfg.Hs else None
+    t0 = time.perf_counter()
+    ref = oracle.layer_forward_tokens(
+        host.x[tokens] if False else x, wg, cfg.k,
+        lambda e: tuple(oracle.widen(a, cfg.dtype) for a in raw[e]),
+        (lambda: tuple(oracle.widen(a, cfg.dtype) for a in shared_raw)) if shared_raw else None,
+        host.logit_bias)
+    dt = time.perf_counter() - t0
+    assert ref["out"].shape == (len(tokens), cfg.d)
+    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(tokens)} of {cfg.T} tokens of {cfg.name} (routing, bf16->fp64 widening of the "
+                      f"{len(raw)} selected experts{' + shared' if shared_raw else ''}, SwiGLU, combine), "
+                      f"{dt:.1f} s; expert weight generation excluded"}
+
+
+# ----------------------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (expert-parallel "
+              "all-to-all is out of scope); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import sparse_moe_layer_router_amd as moe
+
+    cfg = synth.CONFIG_BY_NAME[args.workload]
+    prefill = cfg.T * cfg.k / cfg.E > 32
+    K = args.steps if args.steps is not None else (20 if prefill else 50)
+    W = args.warmup if args.warmup is not None else 5
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[cfg.dtype]
+    es = 2 if cfg.dtype == "bf16" else 4
+
+    t_setup = time.perf_counter()
+    # weights: drawn directly in device memory (same generator streams as the host oracle)
+    E, H, d = cfg.E, cfg.H, cfg.d
+    wgt = torch.empty(E, H, d, dtype=dt, device=dev)
+    wup = torch.empty(E, H, d, dtype=dt, device=dev)
+    wdn = torch.empty(E, d, H, dtype=dt, device=dev)
+    shared = None
+    if cfg.Hs:
+        shared = (torch.empty(cfg.Hs, d, dtype=dt, device=dev), torch.empty(cfg.Hs, d, dtype=dt, device=dev),
+                  torch.empty(d, cfg.Hs, dtype=dt, device=dev))
+    synth.fill_expert_weights_device(cfg, 0, wgt, wup, wdn, shared)
+    host = synth.host_small_inputs(cfg, 0)
+
+    def up(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    w_router = up(host.w_router)
+    bias = torch.from_numpy(host.logit_bias).to(dev) if host.logit_bias is not None else None
+    xs = [up(host.x)] + [up(synth.normal_host((cfg.T, d), 100 + b, synth.stream_id(synth.K_X), 1.0, cfg.dtype))
+                         for b in range(1, N_BATCHES)]
+    shape = moe.make_shape(cfg.T, d, E, cfg.k, H, cfg.Hs, cfg.dtype)
+    ws = moe.allocate_workspace(shape)
+    outs = [torch.empty(cfg.T, d, dtype=dt, device=dev) for _ in range(N_BATCHES)]
+    counts = [torch.zeros(E, dtype=torch.int32, device=dev) for _ in range(N_BATCHES)]
+    sg, su, sd = shared if shared else (None, None, None)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    def step(i, events=None):
+        b = i % N_BATCHES
+        if events is None:
+            moe.moe_layer_forward(shape, xs[b], w_router, bias, wgt, wup, wdn, sg, su, sd, outs[b],
+                                  counts_out=counts[b], workspace=ws, stream=stream)
+        else:
+            moe.moe_layer_forward_timed(shape, xs[b], w_router, bias, wgt, wup, wdn, sg, su, sd, outs[b],
+                                        counts_out=counts[b], workspace=ws, stream=stream, events=events)
+
+    for i in range(max(W, N_BATCHES)):
+        step(i)
+    torch.cuda.synchronize()
+
+    n_st = moe.MOE_NUM_STAGES
+    ev = HipEvents(2 * n_st * K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, ev.array(2 * n_st * i, 2 * n_st))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {}
+    for s in range(n_st):
+        durs = [ev.elapsed_ms(2 * n_st * i + 2 * s, 2 * n_st * i + 2 * s + 1) for i in range(K)]
+        stage_ms[moe.STAGES[s]] = sum(durs) / K
+    ev.close()
+
+    counts_np = [c.cpu().numpy() for c in counts]
+    work = alg_bytes_and_flops(cfg, counts_np, es)
+    ms_per_step = elapsed * 1e3 / K
+    dominant = max(("ffn_gate_up", "ffn_down"), key=lambda s: stage_ms[s])
+    kname = moe.moe_stage_kernel_name(shape, moe.STAGES.index(dominant))
+    kms = stage_ms[dominant]
+    if prefill:
+        flops = work["flops_gate_up" if dominant == "ffn_gate_up" else "flops_down"]
+        achieved = flops / (kms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    else:
+        byt = work["gate_up" if dominant == "ffn_gate_up" else "down"]
+        achieved = byt / (kms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4)}
+    roof["kernel"] = kname
+    roof["kernel_ms"] = round(kms, 4)
+    roof["traffic"] = traffic_for(cfg.name, kname)
+
+    line = {
+        "metric": METRIC,
+        "value": round(cfg.T * K / elapsed, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Philox normal draws; random-init weights of the named layer shape)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
+                   "d_hidden": cfg.H, "d_shared_hidden": cfg.Hs, "zipf_bias": cfg.zipf_s,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"alg_bytes": int(work["layer"]), "alg_flops": int(work["flops_layer"]),
+                  "hbm_GBps": round(work["layer"] / (ms_per_step * 1e-3) / 1e9, 1),
+                  "tflops": round(work["flops_layer"] / (ms_per_step * 1e-3) / 1e12, 2),
+                  "active_experts_mean": work["n_act"]},
+        "stage_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
+        "setup_s": round(t_setup, 1),
+    }
+    if not args.no_cpu_baseline:
+        n_tok = args.cpu_sample_tokens or (4 if cfg.Hs or cfg.E > 8 else 16)
+        line["cpu_baseline"] = cpu_baseline(cfg, host, n_tok)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

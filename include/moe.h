@@ -1,0 +1,174 @@
+/*
+ * moe.h -- C ABI of the sparse Mixture-of-Experts FFN layer forward on one MI355X (gfx950).
+ *
+ * One layer forward is: router scoring, top-k selection, softmax over the k selected scores,
+ * dispatch of (token, slot) pairs into expert-contiguous order, the routed SwiGLU experts over
+ * their buckets plus an always-on shared expert, and the weighted-sum combine back into token
+ * order. Pages this follows:
+ *   - Sparse-MoE overview article (adg.csdn.net), section 2.2 "router mechanism": Top-K routing as
+ *     scoring -> selection -> softmax weighting -> weighted combination; section 4.1 layer code.
+ *   - "MoE inference kernels: expert parallelism, dynamic routing gates and all-to-all overlap"
+ *     (blog.llmgo.top): section 1.1 shared + fine-grained routed experts; section 1.2 W_gate, W_up,
+ *     W_down per expert; section 4.2 one grouped GEMM over ragged groups given by an offsets array,
+ *     empty experts skipped; section 4.3 token permutation (flatten ids, sort, bincount, offsets).
+ *   - "Computation and Data Movement for Inference", sections 4 and 15: route records sorted by
+ *     expert so one weight load serves a bucket; outputs restored to token order, weighted, merged.
+ *
+ * Conventions for every entry point
+ *   - Device pointers unless stated. The caller allocates and owns every buffer, including the
+ *     workspace; the library never allocates or frees memory and keeps no pointer past the call.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream). Nothing synchronizes the host and nothing is copied device-to-host. Results are
+ *     valid once `stream` reaches the point of the call.
+ *   - Row-major layouts. Weights are stored [out, in] like a linear layer's weight:
+ *     w_router [E, d]; w_gate, w_up [E, H, d]; w_down [E, d, H]; shared weights [Hs, d], [Hs, d],
+ *     [d, Hs]. x, y and out are [rows, d]. `dtype` applies to x, all weights, y and out; routing
+ *     weights, logits and the logit bias are always float32; indices are int32.
+ *   - Validation happens on the host before anything is enqueued; on any error nothing is
+ *     enqueued. Limits: 0 <= T, T * top_k < 2^31, 1 <= top_k <= n_experts <= 1024, d_model,
+ *     d_hidden >= 8 and multiples of 8, d_shared_hidden 0 or a multiple of 8, 16-byte aligned
+ *     x / weight / y / out pointers and 4-byte aligned int32 / float32 pointers. T == 0 (with a
+ *     valid shape) returns MOE_OK at once: nothing is read, checked or enqueued, so empty tensors
+ *     may pass NULL. Experts that receive no token cost no work.
+ *   - Deterministic: identical inputs give bitwise-identical outputs (no floating-point atomics).
+ *   - Not thread-hostile: the library has no mutable global state.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null required pointer, bad sizes, k outside [1, E] ... */
+  MOE_ERR_UNSUPPORTED = 2, /* dtype or size outside the supported range */
+  MOE_ERR_ALIGNMENT = 3,   /* d_model / hidden sizes or pointers not aligned as required */
+  MOE_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = 5          /* a kernel launch or event record failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer sizes (host pointer). */
+typedef struct {
+  int32_t T;               /* tokens in this batch */
+  int32_t d_model;         /* d */
+  int32_t n_experts;       /* E routed experts */
+  int32_t top_k;           /* k experts per token */
+  int32_t d_hidden;        /* H, hidden size of each routed expert */
+  int32_t d_shared_hidden; /* Hs, hidden size of the shared expert; 0 = no shared expert */
+  int32_t dtype;           /* moe_dtype */
+} moe_shape;
+
+/* Bytes of workspace that every entry point below accepts for shape `s` (0 if `s` is invalid). */
+size_t moe_workspace_bytes(const moe_shape* s);
+
+/* Short English description of a status code (static string). */
+const char* moe_status_string(moe_status st);
+
+/*
+ * moe_route -- scoring, selection and weighting for every token.
+ * Overview article section 2.2 steps 1-3; MoE-kernels page section 4.3 (gate, top-k).
+ *   logits[t, e] = sum_i x[t, i] * w_router[e, i] (+ logit_bias[e]), accumulated in float32.
+ *   topk_idx[t, 0..k-1] = the k largest logits, ordered by value descending, ties to the lower e.
+ *   topk_w[t, j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected (sums to 1).
+ * x [T, d] (dtype); w_router [E, d] (dtype); logit_bias [E] float32 or NULL (added before both
+ * selection and softmax); logits_out [T, E] float32 or NULL (post-bias logits);
+ * topk_idx [T, k] int32 and topk_w [T, k] float32 are required outputs.
+ */
+moe_status moe_route(const moe_shape* s, const void* x, const void* w_router, const float* logit_bias,
+                     float* logits_out, int32_t* topk_idx, float* topk_w, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * moe_permute -- dispatch bookkeeping (MoE-kernels page section 4.3; data-movement page section 4).
+ *   expert_counts[e]  = number of (t, j) with topk_idx[t, j] == e          int32 [E]
+ *   expert_offsets    = exclusive running sum, offsets[0] = 0, offsets[E] = T*k   int32 [E+1]
+ *   perm_src[r]       = flat slot t*k + j of dispatched row r; the rows of expert e are
+ *                       [offsets[e], offsets[e+1]) in increasing t                int32 [T*k]
+ *   inv_perm[t*k + j] = r, the inverse permutation                               int32 [T*k]
+ * topk_idx [T, k] int32 with every entry in [0, E) (entries outside give unspecified results but
+ * never out-of-bounds accesses). expert_counts may be NULL.
+ */
+moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* perm_src, int32_t* inv_perm, void* workspace,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn -- every expert over its own contiguous bucket of rows, in one pass
+ * (MoE-kernels page sections 1.2 and 4.2):
+ *   for each e and each row r in [expert_offsets[e], expert_offsets[e+1]):
+ *     src = perm_src ? perm_src[r] / k : r
+ *     h = SiLU(w_gate[e] . x[src]) * (w_up[e] . x[src]),  SiLU(z) = z * sigmoid(z)
+ *     y[r] = w_down[e] . h
+ * With perm_src == NULL, x is read as [T*k, d] rows in bucket order (for the shared expert pass
+ * {E=1, k=1, H=Hs} with offsets {0, T}). Rows = T*k; offsets must be non-decreasing with
+ * offsets[E] == T*k. y [T*k, d] (dtype). Accumulation in float32; for bfloat16 the hidden
+ * activation h is rounded to bfloat16 before the down projection and y is rounded once.
+ */
+moe_status moe_grouped_ffn(const moe_shape* s, const void* x, const int32_t* perm_src,
+                           const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                           const void* w_down, void* y, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine -- back to token order and weighted merge (overview article section 2.2 step 4;
+ * MoE-kernels page section 1.1: the shared expert's output is added for every token):
+ *   out[t] = shared_out[t] + sum_{j<k} topk_w[t, j] * y_perm[inv_perm[t*k + j]]
+ * y_perm [T*k, d], shared_out [T, d] or NULL, out [T, d] (all dtype). float32 accumulation in
+ * fixed j order, one rounding to dtype.
+ */
+moe_status moe_combine(const moe_shape* s, const void* y_perm, const int32_t* inv_perm, const float* topk_w,
+                       const void* shared_out, void* out, void* stream);
+
+/*
+ * moe_layer_forward -- the whole layer: moe_route, moe_permute, the grouped FFN of the routed
+ * experts together with the shared expert (w_shared_* may be NULL when d_shared_hidden == 0),
+ * and moe_combine. out [T, d] is required. topk_idx_out [T, k], topk_w_out [T, k],
+ * counts_out [E] and logits_out [T, E] are optional copies of the intermediates (NULL = keep
+ * them in the workspace).
+ */
+moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* w_router, const float* logit_bias,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const void* w_shared_gate, const void* w_shared_up, const void* w_shared_down,
+                             void* out, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                             float* logits_out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel stages of moe_layer_forward, for per-kernel timing. moe_layer_forward_timed() is
+ * moe_layer_forward with hipEvent_t `events[2*i]` recorded on `stream` just before stage i's
+ * kernel launch and `events[2*i+1]` just after it (NULL entries are skipped; a stage that
+ * launches nothing records both events back to back). `events` may be NULL.
+ */
+enum {
+  MOE_STAGE_ROUTE_LOGITS = 0,
+  MOE_STAGE_ROUTE_TOPK = 1,
+  MOE_STAGE_PERMUTE_COUNT = 2,
+  MOE_STAGE_PERMUTE_SCAN = 3,
+  MOE_STAGE_PERMUTE_SCATTER = 4,
+  MOE_STAGE_FFN_GATE_UP = 5,
+  MOE_STAGE_FFN_DOWN = 6,
+  MOE_STAGE_COMBINE = 7,
+  MOE_NUM_STAGES = 8
+};
+
+moe_status moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_router,
+                                   const float* logit_bias, const void* w_gate, const void* w_up,
+                                   const void* w_down, const void* w_shared_gate, const void* w_shared_up,
+                                   const void* w_shared_down, void* out, int32_t* topk_idx_out,
+                                   float* topk_w_out, int32_t* counts_out, float* logits_out, void* workspace,
+                                   size_t ws_bytes, void* stream, void* const* events);
+
+/* Name of the kernel (as a profiler lists it) that stage `stage` launches for shape `s`, or ""
+ * if it launches none. */
+const char* moe_stage_kernel_name(const moe_shape* s, int stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

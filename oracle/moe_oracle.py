@@ -226,22 +226,18 @@ def layer_forward(x, w_router, k, expert_fn, shared_fn=None, logit_bias=None):
 
 
 def layer_forward_tokens(x_rows, w_router, k, expert_fn, shared_fn=None, logit_bias=None):
-    """Output rows for a sample of tokens, one token at a time (each token's result depends only on
-    its own row: routing is per token and the experts are applied row by row)."""
+    """Output rows for a sample of tokens. Each token's result depends only on its own row (routing
+    is per token and the experts act row by row), so a sample of rows can be checked on its own at
+    any batch size. Experts are visited once each, in increasing id, and their weighted outputs
+    added to the tokens that selected them: the same sum over the k selected experts as
+    ``combine``, in another order of addition."""
     x_rows = np.asarray(x_rows, np.float64)
     L, idx, w = route(x_rows, w_router, k, logit_bias)
     out = np.zeros_like(x_rows)
-    cache = {}
-    for t in range(x_rows.shape[0]):
-        acc = np.zeros(x_rows.shape[1])
-        if shared_fn is not None:
-            if "shared" not in cache:
-                cache["shared"] = shared_fn()
-            acc += swiglu(x_rows[t:t + 1], *cache["shared"])[0]
-        for j in range(k):
-            e = int(idx[t, j])
-            if e not in cache:
-                cache[e] = expert_fn(e)
-            acc += w[t, j] * swiglu(x_rows[t:t + 1], *cache[e])[0]
-        out[t] = acc
+    if shared_fn is not None:
+        out += swiglu(x_rows, *shared_fn())
+    for e in np.unique(idx):
+        t_sel, j_sel = np.nonzero(idx == e)
+        g, u, dn = expert_fn(int(e))
+        out[t_sel] += w[t_sel, j_sel][:, None] * swiglu(x_rows[t_sel], g, u, dn)
     return dict(logits=L, idx=idx, w=w, out=out)

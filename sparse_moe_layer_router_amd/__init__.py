@@ -1,0 +1,163 @@
+"""Python binding of libmoe.so, the MI355X sparse-MoE layer forward (C ABI in include/moe.h).
+
+Argument marshalling only: every function here passes device pointers and sizes to the
+C entry point of the same name, on the current (or given) HIP stream. PyTorch provides device
+memory and streams. There is no fallback: if the HIP library is missing, importing this package
+fails with an error that says how to build it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime first, so libmoe.so binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_moe_layer_router_amd.build` "
+                      "(hipcc, gfx950). There is no CPU fallback.")
+_lib = ctypes.CDLL(LIB_PATH)
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
+MOE_F32, MOE_BF16 = 0, 1
+STAGES = ["route_logits", "route_topk", "permute_count", "permute_scan", "permute_scatter", "ffn_gate_up",
+          "ffn_down", "combine"]
+MOE_NUM_STAGES = len(STAGES)
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("d_hidden", ctypes.c_int32), ("d_shared_hidden", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+def make_shape(T, d_model, n_experts, top_k, d_hidden, d_shared_hidden=0, dtype=MOE_BF16) -> moe_shape:
+    if isinstance(dtype, str):
+        dtype = {"bf16": MOE_BF16, "f32": MOE_F32}[dtype]
+    elif isinstance(dtype, torch.dtype):
+        dtype = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[dtype]
+    return moe_shape(T, d_model, n_experts, top_k, d_hidden, d_shared_hidden, dtype)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {moe_status_string(status)} (status {status})")
+
+
+_P = ctypes.c_void_p
+_S = ctypes.POINTER(moe_shape)
+_sigs = {
+    "moe_workspace_bytes": (ctypes.c_size_t, [_S]),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_route": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_permute": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_grouped_ffn": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_combine": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
+    "moe_layer_forward": (ctypes.c_int, [_S] + [_P] * 15 + [ctypes.c_size_t, _P]),
+    "moe_layer_forward_timed": (ctypes.c_int, [_S] + [_P] * 15 + [ctypes.c_size_t, _P, _P]),
+    "moe_stage_kernel_name": (ctypes.c_char_p, [_S, ctypes.c_int]),
+}
+for _name, (_res, _args) in _sigs.items():
+    _f = getattr(_lib, _name)
+    _f.restype, _f.argtypes = _res, _args
+
+EXPORTED = tuple(_sigs)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    if isinstance(workspace, tuple):
+        return workspace
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _check(fn, st):
+    if st != MOE_OK:
+        raise MoeError(fn, st)
+
+
+def moe_status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+def moe_workspace_bytes(shape: moe_shape) -> int:
+    return int(_lib.moe_workspace_bytes(ctypes.byref(shape)))
+
+
+def allocate_workspace(shape: moe_shape, device="cuda") -> torch.Tensor:
+    return torch.empty(max(moe_workspace_bytes(shape), 1), dtype=torch.uint8, device=device)
+
+
+def moe_route(shape, x, w_router, logit_bias, logits_out, topk_idx, topk_w, workspace=None, stream=None):
+    ws, nb = _ws(workspace)
+    _check("moe_route", _lib.moe_route(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(logit_bias),
+                                       _ptr(logits_out), _ptr(topk_idx), _ptr(topk_w), ws, nb, _stream(stream)))
+
+
+def moe_permute(shape, topk_idx, expert_counts, expert_offsets, perm_src, inv_perm, workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check("moe_permute", _lib.moe_permute(ctypes.byref(shape), _ptr(topk_idx), _ptr(expert_counts),
+                                           _ptr(expert_offsets), _ptr(perm_src), _ptr(inv_perm), ws, nb,
+                                           _stream(stream)))
+
+
+def moe_grouped_ffn(shape, x, perm_src, expert_offsets, w_gate, w_up, w_down, y, workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check("moe_grouped_ffn", _lib.moe_grouped_ffn(ctypes.byref(shape), _ptr(x), _ptr(perm_src),
+                                                   _ptr(expert_offsets), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                                   _ptr(y), ws, nb, _stream(stream)))
+
+
+def moe_combine(shape, y_perm, inv_perm, topk_w, shared_out, out, stream=None):
+    _check("moe_combine", _lib.moe_combine(ctypes.byref(shape), _ptr(y_perm), _ptr(inv_perm), _ptr(topk_w),
+                                           _ptr(shared_out), _ptr(out), _stream(stream)))
+
+
+def _layer_args(shape, x, w_router, logit_bias, w_gate, w_up, w_down, w_shared_gate, w_shared_up,
+                w_shared_down, out, topk_idx_out, topk_w_out, counts_out, logits_out, workspace, stream):
+    ws, nb = _ws(workspace)
+    return [ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w_gate), _ptr(w_up),
+            _ptr(w_down), _ptr(w_shared_gate), _ptr(w_shared_up), _ptr(w_shared_down), _ptr(out),
+            _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(counts_out), _ptr(logits_out), ws, nb, _stream(stream)]
+
+
+def moe_layer_forward(shape, x, w_router, logit_bias, w_gate, w_up, w_down, w_shared_gate, w_shared_up,
+                      w_shared_down, out, topk_idx_out=None, topk_w_out=None, counts_out=None, logits_out=None,
+                      workspace=None, stream=None):
+    _check("moe_layer_forward", _lib.moe_layer_forward(*_layer_args(
+        shape, x, w_router, logit_bias, w_gate, w_up, w_down, w_shared_gate, w_shared_up, w_shared_down, out,
+        topk_idx_out, topk_w_out, counts_out, logits_out, workspace, stream)))
+
+
+def moe_layer_forward_timed(shape, x, w_router, logit_bias, w_gate, w_up, w_down, w_shared_gate, w_shared_up,
+                            w_shared_down, out, topk_idx_out=None, topk_w_out=None, counts_out=None,
+                            logits_out=None, workspace=None, stream=None, events=None):
+    """`events` is a ctypes array of 2 * MOE_NUM_STAGES hipEvent_t handles (or None)."""
+    _check("moe_layer_forward_timed", _lib.moe_layer_forward_timed(*_layer_args(
+        shape, x, w_router, logit_bias, w_gate, w_up, w_down, w_shared_gate, w_shared_up, w_shared_down, out,
+        topk_idx_out, topk_w_out, counts_out, logits_out, workspace, stream), events))
+
+
+def moe_stage_kernel_name(shape, stage: int) -> str:
+    return _lib.moe_stage_kernel_name(ctypes.byref(shape), stage).decode()

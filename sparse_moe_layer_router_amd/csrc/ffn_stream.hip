@@ -1,0 +1,326 @@
+// Grouped SwiGLU experts, weight-streaming form (bf16, MFMA 16x16x32).
+//
+// MoE-kernels page (blog.llmgo.top), section 1.2: with few tokens per expert, every selected
+// expert's W_gate, W_up and W_down must be read in full from HBM for one or two token vectors, so
+// the expert FFN is a GEMV bound by memory bandwidth; section 4.2: one launch covers all experts,
+// the work of each expert found from the offsets array, empty experts skipped.
+//
+// Layout of the work: block (hb, g) owns 64 consecutive output rows of group g's weight matrix
+// (4 waves x 16 rows). A wave streams its 16 weight rows once, front to back, 16 bytes per lane
+// per step (each step is one 16x16x32 MFMA A-fragment: lane l reads row l%16, k-chunk l/16), and
+// applies each fragment to every 16-token tile of the group's rows (the B-fragment, x^T, read
+// from L2). Tokens beyond the group's count are zero-padded columns. Accumulation is fp32 inside
+// the MFMA; gate and up share one B-fragment and their accumulators have identical layouts, so
+// SiLU(g) * u is formed in registers and stored as bf16. The down projection is the same loop
+// with W_down rows against the stored hidden rows.
+#include "kernels.h"
+#include "moe_device.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kRowsPerBlock = 64;   // 4 waves x 16 weight rows
+constexpr int kUnroll = 8;          // k-steps of 32 issued back to back (8 KB per matrix per wave)
+
+struct GroupView {
+  long long r0;        // first row of the group in the (routed or shared) row space
+  int n;               // rows in the group
+  int Hg;              // hidden size of the group's expert
+  const uint16_t* wg;  // [Hg, d]
+  const uint16_t* wu;  // [Hg, d]
+  const uint16_t* wd;  // [d, Hg]
+  uint16_t* hid;       // hidden rows of this row space, row stride Hg
+  uint16_t* y;         // output rows of this row space, row stride d
+  bool routed;
+};
+
+__device__ __forceinline__ GroupView group_view(const FfnGroups& p, int g) {
+  GroupView v;
+  if (g < p.E) {
+    // clamp to [0, rows] so inconsistent offsets can never address outside the row buffers
+    long long a = p.offsets[g], b = p.offsets[g + 1];
+    a = a < 0 ? 0 : (a > p.rows ? p.rows : a);
+    b = b < a ? a : (b > p.rows ? p.rows : b);
+    v.r0 = a;
+    v.n = (int)(b - a);
+    v.Hg = p.H;
+    const size_t wsz = (size_t)p.H * p.d;
+    v.wg = (const uint16_t*)p.w_gate + (size_t)g * wsz;
+    v.wu = (const uint16_t*)p.w_up + (size_t)g * wsz;
+    v.wd = (const uint16_t*)p.w_down + (size_t)g * wsz;
+    v.hid = (uint16_t*)p.hid;
+    v.y = (uint16_t*)p.y;
+    v.routed = true;
+  } else {
+    v.r0 = 0;
+    v.n = p.T;
+    v.Hg = p.Hs;
+    v.wg = (const uint16_t*)p.ws_gate;
+    v.wu = (const uint16_t*)p.ws_up;
+    v.wd = (const uint16_t*)p.ws_down;
+    v.hid = (uint16_t*)p.hid + (size_t)p.rows * p.H;
+    v.y = (uint16_t*)p.y + (size_t)p.rows * p.d;
+    v.routed = false;
+  }
+  return v;
+}
+
+// source token (x row) of row r of a group
+__device__ __forceinline__ long long source_row(const FfnGroups& p, const GroupView& v, long long r) {
+  if (!v.routed) return r;
+  long long s = p.perm_src ? (long long)(p.perm_src[r] / p.k) : r;
+  long long lim = p.perm_src ? (long long)p.T : p.rows;
+  return s < 0 ? 0 : (s >= lim ? lim - 1 : s);  // never read outside x, whatever the indices hold
+}
+
+}  // namespace
+
+template <int NTT>
+__global__ void __launch_bounds__(256)
+ffn_gate_up_stream(const FfnGroups p) {
+  const GroupView v = group_view(p, blockIdx.y);
+  if (v.n <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int h0 = blockIdx.x * kRowsPerBlock + wave * 16;
+  if (h0 >= v.Hg) return;
+  const int d = p.d;
+  const int ar = lane & 15, kq = lane >> 4;
+  const int hrow = (h0 + ar < v.Hg) ? h0 + ar : v.Hg - 1;  // rows past Hg are computed and dropped
+  const uint16_t* ag = v.wg + (size_t)hrow * d + kq * 8;
+  const uint16_t* au = v.wu + (size_t)hrow * d + kq * 8;
+  const uint16_t* xb = (const uint16_t*)p.x;
+
+  for (int tt = 0; tt < v.n; tt += 16 * NTT) {
+    const uint16_t* bx[NTT];
+    bool bok[NTT];
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) {
+      const int rr = tt + j * 16 + ar;
+      bok[j] = rr < v.n;
+      const long long src = bok[j] ? source_row(p, v, v.r0 + rr) : 0;
+      bx[j] = xb + (size_t)src * d + kq * 8;
+    }
+    f32x4_t accg[NTT], accu[NTT];
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) { accg[j] = f32x4_t{0, 0, 0, 0}; accu[j] = f32x4_t{0, 0, 0, 0}; }
+    const u32x4_t zero = {0, 0, 0, 0};
+    int k0 = 0;
+    for (; k0 + 32 * kUnroll <= d; k0 += 32 * kUnroll) {
+      u32x4_t a_g[kUnroll], a_u[kUnroll], b[kUnroll][NTT];
+#pragma unroll
+      for (int s = 0; s < kUnroll; ++s) {
+        a_g[s] = ld16_stream(ag + k0 + 32 * s);
+        a_u[s] = ld16_stream(au + k0 + 32 * s);
+      }
+#pragma unroll
+      for (int s = 0; s < kUnroll; ++s)
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bx[j] + k0 + 32 * s) : zero;
+#pragma unroll
+      for (int s = 0; s < kUnroll; ++s)
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) {
+          accg[j] = mfma16x16x32(a_g[s], b[s][j], accg[j]);
+          accu[j] = mfma16x16x32(a_u[s], b[s][j], accu[j]);
+        }
+    }
+    for (; k0 < d; k0 += 32) {  // tail: d is a multiple of 8, so a lane's 8-chunk is all in or all out
+      const bool kok = k0 + kq * 8 < d;
+      const u32x4_t a_g = kok ? ld16_stream(ag + k0) : zero;
+      const u32x4_t a_u = kok ? ld16_stream(au + k0) : zero;
+#pragma unroll
+      for (int j = 0; j < NTT; ++j) {
+        const u32x4_t b = (kok && bok[j]) ? ld16(bx[j] + k0) : zero;
+        accg[j] = mfma16x16x32(a_g, b, accg[j]);
+        accu[j] = mfma16x16x32(a_u, b, accu[j]);
+      }
+    }
+    // lane holds rows h0 + kq*4 + {0..3} of token column (lane & 15)
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) {
+      const int rr = tt + j * 16 + ar;
+      const int h = h0 + kq * 4;
+      if (rr < v.n && h < v.Hg) {
+        uint32_t lo = pack_bf16x2(silu(accg[j][0]) * accu[j][0], silu(accg[j][1]) * accu[j][1]);
+        uint32_t hi = pack_bf16x2(silu(accg[j][2]) * accu[j][2], silu(accg[j][3]) * accu[j][3]);
+        *(u32x2_t*)(v.hid + (size_t)(v.r0 + rr) * v.Hg + h) = u32x2_t{lo, hi};
+      }
+    }
+  }
+}
+
+template <int NTT>
+__global__ void __launch_bounds__(256)
+ffn_down_stream(const FfnGroups p) {
+  const GroupView v = group_view(p, blockIdx.y);
+  if (v.n <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int d = p.d;
+  const int i0 = blockIdx.x * kRowsPerBlock + wave * 16;
+  if (i0 >= d) return;
+  const int K = v.Hg;
+  const int ar = lane & 15, kq = lane >> 4;
+  const int irow = (i0 + ar < d) ? i0 + ar : d - 1;
+  const uint16_t* aw = v.wd + (size_t)irow * K + kq * 8;
+
+  for (int tt = 0; tt < v.n; tt += 16 * NTT) {
+    const uint16_t* bh[NTT];
+    bool bok[NTT];
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) {
+      const int rr = tt + j * 16 + ar;
+      bok[j] = rr < v.n;
+      bh[j] = v.hid + (size_t)(v.r0 + (bok[j] ? rr : 0)) * K + kq * 8;
+    }
+    f32x4_t acc[NTT];
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) acc[j] = f32x4_t{0, 0, 0, 0};
+    const u32x4_t zero = {0, 0, 0, 0};
+    int k0 = 0;
+    for (; k0 + 32 * kUnroll <= K; k0 += 32 * kUnroll) {
+      u32x4_t a[kUnroll], b[kUnroll][NTT];
+#pragma unroll
+      for (int s = 0; s < kUnroll; ++s) a[s] = ld16_stream(aw + k0 + 32 * s);
+#pragma unroll
+      for (int s = 0; s < kUnroll; ++s)
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bh[j] + k0 + 32 * s) : zero;
+#pragma unroll
+      for (int s = 0; s < kUnroll; ++s)
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) acc[j] = mfma16x16x32(a[s], b[s][j], acc[j]);
+    }
+    for (; k0 < K; k0 += 32) {
+      const bool kok = k0 + kq * 8 < K;
+      const u32x4_t a = kok ? ld16_stream(aw + k0) : zero;
+#pragma unroll
+      for (int j = 0; j < NTT; ++j) {
+        const u32x4_t b = (kok && bok[j]) ? ld16(bh[j] + k0) : zero;
+        acc[j] = mfma16x16x32(a, b, acc[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) {
+      const int rr = tt + j * 16 + ar;
+      const int i = i0 + kq * 4;
+      if (rr < v.n && i < d) {
+        uint32_t lo = pack_bf16x2(acc[j][0], acc[j][1]);
+        uint32_t hi = pack_bf16x2(acc[j][2], acc[j][3]);
+        *(u32x2_t*)(v.y + (size_t)(v.r0 + rr) * d + i) = u32x2_t{lo, hi};
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ fp32 (VALU)
+// Plain per-element form for float32 layers: one thread per (row, output column).
+
+__device__ __forceinline__ int find_group(const int32_t* offsets, int E, long long r) {
+  int lo = 0, hi = E;  // last g with offsets[g] <= r
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= r) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(256)
+ffn_gate_up_f32(const FfnGroups p) {
+  const long long r = blockIdx.x;  // row in routed space [0, rows), then shared [rows, rows+T)
+  const bool shared = r >= p.rows;
+  const int Hg = shared ? p.Hs : p.H;
+  const int h = blockIdx.y * 256 + threadIdx.x;
+  if (h >= Hg) return;
+  const int d = p.d;
+  const float *wg, *wu, *xr;
+  float* hid;
+  if (shared) {
+    const long long t = r - p.rows;
+    wg = (const float*)p.ws_gate; wu = (const float*)p.ws_up;
+    xr = (const float*)p.x + (size_t)t * d;
+    hid = (float*)p.hid + (size_t)p.rows * p.H + (size_t)t * Hg;
+  } else {
+    if (r >= p.offsets[p.E]) return;
+    const int g = find_group(p.offsets, p.E, r);  // any g in [0, E) keeps the weight reads in bounds
+    wg = (const float*)p.w_gate + (size_t)g * p.H * d;
+    wu = (const float*)p.w_up + (size_t)g * p.H * d;
+    long long s = p.perm_src ? (long long)(p.perm_src[r] / p.k) : r;
+    const long long lim = p.perm_src ? (long long)p.T : p.rows;
+    s = s < 0 ? 0 : (s >= lim ? lim - 1 : s);
+    xr = (const float*)p.x + (size_t)s * d;
+    hid = (float*)p.hid + (size_t)r * Hg;
+  }
+  const float* gr = wg + (size_t)h * d;
+  const float* ur = wu + (size_t)h * d;
+  float gs = 0.f, us = 0.f;
+  for (int i = 0; i < d; ++i) { gs += xr[i] * gr[i]; us += xr[i] * ur[i]; }
+  hid[h] = silu(gs) * us;
+}
+
+__global__ void __launch_bounds__(256)
+ffn_down_f32(const FfnGroups p) {
+  const long long r = blockIdx.x;
+  const bool shared = r >= p.rows;
+  const int d = p.d;
+  const int i = blockIdx.y * 256 + threadIdx.x;
+  if (i >= d) return;
+  const int Hg = shared ? p.Hs : p.H;
+  const float *wd, *hr;
+  float* yr;
+  if (shared) {
+    const long long t = r - p.rows;
+    wd = (const float*)p.ws_down;
+    hr = (const float*)p.hid + (size_t)p.rows * p.H + (size_t)t * Hg;
+    yr = (float*)p.y + (size_t)p.rows * d + (size_t)t * d;
+  } else {
+    if (r >= p.offsets[p.E]) return;
+    const int g = find_group(p.offsets, p.E, r);
+    wd = (const float*)p.w_down + (size_t)g * p.H * d;
+    hr = (const float*)p.hid + (size_t)r * Hg;
+    yr = (float*)p.y + (size_t)r * d;
+  }
+  const float* w = wd + (size_t)i * Hg;
+  float s = 0.f;
+  for (int h = 0; h < Hg; ++h) s += hr[h] * w[h];
+  yr[i] = s;
+}
+
+// --------------------------------------------------------------------------------- launchers
+namespace {
+int groups_of(const FfnGroups& g) { return g.E + (g.Hs > 0 ? 1 : 0); }
+int hmax(const FfnGroups& g) { return g.H > g.Hs ? g.H : g.Hs; }
+}  // namespace
+
+hipError_t launch_ffn_gate_up(const FfnGroups& g, hipStream_t stream) {
+  if (g.dtype == kF32) {
+    long long nrows = g.rows + (g.Hs > 0 ? g.T : 0);
+    dim3 grid((unsigned)nrows, (hmax(g) + 255) / 256);
+    hipLaunchKernelGGL(ffn_gate_up_f32, grid, dim3(256), 0, stream, g);
+  } else {
+    dim3 grid((hmax(g) + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
+    hipLaunchKernelGGL(ffn_gate_up_stream<1>, grid, dim3(256), 0, stream, g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_down(const FfnGroups& g, hipStream_t stream) {
+  if (g.dtype == kF32) {
+    long long nrows = g.rows + (g.Hs > 0 ? g.T : 0);
+    dim3 grid((unsigned)nrows, (g.d + 255) / 256);
+    hipLaunchKernelGGL(ffn_down_f32, grid, dim3(256), 0, stream, g);
+  } else {
+    dim3 grid((g.d + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
+    hipLaunchKernelGGL(ffn_down_stream<1>, grid, dim3(256), 0, stream, g);
+  }
+  return hipGetLastError();
+}
+
+const char* ffn_gate_up_kernel_name(const FfnGroups& g) {
+  return g.dtype == kF32 ? "ffn_gate_up_f32" : "ffn_gate_up_stream<1>";
+}
+const char* ffn_down_kernel_name(const FfnGroups& g) {
+  return g.dtype == kF32 ? "ffn_down_f32" : "ffn_down_stream<1>";
+}
+
+}  // namespace moe

@@ -1,0 +1,72 @@
+// Host-side launchers of the MoE kernels. Every launcher enqueues on `stream` and returns the
+// launch status; shapes were validated by the caller (moe_abi.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+// ---- routing -------------------------------------------------------------------------------
+hipError_t launch_route_logits(int dtype, const void* x, const void* w_router, const float* bias,
+                               float* logits, int T, int E, int d, hipStream_t stream);
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
+                             hipStream_t stream);
+const char* route_logits_kernel_name(int dtype, int T, int E);
+const char* route_topk_kernel_name();
+
+// ---- permutation ---------------------------------------------------------------------------
+// Rows are cut into tiles of `tile` flat slots; `tile_counts` holds [n_tiles, E] int32.
+int permute_tile_size(long long rows);
+size_t permute_scratch_bytes(long long rows, int E);
+hipError_t launch_permute_count(const int32_t* topk_idx, long long rows, int E, int tile, int32_t* tile_counts,
+                                hipStream_t stream);
+hipError_t launch_permute_scan(int32_t* tile_counts, long long rows, int E, int tile, int32_t* counts,
+                               int32_t* offsets, hipStream_t stream);
+hipError_t launch_permute_scatter(const int32_t* topk_idx, long long rows, int E, int tile,
+                                  const int32_t* tile_counts, int32_t* perm_src, int32_t* inv_perm,
+                                  hipStream_t stream);
+
+// ---- grouped SwiGLU experts ------------------------------------------------------------------
+// A set of expert groups: routed groups 0..E-1 take rows [offsets[g], offsets[g+1]) of the
+// dispatched order (source token perm_src[r] / k, or r when perm_src is NULL); the optional
+// shared group (index E) takes rows [shared_row0, shared_row0 + T) with source token r - row0.
+struct FfnGroups {
+  int dtype;
+  int d;                       // model width
+  int E;                       // routed groups
+  int k;                       // slots per token (perm_src divisor)
+  int H;                       // routed hidden size
+  long long rows;              // routed rows (T*k)
+  const int32_t* offsets;      // [E+1]
+  const int32_t* perm_src;     // [rows] or NULL
+  const void* x;               // [T, d] (or [rows, d] when perm_src is NULL)
+  const void* w_gate;          // [E, H, d]
+  const void* w_up;            // [E, H, d]
+  const void* w_down;          // [E, d, H]
+  // shared expert (Hs == 0: none)
+  int Hs;
+  int T;
+  const void* ws_gate;         // [Hs, d]
+  const void* ws_up;           // [Hs, d]
+  const void* ws_down;         // [d, Hs]
+  // outputs
+  void* hid;                   // routed hidden [rows, H], then shared hidden [T, Hs] (dtype)
+  void* y;                     // routed outputs [rows, d], then shared outputs [T, d] (dtype)
+  float mean_rows_per_group;   // host-side regime hint (T*k / E)
+};
+
+hipError_t launch_ffn_gate_up(const FfnGroups& g, hipStream_t stream);
+hipError_t launch_ffn_down(const FfnGroups& g, hipStream_t stream);
+const char* ffn_gate_up_kernel_name(const FfnGroups& g);
+const char* ffn_down_kernel_name(const FfnGroups& g);
+
+// ---- combine ---------------------------------------------------------------------------------
+hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_perm, const float* topk_w,
+                          const void* shared_out, void* out, int T, int k, int d, hipStream_t stream);
+const char* combine_kernel_name(int dtype);
+
+}  // namespace moe

@@ -20,9 +20,14 @@ def _ensure_built():
         from synth import build as b
         b.build()
     lib = os.path.join(ROOT, "sparse_moe_layer_router_amd", "libmoe.so")
-    if not os.path.exists(lib) and os.path.exists(os.path.join(ROOT, "sparse_moe_layer_router_amd", "build.py")):
-        from sparse_moe_layer_router_amd import build as mb
-        mb.build()
+    if not os.path.exists(lib):
+        # load the build script by path: importing the package itself requires the library
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_moe_build", os.path.join(ROOT, "sparse_moe_layer_router_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
 
 
 _ensure_built()

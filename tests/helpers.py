@@ -29,18 +29,25 @@ def screen_gaps(inp: synth.HostInputs, min_gap: float = MIN_GAP, max_rounds: int
     raise RuntimeError("gap screening did not converge")
 
 
-def expert_fn_host(cfg: synth.LayerConfig, seed: int, stacked=None):
-    """float64 expert weights for the oracle, regenerated on the host (cached)."""
-    cache = {}
+def expert_fn_host(cfg: synth.LayerConfig, seed: int, stacked=None, cache: bool = True):
+    """float64 expert weights for the oracle, regenerated on the host from the generator streams.
+
+    ``cache=False`` regenerates on every call (large layers: one expert in memory at a time)."""
+    store = {}
+
+    def make(e):
+        if stacked is not None:
+            g, u, dn = (s[e] for s in stacked)
+        else:
+            g, u, dn = synth.expert_weights_host(cfg, seed, e)
+        return tuple(oracle.widen(a, cfg.dtype) for a in (g, u, dn))
 
     def fn(e):
-        if e not in cache:
-            if stacked is not None:
-                g, u, dn = (s[e] for s in stacked)
-            else:
-                g, u, dn = synth.expert_weights_host(cfg, seed, e)
-            cache[e] = tuple(oracle.widen(a, cfg.dtype) for a in (g, u, dn))
-        return cache[e]
+        if not cache:
+            return make(e)
+        if e not in store:
+            store[e] = make(e)
+        return store[e]
 
     return fn
 
