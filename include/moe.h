@@ -150,10 +150,11 @@ enum {
   MOE_STAGE_PERMUTE_COUNT = 2,
   MOE_STAGE_PERMUTE_SCAN = 3,
   MOE_STAGE_PERMUTE_SCATTER = 4,
-  MOE_STAGE_FFN_GATE_UP = 5,
-  MOE_STAGE_FFN_DOWN = 6,
-  MOE_STAGE_COMBINE = 7,
-  MOE_NUM_STAGES = 8
+  MOE_STAGE_FFN_SCHEDULE = 5, /* tile schedule of the grouped GEMM (launches nothing on the GEMV path) */
+  MOE_STAGE_FFN_GATE_UP = 6,
+  MOE_STAGE_FFN_DOWN = 7,
+  MOE_STAGE_COMBINE = 8,
+  MOE_NUM_STAGES = 9
 };
 
 moe_status moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_router,

@@ -23,8 +23,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
 MOE_F32, MOE_BF16 = 0, 1
-STAGES = ["route_logits", "route_topk", "permute_count", "permute_scan", "permute_scatter", "ffn_gate_up",
-          "ffn_down", "combine"]
+STAGES = ["route_logits", "route_topk", "permute_count", "permute_scan", "permute_scatter", "ffn_schedule",
+          "ffn_gate_up", "ffn_down", "combine"]
 MOE_NUM_STAGES = len(STAGES)
 
 

@@ -1,0 +1,365 @@
+// Grouped GEMM on MFMA (bf16 in, fp32 accumulate) for expert buckets with many rows (prefill),
+// and the dense router GEMM for large batches.
+//
+// MoE-kernels page (blog.llmgo.top), section 1.2: with hundreds of tokens per expert the expert
+// FFN is a large, compute-bound GEMM; section 4.2: one launch computes many GEMMs that share K and
+// N but have their own M, each block taking its tile from the running offsets of the experts, so
+// no expert waits on a separate launch; data-movement page, section 15: once routes are sorted by
+// expert, each expert's weights are loaded once and reused across its whole bucket of tokens.
+//
+// Tiles: BM = 128 rows (tokens) x BN weight rows x BK = 64 along K, 256 threads as 2 x 2 waves,
+// each wave a 64 x (BN/2) block built from 32x32x16 MFMAs. Gate and up projections are computed
+// by the same block for the same rows (two B tiles), so SiLU(g) * u is formed in registers and the
+// hidden activation leaves as bf16. Operands are staged through a double-buffered LDS ring with a
+// 16-byte-chunk XOR swizzle (chunk ^ (row & 7)) so MFMA fragment reads are bank-conflict free;
+// the next K slice is fetched into registers while the current one is multiplied.
+//
+// Tile order: tiles are numbered expert by expert, N-tile by N-tile, with the M-tiles of one
+// (expert, N-tile) adjacent. Workgroups are dealt round-robin to the 8 XCDs, so block L runs tile
+// (L % 8) * per_xcd + L / 8: adjacent tiles run at the same time on the same XCD and the second
+// and third M-tiles of a weight tile find it in that XCD's L2 instead of HBM.
+#include "kernels.h"
+#include "moe_device.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int BM = 128;
+constexpr int BK = 64;
+constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+
+enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2 };
+
+template <int MODE> struct Geo {
+  static constexpr int NB = MODE == kGateUp ? 2 : 1;        // B matrices per tile
+  static constexpr int BN = MODE == kGateUp ? 128 : 256;    // rows of each B tile
+  static constexpr int WN = BN / 2;                         // per-wave columns
+  static constexpr int NBLK = WN / 32;                      // 32-wide MFMA blocks per wave
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = NB * BN * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = BM * BK / 8 / kThreads;       // 16-byte chunks per thread
+  static constexpr int B_LOADS = NB * BN * BK / 8 / kThreads;
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * (BK * 2) + ((chunk ^ (row & 7)) << 4); }
+
+}  // namespace
+
+// ------------------------------------------------------------------------------- schedule
+// One block: for every group, m-tiles = ceil(rows / BM); tiles = m-tiles * n-tiles of that group.
+// Writes exclusive prefix sums for the gate/up pass (sched_gu) and the down pass (sched_dn),
+// 1024 groups per round with the running total carried between rounds.
+__global__ void __launch_bounds__(1024)
+gemm_schedule_kernel(const FfnGroups p, int32_t* __restrict__ sched_gu, int32_t* __restrict__ sched_dn) {
+  __shared__ int32_t wtot_gu[16], wtot_dn[16];
+  const int ngroups = p.E + (p.Hs > 0 ? 1 : 0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t carry_a = 0, carry_b = 0;
+  for (int base = 0; base < ngroups; base += 1024) {
+    const int g = base + (int)threadIdx.x;
+    int32_t a = 0, b = 0;
+    if (g < ngroups) {
+      long long n;
+      int Hg;
+      if (g < p.E) {
+        long long lo = p.offsets[g], hi = p.offsets[g + 1];
+        lo = lo < 0 ? 0 : (lo > p.rows ? p.rows : lo);
+        hi = hi < lo ? lo : (hi > p.rows ? p.rows : hi);
+        n = hi - lo;
+        Hg = p.H;
+      } else {
+        n = p.T;
+        Hg = p.Hs;
+      }
+      const int mt = (int)((n + BM - 1) / BM);
+      a = mt * ((Hg + Geo<kGateUp>::BN - 1) / Geo<kGateUp>::BN);
+      b = mt * ((p.d + Geo<kDown>::BN - 1) / Geo<kDown>::BN);
+    }
+    int32_t ia = a, ib = b;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t oa = __shfl_up(ia, off, 64), ob = __shfl_up(ib, off, 64);
+      if (lane >= off) { ia += oa; ib += ob; }
+    }
+    if (lane == 63) { wtot_gu[wave] = ia; wtot_dn[wave] = ib; }
+    __syncthreads();
+    int32_t ba = carry_a, bb = carry_b;
+    for (int w = 0; w < wave; ++w) { ba += wtot_gu[w]; bb += wtot_dn[w]; }
+    if (g < ngroups) {
+      sched_gu[g] = ba + ia - a;
+      sched_dn[g] = bb + ib - b;
+      if (g == ngroups - 1) { sched_gu[ngroups] = ba + ia; sched_dn[ngroups] = bb + ib; }
+    }
+    for (int w = 0; w < 16; ++w) { carry_a += wtot_gu[w]; carry_b += wtot_dn[w]; }
+    __syncthreads();  // wtot_* are rewritten in the next round
+  }
+}
+
+// ------------------------------------------------------------------------------- the GEMM
+struct GemmArgs {
+  FfnGroups p;
+  const int32_t* sched;   // [ngroups + 1] (kGateUp / kDown); unused for the router
+  // router mode
+  const void* x;          // [T, d]
+  const void* w;          // [E, d]
+  const float* bias;      // [E] or NULL
+  float* logits;          // [T, E]
+  int T, E, d;
+};
+
+template <int MODE>
+__global__ void __launch_bounds__(kThreads, 1)
+grouped_gemm_kernel(const GemmArgs ga) {
+  using G = Geo<MODE>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][G::STAGE];
+
+  const FfnGroups& p = ga.p;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- which tile --------------------------------------------------------------------------
+  int g = 0, mt = 0, nt = 0;
+  long long r0 = 0;      // first row of the group in its row space
+  int nrows = 0;         // rows in the group
+  int N = 0, K = 0;      // output columns (weight rows) and reduction length of this group
+  const uint16_t* Bp[2] = {nullptr, nullptr};
+  {
+    const int L = blockIdx.x;
+    int t;
+    if (MODE == kRouter) {
+      const int ntn = (ga.E + G::BN - 1) / G::BN;
+      const int total = ((ga.T + BM - 1) / BM) * ntn;
+      const int per = (total + kXcds - 1) / kXcds;
+      if (L / kXcds >= per) return;
+      t = (L % kXcds) * per + L / kXcds;
+      if (t >= total) return;
+      nt = t / ((ga.T + BM - 1) / BM);
+      mt = t % ((ga.T + BM - 1) / BM);
+      nrows = ga.T;
+      N = ga.E;
+      K = ga.d;
+      Bp[0] = (const uint16_t*)ga.w;
+    } else {
+      const int ngroups = p.E + (p.Hs > 0 ? 1 : 0);
+      const int total = ga.sched[ngroups];
+      const int per = (total + kXcds - 1) / kXcds;
+      if (L / kXcds >= per) return;
+      t = (L % kXcds) * per + L / kXcds;
+      if (t >= total) return;
+      int lo = 0, hi = ngroups;  // last group with sched[g] <= t
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (ga.sched[mid] <= t) lo = mid; else hi = mid;
+      }
+      g = lo;
+      int Hg;
+      if (g < p.E) {
+        long long a = p.offsets[g], b = p.offsets[g + 1];
+        a = a < 0 ? 0 : (a > p.rows ? p.rows : a);
+        b = b < a ? a : (b > p.rows ? p.rows : b);
+        r0 = a;
+        nrows = (int)(b - a);
+        Hg = p.H;
+      } else {
+        r0 = 0;
+        nrows = p.T;
+        Hg = p.Hs;
+      }
+      const int mtiles = (nrows + BM - 1) / BM;
+      const int local = t - ga.sched[g];
+      nt = local / mtiles;
+      mt = local % mtiles;
+      const size_t wsz = (size_t)p.H * p.d;
+      if (MODE == kGateUp) {
+        N = Hg;
+        K = p.d;
+        Bp[0] = g < p.E ? (const uint16_t*)p.w_gate + (size_t)g * wsz : (const uint16_t*)p.ws_gate;
+        Bp[1] = g < p.E ? (const uint16_t*)p.w_up + (size_t)g * wsz : (const uint16_t*)p.ws_up;
+      } else {
+        N = p.d;
+        K = Hg;
+        Bp[0] = g < p.E ? (const uint16_t*)p.w_down + (size_t)g * wsz : (const uint16_t*)p.ws_down;
+      }
+    }
+  }
+  const int m0 = mt * BM, n0 = nt * G::BN;
+
+  // ---- per-thread global source pointers (row pointers, chunk offset added per K slice) ------
+  const int lc = tid & 7;            // 16-byte chunk within a 64-wide K slice
+  const uint16_t* a_src[G::A_LOADS];
+  const uint16_t* b_src[G::B_LOADS];
+#pragma unroll
+  for (int i = 0; i < G::A_LOADS; ++i) {
+    const int row = (tid >> 3) + 32 * i;
+    int rr = m0 + row;
+    rr = rr < nrows ? rr : (nrows > 0 ? nrows - 1 : 0);  // rows past the bucket: any valid row, never stored
+    long long src;
+    if (MODE == kRouter) {
+      src = rr;
+      a_src[i] = (const uint16_t*)ga.x + (size_t)src * K;
+    } else if (MODE == kGateUp) {
+      if (g < p.E) {
+        src = p.perm_src ? (long long)(p.perm_src[r0 + rr] / p.k) : r0 + rr;
+        const long long lim = p.perm_src ? (long long)p.T : p.rows;
+        src = src < 0 ? 0 : (src >= lim ? lim - 1 : src);
+      } else {
+        src = rr;
+      }
+      a_src[i] = (const uint16_t*)p.x + (size_t)src * K;
+    } else {
+      const uint16_t* hid = (const uint16_t*)p.hid + (g < p.E ? 0 : (size_t)p.rows * p.H);
+      a_src[i] = hid + (size_t)(r0 + rr) * K;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < G::B_LOADS; ++i) {
+    const int row = (tid >> 3) + 32 * i;       // stacked rows of the NB B tiles
+    const int b = row / G::BN;
+    int n = n0 + (row % G::BN);
+    n = n < N ? n : N - 1;                     // rows past N: any valid row, never stored
+    b_src[i] = Bp[b] + (size_t)n * K;
+  }
+
+  const u32x4_t zero = {0, 0, 0, 0};
+  u32x4_t ra[G::A_LOADS], rb[G::B_LOADS];
+  auto gload = [&](int k0) {
+    const int k = k0 + lc * 8;
+    const bool ok = k < K;                     // K is a multiple of 8: a chunk is all in or all out
+#pragma unroll
+    for (int i = 0; i < G::A_LOADS; ++i) ra[i] = ok ? ld16(a_src[i] + k) : zero;
+#pragma unroll
+    for (int i = 0; i < G::B_LOADS; ++i) rb[i] = ok ? ld16(b_src[i] + k) : zero;
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* sa = smem[buf];
+    uint8_t* sb = smem[buf] + G::A_BYTES;
+#pragma unroll
+    for (int i = 0; i < G::A_LOADS; ++i) *(u32x4_t*)(sa + swz((tid >> 3) + 32 * i, lc)) = ra[i];
+#pragma unroll
+    for (int i = 0; i < G::B_LOADS; ++i) *(u32x4_t*)(sb + swz((tid >> 3) + 32 * i, lc)) = rb[i];
+  };
+
+  f32x16_t acc[G::NB][2][G::NBLK];
+#pragma unroll
+  for (int b = 0; b < G::NB; ++b)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < G::NBLK; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[b][mb][nb][e] = 0.f;
+
+  const int nk = (K + BK - 1) / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int fr = lane & 31, fh = lane >> 5;   // fragment row / k-half of this lane
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+    const uint8_t* sa = smem[cur];
+    const uint8_t* sb = smem[cur] + G::A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int ch = kk * 2 + fh;
+      u32x4_t af[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) af[mb] = *(const u32x4_t*)(sa + swz(wm * 64 + mb * 32 + fr, ch));
+#pragma unroll
+      for (int b = 0; b < G::NB; ++b)
+#pragma unroll
+        for (int nb = 0; nb < G::NBLK; ++nb) {
+          const u32x4_t bf = *(const u32x4_t*)(sb + swz(b * G::BN + wn * G::WN + nb * 32 + fr, ch));
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) acc[b][mb][nb] = mfma32x32x16(af[mb], bf, acc[b][mb][nb]);
+        }
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds column n = fr of each 32x32 block, rows (e/4)*8 + fh*4 + e%4 --------
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < G::NBLK; ++nb) {
+      const int n = n0 + wn * G::WN + nb * 32 + fr;
+      if (n >= N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * 64 + mb * 32 + (e >> 2) * 8 + fh * 4 + (e & 3);
+        if (row >= nrows) continue;
+        if (MODE == kGateUp) {
+          const float gv = acc[0][mb][nb][e], uv = acc[1][mb][nb][e];
+          uint16_t* hid = (uint16_t*)p.hid + (g < p.E ? 0 : (size_t)p.rows * p.H);
+          hid[(size_t)(r0 + row) * N + n] = (uint16_t)f32_to_bf16(silu(gv) * uv);
+        } else if (MODE == kDown) {
+          uint16_t* y = (uint16_t*)p.y + (g < p.E ? 0 : (size_t)p.rows * p.d);
+          y[(size_t)(r0 + row) * N + n] = (uint16_t)f32_to_bf16(acc[0][mb][nb][e]);
+        } else {
+          ga.logits[(size_t)row * N + n] = acc[0][mb][nb][e] + (ga.bias ? ga.bias[n] : 0.f);
+        }
+      }
+    }
+}
+
+// ------------------------------------------------------------------------------- launchers
+namespace {
+int round8(long long v) { return (int)((v + kXcds - 1) / kXcds * kXcds); }
+}  // namespace
+
+long long gemm_tiles_upper(const FfnGroups& p, int mode) {
+  const long long mt_routed = p.rows / BM + p.E;  // each group adds at most one partial tile
+  const long long mt_shared = p.Hs > 0 ? (p.T + BM - 1) / BM : 0;
+  if (mode == kGateUp) {
+    const int bn = Geo<kGateUp>::BN;
+    return mt_routed * ((p.H + bn - 1) / bn) + mt_shared * ((p.Hs + bn - 1) / bn);
+  }
+  const int bn = Geo<kDown>::BN;
+  return (mt_routed + mt_shared) * ((p.d + bn - 1) / bn);
+}
+
+size_t gemm_schedule_ints(int E) { return 2 * (size_t)(E + 2); }
+
+hipError_t launch_gemm_schedule(const FfnGroups& p, int32_t* sched, hipStream_t stream) {
+  hipLaunchKernelGGL(gemm_schedule_kernel, dim3(1), dim3(1024), 0, stream, p, sched, sched + p.E + 2);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_gate_up(const FfnGroups& p, const int32_t* sched, hipStream_t stream) {
+  GemmArgs a{};
+  a.p = p;
+  a.sched = sched;
+  hipLaunchKernelGGL(grouped_gemm_kernel<kGateUp>, dim3(round8(gemm_tiles_upper(p, kGateUp))), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_down(const FfnGroups& p, const int32_t* sched, hipStream_t stream) {
+  GemmArgs a{};
+  a.p = p;
+  a.sched = sched + p.E + 2;
+  hipLaunchKernelGGL(grouped_gemm_kernel<kDown>, dim3(round8(gemm_tiles_upper(p, kDown))), dim3(kThreads), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_gemm(const void* x, const void* w, const float* bias, float* logits, int T, int E, int d,
+                              hipStream_t stream) {
+  GemmArgs a{};
+  a.x = x;
+  a.w = w;
+  a.bias = bias;
+  a.logits = logits;
+  a.T = T;
+  a.E = E;
+  a.d = d;
+  const long long tiles = (long long)((T + BM - 1) / BM) * ((E + Geo<kRouter>::BN - 1) / Geo<kRouter>::BN);
+  hipLaunchKernelGGL(grouped_gemm_kernel<kRouter>, dim3(round8(tiles)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

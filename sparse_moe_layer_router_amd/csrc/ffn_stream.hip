@@ -290,37 +290,54 @@ ffn_down_f32(const FfnGroups p) {
 namespace {
 int groups_of(const FfnGroups& g) { return g.E + (g.Hs > 0 ? 1 : 0); }
 int hmax(const FfnGroups& g) { return g.H > g.Hs ? g.H : g.Hs; }
+long long all_rows(const FfnGroups& g) { return g.rows + (g.Hs > 0 ? g.T : 0); }
 }  // namespace
 
-hipError_t launch_ffn_gate_up(const FfnGroups& g, hipStream_t stream) {
-  if (g.dtype == kF32) {
-    long long nrows = g.rows + (g.Hs > 0 ? g.T : 0);
-    dim3 grid((unsigned)nrows, (hmax(g) + 255) / 256);
-    hipLaunchKernelGGL(ffn_gate_up_f32, grid, dim3(256), 0, stream, g);
-  } else {
-    dim3 grid((hmax(g) + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
-    hipLaunchKernelGGL(ffn_gate_up_stream<1>, grid, dim3(256), 0, stream, g);
-  }
+FfnPath ffn_path(const FfnGroups& g) {
+  if (g.dtype == kF32) return kPathF32;
+  return g.mean_rows_per_group >= kGemmMinRowsPerExpert ? kPathGemm : kPathStream;
+}
+
+hipError_t launch_ffn_gate_up_stream(const FfnGroups& g, hipStream_t stream) {
+  dim3 grid((hmax(g) + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
+  hipLaunchKernelGGL(ffn_gate_up_stream<1>, grid, dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_down(const FfnGroups& g, hipStream_t stream) {
-  if (g.dtype == kF32) {
-    long long nrows = g.rows + (g.Hs > 0 ? g.T : 0);
-    dim3 grid((unsigned)nrows, (g.d + 255) / 256);
-    hipLaunchKernelGGL(ffn_down_f32, grid, dim3(256), 0, stream, g);
-  } else {
-    dim3 grid((g.d + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
-    hipLaunchKernelGGL(ffn_down_stream<1>, grid, dim3(256), 0, stream, g);
-  }
+hipError_t launch_ffn_down_stream(const FfnGroups& g, hipStream_t stream) {
+  dim3 grid((g.d + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
+  hipLaunchKernelGGL(ffn_down_stream<1>, grid, dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 
+hipError_t launch_ffn_gate_up_f32(const FfnGroups& g, hipStream_t stream) {
+  dim3 grid((unsigned)all_rows(g), (hmax(g) + 255) / 256);
+  hipLaunchKernelGGL(ffn_gate_up_f32, grid, dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_down_f32(const FfnGroups& g, hipStream_t stream) {
+  dim3 grid((unsigned)all_rows(g), (g.d + 255) / 256);
+  hipLaunchKernelGGL(ffn_down_f32, grid, dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+const char* ffn_schedule_kernel_name(const FfnGroups& g) {
+  return ffn_path(g) == kPathGemm ? "gemm_schedule_kernel" : "";
+}
 const char* ffn_gate_up_kernel_name(const FfnGroups& g) {
-  return g.dtype == kF32 ? "ffn_gate_up_f32" : "ffn_gate_up_stream<1>";
+  switch (ffn_path(g)) {
+    case kPathF32: return "ffn_gate_up_f32";
+    case kPathStream: return "ffn_gate_up_stream<1>";
+    default: return "grouped_gemm_kernel<0>";
+  }
 }
 const char* ffn_down_kernel_name(const FfnGroups& g) {
-  return g.dtype == kF32 ? "ffn_down_f32" : "ffn_down_stream<1>";
+  switch (ffn_path(g)) {
+    case kPathF32: return "ffn_down_f32";
+    case kPathStream: return "ffn_down_stream<1>";
+    default: return "grouped_gemm_kernel<1>";
+  }
 }
 
 }  // namespace moe

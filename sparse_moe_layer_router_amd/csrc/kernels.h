@@ -59,8 +59,31 @@ struct FfnGroups {
   float mean_rows_per_group;   // host-side regime hint (T*k / E)
 };
 
-hipError_t launch_ffn_gate_up(const FfnGroups& g, hipStream_t stream);
-hipError_t launch_ffn_down(const FfnGroups& g, hipStream_t stream);
+// Which kernels run the experts, chosen from shapes only (no device data):
+//   kPathF32    float32 layers: plain VALU kernels;
+//   kPathStream bf16, few rows per expert (decode): weight-streaming MFMA GEMV, every weight read once;
+//   kPathGemm   bf16, many rows per expert (prefill): tiled MFMA grouped GEMM with a tile schedule.
+enum FfnPath { kPathF32 = 0, kPathStream = 1, kPathGemm = 2 };
+constexpr float kGemmMinRowsPerExpert = 32.f;
+FfnPath ffn_path(const FfnGroups& g);
+
+hipError_t launch_ffn_gate_up_stream(const FfnGroups& g, hipStream_t stream);
+hipError_t launch_ffn_down_stream(const FfnGroups& g, hipStream_t stream);
+hipError_t launch_ffn_gate_up_f32(const FfnGroups& g, hipStream_t stream);
+hipError_t launch_ffn_down_f32(const FfnGroups& g, hipStream_t stream);
+
+// grouped GEMM: `sched` holds gemm_schedule_ints(E) int32 (tile prefix sums of both passes)
+size_t gemm_schedule_ints(int E);
+hipError_t launch_gemm_schedule(const FfnGroups& g, int32_t* sched, hipStream_t stream);
+hipError_t launch_gemm_gate_up(const FfnGroups& g, const int32_t* sched, hipStream_t stream);
+hipError_t launch_gemm_down(const FfnGroups& g, const int32_t* sched, hipStream_t stream);
+
+// dense router GEMM (bf16, large T): logits = x . w^T + bias
+constexpr int kRouterGemmMinTokens = 2048;
+hipError_t launch_router_gemm(const void* x, const void* w, const float* bias, float* logits, int T, int E, int d,
+                              hipStream_t stream);
+
+const char* ffn_schedule_kernel_name(const FfnGroups& g);
 const char* ffn_gate_up_kernel_name(const FfnGroups& g);
 const char* ffn_down_kernel_name(const FfnGroups& g);
 

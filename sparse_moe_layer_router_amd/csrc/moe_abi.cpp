@@ -15,7 +15,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t logits, topk_idx, topk_w, counts, offsets, perm_src, inv_perm, tile_counts, hid, y, total;
+  size_t logits, topk_idx, topk_w, counts, offsets, perm_src, inv_perm, tile_counts, sched, hid, y, total;
 };
 
 size_t elem_size(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
@@ -35,6 +35,7 @@ Layout layout_of(const moe_shape& s) {
   L.perm_src = take(rows * 4);
   L.inv_perm = take(rows * 4);
   L.tile_counts = take(moe::permute_scratch_bytes((long long)rows, (int)E));
+  L.sched = take(moe::gemm_schedule_ints((int)E) * 4);
   L.hid = take((rows * H + (Hs ? T * Hs : 0)) * es);
   L.y = take((rows + (Hs ? T : 0)) * d * es);
   L.total = off;
@@ -153,12 +154,24 @@ moe::FfnGroups groups_for(const moe_shape& s, const void* x, const int32_t* perm
   return g;
 }
 
-moe_status ffn_impl(const moe::FfnGroups& g, const Events& ev, hipStream_t stream) {
+moe_status ffn_impl(const moe::FfnGroups& g, int32_t* sched, const Events& ev, hipStream_t stream) {
+  const moe::FfnPath path = moe::ffn_path(g);
+  MOE_MARK(ev, MOE_STAGE_FFN_SCHEDULE, 0);
+  if (path == moe::kPathGemm) MOE_LAUNCH(moe::launch_gemm_schedule(g, sched, stream));
+  MOE_MARK(ev, MOE_STAGE_FFN_SCHEDULE, 1);
   MOE_MARK(ev, MOE_STAGE_FFN_GATE_UP, 0);
-  MOE_LAUNCH(moe::launch_ffn_gate_up(g, stream));
+  switch (path) {
+    case moe::kPathF32: MOE_LAUNCH(moe::launch_ffn_gate_up_f32(g, stream)); break;
+    case moe::kPathStream: MOE_LAUNCH(moe::launch_ffn_gate_up_stream(g, stream)); break;
+    case moe::kPathGemm: MOE_LAUNCH(moe::launch_gemm_gate_up(g, sched, stream)); break;
+  }
   MOE_MARK(ev, MOE_STAGE_FFN_GATE_UP, 1);
   MOE_MARK(ev, MOE_STAGE_FFN_DOWN, 0);
-  MOE_LAUNCH(moe::launch_ffn_down(g, stream));
+  switch (path) {
+    case moe::kPathF32: MOE_LAUNCH(moe::launch_ffn_down_f32(g, stream)); break;
+    case moe::kPathStream: MOE_LAUNCH(moe::launch_ffn_down_stream(g, stream)); break;
+    case moe::kPathGemm: MOE_LAUNCH(moe::launch_gemm_down(g, sched, stream)); break;
+  }
   MOE_MARK(ev, MOE_STAGE_FFN_DOWN, 1);
   return MOE_OK;
 }
@@ -206,7 +219,7 @@ moe_status layer_impl(const moe_shape* sp, const void* x, const void* w_router, 
   MOE_TRY(route_impl(s, x, w_router, bias, logits, idx, w, ev, stream));
   MOE_TRY(permute_impl(s, idx, counts, offsets, perm_src, inv_perm, tiles, ev, stream));
   const moe::FfnGroups g = groups_for(s, x, perm_src, offsets, wg, wu, wd, sg, su, sd, hid, y);
-  MOE_TRY(ffn_impl(g, ev, stream));
+  MOE_TRY(ffn_impl(g, (int32_t*)at(ws, L.sched), ev, stream));
   const void* shared_out =
       s.d_shared_hidden > 0 ? (const void*)((const char*)y + (size_t)s.T * s.top_k * s.d_model * elem_size(s.dtype))
                             : nullptr;
@@ -284,9 +297,10 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* x, const int32_t* per
   MOE_TRY(check_workspace(*s, workspace, ws_bytes));
   moe_shape routed = *s;
   routed.d_shared_hidden = 0;  // this entry point runs the routed groups only
+  const Layout L = layout_of(*s);
   const moe::FfnGroups g = groups_for(routed, x, perm_src, expert_offsets, w_gate, w_up, w_down, nullptr, nullptr,
-                                      nullptr, at(workspace, layout_of(*s).hid), y);
-  return ffn_impl(g, Events{nullptr, nullptr}, (hipStream_t)stream);
+                                      nullptr, at(workspace, L.hid), y);
+  return ffn_impl(g, (int32_t*)at(workspace, L.sched), Events{nullptr, nullptr}, (hipStream_t)stream);
 }
 
 moe_status moe_combine(const moe_shape* s, const void* y_perm, const int32_t* inv_perm, const float* topk_w,
@@ -332,6 +346,7 @@ const char* moe_stage_kernel_name(const moe_shape* s, int stage) {
     case MOE_STAGE_PERMUTE_COUNT: return "permute_count_kernel";
     case MOE_STAGE_PERMUTE_SCAN: return "permute_scan_kernel";
     case MOE_STAGE_PERMUTE_SCATTER: return "permute_scatter_kernel";
+    case MOE_STAGE_FFN_SCHEDULE: return moe::ffn_schedule_kernel_name(g);
     case MOE_STAGE_FFN_GATE_UP: return moe::ffn_gate_up_kernel_name(g);
     case MOE_STAGE_FFN_DOWN: return moe::ffn_down_kernel_name(g);
     case MOE_STAGE_COMBINE: return moe::combine_kernel_name(s->dtype);

@@ -117,6 +117,7 @@ route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t
 // ------------------------------------------------------------------------------------ launchers
 hipError_t launch_route_logits(int dtype, const void* x, const void* w_router, const float* bias, float* logits,
                                int T, int E, int d, hipStream_t stream) {
+  if (dtype == kBF16 && T >= kRouterGemmMinTokens) return launch_router_gemm(x, w_router, bias, logits, T, E, d, stream);
   dim3 grid(T, (E + 3) / 4), block(256);
   if (dtype == kBF16)
     hipLaunchKernelGGL(route_logits_valu<kBF16>, grid, block, 0, stream, x, w_router, bias, logits, T, E, d);
@@ -131,7 +132,8 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
   return hipGetLastError();
 }
 
-const char* route_logits_kernel_name(int dtype, int, int) {
+const char* route_logits_kernel_name(int dtype, int T, int) {
+  if (dtype == kBF16 && T >= kRouterGemmMinTokens) return "grouped_gemm_kernel<2>";
   return dtype == kBF16 ? "route_logits_valu<1>" : "route_logits_valu<0>";
 }
 const char* route_topk_kernel_name() { return "route_topk_kernel"; }

@@ -127,7 +127,10 @@ def test_status_strings_and_stage_names():
     assert moe.moe_status_string(99) == "unknown status"
     s = dsv3()
     names = [moe.moe_stage_kernel_name(s, i) for i in range(moe.MOE_NUM_STAGES)]
-    assert all(names) and "gate_up" in names[5] and "down" in names[6]
+    assert names[5] == "" and "gate_up" in names[6] and "down" in names[7]     # decode: GEMV, no schedule
+    names = [moe.moe_stage_kernel_name(dsv3(T=8192), i) for i in range(moe.MOE_NUM_STAGES)]
+    assert names[0] == "grouped_gemm_kernel<2>" and names[5] == "gemm_schedule_kernel"
+    assert names[6] == "grouped_gemm_kernel<0>" and names[7] == "grouped_gemm_kernel<1>"
     assert moe.moe_stage_kernel_name(dsv3(top_k=0), 0) == ""
 
 

@@ -32,6 +32,10 @@ MID = [
     LayerConfig("one_token", 1, 256, 32, 8, 128, 64, "bf16"),
     LayerConfig("wide_E1024", 40, 64, 1024, 2, 16, 0, "bf16"),
     synth.CONFIGS[0],
+    # many rows per expert: tiled MFMA grouped GEMM (K tails of 8, partial N and M tiles)
+    LayerConfig("gemm_ragged_shared", 600, 264, 16, 2, 200, 136, "bf16"),
+    # 2048 tokens: router GEMM too (E = 8 < one N tile), skewed buckets
+    LayerConfig("gemm_zipf_router", 2048, 512, 8, 2, 384, 0, "bf16", zipf_s=1.2),
 ]
 
 
@@ -81,7 +85,7 @@ def test_layer_matches_oracle_mid_sizes(cfg):
     assert ok, (err, bound)
 
 
-@pytest.mark.parametrize("cfg", MID[:3], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", MID[:3] + MID[-2:], ids=lambda c: c.name)
 def test_entry_points_separately(cfg):
     """moe_route -> moe_permute -> moe_grouped_ffn (routed, then shared as a one-group call) -> moe_combine."""
     L = G.make_layer(cfg)
