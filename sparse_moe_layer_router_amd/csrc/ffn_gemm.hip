@@ -7,12 +7,15 @@
 // no expert waits on a separate launch; data-movement page, section 15: once routes are sorted by
 // expert, each expert's weights are loaded once and reused across its whole bucket of tokens.
 //
-// Tiles: BM = 128 rows (tokens) x BN weight rows x BK = 64 along K, 256 threads as 2 x 2 waves,
-// each wave a 64 x (BN/2) block built from 32x32x16 MFMAs. Gate and up projections are computed
-// by the same block for the same rows (two B tiles), so SiLU(g) * u is formed in registers and the
-// hidden activation leaves as bf16. Operands are staged through a double-buffered LDS ring with a
-// 16-byte-chunk XOR swizzle (chunk ^ (row & 7)) so MFMA fragment reads are bank-conflict free;
-// the next K slice is fetched into registers while the current one is multiplied.
+// Tiles: BM = 128 rows (tokens) x BN weight rows per B matrix x BK = 32 along K; 512 threads as
+// 2 x 4 waves (two per SIMD, so one wave's LDS or barrier wait is covered by the other's MFMAs),
+// wave (wm, wn) owning rows [64 wm, 64 wm + 64) x BN/4 columns of every B matrix as 32x32x16 MFMA
+// blocks. Gate and up projections are computed by the same block for the same rows (two B tiles),
+// so SiLU(g) * u is formed in registers and the hidden activation leaves as bf16. Operands go
+// straight from global memory into a three-slice LDS ring (global_load_lds, 16 bytes per lane, no
+// register staging): while slice kt is multiplied, slices kt+1 and kt+2 are in flight, and waves
+// wait (s_waitcnt vmcnt) only for slice kt itself. A 16-byte-chunk XOR swizzle keeps MFMA
+// fragment reads bank-conflict free.
 //
 // Tile order: tiles are numbered expert by expert, N-tile by N-tile, with the M-tiles of one
 // (expert, N-tile) adjacent. Workgroups are dealt round-robin to the 8 XCDs, so block L runs tile
@@ -26,25 +29,37 @@ namespace moe {
 namespace {
 
 constexpr int BM = 128;
-constexpr int BK = 64;
-constexpr int kThreads = 256;
+constexpr int BK = 32;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kWavesM = 2, kWavesN = 4;
 constexpr int kXcds = 8;
+constexpr int kStages = 3;
+constexpr int kRowBytes = BK * 2;  // one tile row in LDS: 64 bytes = 4 chunks of 16
 
 enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2 };
 
 template <int MODE> struct Geo {
-  static constexpr int NB = MODE == kGateUp ? 2 : 1;        // B matrices per tile
-  static constexpr int BN = MODE == kGateUp ? 128 : 256;    // rows of each B tile
-  static constexpr int WN = BN / 2;                         // per-wave columns
-  static constexpr int NBLK = WN / 32;                      // 32-wide MFMA blocks per wave
-  static constexpr int A_BYTES = BM * BK * 2;
-  static constexpr int B_BYTES = NB * BN * BK * 2;
+  static constexpr int NB = MODE == kGateUp ? 2 : 1;                          // B matrices per tile
+  static constexpr int BN = MODE == kGateUp ? 256 : (MODE == kDown ? 512 : 256);  // rows of each B tile
+  static constexpr int WM = BM / kWavesM;                                      // rows per wave
+  static constexpr int WN = BN / kWavesN;                                     // columns per wave
+  static constexpr int NBLK = WN / 32;                                        // 32-wide MFMA blocks
+  static constexpr int MBLK = WM / 32;                                        // 32-high MFMA blocks
+  static constexpr int A_BYTES = BM * kRowBytes;
+  static constexpr int B_BYTES = NB * BN * kRowBytes;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_LOADS = BM * BK / 8 / kThreads;       // 16-byte chunks per thread
-  static constexpr int B_LOADS = NB * BN * BK / 8 / kThreads;
+  static constexpr int A_LOADS = BM * (BK / 8) / kThreads;         // 16-byte chunks per lane
+  static constexpr int B_LOADS = NB * BN * (BK / 8) / kThreads;
+  static constexpr int LOADS = A_LOADS + B_LOADS;                  // global_load_lds per wave per slice
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * (BK * 2) + ((chunk ^ (row & 7)) << 4); }
+// LDS byte offset of 16-byte chunk `chunk` (0..3) of tile row `row`. The XOR key takes four
+// distinct values over any four rows of equal parity among 8 consecutive rows and over any four
+// rows of equal residue mod 4 among 16 consecutive rows, so a fragment read (16 or 8 consecutive
+// rows, one chunk column) touches distinct 16-byte bank groups.
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 2)) & 3); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + (swz_chunk(row, chunk) << 4); }
 
 }  // namespace
 
@@ -114,11 +129,11 @@ template <int MODE>
 __global__ void __launch_bounds__(kThreads, 1)
 grouped_gemm_kernel(const GemmArgs ga) {
   using G = Geo<MODE>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][G::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages][G::STAGE];
 
   const FfnGroups& p = ga.p;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave index, 0..7
 
   // ---- which tile --------------------------------------------------------------------------
   int g = 0, mt = 0, nt = 0;
@@ -187,13 +202,20 @@ grouped_gemm_kernel(const GemmArgs ga) {
   }
   const int m0 = mt * BM, n0 = nt * G::BN;
 
-  // ---- per-thread global source pointers (row pointers, chunk offset added per K slice) ------
-  const int lc = tid & 7;            // 16-byte chunk within a 64-wide K slice
+  // ---- per-lane global sources -----------------------------------------------------------------
+  // A slice holds BM*4 chunks of A and NB*BN*4 chunks of B (4 chunks of 16 bytes per 32-wide row).
+  // Wave w fills chunk positions [w*BM*4/8, (w+1)*BM*4/8) of A and the matching share of the stacked
+  // B tiles, 64 consecutive positions per instruction (lane l -> position base + l). Position p
+  // holds row p/4, physical chunk p%4, i.e. logical chunk swz_chunk(row, p%4): the lane loads that
+  // logical chunk of that row.
+  const int phys = lane & 3;
   const uint16_t* a_src[G::A_LOADS];
   const uint16_t* b_src[G::B_LOADS];
+  int a_kc[G::A_LOADS], b_kc[G::B_LOADS];     // element offset of the lane's chunk inside a K slice
 #pragma unroll
   for (int i = 0; i < G::A_LOADS; ++i) {
-    const int row = (tid >> 3) + 32 * i;
+    const int row = wv * (BM / kWaves) + i * 16 + (lane >> 2);
+    a_kc[i] = swz_chunk(row, phys) * 8;
     int rr = m0 + row;
     rr = rr < nrows ? rr : (nrows > 0 ? nrows - 1 : 0);  // rows past the bucket: any valid row, never stored
     long long src;
@@ -216,81 +238,110 @@ grouped_gemm_kernel(const GemmArgs ga) {
   }
 #pragma unroll
   for (int i = 0; i < G::B_LOADS; ++i) {
-    const int row = (tid >> 3) + 32 * i;       // stacked rows of the NB B tiles
+    const int row = wv * (G::NB * G::BN / kWaves) + i * 16 + (lane >> 2);   // stacked rows of the B tiles
+    b_kc[i] = swz_chunk(row, phys) * 8;
     const int b = row / G::BN;
     int n = n0 + (row % G::BN);
     n = n < N ? n : N - 1;                     // rows past N: any valid row, never stored
     b_src[i] = Bp[b] + (size_t)n * K;
   }
 
-  const u32x4_t zero = {0, 0, 0, 0};
-  u32x4_t ra[G::A_LOADS], rb[G::B_LOADS];
-  auto gload = [&](int k0) {
-    const int k = k0 + lc * 8;
-    const bool ok = k < K;                     // K is a multiple of 8: a chunk is all in or all out
+  typedef __attribute__((address_space(3))) void lds_t;
+  // LDS byte offsets (wave-uniform) of this wave's instruction i inside a slice
+  auto a_dst = [&](int i) { return (wv * (BM / kWaves) + i * 16) * kRowBytes; };
+  auto b_dst = [&](int i) { return G::A_BYTES + (wv * (G::NB * G::BN / kWaves) + i * 16) * kRowBytes; };
+  auto issue = [&](int kt, int buf) {
+    const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < G::A_LOADS; ++i) ra[i] = ok ? ld16(a_src[i] + k) : zero;
+    for (int i = 0; i < G::A_LOADS; ++i) {
+      const int k = k0 + a_kc[i];
+      const uint16_t* src = a_src[i] + (k < K ? k : 0);    // out-of-range chunks are zeroed after landing
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_t*)(smem[buf] + a_dst(i)), 16, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < G::B_LOADS; ++i) rb[i] = ok ? ld16(b_src[i] + k) : zero;
+    for (int i = 0; i < G::B_LOADS; ++i) {
+      const int k = k0 + b_kc[i];
+      const uint16_t* src = b_src[i] + (k < K ? k : 0);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_t*)(smem[buf] + b_dst(i)), 16, 0, 0);
+    }
   };
-  auto lstore = [&](int buf) {
-    uint8_t* sa = smem[buf];
-    uint8_t* sb = smem[buf] + G::A_BYTES;
+  // chunks past K in the last slice: write zeros over what the loads brought in
+  auto zero_tail = [&](int kt, int buf) {
+    const int k0 = kt * BK;
+    const u32x4_t zero = {0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < G::A_LOADS; ++i) *(u32x4_t*)(sa + swz((tid >> 3) + 32 * i, lc)) = ra[i];
+    for (int i = 0; i < G::A_LOADS; ++i)
+      if (k0 + a_kc[i] >= K) *(u32x4_t*)(smem[buf] + a_dst(i) + lane * 16) = zero;
 #pragma unroll
-    for (int i = 0; i < G::B_LOADS; ++i) *(u32x4_t*)(sb + swz((tid >> 3) + 32 * i, lc)) = rb[i];
+    for (int i = 0; i < G::B_LOADS; ++i)
+      if (k0 + b_kc[i] >= K) *(u32x4_t*)(smem[buf] + b_dst(i) + lane * 16) = zero;
   };
 
-  f32x16_t acc[G::NB][2][G::NBLK];
+  f32x16_t acc[G::NB][G::MBLK][G::NBLK];
 #pragma unroll
   for (int b = 0; b < G::NB; ++b)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < G::MBLK; ++mb)
 #pragma unroll
       for (int nb = 0; nb < G::NBLK; ++nb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[b][mb][nb][e] = 0.f;
 
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const int fr = lane & 31, fh = lane >> 5;   // fragment row / k-half of this lane
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const uint8_t* sa = smem[cur];
-    const uint8_t* sb = smem[cur] + G::A_BYTES;
+  const int wm = wv / kWavesN, wn = wv % kWavesN;
+  auto compute = [&](int buf) {
+    const uint8_t* sa = smem[buf];
+    const uint8_t* sb = smem[buf] + G::A_BYTES;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int ch = kk * 2 + fh;
-      u32x4_t af[2];
+      u32x4_t af[G::MBLK], bf[G::NB][G::NBLK];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) af[mb] = *(const u32x4_t*)(sa + swz(wm * 64 + mb * 32 + fr, ch));
+      for (int mb = 0; mb < G::MBLK; ++mb) af[mb] = *(const u32x4_t*)(sa + swz(wm * G::WM + mb * 32 + fr, ch));
 #pragma unroll
       for (int b = 0; b < G::NB; ++b)
 #pragma unroll
-        for (int nb = 0; nb < G::NBLK; ++nb) {
-          const u32x4_t bf = *(const u32x4_t*)(sb + swz(b * G::BN + wn * G::WN + nb * 32 + fr, ch));
+        for (int nb = 0; nb < G::NBLK; ++nb)
+          bf[b][nb] = *(const u32x4_t*)(sb + swz(b * G::BN + wn * G::WN + nb * 32 + fr, ch));
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) acc[b][mb][nb] = mfma32x32x16(af[mb], bf, acc[b][mb][nb]);
-        }
+      for (int b = 0; b < G::NB; ++b)
+#pragma unroll
+        for (int nb = 0; nb < G::NBLK; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < G::MBLK; ++mb) acc[b][mb][nb] = mfma32x32x16(af[mb], bf[b][nb], acc[b][mb][nb]);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+  };
+
+  // Pipeline over K slices: slices kt+1 and kt+2 are in flight while slice kt is multiplied.
+  // Each wave waits for its own loads of slice kt (vmcnt counts this wave's loads in issue order,
+  // G::LOADS per slice), then the barrier makes every wave's slice kt visible and guarantees that
+  // slice kt-1, whose buffer the loads of slice kt+2 overwrite, is no longer being read.
+  const int nk = (K + BK - 1) / BK;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt % kStages;
+    if (kt + 1 < nk) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::LOADS) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (K % BK) zero_tail(kt, buf);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kt + 2 < nk) issue(kt + 2, (kt + 2) % kStages);
+    compute(buf);
   }
 
   // ---- epilogue: lane holds column n = fr of each 32x32 block, rows (e/4)*8 + fh*4 + e%4 --------
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < G::MBLK; ++mb)
 #pragma unroll
     for (int nb = 0; nb < G::NBLK; ++nb) {
       const int n = n0 + wn * G::WN + nb * 32 + fr;
       if (n >= N) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * 64 + mb * 32 + (e >> 2) * 8 + fh * 4 + (e & 3);
+        const int row = m0 + wm * G::WM + mb * 32 + (e >> 2) * 8 + fh * 4 + (e & 3);
         if (row >= nrows) continue;
         if (MODE == kGateUp) {
           const float gv = acc[0][mb][nb][e], uv = acc[1][mb][nb][e];
