@@ -24,6 +24,10 @@
  *     w_router [E, d]; w_gate, w_up [E, H, d]; w_down [E, d, H]; shared weights [Hs, d], [Hs, d],
  *     [d, Hs]. x, y and out are [rows, d]. `dtype` applies to x, all weights, y and out; routing
  *     weights, logits and the logit bias are always float32; indices are int32.
+ *   - Expert weights may instead be passed in the fragment-tiled layout MOE_LAYOUT_FRAG16 made
+ *     by moe_pack_weights (bf16 only; every expert matrix's row count a multiple of 16 and column
+ *     count a multiple of 32): the matrix-core operand order, so every 1 KB of a weight is one
+ *     contiguous 16-row x 32-column MFMA operand. The router weight is always row-major.
  *   - Validation happens on the host before anything is enqueued; on any error nothing is
  *     enqueued. Limits: 0 <= T, T * top_k < 2^31, 1 <= top_k <= n_experts <= 1024, d_model,
  *     d_hidden >= 8 and multiples of 8, d_shared_hidden 0 or a multiple of 8, 16-byte aligned
@@ -54,6 +58,12 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Storage layout of the expert weight matrices (w_gate, w_up, w_down and the shared ones). */
+typedef enum {
+  MOE_LAYOUT_ROWMAJOR = 0, /* [out, in] row-major, like a linear layer's weight */
+  MOE_LAYOUT_FRAG16 = 1    /* fragment-tiled, see moe_pack_weights */
+} moe_weight_layout;
+
 /* Layer sizes (host pointer). */
 typedef struct {
   int32_t T;               /* tokens in this batch */
@@ -63,7 +73,20 @@ typedef struct {
   int32_t d_hidden;        /* H, hidden size of each routed expert */
   int32_t d_shared_hidden; /* Hs, hidden size of the shared expert; 0 = no shared expert */
   int32_t dtype;           /* moe_dtype */
+  int32_t weight_layout;   /* moe_weight_layout of the expert weights */
 } moe_shape;
+
+/*
+ * moe_pack_weights -- re-lay n_mats row-major bf16 matrices [n_mats, rows, cols] into the
+ * fragment-tiled layout MOE_LAYOUT_FRAG16 (same size). rows % 16 == 0, cols % 32 == 0. Element
+ * (r, c) of a matrix moves to
+ *     ((r / 16) * (cols / 32) + c / 32) * 512  +  ((r % 16) + 16 * ((c % 32) / 8)) * 8  +  c % 8
+ * i.e. the matrix is cut into 16 x 32 blocks stored one after another along each 16-row band,
+ * and inside a block lane l = (r % 16) + 16 * ((c % 32) / 8) of a wave holds 8 consecutive
+ * columns: the A-operand order of the 16x16x32 bf16 MFMA. src and dst must not overlap; both
+ * 16-byte aligned. A one-time preparation step (weight load), not part of the layer forward.
+ */
+moe_status moe_pack_weights(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols, void* stream);
 
 /* Bytes of workspace that every entry point below accepts for shape `s` (0 if `s` is invalid). */
 size_t moe_workspace_bytes(const moe_shape* s);

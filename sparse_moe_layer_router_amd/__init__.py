@@ -17,12 +17,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_moe_layer_router_amd.build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_moe_layer_router_amd/build.py` "
                       "(hipcc, gfx950). There is no CPU fallback.")
 _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
 MOE_F32, MOE_BF16 = 0, 1
+MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_FRAG16 = 0, 1
 STAGES = ["route_logits", "route_topk", "permute_count", "permute_scan", "permute_scatter", "ffn_schedule",
           "ffn_gate_up", "ffn_down", "combine"]
 MOE_NUM_STAGES = len(STAGES)
@@ -31,15 +32,16 @@ MOE_NUM_STAGES = len(STAGES)
 class moe_shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("d_hidden", ctypes.c_int32), ("d_shared_hidden", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
 
 
-def make_shape(T, d_model, n_experts, top_k, d_hidden, d_shared_hidden=0, dtype=MOE_BF16) -> moe_shape:
+def make_shape(T, d_model, n_experts, top_k, d_hidden, d_shared_hidden=0, dtype=MOE_BF16,
+               weight_layout=MOE_LAYOUT_ROWMAJOR) -> moe_shape:
     if isinstance(dtype, str):
         dtype = {"bf16": MOE_BF16, "f32": MOE_F32}[dtype]
     elif isinstance(dtype, torch.dtype):
         dtype = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[dtype]
-    return moe_shape(T, d_model, n_experts, top_k, d_hidden, d_shared_hidden, dtype)
+    return moe_shape(T, d_model, n_experts, top_k, d_hidden, d_shared_hidden, dtype, weight_layout)
 
 
 class MoeError(RuntimeError):
@@ -60,6 +62,7 @@ _sigs = {
     "moe_layer_forward": (ctypes.c_int, [_S] + [_P] * 15 + [ctypes.c_size_t, _P]),
     "moe_layer_forward_timed": (ctypes.c_int, [_S] + [_P] * 15 + [ctypes.c_size_t, _P, _P]),
     "moe_stage_kernel_name": (ctypes.c_char_p, [_S, ctypes.c_int]),
+    "moe_pack_weights": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -157,6 +160,22 @@ def moe_layer_forward_timed(shape, x, w_router, logit_bias, w_gate, w_up, w_down
     _check("moe_layer_forward_timed", _lib.moe_layer_forward_timed(*_layer_args(
         shape, x, w_router, logit_bias, w_gate, w_up, w_down, w_shared_gate, w_shared_up, w_shared_down, out,
         topk_idx_out, topk_w_out, counts_out, logits_out, workspace, stream), events))
+
+
+def moe_pack_weights(src, dst, n_mats, rows, cols, stream=None):
+    """Fragment-tiled copy of n_mats row-major bf16 [rows, cols] matrices (MOE_LAYOUT_FRAG16)."""
+    _check("moe_pack_weights", _lib.moe_pack_weights(_ptr(src), _ptr(dst), n_mats, rows, cols, _stream(stream)))
+
+
+def pack_expert_weights(w_gate, w_up, w_down, shared=None, stream=None):
+    """Packed copies of [E,H,d], [E,H,d], [E,d,H] (and an optional shared triple) bf16 weights."""
+    out = []
+    for w in (w_gate, w_up, w_down) + (tuple(shared) if shared is not None else ()):
+        p = torch.empty_like(w)
+        n = 1 if w.dim() == 2 else w.shape[0]
+        moe_pack_weights(w, p, n, w.shape[-2], w.shape[-1], stream)
+        out.append(p)
+    return out
 
 
 def moe_stage_kernel_name(shape, stage: int) -> str:

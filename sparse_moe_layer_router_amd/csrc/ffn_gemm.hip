@@ -125,7 +125,7 @@ struct GemmArgs {
   int T, E, d;
 };
 
-template <int MODE>
+template <int MODE, int LAYOUT>
 __global__ void __launch_bounds__(kThreads, 1)
 grouped_gemm_kernel(const GemmArgs ga) {
   using G = Geo<MODE>;
@@ -238,18 +238,32 @@ grouped_gemm_kernel(const GemmArgs ga) {
   }
 #pragma unroll
   for (int i = 0; i < G::B_LOADS; ++i) {
-    const int row = wv * (G::NB * G::BN / kWaves) + i * 16 + (lane >> 2);   // stacked rows of the B tiles
-    b_kc[i] = swz_chunk(row, phys) * 8;
-    const int b = row / G::BN;
-    int n = n0 + (row % G::BN);
-    n = n < N ? n : N - 1;                     // rows past N: any valid row, never stored
-    b_src[i] = Bp[b] + (size_t)n * K;
+    if (LAYOUT == kFrag16) {
+      // one 16 x 32 block (1 KB, contiguous in the packed weight) per instruction: block q of the
+      // stacked B tiles is band n0/16 + q % (BN/16) of matrix q / (BN/16)
+      const int q = wv * G::B_LOADS + i;
+      const int b = q / (G::BN / 16);
+      int band = n0 / 16 + q % (G::BN / 16);
+      band = band < N / 16 ? band : N / 16 - 1;  // bands past N: any valid band, never stored
+      b_kc[i] = 0;
+      b_src[i] = Bp[b] + (size_t)band * (K / 32) * 512 + lane * 8;
+    } else {
+      const int row = wv * (G::NB * G::BN / kWaves) + i * 16 + (lane >> 2);   // stacked rows of the B tiles
+      b_kc[i] = swz_chunk(row, phys) * 8;
+      const int b = row / G::BN;
+      int n = n0 + (row % G::BN);
+      n = n < N ? n : N - 1;                     // rows past N: any valid row, never stored
+      b_src[i] = Bp[b] + (size_t)n * K;
+    }
   }
 
   typedef __attribute__((address_space(3))) void lds_t;
   // LDS byte offsets (wave-uniform) of this wave's instruction i inside a slice
   auto a_dst = [&](int i) { return (wv * (BM / kWaves) + i * 16) * kRowBytes; };
-  auto b_dst = [&](int i) { return G::A_BYTES + (wv * (G::NB * G::BN / kWaves) + i * 16) * kRowBytes; };
+  auto b_dst = [&](int i) {
+    return LAYOUT == kFrag16 ? G::A_BYTES + (wv * G::B_LOADS + i) * 1024
+                             : G::A_BYTES + (wv * (G::NB * G::BN / kWaves) + i * 16) * kRowBytes;
+  };
   auto issue = [&](int kt, int buf) {
     const int k0 = kt * BK;
 #pragma unroll
@@ -260,8 +274,13 @@ grouped_gemm_kernel(const GemmArgs ga) {
     }
 #pragma unroll
     for (int i = 0; i < G::B_LOADS; ++i) {
-      const int k = k0 + b_kc[i];
-      const uint16_t* src = b_src[i] + (k < K ? k : 0);
+      const uint16_t* src;
+      if (LAYOUT == kFrag16) {
+        src = b_src[i] + (size_t)kt * 512;  // K is a multiple of 32 in this layout: no tail
+      } else {
+        const int k = k0 + b_kc[i];
+        src = b_src[i] + (k < K ? k : 0);
+      }
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_t*)(smem[buf] + b_dst(i)), 16, 0, 0);
     }
   };
@@ -272,9 +291,11 @@ grouped_gemm_kernel(const GemmArgs ga) {
 #pragma unroll
     for (int i = 0; i < G::A_LOADS; ++i)
       if (k0 + a_kc[i] >= K) *(u32x4_t*)(smem[buf] + a_dst(i) + lane * 16) = zero;
+    if (LAYOUT != kFrag16) {
 #pragma unroll
-    for (int i = 0; i < G::B_LOADS; ++i)
-      if (k0 + b_kc[i] >= K) *(u32x4_t*)(smem[buf] + b_dst(i) + lane * 16) = zero;
+      for (int i = 0; i < G::B_LOADS; ++i)
+        if (k0 + b_kc[i] >= K) *(u32x4_t*)(smem[buf] + b_dst(i) + lane * 16) = zero;
+    }
   };
 
   f32x16_t acc[G::NB][G::MBLK][G::NBLK];
@@ -301,8 +322,13 @@ grouped_gemm_kernel(const GemmArgs ga) {
 #pragma unroll
       for (int b = 0; b < G::NB; ++b)
 #pragma unroll
-        for (int nb = 0; nb < G::NBLK; ++nb)
-          bf[b][nb] = *(const u32x4_t*)(sb + swz(b * G::BN + wn * G::WN + nb * 32 + fr, ch));
+        for (int nb = 0; nb < G::NBLK; ++nb) {
+          const int n = wn * G::WN + nb * 32 + fr;   // row inside B matrix b's tile
+          if (LAYOUT == kFrag16)  // block n/16 of matrix b; lane position (n%16) + 16*chunk
+            bf[b][nb] = *(const u32x4_t*)(sb + (b * (G::BN / 16) + n / 16) * 1024 + ((n & 15) + 16 * ch) * 16);
+          else
+            bf[b][nb] = *(const u32x4_t*)(sb + swz(b * G::BN + n, ch));
+        }
 #pragma unroll
       for (int b = 0; b < G::NB; ++b)
 #pragma unroll
@@ -384,8 +410,11 @@ hipError_t launch_gemm_gate_up(const FfnGroups& p, const int32_t* sched, hipStre
   GemmArgs a{};
   a.p = p;
   a.sched = sched;
-  hipLaunchKernelGGL(grouped_gemm_kernel<kGateUp>, dim3(round8(gemm_tiles_upper(p, kGateUp))), dim3(kThreads), 0,
-                     stream, a);
+  const dim3 grid(round8(gemm_tiles_upper(p, kGateUp)));
+  if (p.layout == kFrag16)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kGateUp, kFrag16>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<kGateUp, kRowMajor>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -393,8 +422,11 @@ hipError_t launch_gemm_down(const FfnGroups& p, const int32_t* sched, hipStream_
   GemmArgs a{};
   a.p = p;
   a.sched = sched + p.E + 2;
-  hipLaunchKernelGGL(grouped_gemm_kernel<kDown>, dim3(round8(gemm_tiles_upper(p, kDown))), dim3(kThreads), 0, stream,
-                     a);
+  const dim3 grid(round8(gemm_tiles_upper(p, kDown)));
+  if (p.layout == kFrag16)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kDown, kFrag16>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<kDown, kRowMajor>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -409,7 +441,7 @@ hipError_t launch_router_gemm(const void* x, const void* w, const float* bias, f
   a.E = E;
   a.d = d;
   const long long tiles = (long long)((T + BM - 1) / BM) * ((E + Geo<kRouter>::BN - 1) / Geo<kRouter>::BN);
-  hipLaunchKernelGGL(grouped_gemm_kernel<kRouter>, dim3(round8(tiles)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<kRouter, kRowMajor>), dim3(round8(tiles)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

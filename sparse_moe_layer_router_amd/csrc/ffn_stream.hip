@@ -76,7 +76,22 @@ __device__ __forceinline__ long long source_row(const FfnGroups& p, const GroupV
 
 }  // namespace
 
-template <int NTT>
+// Weight fragment source for a wave streaming the 16 rows [r0, r0+16) of a [rows, K] matrix: the
+// lane's 16 bytes of k-step s (32 columns) are at base + s * step.
+//   row-major: row r0 + lane%16, columns 8*(lane/16) .. +8 of the step: 16 rows x 64 B per load;
+//   fragment-tiled: block (r0/16, s), lane's 16 bytes: one contiguous 1 KB per load.
+template <int LAYOUT>
+__device__ __forceinline__ const uint16_t* frag_base(const uint16_t* w, int r0, int rows, int K, int lane, int* step) {
+  if (LAYOUT == kFrag16) {
+    *step = 512;
+    return w + (size_t)(r0 / 16) * (K / 32) * 512 + lane * 8;
+  }
+  *step = 32;
+  const int r = (r0 + (lane & 15) < rows) ? r0 + (lane & 15) : rows - 1;  // rows past the matrix: dropped
+  return w + (size_t)r * K + (lane >> 4) * 8;
+}
+
+template <int NTT, int LAYOUT>
 __global__ void __launch_bounds__(256)
 ffn_gate_up_stream(const FfnGroups p) {
   const GroupView v = group_view(p, blockIdx.y);
@@ -86,9 +101,9 @@ ffn_gate_up_stream(const FfnGroups p) {
   if (h0 >= v.Hg) return;
   const int d = p.d;
   const int ar = lane & 15, kq = lane >> 4;
-  const int hrow = (h0 + ar < v.Hg) ? h0 + ar : v.Hg - 1;  // rows past Hg are computed and dropped
-  const uint16_t* ag = v.wg + (size_t)hrow * d + kq * 8;
-  const uint16_t* au = v.wu + (size_t)hrow * d + kq * 8;
+  int ws;  // elements between consecutive k-steps of a weight fragment
+  const uint16_t* ag = frag_base<LAYOUT>(v.wg, h0, v.Hg, d, lane, &ws);
+  const uint16_t* au = frag_base<LAYOUT>(v.wu, h0, v.Hg, d, lane, &ws);
   const uint16_t* xb = (const uint16_t*)p.x;
 
   for (int tt = 0; tt < v.n; tt += 16 * NTT) {
@@ -110,8 +125,8 @@ ffn_gate_up_stream(const FfnGroups p) {
       u32x4_t a_g[kUnroll], a_u[kUnroll], b[kUnroll][NTT];
 #pragma unroll
       for (int s = 0; s < kUnroll; ++s) {
-        a_g[s] = ld16_stream(ag + k0 + 32 * s);
-        a_u[s] = ld16_stream(au + k0 + 32 * s);
+        a_g[s] = ld16_stream(ag + (size_t)(k0 / 32 + s) * ws);
+        a_u[s] = ld16_stream(au + (size_t)(k0 / 32 + s) * ws);
       }
 #pragma unroll
       for (int s = 0; s < kUnroll; ++s)
@@ -127,8 +142,8 @@ ffn_gate_up_stream(const FfnGroups p) {
     }
     for (; k0 < d; k0 += 32) {  // tail: d is a multiple of 8, so a lane's 8-chunk is all in or all out
       const bool kok = k0 + kq * 8 < d;
-      const u32x4_t a_g = kok ? ld16_stream(ag + k0) : zero;
-      const u32x4_t a_u = kok ? ld16_stream(au + k0) : zero;
+      const u32x4_t a_g = kok ? ld16_stream(ag + (size_t)(k0 / 32) * ws) : zero;
+      const u32x4_t a_u = kok ? ld16_stream(au + (size_t)(k0 / 32) * ws) : zero;
 #pragma unroll
       for (int j = 0; j < NTT; ++j) {
         const u32x4_t b = (kok && bok[j]) ? ld16(bx[j] + k0) : zero;
@@ -150,7 +165,7 @@ ffn_gate_up_stream(const FfnGroups p) {
   }
 }
 
-template <int NTT>
+template <int NTT, int LAYOUT>
 __global__ void __launch_bounds__(256)
 ffn_down_stream(const FfnGroups p) {
   const GroupView v = group_view(p, blockIdx.y);
@@ -161,8 +176,8 @@ ffn_down_stream(const FfnGroups p) {
   if (i0 >= d) return;
   const int K = v.Hg;
   const int ar = lane & 15, kq = lane >> 4;
-  const int irow = (i0 + ar < d) ? i0 + ar : d - 1;
-  const uint16_t* aw = v.wd + (size_t)irow * K + kq * 8;
+  int ws;
+  const uint16_t* aw = frag_base<LAYOUT>(v.wd, i0, d, K, lane, &ws);
 
   for (int tt = 0; tt < v.n; tt += 16 * NTT) {
     const uint16_t* bh[NTT];
@@ -181,7 +196,7 @@ ffn_down_stream(const FfnGroups p) {
     for (; k0 + 32 * kUnroll <= K; k0 += 32 * kUnroll) {
       u32x4_t a[kUnroll], b[kUnroll][NTT];
 #pragma unroll
-      for (int s = 0; s < kUnroll; ++s) a[s] = ld16_stream(aw + k0 + 32 * s);
+      for (int s = 0; s < kUnroll; ++s) a[s] = ld16_stream(aw + (size_t)(k0 / 32 + s) * ws);
 #pragma unroll
       for (int s = 0; s < kUnroll; ++s)
 #pragma unroll
@@ -193,7 +208,7 @@ ffn_down_stream(const FfnGroups p) {
     }
     for (; k0 < K; k0 += 32) {
       const bool kok = k0 + kq * 8 < K;
-      const u32x4_t a = kok ? ld16_stream(aw + k0) : zero;
+      const u32x4_t a = kok ? ld16_stream(aw + (size_t)(k0 / 32) * ws) : zero;
 #pragma unroll
       for (int j = 0; j < NTT; ++j) {
         const u32x4_t b = (kok && bok[j]) ? ld16(bh[j] + k0) : zero;
@@ -300,13 +315,19 @@ FfnPath ffn_path(const FfnGroups& g) {
 
 hipError_t launch_ffn_gate_up_stream(const FfnGroups& g, hipStream_t stream) {
   dim3 grid((hmax(g) + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
-  hipLaunchKernelGGL(ffn_gate_up_stream<1>, grid, dim3(256), 0, stream, g);
+  if (g.layout == kFrag16)
+    hipLaunchKernelGGL((ffn_gate_up_stream<1, kFrag16>), grid, dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL((ffn_gate_up_stream<1, kRowMajor>), grid, dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 
 hipError_t launch_ffn_down_stream(const FfnGroups& g, hipStream_t stream) {
   dim3 grid((g.d + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
-  hipLaunchKernelGGL(ffn_down_stream<1>, grid, dim3(256), 0, stream, g);
+  if (g.layout == kFrag16)
+    hipLaunchKernelGGL((ffn_down_stream<1, kFrag16>), grid, dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL((ffn_down_stream<1, kRowMajor>), grid, dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -328,15 +349,15 @@ const char* ffn_schedule_kernel_name(const FfnGroups& g) {
 const char* ffn_gate_up_kernel_name(const FfnGroups& g) {
   switch (ffn_path(g)) {
     case kPathF32: return "ffn_gate_up_f32";
-    case kPathStream: return "ffn_gate_up_stream<1>";
-    default: return "grouped_gemm_kernel<0>";
+    case kPathStream: return g.layout == kFrag16 ? "ffn_gate_up_stream<1, 1>" : "ffn_gate_up_stream<1, 0>";
+    default: return g.layout == kFrag16 ? "grouped_gemm_kernel<0, 1>" : "grouped_gemm_kernel<0, 0>";
   }
 }
 const char* ffn_down_kernel_name(const FfnGroups& g) {
   switch (ffn_path(g)) {
     case kPathF32: return "ffn_down_f32";
-    case kPathStream: return "ffn_down_stream<1>";
-    default: return "grouped_gemm_kernel<1>";
+    case kPathStream: return g.layout == kFrag16 ? "ffn_down_stream<1, 1>" : "ffn_down_stream<1, 0>";
+    default: return g.layout == kFrag16 ? "grouped_gemm_kernel<1, 1>" : "grouped_gemm_kernel<1, 0>";
   }
 }
 

@@ -34,8 +34,20 @@ hipError_t launch_permute_scatter(const int32_t* topk_idx, long long rows, int E
 // A set of expert groups: routed groups 0..E-1 take rows [offsets[g], offsets[g+1]) of the
 // dispatched order (source token perm_src[r] / k, or r when perm_src is NULL); the optional
 // shared group (index E) takes rows [shared_row0, shared_row0 + T) with source token r - row0.
+enum WeightLayout { kRowMajor = 0, kFrag16 = 1 };
+
+// Offset (elements) of element (r, c) of a [rows, cols] matrix in the fragment-tiled layout:
+// 16 x 32 blocks along each 16-row band; inside a block, 64 lanes x 8 consecutive columns in the
+// A-operand order of the 16x16x32 MFMA (lane = r%16 + 16 * ((c%32)/8)).
+__host__ __device__ inline size_t frag16_offset(size_t r, size_t c, size_t cols) {
+  return ((r / 16) * (cols / 32) + c / 32) * 512 + ((r % 16) + 16 * ((c % 32) / 8)) * 8 + c % 8;
+}
+
+hipError_t launch_pack_weights(const void* src, void* dst, long long n_mats, int rows, int cols, hipStream_t stream);
+
 struct FfnGroups {
   int dtype;
+  int layout;                  // WeightLayout of the expert weights
   int d;                       // model width
   int E;                       // routed groups
   int k;                       // slots per token (perm_src divisor)

@@ -53,6 +53,12 @@ moe_status check_shape(const moe_shape* s) {
   if (s->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
   if ((long long)s->T * s->top_k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (s->d_model % 8 || s->d_hidden % 8 || s->d_shared_hidden % 8) return MOE_ERR_ALIGNMENT;
+  if (s->weight_layout != MOE_LAYOUT_ROWMAJOR && s->weight_layout != MOE_LAYOUT_FRAG16) return MOE_ERR_UNSUPPORTED;
+  if (s->weight_layout == MOE_LAYOUT_FRAG16) {
+    // every expert matrix ([H, d], [d, H], [Hs, d], [d, Hs]) must tile into 16 x 32 blocks
+    if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (s->d_model % 32 || s->d_hidden % 32 || s->d_shared_hidden % 32) return MOE_ERR_ALIGNMENT;
+  }
   return MOE_OK;
 }
 
@@ -132,6 +138,7 @@ moe::FfnGroups groups_for(const moe_shape& s, const void* x, const int32_t* perm
                           const void* sd, void* hid, void* y) {
   moe::FfnGroups g{};
   g.dtype = s.dtype;
+  g.layout = s.weight_layout;
   g.d = s.d_model;
   g.E = s.n_experts;
   g.k = s.top_k;
@@ -248,6 +255,19 @@ const char* moe_status_string(moe_status st) {
     case MOE_ERR_HIP: return "HIP launch failed";
   }
   return "unknown status";
+}
+
+moe_status moe_pack_weights(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols, void* stream) {
+  if (n_mats < 0 || rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
+  if (rows % 16 || cols % 32) return MOE_ERR_ALIGNMENT;
+  if (n_mats == 0 || rows == 0 || cols == 0) return MOE_OK;
+  MOE_TRY(need(src, 16));
+  MOE_TRY(need(dst, 16));
+  const uintptr_t bytes = (uintptr_t)n_mats * (uintptr_t)rows * (uintptr_t)cols * 2;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;  // overlapping buffers
+  MOE_LAUNCH(moe::launch_pack_weights(src, dst, n_mats, rows, cols, (hipStream_t)stream));
+  return MOE_OK;
 }
 
 moe_status moe_route(const moe_shape* s, const void* x, const void* w_router, const float* logit_bias,

@@ -133,7 +133,7 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 }
 
 const char* route_logits_kernel_name(int dtype, int T, int) {
-  if (dtype == kBF16 && T >= kRouterGemmMinTokens) return "grouped_gemm_kernel<2>";
+  if (dtype == kBF16 && T >= kRouterGemmMinTokens) return "grouped_gemm_kernel<2, 0>";
   return dtype == kBF16 ? "route_logits_valu<1>" : "route_logits_valu<0>";
 }
 const char* route_topk_kernel_name() { return "route_topk_kernel"; }

@@ -42,11 +42,12 @@ class DeviceLayer:
     ws_up: torch.Tensor | None
     ws_down: torch.Tensor | None
     stacked_host: tuple | None   # host copies of all expert weights (small layers only)
+    layout: int = moe.MOE_LAYOUT_ROWMAJOR
 
     @property
     def shape(self):
         c = self.cfg
-        return moe.make_shape(c.T, c.d, c.E, c.k, c.H, c.Hs, c.dtype)
+        return moe.make_shape(c.T, c.d, c.E, c.k, c.H, c.Hs, c.dtype, self.layout)
 
     def expert_fn(self, cache=True):
         return helpers.expert_fn_host(self.cfg, self.seed, self.stacked_host, cache=cache)
@@ -77,17 +78,29 @@ def make_weights(cfg: synth.LayerConfig, seed: int, host_copy: bool):
     return dev, shared, stacked
 
 
-def make_layer(cfg: synth.LayerConfig, seed: int = 0, screen: bool = True, weights=None) -> DeviceLayer:
+def packed_weights(weights):
+    """The same weights in the fragment-tiled layout (device copies)."""
+    (g, u, dn), shared, stacked = weights
+    sh = tuple(shared) if shared[0] is not None else None
+    out = moe.pack_expert_weights(g, u, dn, sh)
+    torch.cuda.synchronize()
+    return (tuple(out[:3]), tuple(out[3:]) if sh else (None, None, None), stacked)
+
+
+def make_layer(cfg: synth.LayerConfig, seed: int = 0, screen: bool = True, weights=None,
+               layout: int = moe.MOE_LAYOUT_ROWMAJOR) -> DeviceLayer:
     host = synth.host_small_inputs(cfg, seed)
     if screen:
         helpers.screen_gaps(host)
     small = cfg.E * cfg.H * cfg.d <= 64 * 1024 * 1024
     if weights is None:
         weights = make_weights(cfg, seed, host_copy=small)
+        if layout == moe.MOE_LAYOUT_FRAG16:
+            weights = packed_weights(weights)
     (g, u, dn), (sg, su, sd), stacked = weights
     bias = torch.from_numpy(host.logit_bias).cuda() if host.logit_bias is not None else None
     return DeviceLayer(cfg, seed, host, to_dev(host.x, cfg.dtype), to_dev(host.w_router, cfg.dtype), bias,
-                       g, u, dn, sg, su, sd, stacked)
+                       g, u, dn, sg, su, sd, stacked, layout)
 
 
 @dataclass

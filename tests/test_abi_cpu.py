@@ -129,8 +129,10 @@ def test_status_strings_and_stage_names():
     names = [moe.moe_stage_kernel_name(s, i) for i in range(moe.MOE_NUM_STAGES)]
     assert names[5] == "" and "gate_up" in names[6] and "down" in names[7]     # decode: GEMV, no schedule
     names = [moe.moe_stage_kernel_name(dsv3(T=8192), i) for i in range(moe.MOE_NUM_STAGES)]
-    assert names[0] == "grouped_gemm_kernel<2>" and names[5] == "gemm_schedule_kernel"
-    assert names[6] == "grouped_gemm_kernel<0>" and names[7] == "grouped_gemm_kernel<1>"
+    assert names[0] == "grouped_gemm_kernel<2, 0>" and names[5] == "gemm_schedule_kernel"
+    assert names[6] == "grouped_gemm_kernel<0, 0>" and names[7] == "grouped_gemm_kernel<1, 0>"
+    packed = dsv3(T=8, weight_layout=moe.MOE_LAYOUT_FRAG16)
+    assert moe.moe_stage_kernel_name(packed, 6) == "ffn_gate_up_stream<1, 1>"
     assert moe.moe_stage_kernel_name(dsv3(top_k=0), 0) == ""
 
 
@@ -140,3 +142,29 @@ def test_empty_batch_accepts_null_tensors():
     assert status_of(moe.moe_combine, s, None, None, None, None, None, 0) == moe.MOE_OK
     # an invalid shape is still reported when T == 0
     assert status_of(moe.moe_layer_forward, dsv3(T=0, top_k=0), **layer(s)) == moe.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("shape,status", [
+    (dict(weight_layout=7), moe.MOE_ERR_UNSUPPORTED),
+    (dict(weight_layout=moe.MOE_LAYOUT_FRAG16, dtype=moe.MOE_F32), moe.MOE_ERR_UNSUPPORTED),
+    (dict(weight_layout=moe.MOE_LAYOUT_FRAG16, d_model=7176), moe.MOE_ERR_ALIGNMENT),
+    (dict(weight_layout=moe.MOE_LAYOUT_FRAG16, d_hidden=2056), moe.MOE_ERR_ALIGNMENT),
+    (dict(weight_layout=moe.MOE_LAYOUT_FRAG16, d_shared_hidden=2056), moe.MOE_ERR_ALIGNMENT),
+    (dict(weight_layout=moe.MOE_LAYOUT_FRAG16), moe.MOE_ERR_HIP),   # valid: reaches the launch (no GPU here)
+])
+def test_weight_layout_validation(shape, status):
+    s = dsv3(**shape)
+    if status == moe.MOE_ERR_HIP:
+        assert moe.moe_workspace_bytes(s) > 0
+        return
+    assert status_of(moe.moe_layer_forward, s, **layer(s)) == status
+
+
+def test_pack_weights_validation():
+    assert status_of(moe.moe_pack_weights, A, B, 2, 24, 64) == moe.MOE_ERR_ALIGNMENT
+    assert status_of(moe.moe_pack_weights, A, B, 2, 32, 48) == moe.MOE_ERR_ALIGNMENT
+    assert status_of(moe.moe_pack_weights, A, A + 1024, 2, 32, 64) == moe.MOE_ERR_INVALID_ARG   # overlap
+    assert status_of(moe.moe_pack_weights, None, B, 2, 32, 64) == moe.MOE_ERR_INVALID_ARG
+    assert status_of(moe.moe_pack_weights, A + 8, B, 2, 32, 64) == moe.MOE_ERR_ALIGNMENT
+    assert status_of(moe.moe_pack_weights, A, B, 0, 32, 64) == moe.MOE_OK
+    assert status_of(moe.moe_pack_weights, A, B, -1, 32, 64) == moe.MOE_ERR_INVALID_ARG

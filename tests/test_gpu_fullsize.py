@@ -17,6 +17,8 @@ import synth
 from tests import gpu_util as G
 from tests.test_gpu_parity import check_logits_close, check_routing_on_gpu_logits
 
+import sparse_moe_layer_router_amd as moe
+
 pytestmark = pytest.mark.gpu
 
 
@@ -24,7 +26,7 @@ pytestmark = pytest.mark.gpu
 def dsv3_weights():
     cfg = synth.CONFIG_BY_NAME["dsv3_decode_t8"]
     w = G.make_weights(cfg, 0, host_copy=False)
-    yield w
+    yield {moe.MOE_LAYOUT_ROWMAJOR: w, moe.MOE_LAYOUT_FRAG16: G.packed_weights(w)}
     del w
     torch.cuda.empty_cache()
 
@@ -42,11 +44,12 @@ def sample_tokens(T, n, seed=0):
     return np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=n - 2, replace=False)]))
 
 
+@pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_FRAG16, moe.MOE_LAYOUT_ROWMAJOR], ids=["frag16", "rowmajor"])
 @pytest.mark.parametrize("name,n_sample", [("dsv3_decode_t8", None), ("dsv3_decode_t256", 12),
                                            ("dsv3_prefill_t8192", 8)])
-def test_dsv3_layer(name, n_sample, dsv3_weights):
+def test_dsv3_layer(name, n_sample, layout, dsv3_weights):
     cfg = synth.CONFIG_BY_NAME[name]
-    L = G.make_layer(cfg, weights=dsv3_weights)
+    L = G.make_layer(cfg, weights=dsv3_weights[layout], layout=layout)
     print(f"[{name}] gap-screen redraws: {sum(L.host.redraws.values())}", flush=True)
     r = G.run_layer(L)
     check_logits_close(L, r)
@@ -55,9 +58,10 @@ def test_dsv3_layer(name, n_sample, dsv3_weights):
     sampled_check(L, r, tokens)
 
 
-def test_skewed_mixtral_layer():
+@pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_FRAG16, moe.MOE_LAYOUT_ROWMAJOR], ids=["frag16", "rowmajor"])
+def test_skewed_mixtral_layer(layout):
     cfg = synth.CONFIG_BY_NAME["skewed_mixtral_t4096"]
-    L = G.make_layer(cfg)
+    L = G.make_layer(cfg, layout=layout)
     r = G.run_layer(L)
     counts = r.counts.cpu().numpy()
     print(f"[skewed] expert counts {counts.tolist()}", flush=True)

@@ -197,3 +197,44 @@ def test_device_generator_matches_host_bits():
     host = synth.normal_host((3, 100_003), 0, synth.stream_id(synth.K_GATE, 17), synth.weight_std(cfg.d), "bf16",
                              nblk=3)
     assert np.array_equal(dev.view(torch.int16).cpu().numpy().view(np.uint16), host.reshape(-1))
+
+
+# ------------------------------------------------------------------ fragment-tiled weights
+
+def frag16_reference(w: np.ndarray) -> np.ndarray:
+    """The packed layout built by array reshaping: [R, C] -> bands of 16 rows, blocks of 32
+    columns, inside a block (chunk of 8 columns, row in band, 8 columns) -- lane = row + 16 chunk."""
+    R, C = w.shape
+    return w.reshape(R // 16, 16, C // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+
+
+@pytest.mark.parametrize("n,rows,cols", [(1, 16, 32), (3, 48, 96), (2, 2048, 7168 // 4)])
+def test_pack_weights_bit_exact(n, rows, cols):
+    rng = np.random.default_rng(rows + cols)
+    w = rng.integers(0, 1 << 16, size=(n, rows, cols), dtype=np.uint16)
+    src = torch.from_numpy(w.view(np.int16)).cuda()
+    dst = torch.empty_like(src)
+    moe.moe_pack_weights(src, dst, n, rows, cols)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(np.uint16).reshape(n, -1)
+    for m in range(n):
+        np.testing.assert_array_equal(got[m], frag16_reference(w[m]))
+
+
+PACKABLE = [c for c in MID if c.dtype == "bf16" and c.d % 32 == 0 and c.H % 32 == 0 and c.Hs % 32 == 0]
+
+
+@pytest.mark.parametrize("cfg", PACKABLE, ids=lambda c: c.name)
+def test_layer_matches_oracle_packed_weights(cfg):
+    L = G.make_layer(cfg, layout=moe.MOE_LAYOUT_FRAG16)
+    r = G.run_layer(L)
+    check_routing_on_gpu_logits(L, r)
+    x, wg, b = G.oracle_inputs(L)
+    ref = oracle.layer_forward(x, wg, cfg.k, L.expert_fn(), L.shared_fn(), b)
+    np.testing.assert_array_equal(np.sort(r.idx.cpu().numpy(), 1), np.sort(ref["idx"], 1))
+    ok, err, bound = G.tolerance_ok(G.to_f64(r.out), ref["out"])
+    assert ok, (err, bound)
+    # same bits as the row-major path (same kernels' arithmetic, only the operand addressing differs)
+    Lr = G.make_layer(cfg)
+    rr = G.run_layer(Lr)
+    assert torch.equal(r.out.view(torch.int16), rr.out.view(torch.int16))
