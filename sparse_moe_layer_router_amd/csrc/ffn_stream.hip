@@ -35,7 +35,10 @@ struct GroupView {
   bool routed;
 };
 
-__device__ __forceinline__ GroupView group_view(const FfnGroups& p, int g) {
+// Group g < E is routed expert g. The shared expert's T rows are cut into chunks of `chunk` rows,
+// one group each (g = E + c): every chunk streams the shared weights once for its own tokens, and
+// the chunks run side by side instead of one group re-streaming the weights for every token tile.
+__device__ __forceinline__ GroupView group_view(const FfnGroups& p, int g, int chunk) {
   GroupView v;
   if (g < p.E) {
     // clamp to [0, rows] so inconsistent offsets can never address outside the row buffers
@@ -53,8 +56,8 @@ __device__ __forceinline__ GroupView group_view(const FfnGroups& p, int g) {
     v.y = (uint16_t*)p.y;
     v.routed = true;
   } else {
-    v.r0 = 0;
-    v.n = p.T;
+    v.r0 = (long long)(g - p.E) * chunk;
+    v.n = (int)(p.T - v.r0 < chunk ? p.T - v.r0 : chunk);
     v.Hg = p.Hs;
     v.wg = (const uint16_t*)p.ws_gate;
     v.wu = (const uint16_t*)p.ws_up;
@@ -94,7 +97,7 @@ __device__ __forceinline__ const uint16_t* frag_base(const uint16_t* w, int r0, 
 template <int NTT, int LAYOUT>
 __global__ void __launch_bounds__(256)
 ffn_gate_up_stream(const FfnGroups p) {
-  const GroupView v = group_view(p, blockIdx.y);
+  const GroupView v = group_view(p, blockIdx.y, 16 * NTT);
   if (v.n <= 0) return;
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int h0 = blockIdx.x * kRowsPerBlock + wave * 16;
@@ -168,7 +171,7 @@ ffn_gate_up_stream(const FfnGroups p) {
 template <int NTT, int LAYOUT>
 __global__ void __launch_bounds__(256)
 ffn_down_stream(const FfnGroups p) {
-  const GroupView v = group_view(p, blockIdx.y);
+  const GroupView v = group_view(p, blockIdx.y, 16 * NTT);
   if (v.n <= 0) return;
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int d = p.d;
@@ -303,7 +306,8 @@ ffn_down_f32(const FfnGroups p) {
 
 // --------------------------------------------------------------------------------- launchers
 namespace {
-int groups_of(const FfnGroups& g) { return g.E + (g.Hs > 0 ? 1 : 0); }
+// routed groups + one group per 16-row chunk of the shared expert (NTT = 1)
+int groups_of(const FfnGroups& g) { return g.E + (g.Hs > 0 ? (g.T + 15) / 16 : 0); }
 int hmax(const FfnGroups& g) { return g.H > g.Hs ? g.H : g.Hs; }
 long long all_rows(const FfnGroups& g) { return g.rows + (g.Hs > 0 ? g.T : 0); }
 }  // namespace
