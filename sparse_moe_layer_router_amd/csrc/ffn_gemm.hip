@@ -8,14 +8,19 @@
 // expert, each expert's weights are loaded once and reused across its whole bucket of tokens.
 //
 // Tiles: BM = 128 rows (tokens) x BN weight rows per B matrix x BK = 32 along K; 512 threads as
-// 2 x 4 waves (two per SIMD, so one wave's LDS or barrier wait is covered by the other's MFMAs),
-// wave (wm, wn) owning rows [64 wm, 64 wm + 64) x BN/4 columns of every B matrix as 32x32x16 MFMA
-// blocks. Gate and up projections are computed by the same block for the same rows (two B tiles),
-// so SiLU(g) * u is formed in registers and the hidden activation leaves as bf16. Operands go
-// straight from global memory into a three-slice LDS ring (global_load_lds, 16 bytes per lane, no
-// register staging): while slice kt is multiplied, slices kt+1 and kt+2 are in flight, and waves
-// wait (s_waitcnt vmcnt) only for slice kt itself. A 16-byte-chunk XOR swizzle keeps MFMA
-// fragment reads bank-conflict free.
+// 2 x 4 waves (two per SIMD), wave (wm, wn) owning rows [64 wm, 64 wm + 64) x BN/4 columns of
+// every B matrix as 32x32x16 MFMA blocks: 8 MFMAs per 16-wide K step from 2 A and 4 B fragments,
+// 128 accumulator registers per wave, which leaves room for double-buffered fragments at two
+// waves per SIMD. Gate and up projections are computed by the same block for the same rows (two B
+// tiles), so SiLU(g)*u is formed in registers and the hidden activation leaves as bf16.
+//
+// Operands go straight from global memory into a three-slice LDS ring (global_load_lds, 16 bytes
+// per lane, no register staging); waves wait (s_waitcnt vmcnt) only for the slice they need next,
+// with two slices in flight. Fragments are double-buffered in registers across K steps: while the
+// MFMAs of step j run, the LDS reads of step j+1 are issued between them (scheduling groups pin
+// one read after each of the first MFMAs), so LDS latency hides behind matrix work. The
+// slice barrier sits between the two steps of a slice. A 16-byte-chunk XOR swizzle (activations)
+// and the fragment-tiled weight layout keep fragment reads bank-conflict free.
 //
 // Tile order: tiles are numbered expert by expert, N-tile by N-tile, with the M-tiles of one
 // (expert, N-tile) adjacent. Workgroups are dealt round-robin to the 8 XCDs, so block L runs tile
@@ -34,7 +39,7 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kWavesM = 2, kWavesN = 4;
 constexpr int kXcds = 8;
-constexpr int kStages = 3;
+constexpr int kStages = 3;   // LDS ring depth: kStages-1 slices in flight (a 4th slice measured no faster)
 constexpr int kRowBytes = BK * 2;  // one tile row in LDS: 64 bytes = 4 chunks of 16
 
 enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2 };
@@ -60,6 +65,49 @@ template <int MODE> struct Geo {
 // rows, one chunk column) touches distinct 16-byte bank groups.
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 2)) & 3); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + (swz_chunk(row, chunk) << 4); }
+
+// LDS reads of one 16-wide K step: the wave's MBLK A fragments (rows wm*WM + 32*mb + fr) and the
+// NB x NBLK B fragments (rows wn*WN + 32*nb + fr of each B tile), chunk column ch.
+template <class G, int LAYOUT>
+__device__ __forceinline__ void load_frags(u32x4_t (&fa)[G::MBLK], u32x4_t (&fb)[G::NB][G::NBLK], const uint8_t* sa,
+                                           const uint8_t* sb, int wm, int wn, int fr, int ch) {
+#pragma unroll
+  for (int mb = 0; mb < G::MBLK; ++mb) fa[mb] = *(const u32x4_t*)(sa + swz(wm * G::WM + mb * 32 + fr, ch));
+#pragma unroll
+  for (int b = 0; b < G::NB; ++b)
+#pragma unroll
+    for (int nb = 0; nb < G::NBLK; ++nb) {
+      const int n = wn * G::WN + nb * 32 + fr;   // row inside B matrix b's tile
+      if (LAYOUT == kFrag16)  // block n/16 of matrix b; lane position (n%16) + 16*chunk
+        fb[b][nb] = *(const u32x4_t*)(sb + (b * (G::BN / 16) + n / 16) * 1024 + ((n & 15) + 16 * ch) * 16);
+      else
+        fb[b][nb] = *(const u32x4_t*)(sb + swz(b * G::BN + n, ch));
+    }
+}
+
+template <class G>
+__device__ __forceinline__ void mma_step(f32x16_t (&acc)[G::NB][G::MBLK][G::NBLK], const u32x4_t (&fa)[G::MBLK],
+                                         const u32x4_t (&fb)[G::NB][G::NBLK]) {
+#pragma unroll
+  for (int b = 0; b < G::NB; ++b)
+#pragma unroll
+    for (int nb = 0; nb < G::NBLK; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < G::MBLK; ++mb) acc[b][mb][nb] = mfma32x32x16(fa[mb], fb[b][nb], acc[b][mb][nb]);
+}
+
+// Pin the order of the instructions just emitted: MFMA, LDS read, MFMA, LDS read, ... and then the
+// remaining MFMAs, so each LDS read issues under an MFMA instead of in a block before them.
+template <int MFMAS, int READS>
+__device__ __forceinline__ void interleave_mfma_lds() {
+  static_assert(READS <= MFMAS, "one LDS read after each of the first READS MFMAs");
+#pragma unroll
+  for (int i = 0; i < READS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  if (MFMAS > READS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
+}
 
 }  // namespace
 
@@ -310,52 +358,47 @@ grouped_gemm_kernel(const GemmArgs ga) {
 
   const int fr = lane & 31, fh = lane >> 5;   // fragment row / k-half of this lane
   const int wm = wv / kWavesN, wn = wv % kWavesN;
-  auto compute = [&](int buf) {
-    const uint8_t* sa = smem[buf];
-    const uint8_t* sb = smem[buf] + G::A_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = kk * 2 + fh;
-      u32x4_t af[G::MBLK], bf[G::NB][G::NBLK];
-#pragma unroll
-      for (int mb = 0; mb < G::MBLK; ++mb) af[mb] = *(const u32x4_t*)(sa + swz(wm * G::WM + mb * 32 + fr, ch));
-#pragma unroll
-      for (int b = 0; b < G::NB; ++b)
-#pragma unroll
-        for (int nb = 0; nb < G::NBLK; ++nb) {
-          const int n = wn * G::WN + nb * 32 + fr;   // row inside B matrix b's tile
-          if (LAYOUT == kFrag16)  // block n/16 of matrix b; lane position (n%16) + 16*chunk
-            bf[b][nb] = *(const u32x4_t*)(sb + (b * (G::BN / 16) + n / 16) * 1024 + ((n & 15) + 16 * ch) * 16);
-          else
-            bf[b][nb] = *(const u32x4_t*)(sb + swz(b * G::BN + n, ch));
-        }
-#pragma unroll
-      for (int b = 0; b < G::NB; ++b)
-#pragma unroll
-        for (int nb = 0; nb < G::NBLK; ++nb)
-#pragma unroll
-          for (int mb = 0; mb < G::MBLK; ++mb) acc[b][mb][nb] = mfma32x32x16(af[mb], bf[b][nb], acc[b][mb][nb]);
-    }
-  };
+  constexpr int kMfmas = G::NB * G::NBLK * G::MBLK;          // per K step
+  constexpr int kReads = G::MBLK + G::NB * G::NBLK;          // per K step
 
-  // Pipeline over K slices: slices kt+1 and kt+2 are in flight while slice kt is multiplied.
-  // Each wave waits for its own loads of slice kt (vmcnt counts this wave's loads in issue order,
-  // G::LOADS per slice), then the barrier makes every wave's slice kt visible and guarantees that
-  // slice kt-1, whose buffer the loads of slice kt+2 overwrite, is no longer being read.
+  // Slice kt waits for its own loads, then a barrier: every wave's part of slice kt is visible and
+  // no wave still reads the buffer that the loads of slice kt+kStages-1 (issued right after)
+  // overwrite. Loads complete in issue order, so waiting for slice kt means allowing the loads of
+  // the later slices already issued (up to kStages-2 of them) to stay outstanding.
   const int nk = (K + BK - 1) / BK;
-  issue(0, 0);
-  if (nk > 1) issue(1, 1);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt % kStages;
-    if (kt + 1 < nk) {
+  auto arrive = [&](int kt) {
+    const int later = nk - 1 - kt < kStages - 2 ? nk - 1 - kt : kStages - 2;  // slices issued after kt
+    static_assert(kStages >= 2 && kStages <= 4, "vmcnt cases below");
+    if (later >= 2) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::LOADS) : "memory");
+    } else if (later == 1) {
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::LOADS) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (K % BK) zero_tail(kt, buf);
     }
+    if (kt == nk - 1 && (K % BK)) zero_tail(kt, kt % kStages);  // its loads have all landed here
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kt + 2 < nk) issue(kt + 2, (kt + 2) % kStages);
-    compute(buf);
+    if (kt + kStages - 1 < nk) issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
+  };
+
+  static_assert(BK / 16 == 2, "the loop below is written for two K steps per slice");
+  u32x4_t fa0[G::MBLK], fb0[G::NB][G::NBLK], fa1[G::MBLK], fb1[G::NB][G::NBLK];
+  for (int i = 0; i < kStages - 1 && i < nk; ++i) issue(i, i);
+  arrive(0);
+  load_frags<G, LAYOUT>(fa0, fb0, smem[0], smem[0] + G::A_BYTES, wm, wn, fr, fh);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt % kStages;
+    // step 0 of slice kt: multiply fragments 0 while reading step 1 into fragments 1
+    mma_step<G>(acc, fa0, fb0);
+    load_frags<G, LAYOUT>(fa1, fb1, smem[buf], smem[buf] + G::A_BYTES, wm, wn, fr, 2 + fh);
+    interleave_mfma_lds<kMfmas, kReads>();
+    // step 1 of slice kt: multiply fragments 1 while reading step 0 of slice kt+1 into fragments 0
+    // (after the last slice that read re-reads the current buffer and is never used)
+    if (kt + 1 < nk) arrive(kt + 1);
+    const int nbuf = kt + 1 < nk ? (kt + 1) % kStages : buf;
+    mma_step<G>(acc, fa1, fb1);
+    load_frags<G, LAYOUT>(fa0, fb0, smem[nbuf], smem[nbuf] + G::A_BYTES, wm, wn, fr, fh);
+    interleave_mfma_lds<kMfmas, kReads>();
   }
 
   // ---- epilogue: lane holds column n = fr of each 32x32 block, rows (e/4)*8 + fh*4 + e%4 --------
