@@ -14,9 +14,10 @@
 // waves per SIMD. Gate and up projections are computed by the same block for the same rows (two B
 // tiles), so SiLU(g)*u is formed in registers and the hidden activation leaves as bf16.
 //
-// Operands go straight from global memory into a three-slice LDS ring (global_load_lds, 16 bytes
-// per lane, no register staging); waves wait (s_waitcnt vmcnt) only for the slice they need next,
-// with two slices in flight. Fragments are double-buffered in registers across K steps: while the
+// Operands go straight from global memory into a four-slice LDS ring (global_load_lds, 16 bytes
+// per lane, no register staging), the loads of each slice spread over the MFMAs of the two K steps
+// after the barrier that frees its buffer; waves wait (s_waitcnt vmcnt) only for the slice they
+// need next, with two further slices in flight. Fragments are double-buffered in registers across K steps: while the
 // MFMAs of step j run, the LDS reads of step j+1 are issued between them (scheduling groups pin
 // one read after each of the first MFMAs), so LDS latency hides behind matrix work. The
 // slice barrier sits between the two steps of a slice. A 16-byte-chunk XOR swizzle (activations)
@@ -39,7 +40,7 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kWavesM = 2, kWavesN = 4;
 constexpr int kXcds = 8;
-constexpr int kStages = 3;   // LDS ring depth: kStages-1 slices in flight (a 4th slice measured no faster)
+constexpr int kStages = 4;   // LDS ring depth (4 x 40 KB = all 160 KB of LDS): two slices fully in flight
 constexpr int kRowBytes = BK * 2;  // one tile row in LDS: 64 bytes = 4 chunks of 16
 
 enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2 };
@@ -107,6 +108,20 @@ __device__ __forceinline__ void interleave_mfma_lds() {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
   }
   if (MFMAS > READS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
+}
+
+// The same with VMEMS global-to-LDS loads after each of the last VMEMS MFMAs. The loads write LDS
+// that the compiler cannot tell apart from the buffer being read, so they stay after the reads
+// (their program order): MFMA, read, ..., MFMA, read, load, ..., MFMA, load.
+template <int MFMAS, int READS, int VMEMS>
+__device__ __forceinline__ void interleave_mfma_lds_vmem() {
+  static_assert(READS <= MFMAS && VMEMS <= MFMAS, "at most one read and one load after each MFMA");
+#pragma unroll
+  for (int i = 0; i < MFMAS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // one MFMA
+    if (i < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);           // one LDS read
+    if (i >= MFMAS - VMEMS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
+  }
 }
 
 }  // namespace
@@ -305,6 +320,7 @@ grouped_gemm_kernel(const GemmArgs ga) {
     }
   }
 
+  const int nk = (K + BK - 1) / BK;  // K slices
   typedef __attribute__((address_space(3))) void lds_t;
   // LDS byte offsets (wave-uniform) of this wave's instruction i inside a slice
   auto a_dst = [&](int i) { return (wv * (BM / kWaves) + i * 16) * kRowBytes; };
@@ -312,19 +328,25 @@ grouped_gemm_kernel(const GemmArgs ga) {
     return LAYOUT == kFrag16 ? G::A_BYTES + (wv * G::B_LOADS + i) * 1024
                              : G::A_BYTES + (wv * (G::NB * G::BN / kWaves) + i * 16) * kRowBytes;
   };
-  auto issue = [&](int kt, int buf) {
-    const int k0 = kt * BK;
+  // Loads j in [J0, J1) of slice kt (A loads first, then B loads) into ring buffer `buf`. A slice
+  // index past the end is clamped to the last slice: such loads fill a buffer that is never read
+  // again, which keeps the number of loads per slice fixed for the vmcnt arithmetic below.
+  auto issue = [&](int kt, int buf, int j0, int j1) {
+    const int kc = kt < nk ? kt : nk - 1;
+    const int k0 = kc * BK;
 #pragma unroll
     for (int i = 0; i < G::A_LOADS; ++i) {
+      if (i < j0 || i >= j1) continue;
       const int k = k0 + a_kc[i];
       const uint16_t* src = a_src[i] + (k < K ? k : 0);    // out-of-range chunks are zeroed after landing
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_t*)(smem[buf] + a_dst(i)), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < G::B_LOADS; ++i) {
+      if (G::A_LOADS + i < j0 || G::A_LOADS + i >= j1) continue;
       const uint16_t* src;
       if (LAYOUT == kFrag16) {
-        src = b_src[i] + (size_t)kt * 512;  // K is a multiple of 32 in this layout: no tail
+        src = b_src[i] + (size_t)kc * 512;  // K is a multiple of 32 in this layout: no tail
       } else {
         const int k = k0 + b_kc[i];
         src = b_src[i] + (k < K ? k : 0);
@@ -361,45 +383,57 @@ grouped_gemm_kernel(const GemmArgs ga) {
   constexpr int kMfmas = G::NB * G::NBLK * G::MBLK;          // per K step
   constexpr int kReads = G::MBLK + G::NB * G::NBLK;          // per K step
 
-  // Slice kt waits for its own loads, then a barrier: every wave's part of slice kt is visible and
-  // no wave still reads the buffer that the loads of slice kt+kStages-1 (issued right after)
-  // overwrite. Loads complete in issue order, so waiting for slice kt means allowing the loads of
-  // the later slices already issued (up to kStages-2 of them) to stay outstanding.
-  const int nk = (K + BK - 1) / BK;
+  // Ring protocol (S = kStages). The loads of slice s go to buffer s % S and are issued in two
+  // parts spread over the MFMAs: part 1 (loads [0, kSplit)) during step 1 of slice s-S, part 2
+  // (the rest) during step 0 of slice s-S+1, both after the barrier that ends every wave's reads
+  // of slice s-S, the previous tenant of the buffer. Spreading them keeps the vector-memory issue
+  // queue from stalling all waves at once right after the barrier. Before step 1 of slice kt a
+  // wave waits for its loads of slice kt+1: slices kt+2 .. kt+S-1 have been issued in full by
+  // then and loads complete in issue order, so vmcnt((S-2) * LOADS) leaves exactly those
+  // outstanding. The barrier that follows makes every wave's part of slice kt+1 visible.
+  // Slices past the end are clamped copies of the last one (see issue); in the last step the
+  // buffer of slice kt+1 (free: its previous tenant was slice kt+1-S) takes them, since the
+  // current buffer may still be read by waves that are behind and no barrier follows.
+  constexpr int S = kStages;
+  static_assert(S >= 3, "the issue schedule below needs a ring of at least 3 slices");
+  constexpr int kSplit = (G::LOADS + 1) / 2;
+  constexpr int kAhead = (S - 2) * G::LOADS;   // loads allowed in flight when slice kt+1 must land
+  static_assert(kAhead + kSplit < 64, "vmcnt holds 6 bits");
   auto arrive = [&](int kt) {
-    const int later = nk - 1 - kt < kStages - 2 ? nk - 1 - kt : kStages - 2;  // slices issued after kt
-    static_assert(kStages >= 2 && kStages <= 4, "vmcnt cases below");
-    if (later >= 2) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::LOADS) : "memory");
-    } else if (later == 1) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::LOADS) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    if (kt == nk - 1 && (K % BK)) zero_tail(kt, kt % kStages);  // its loads have all landed here
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAhead) : "memory");
+    if (kt == nk - 1 && (K % BK)) zero_tail(kt, kt % S);  // its loads have all landed here
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kt + kStages - 1 < nk) issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
   };
 
   static_assert(BK / 16 == 2, "the loop below is written for two K steps per slice");
   u32x4_t fa0[G::MBLK], fb0[G::NB][G::NBLK], fa1[G::MBLK], fb1[G::NB][G::NBLK];
-  for (int i = 0; i < kStages - 1 && i < nk; ++i) issue(i, i);
-  arrive(0);
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) issue(i, i, 0, G::LOADS);
+  issue(S - 1, S - 1, 0, kSplit);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAhead + kSplit) : "memory");
+  if (nk == 1 && (K % BK)) zero_tail(0, 0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   load_frags<G, LAYOUT>(fa0, fb0, smem[0], smem[0] + G::A_BYTES, wm, wn, fr, fh);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt % kStages;
-    // step 0 of slice kt: multiply fragments 0 while reading step 1 into fragments 1
+    const int buf = kt % S;
+    // step 0 of slice kt: multiply fragments 0 while reading step 1 into fragments 1 and issuing
+    // part 2 of slice kt+S-1
     mma_step<G>(acc, fa0, fb0);
     load_frags<G, LAYOUT>(fa1, fb1, smem[buf], smem[buf] + G::A_BYTES, wm, wn, fr, 2 + fh);
-    interleave_mfma_lds<kMfmas, kReads>();
+    issue(kt + S - 1, (kt + S - 1) % S, kSplit, G::LOADS);
+    interleave_mfma_lds_vmem<kMfmas, kReads, G::LOADS - kSplit>();
     // step 1 of slice kt: multiply fragments 1 while reading step 0 of slice kt+1 into fragments 0
-    // (after the last slice that read re-reads the current buffer and is never used)
+    // and issuing part 1 of slice kt+S into this slice's buffer (after the last slice the reads
+    // re-read the current buffer and are never used)
     if (kt + 1 < nk) arrive(kt + 1);
-    const int nbuf = kt + 1 < nk ? (kt + 1) % kStages : buf;
+    const int nbuf = kt + 1 < nk ? (kt + 1) % S : buf;
+    const int lbuf = kt + 1 < nk ? buf : (kt + 1) % S;
     mma_step<G>(acc, fa1, fb1);
     load_frags<G, LAYOUT>(fa0, fb0, smem[nbuf], smem[nbuf] + G::A_BYTES, wm, wn, fr, fh);
-    interleave_mfma_lds<kMfmas, kReads>();
+    issue(kt + S, lbuf, 0, kSplit);
+    interleave_mfma_lds_vmem<kMfmas, kReads, kSplit>();
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still write LDS when the block exits
 
   // ---- epilogue: lane holds column n = fr of each 32x32 block, rows (e/4)*8 + fh*4 + e%4 --------
 #pragma unroll
