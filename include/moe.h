@@ -169,7 +169,8 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* w_ro
  */
 enum {
   MOE_STAGE_ROUTE_LOGITS = 0,
-  MOE_STAGE_ROUTE_TOPK = 1,
+  MOE_STAGE_ROUTE_TOPK = 1,   /* with T <= 16 and T*k <= 4096: top-k, softmax and the whole
+                                 dispatch in one launch, and the three permute stages launch nothing */
   MOE_STAGE_PERMUTE_COUNT = 2,
   MOE_STAGE_PERMUTE_SCAN = 3,
   MOE_STAGE_PERMUTE_SCATTER = 4,

@@ -16,7 +16,19 @@ hipError_t launch_route_logits(int dtype, const void* x, const void* w_router, c
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
                              hipStream_t stream);
 const char* route_logits_kernel_name(int dtype, int T, int E);
-const char* route_topk_kernel_name();
+const char* route_topk_kernel_name(int E);
+
+// Decode-sized batches (T <= 16 tokens, one per wave of the block; T*k <= 4096 slots): top-k,
+// softmax and the whole dispatch (counts, offsets, perm_src, inv_perm) in one single-block launch
+// after the logits. Each top-k is a chain of cross-lane exchanges, so more tokens per wave would
+// serialize them; larger batches keep the one-wave-per-token kernel and the three permute kernels.
+constexpr int kSmallTailMaxTokens = 16;
+constexpr int kSmallTailMaxRows = 4096;
+bool route_tail_fused(int T, int k);
+hipError_t launch_route_tail_small(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
+                                   int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
+                                   hipStream_t stream);
+const char* route_tail_small_kernel_name(int E);
 
 // ---- permutation ---------------------------------------------------------------------------
 // Rows are cut into tiles of `tile` flat slots; `tile_counts` holds [n_tiles, E] int32.

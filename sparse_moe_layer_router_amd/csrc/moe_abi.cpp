@@ -223,8 +223,23 @@ moe_status layer_impl(const moe_shape* sp, const void* x, const void* w_router, 
   void* hid = at(ws, L.hid);
   void* y = at(ws, L.y);
 
-  MOE_TRY(route_impl(s, x, w_router, bias, logits, idx, w, ev, stream));
-  MOE_TRY(permute_impl(s, idx, counts, offsets, perm_src, inv_perm, tiles, ev, stream));
+  if (moe::route_tail_fused(s.T, s.top_k)) {
+    // decode-sized batch: top-k, softmax and the dispatch in one launch after the logits
+    MOE_MARK(ev, MOE_STAGE_ROUTE_LOGITS, 0);
+    MOE_LAUNCH(moe::launch_route_logits(s.dtype, x, w_router, bias, logits, s.T, s.n_experts, s.d_model, stream));
+    MOE_MARK(ev, MOE_STAGE_ROUTE_LOGITS, 1);
+    MOE_MARK(ev, MOE_STAGE_ROUTE_TOPK, 0);
+    MOE_LAUNCH(moe::launch_route_tail_small(logits, s.T, s.n_experts, s.top_k, idx, w, counts, offsets, perm_src,
+                                            inv_perm, stream));
+    MOE_MARK(ev, MOE_STAGE_ROUTE_TOPK, 1);
+    for (int st = MOE_STAGE_PERMUTE_COUNT; st <= MOE_STAGE_PERMUTE_SCATTER; ++st) {
+      MOE_MARK(ev, st, 0);
+      MOE_MARK(ev, st, 1);
+    }
+  } else {
+    MOE_TRY(route_impl(s, x, w_router, bias, logits, idx, w, ev, stream));
+    MOE_TRY(permute_impl(s, idx, counts, offsets, perm_src, inv_perm, tiles, ev, stream));
+  }
   const moe::FfnGroups g = groups_for(s, x, perm_src, offsets, wg, wu, wd, sg, su, sd, hid, y);
   MOE_TRY(ffn_impl(g, (int32_t*)at(ws, L.sched), ev, stream));
   const void* shared_out =
@@ -362,10 +377,12 @@ const char* moe_stage_kernel_name(const moe_shape* s, int stage) {
                                       nullptr, nullptr, nullptr);
   switch (stage) {
     case MOE_STAGE_ROUTE_LOGITS: return moe::route_logits_kernel_name(s->dtype, s->T, s->n_experts);
-    case MOE_STAGE_ROUTE_TOPK: return moe::route_topk_kernel_name();
-    case MOE_STAGE_PERMUTE_COUNT: return "permute_count_kernel";
-    case MOE_STAGE_PERMUTE_SCAN: return "permute_scan_kernel";
-    case MOE_STAGE_PERMUTE_SCATTER: return "permute_scatter_kernel";
+    case MOE_STAGE_ROUTE_TOPK:
+      return moe::route_tail_fused(s->T, s->top_k) ? moe::route_tail_small_kernel_name(s->n_experts)
+                                               : moe::route_topk_kernel_name(s->n_experts);
+    case MOE_STAGE_PERMUTE_COUNT: return moe::route_tail_fused(s->T, s->top_k) ? "" : "permute_count_kernel";
+    case MOE_STAGE_PERMUTE_SCAN: return moe::route_tail_fused(s->T, s->top_k) ? "" : "permute_scan_kernel";
+    case MOE_STAGE_PERMUTE_SCATTER: return moe::route_tail_fused(s->T, s->top_k) ? "" : "permute_scatter_kernel";
     case MOE_STAGE_FFN_SCHEDULE: return moe::ffn_schedule_kernel_name(g);
     case MOE_STAGE_FFN_GATE_UP: return moe::ffn_gate_up_kernel_name(g);
     case MOE_STAGE_FFN_DOWN: return moe::ffn_down_kernel_name(g);

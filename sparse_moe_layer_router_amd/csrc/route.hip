@@ -44,73 +44,166 @@ route_logits_valu(const void* __restrict__ x, const void* __restrict__ w, const 
 }
 
 // ------------------------------------------------------------------------------------- top-k
-// One wave per token. Lane l holds logits l, l+64, ... (E <= 1024 -> at most 16 per lane). Each
-// of the k rounds takes the lane-local best not yet taken, then a butterfly arg-max over the
-// wave with the order (value descending, index ascending); the winner is marked taken. The
-// winning values stay in registers (slot s lives in lane s % 64) for the softmax.
-constexpr int kMaxPerLane = 16;
-
+// One wave per token. Lane l holds logits l, l+64, ... (NPER = ceil(E/64) <= 16 per lane). Each of
+// the k rounds takes the lane-local best not yet taken, then the wave's largest value (a DPP
+// max-reduction inside rows of 16 lanes, then across rows) and, among the lanes holding it, the
+// smallest expert id (the same reduction on ids): the order is value descending, id ascending.
+// The winner is marked taken; slot s's value and id stay in lane s % 64 for the softmax.
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-__global__ void __launch_bounds__(256)
-route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
-                  float* __restrict__ topk_w) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = lane_id();
-  if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  float v[kMaxPerLane];
+// max / min over the 64 lanes, result in every lane (DPP row ops, then row broadcasts, then lane 63)
+template <bool MAX>
+__device__ __forceinline__ int dpp_step(int v, int moved) {
+  if (MAX) return __float_as_int(fmaxf(__int_as_float(v), __int_as_float(moved)));
+  return v < moved ? v : moved;
+}
+template <bool MAX>
+__device__ __forceinline__ int wave_reduce(int v) {
+  v = dpp_step<MAX>(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = dpp_step<MAX>(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = dpp_step<MAX>(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = dpp_step<MAX>(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = dpp_step<MAX>(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xA, 0xF, false));  // row_bcast:15 -> rows 1, 3
+  v = dpp_step<MAX>(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xC, 0xF, false));  // row_bcast:31 -> rows 2, 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Top-k and softmax of one token's logits row by one wave. Writes topk_idx/topk_w of the token
+// (and, when lds_ids is not NULL, a copy of the ids into LDS).
+template <int NPER>
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int32_t* __restrict__ idx_out,
+                                           float* __restrict__ w_out, int32_t* lds_ids, int lane) {
+  float v[NPER];
   uint32_t taken = 0;
-  const int nper = (E + 63) / 64;
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
-    int e = lane + 64 * j;
-    const bool ok = j < nper && e < E;
+  for (int j = 0; j < NPER; ++j) {
+    const int e = lane + 64 * j;
+    const bool ok = e < E;
     const float val = ok ? row[e] : 0.f;
     v[j] = (val != val) ? -__builtin_inff() : val;  // NaN orders like -inf so k ids are always chosen
     if (!ok) taken |= 1u << j;
   }
-  float sel[kMaxPerLane];  // selected value of slot s = lane + 64*j
+  float sel[NPER];  // selected value of slot s = lane + 64*j
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) sel[j] = 0.f;
+  for (int j = 0; j < NPER; ++j) sel[j] = 0.f;
 
   for (int s = 0; s < k; ++s) {
     float bv = -__builtin_inff();
-    int bi = 0x7FFFFFFF;
+    int bi = 0x7FFFFFFF;  // no candidate left in this lane
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-      int e = lane + 64 * j;
+    for (int j = 0; j < NPER; ++j) {
+      const int e = lane + 64 * j;
       if (!((taken >> j) & 1u) && better(v[j], e, bv, bi)) { bv = v[j]; bi = e; }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off, 64);
-      int oi = __shfl_xor(bi, off, 64);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    const float m = __int_as_float(wave_reduce<true>(__float_as_int(bv)));
+    const int win = wave_reduce<false>((bi != 0x7FFFFFFF && bv == m) ? bi : 0x7FFFFFFF);
+    if ((win & 63) == lane) taken |= 1u << (win >> 6);
     if ((s & 63) == lane) {
-      sel[s >> 6] = bv;  // s >> 6 < 16 because k <= E <= 1024
-      topk_idx[(size_t)t * k + s] = bi;
+      sel[s >> 6] = m;  // s >> 6 < NPER because k <= E
+      idx_out[s] = win;
+      if (lds_ids) lds_ids[s] = win;
     }
   }
   // softmax over the k selected, shifted by the largest (slot 0, held by lane 0)
-  const float m = __shfl(sel[0], 0, 64);
-  float ex[kMaxPerLane];
+  const float mx = __shfl(sel[0], 0, 64);
+  float ex[NPER];
   float part = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
-    int s = lane + 64 * j;
-    ex[j] = (s < k) ? expf(sel[j] - m) : 0.f;
+  for (int j = 0; j < NPER; ++j) {
+    const int s = lane + 64 * j;
+    ex[j] = (s < k) ? expf(sel[j] - mx) : 0.f;
     part += ex[j];
   }
   const float total = wave_sum(part);
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
-    int s = lane + 64 * j;
-    if (s < k) topk_w[(size_t)t * k + s] = ex[j] / total;
+  for (int j = 0; j < NPER; ++j) {
+    const int s = lane + 64 * j;
+    if (s < k) w_out[s] = ex[j] / total;
+  }
+}
+
+template <int NPER>
+__global__ void __launch_bounds__(256)
+route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
+                  float* __restrict__ topk_w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_token<NPER>(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, nullptr, lane_id());
+}
+
+// ------------------------------------------------------------------------------ small batches
+// Decode-sized batches: one block of 16 waves does the top-k of every token (one wave per token,
+// the routine above; at most 16 tokens), then the whole dispatch of the T*k slots from LDS: histogram, exclusive
+// offsets, and the stable (expert, flat slot) permutation by one wave walking the slots in
+// order, 64 at a time, lanes with equal expert ids ranked by ballots over the id bits. Same
+// results, bit for bit, as route_topk_kernel followed by the three permute kernels.
+constexpr int kTailWaves = 16;
+static_assert(kSmallTailMaxTokens <= kTailWaves, "one token per wave");
+
+template <int NPER>
+__global__ void __launch_bounds__(kTailWaves * 64)
+route_tail_small_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
+                        float* __restrict__ topk_w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                        int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_perm) {
+  __shared__ int32_t ids[kSmallTailMaxRows];
+  __shared__ int32_t cur[1024];  // per-expert counts, then the next free row of each expert
+  __shared__ int32_t wave_tot[kTailWaves];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  for (int t = wave; t < T; t += kTailWaves)
+    topk_token<NPER>(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, ids + t * k,
+                     lane);
+  for (int e = threadIdx.x; e < E; e += kTailWaves * 64) cur[e] = 0;
+  __syncthreads();
+  const int rows = T * k;
+  for (int p = threadIdx.x; p < rows; p += kTailWaves * 64) atomicAdd(&cur[ids[p]], 1);
+  __syncthreads();
+  // exclusive scan of the counts over experts (one expert per thread, E <= 1024)
+  const int e = threadIdx.x;
+  const int32_t c = e < E ? cur[e] : 0;
+  int32_t incl = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_tot[w];
+  const int32_t excl = before + incl - c;
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = excl;
+    if (e == E - 1) offsets[E] = excl + c;
+    cur[e] = excl;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  int bits = 0;
+  while ((1 << bits) < E) ++bits;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < rows; c0 += 64) {
+    const int p = c0 + lane;
+    const int id = p < rows ? ids[p] : -1;
+    const bool valid = id >= 0;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+      const bool bit = valid && ((id >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    const int rank = __popcll(same & below);
+    const int n = __popcll(same);
+    const int32_t pos = valid ? cur[id] + rank : 0;
+    __builtin_amdgcn_wave_barrier();  // every lane has read cur[] before the group's first lane bumps it
+    if (valid && rank == 0) cur[id] += n;
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      perm_src[pos] = p;
+      inv_perm[p] = pos;
+    }
   }
 }
 
@@ -126,9 +219,29 @@ hipError_t launch_route_logits(int dtype, const void* x, const void* w_router, c
   return hipGetLastError();
 }
 
+// candidates per lane for E experts: 1, 2, 4, 8 or 16
+static int nper_of(int E) {
+  int n = 1;
+  while (64 * n < E) n *= 2;
+  return n;
+}
+
+#define MOE_NPER_SWITCH(E, F) \
+  switch (nper_of(E)) {       \
+    case 1: F(1); break;      \
+    case 2: F(2); break;      \
+    case 4: F(4); break;      \
+    case 8: F(8); break;      \
+    default: F(16); break;    \
+  }
+
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
                              hipStream_t stream) {
-  hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, topk_idx, topk_w);
+#define MOE_TOPK(N)                                                                                               \
+  hipLaunchKernelGGL(route_topk_kernel<N>, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, topk_idx, \
+                     topk_w)
+  MOE_NPER_SWITCH(E, MOE_TOPK)
+#undef MOE_TOPK
   return hipGetLastError();
 }
 
@@ -136,6 +249,31 @@ const char* route_logits_kernel_name(int dtype, int T, int) {
   if (dtype == kBF16 && T >= kRouterGemmMinTokens) return "grouped_gemm_kernel<2, 0>";
   return dtype == kBF16 ? "route_logits_valu<1>" : "route_logits_valu<0>";
 }
-const char* route_topk_kernel_name() { return "route_topk_kernel"; }
+
+bool route_tail_fused(int T, int k) { return T <= kSmallTailMaxTokens && (long long)T * k <= kSmallTailMaxRows; }
+
+hipError_t launch_route_tail_small(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
+                                   int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
+                                   hipStream_t stream) {
+#define MOE_TAIL(N)                                                                                             \
+  hipLaunchKernelGGL(route_tail_small_kernel<N>, dim3(1), dim3(kTailWaves * 64), 0, stream, logits, T, E, k, \
+                     topk_idx, topk_w, counts, offsets, perm_src, inv_perm)
+  MOE_NPER_SWITCH(E, MOE_TAIL)
+#undef MOE_TAIL
+  return hipGetLastError();
+}
+
+static const char* const kTopkNames[] = {"route_topk_kernel<1>", "route_topk_kernel<2>", "route_topk_kernel<4>",
+                                         "route_topk_kernel<8>", "route_topk_kernel<16>"};
+static const char* const kTailNames[] = {"route_tail_small_kernel<1>", "route_tail_small_kernel<2>",
+                                         "route_tail_small_kernel<4>", "route_tail_small_kernel<8>",
+                                         "route_tail_small_kernel<16>"};
+static int nper_slot(int E) {
+  int n = nper_of(E), i = 0;
+  while ((1 << i) < n) ++i;
+  return i;
+}
+const char* route_topk_kernel_name(int E) { return kTopkNames[nper_slot(E)]; }
+const char* route_tail_small_kernel_name(int E) { return kTailNames[nper_slot(E)]; }
 
 }  // namespace moe

@@ -128,8 +128,16 @@ def test_status_strings_and_stage_names():
     s = dsv3()
     names = [moe.moe_stage_kernel_name(s, i) for i in range(moe.MOE_NUM_STAGES)]
     assert names[5] == "" and "gate_up" in names[6] and "down" in names[7]     # decode: GEMV, no schedule
+    # decode-sized batch: top-k, softmax and dispatch in one launch, the permute stages launch nothing
+    assert names[1] == "route_tail_small_kernel<4>" and names[2:5] == ["", "", ""]
+    assert moe.moe_stage_kernel_name(dsv3(T=16, top_k=256), 1) == "route_tail_small_kernel<4>"   # 4096 slots
+    assert moe.moe_stage_kernel_name(dsv3(T=17), 1) == "route_topk_kernel<4>"
+    assert moe.moe_stage_kernel_name(dsv3(T=17), 2) == "permute_count_kernel"
+    assert moe.moe_stage_kernel_name(dsv3(T=256), 1) == "route_topk_kernel<4>"
     names = [moe.moe_stage_kernel_name(dsv3(T=8192), i) for i in range(moe.MOE_NUM_STAGES)]
-    assert names[0] == "grouped_gemm_kernel<2, 0>" and names[5] == "gemm_schedule_kernel"
+    assert names[0] == "grouped_gemm_kernel<2, 0>" and names[1] == "route_topk_kernel<4>"
+    assert names[2:5] == ["permute_count_kernel", "permute_scan_kernel", "permute_scatter_kernel"]
+    assert names[5] == "gemm_schedule_kernel"
     assert names[6] == "grouped_gemm_kernel<0, 0>" and names[7] == "grouped_gemm_kernel<1, 0>"
     packed = dsv3(T=8, weight_layout=moe.MOE_LAYOUT_FRAG16)
     assert moe.moe_stage_kernel_name(packed, 6) == "ffn_gate_up_stream<1, 1>"

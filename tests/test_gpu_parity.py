@@ -128,6 +128,48 @@ def test_entry_points_separately(cfg):
     assert ok, ("out", err, bound)
 
 
+# Decode-sized batches (T <= 16, T*k <= 4096) route and dispatch in one single-block kernel inside
+# moe_layer_forward; the separate entry points keep the multi-kernel path. Both must agree bit for bit.
+FUSED = [
+    LayerConfig("fused_zipf", 16, 512, 64, 6, 256, 0, "bf16", zipf_s=1.2),
+    LayerConfig("fused_E1024", 13, 64, 1024, 2, 16, 0, "bf16"),
+    LayerConfig("fused_boundary_4096_slots", 16, 64, 256, 256, 32, 0, "bf16"),
+    LayerConfig("fused_k_equals_E", 9, 128, 4, 4, 64, 0, "bf16"),
+    LayerConfig("fused_one_token_f32", 1, 64, 8, 3, 32, 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("cfg", FUSED, ids=lambda c: c.name)
+def test_fused_small_batch_dispatch_matches_entry_points(cfg):
+    c = cfg
+    s = moe.make_shape(c.T, c.d, c.E, c.k, c.H, c.Hs, c.dtype)
+    assert moe.moe_stage_kernel_name(s, 1).startswith("route_tail_small_kernel<")
+    L = G.make_layer(cfg)
+    r = G.run_layer(L)
+    dt = G.TORCH_DT[c.dtype]
+    ws = moe.allocate_workspace(s)
+    idx = torch.empty(c.T, c.k, dtype=torch.int32, device="cuda")
+    w = torch.empty(c.T, c.k, dtype=torch.float32, device="cuda")
+    moe.moe_route(s, L.x, L.w_router, L.bias, None, idx, w, ws)
+    cnt = torch.empty(c.E, dtype=torch.int32, device="cuda")
+    offs = torch.empty(c.E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(c.T * c.k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(c.T * c.k, dtype=torch.int32, device="cuda")
+    moe.moe_permute(s, idx, cnt, offs, perm, inv, ws)
+    y = torch.empty(c.T * c.k, c.d, dtype=dt, device="cuda")
+    moe.moe_grouped_ffn(s, L.x, perm, offs, L.w_gate, L.w_up, L.w_down, y, ws)
+    out = torch.empty(c.T, c.d, dtype=dt, device="cuda")
+    moe.moe_combine(s, y, inv, w, None, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(r.idx.cpu().numpy(), idx.cpu().numpy())
+    np.testing.assert_array_equal(r.w.cpu().numpy().view(np.uint32), w.cpu().numpy().view(np.uint32))
+    np.testing.assert_array_equal(r.counts.cpu().numpy(), cnt.cpu().numpy())
+    # the layer's internal permutation fed the same experts in the same order: identical output bits
+    np.testing.assert_array_equal(r.out.view(torch.int16 if c.dtype == "bf16" else torch.int32).cpu().numpy(),
+                                  out.view(torch.int16 if c.dtype == "bf16" else torch.int32).cpu().numpy())
+    check_routing_on_gpu_logits(L, r)
+
+
 def test_permute_stress_patterns():
     """Skewed, duplicate and single-expert id patterns across many tiles: bit-exact."""
     rng = np.random.default_rng(0)
@@ -170,6 +212,42 @@ def test_route_ties_go_to_lower_index():
     torch.cuda.synchronize()
     assert idx.cpu().numpy().tolist() == [[5, 9, 0, 1]] * T
     np.testing.assert_array_equal(idx.cpu().numpy(), oracle.select_topk(lg.cpu().numpy().astype(np.float64), k))
+
+
+@pytest.mark.parametrize("E", [1, 3, 64, 65, 128, 200, 256, 300, 512, 777, 1024])
+def test_topk_tie_heavy_every_lane_width(E):
+    """Router rows drawn from a handful of distinct vectors and biases from a few values, so most
+    logits tie exactly; every candidates-per-lane width (E up to 64, 128, 256, 512, 1024), through
+    both the one-wave-per-token kernel (T=40) and the single-block decode tail (T=9, via the layer)."""
+    g = torch.Generator().manual_seed(E)
+    d = 64
+    protos = torch.randn(5, d, generator=g)
+    wr = protos[torch.randint(0, 5, (E,), generator=g)].to(torch.bfloat16).cuda()
+    bias = torch.tensor([0.0, 0.5, -0.25])[torch.randint(0, 3, (E,), generator=g)].float().cuda()
+    for T in (40, 9):
+        k = min(E, 9)
+        x = torch.randn(T, d, generator=g).to(torch.bfloat16).cuda()
+        s = moe.make_shape(T, d, E, k, 32, 0, "bf16")
+        idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+        lg = torch.empty(T, E, dtype=torch.float32, device="cuda")
+        moe.moe_route(s, x, wr, bias, lg, idx, w, moe.allocate_workspace(s))
+        torch.cuda.synchronize()
+        lg64 = lg.cpu().numpy().astype(np.float64)
+        idx_o = oracle.select_topk(lg64, k)
+        np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+        np.testing.assert_allclose(w.cpu().numpy(), oracle.softmax_selected(lg64, idx_o), rtol=0, atol=1e-6)
+        if T <= 16:   # the layer's fused tail must select the same ids from the same logits
+            wg = torch.zeros(E, 32, d, dtype=torch.bfloat16, device="cuda")
+            wd = torch.zeros(E, d, 32, dtype=torch.bfloat16, device="cuda")
+            out = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+            idx2 = torch.empty_like(idx)
+            w2 = torch.empty_like(w)
+            moe.moe_layer_forward(s, x, wr, bias, wg, wg, wd, None, None, None, out, idx2, w2,
+                                  workspace=moe.allocate_workspace(s))
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(idx2.cpu().numpy(), idx_o)
+            np.testing.assert_array_equal(w2.cpu().numpy().view(np.uint32), w.cpu().numpy().view(np.uint32))
 
 
 def test_deterministic_bitwise():
