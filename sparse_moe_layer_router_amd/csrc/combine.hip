@@ -8,7 +8,7 @@
 // One block per token; each thread owns 8 consecutive features (one 16-byte bf16 load per row),
 // gathers the token's k expert rows through inv_perm in fixed slot order, accumulates in fp32
 // starting from the shared-expert row, and rounds once.
-#include "kernels.h"
+#include "dispatch.h"
 #include "moe_device.h"
 
 namespace moe {

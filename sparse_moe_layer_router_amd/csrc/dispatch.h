@@ -1,0 +1,50 @@
+// Host-side launchers of the routing, dispatch, combine and weight-packing kernels. Every launcher
+// enqueues on `stream` and returns the launch status; shapes were validated by the caller
+// (moe_abi.cpp).
+#pragma once
+
+#include "kernels.h"
+
+namespace moe {
+
+// ---- routing -------------------------------------------------------------------------------
+hipError_t launch_route_logits(int dtype, const void* x, const void* w_router, const float* bias,
+                               float* logits, int T, int E, int d, hipStream_t stream);
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
+                             hipStream_t stream);
+const char* route_logits_kernel_name(int dtype, int T, int E);
+const char* route_topk_kernel_name(int E);
+
+// Decode-sized batches (T <= 16 tokens, one per wave of the block; T*k <= 4096 slots): top-k,
+// softmax and the whole dispatch (counts, offsets, perm_src, inv_perm) in one single-block launch
+// after the logits. Each top-k is a chain of cross-lane exchanges, so more tokens per wave would
+// serialize them; larger batches keep the one-wave-per-token kernel and the three permute kernels.
+constexpr int kSmallTailMaxTokens = 16;
+constexpr int kSmallTailMaxRows = 4096;
+bool route_tail_fused(int T, int k);
+hipError_t launch_route_tail_small(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
+                                   int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
+                                   hipStream_t stream);
+const char* route_tail_small_kernel_name(int E);
+
+// ---- permutation ---------------------------------------------------------------------------
+// Rows are cut into tiles of `tile` flat slots; `tile_counts` holds [n_tiles, E] int32.
+int permute_tile_size(long long rows);
+size_t permute_scratch_bytes(long long rows, int E);
+hipError_t launch_permute_count(const int32_t* topk_idx, long long rows, int E, int tile, int32_t* tile_counts,
+                                hipStream_t stream);
+hipError_t launch_permute_scan(int32_t* tile_counts, long long rows, int E, int tile, int32_t* counts,
+                               int32_t* offsets, hipStream_t stream);
+hipError_t launch_permute_scatter(const int32_t* topk_idx, long long rows, int E, int tile,
+                                  const int32_t* tile_counts, int32_t* perm_src, int32_t* inv_perm,
+                                  hipStream_t stream);
+
+// ---- combine ---------------------------------------------------------------------------------
+hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_perm, const float* topk_w,
+                          const void* shared_out, void* out, int T, int k, int d, hipStream_t stream);
+const char* combine_kernel_name(int dtype);
+
+// ---- weight packing (MOE_LAYOUT_FRAG16) --------------------------------------------------------
+hipError_t launch_pack_weights(const void* src, void* dst, long long n_mats, int rows, int cols, hipStream_t stream);
+
+}  // namespace moe

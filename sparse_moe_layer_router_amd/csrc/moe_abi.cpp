@@ -7,7 +7,7 @@
 #include <cstring>
 
 #include "../../include/moe.h"
-#include "kernels.h"
+#include "dispatch.h"
 
 namespace {
 

@@ -3,7 +3,7 @@
 // Each 1 KB of the packed matrix is one 16-row x 32-column block in the A-operand lane order of
 // the 16x16x32 bf16 MFMA, so a wave reading a weight for a matrix-core instruction reads 1 KB of
 // contiguous memory instead of 16 separate 64-byte row pieces.
-#include "kernels.h"
+#include "dispatch.h"
 #include "moe_device.h"
 
 namespace moe {

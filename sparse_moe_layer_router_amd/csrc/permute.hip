@@ -11,7 +11,7 @@
 // hold the same expert find each other with ballots over the expert-id bits, and a lane's rank
 // among them is the number of such lanes below it. The result is the unique stable order
 // (expert, flat slot), with no dependence on scheduling.
-#include "kernels.h"
+#include "dispatch.h"
 #include "moe_device.h"
 
 namespace moe {

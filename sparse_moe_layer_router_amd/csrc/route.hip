@@ -3,7 +3,7 @@
 // Sparse-MoE overview article (adg.csdn.net), section 2.2: each token is scored against every
 // expert by a small linear layer, the E scores are ordered and the K best kept, and the K kept
 // scores are softmax-normalised into weights that sum to one.
-#include "kernels.h"
+#include "dispatch.h"
 #include "moe_device.h"
 
 namespace moe {
