@@ -20,12 +20,21 @@ Sources (the pages this follows):
                   run each expert once over its bucket, convert back to token order, weight, merge).
   [Inference ch.6] "大模型推理优化基础" (LLM-from-scratch ch. 6), roofline section: a gated MLP is
                   up, gate and down matmuls.
+  [MoE kernels §2.2] the same page, §2.2 (DeepSeek-V3 routing without an auxiliary loss): experts
+                  are picked on sigmoid affinities plus a per-expert bias; the weights use the
+                  selected experts' sigmoid affinities without the bias, normalised to sum to one;
+                  and the router listing of §4.3 (sigmoid of the raw logits plus the bias, top-k on
+                  that, weights from the unbiased sigmoid of the selected).
 
 Readings where the pages are silent or garbled (each is also listed in the design doc):
   * combine: out = Shared(x) + sum_j w_j * Expert_{e_j}(x); the shared expert has weight 1, no
     residual and no norm inside the layer (the [MoE kernels] §1.1 formula is lost in extraction).
   * no learned router bias; an optional per-expert logit bias is an explicit input, added to the
-    logits before both selection and softmax.
+    logits before both selection and softmax (softmax routing).
+  * sigmoid routing ([MoE kernels §2.2]): S_e = sigmoid(l_e) + b_e decides the selection;
+    w_e = sigmoid(l_e) / sum over the selected of sigmoid(l_j). The listing adds 1e-6 to that
+    denominator; the formula of §2.2 does not, and the oracle follows the formula (a sum of k
+    positive sigmoids needs no guard in float64).
   * gate = softmax over the K selected raw logits, temperature 1 ([MoE overview] §2.2 step 3).
   * expert = SwiGLU: h = SiLU(x W_gate^T) * (x W_up^T), y = h W_down^T, SiLU(z) = z * sigmoid(z)
     (standard definition; the pages name the three matrices but never define the activation).
@@ -41,7 +50,10 @@ import numpy as np
 __all__ = [
     "widen", "router_logits", "select_topk", "softmax_selected", "route", "permute", "silu",
     "swiglu", "grouped_ffn", "combine", "layer_forward", "layer_forward_tokens", "topk_gap",
+    "logistic", "selection_scores", "sigmoid_weights_selected", "ROUTINGS",
 ]
+
+ROUTINGS = ("softmax", "sigmoid")
 
 
 # ----------------------------------------------------------------------------- input decoding
@@ -101,11 +113,59 @@ def softmax_selected(L: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=1, keepdims=True)
 
 
-def route(x, w_router, k, logit_bias=None):
-    """Scoring, selection and weighting for every token: (logits [T,E], idx [T,k], w [T,k])."""
-    L = router_logits(x, w_router, logit_bias)
-    idx = select_topk(L, k)
-    return L, idx, softmax_selected(L, idx)
+def logistic(z: np.ndarray) -> np.ndarray:
+    """sigmoid(z) = 1 / (1 + e^-z), written so that neither branch overflows."""
+    z = np.asarray(z, np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def selection_scores(L: np.ndarray, routing: str = "softmax", bias: np.ndarray | None = None) -> np.ndarray:
+    """What the top-K selection ranks.
+
+    softmax routing: the logits themselves (a logit bias is already inside L).
+    sigmoid routing, [MoE kernels §2.2]: the sigmoid affinity plus the per-expert bias,
+    S_e = sigmoid(l_e) + b_e.
+    """
+    if routing == "softmax":
+        return np.asarray(L, np.float64)
+    if routing == "sigmoid":
+        S = logistic(L)
+        if bias is not None:
+            S = S + np.asarray(bias, np.float64)[None, :]
+        return S
+    raise ValueError(routing)
+
+
+def sigmoid_weights_selected(L: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Weighting of sigmoid routing, [MoE kernels §2.2]: the selected experts' sigmoid affinities of
+    the raw logits (no bias), divided by their sum over the selected set."""
+    s = np.take_along_axis(logistic(L), idx, axis=1)
+    if s.shape[1] == 0:
+        return s
+    return s / s.sum(axis=1, keepdims=True)
+
+
+def route(x, w_router, k, bias=None, routing="softmax"):
+    """Scoring, selection and weighting for every token: (logits [T,E], idx [T,k], w [T,k]).
+
+    softmax routing: ``bias`` (optional) is added to the logits, which then decide the selection
+    and are softmax-normalised over the k selected. sigmoid routing: the logits are x . W_g^T
+    without bias; ``bias`` (optional) only shifts the sigmoid scores used for the selection.
+    """
+    if routing == "softmax":
+        L = router_logits(x, w_router, bias)
+        idx = select_topk(L, k)
+        return L, idx, softmax_selected(L, idx)
+    if routing == "sigmoid":
+        L = router_logits(x, w_router, None)
+        idx = select_topk(selection_scores(L, "sigmoid", bias), k)
+        return L, idx, sigmoid_weights_selected(L, idx)
+    raise ValueError(routing)
 
 
 def topk_gap(L: np.ndarray, k: int) -> np.ndarray:
@@ -207,15 +267,16 @@ def combine(y_perm: np.ndarray, inv_perm: np.ndarray, w: np.ndarray, shared_out:
 
 # ----------------------------------------------------------------------------- whole layer
 
-def layer_forward(x, w_router, k, expert_fn, shared_fn=None, logit_bias=None):
+def layer_forward(x, w_router, k, expert_fn, shared_fn=None, bias=None, routing="softmax"):
     """The full layer on float64 inputs. Returns a dict of every intermediate.
 
-    ``expert_fn(e)`` / ``shared_fn()`` return float64 (W_gate, W_up, W_down).
+    ``expert_fn(e)`` / ``shared_fn()`` return float64 (W_gate, W_up, W_down); ``bias`` and
+    ``routing`` as in ``route``.
     """
     x = np.asarray(x, np.float64)
     T = x.shape[0]
     E = np.asarray(w_router).shape[0]
-    L, idx, w = route(x, w_router, k, logit_bias)
+    L, idx, w = route(x, w_router, k, bias, routing)
     counts, offsets, perm_src, inv_perm = permute(idx, E)
     x_rows = x[perm_src // k] if T else np.zeros((0, x.shape[1]))
     y_perm = grouped_ffn(x_rows, offsets, expert_fn)
@@ -225,14 +286,14 @@ def layer_forward(x, w_router, k, expert_fn, shared_fn=None, logit_bias=None):
                 inv_perm=inv_perm, y_perm=y_perm, shared=shared, out=out)
 
 
-def layer_forward_tokens(x_rows, w_router, k, expert_fn, shared_fn=None, logit_bias=None):
+def layer_forward_tokens(x_rows, w_router, k, expert_fn, shared_fn=None, bias=None, routing="softmax"):
     """Output rows for a sample of tokens. Each token's result depends only on its own row (routing
     is per token and the experts act row by row), so a sample of rows can be checked on its own at
     any batch size. Experts are visited once each, in increasing id, and their weighted outputs
     added to the tokens that selected them: the same sum over the k selected experts as
     ``combine``, in another order of addition."""
     x_rows = np.asarray(x_rows, np.float64)
-    L, idx, w = route(x_rows, w_router, k, logit_bias)
+    L, idx, w = route(x_rows, w_router, k, bias, routing)
     out = np.zeros_like(x_rows)
     if shared_fn is not None:
         out += swiglu(x_rows, *shared_fn())

@@ -293,6 +293,111 @@ def test_widen_bf16_exact():
     np.testing.assert_array_equal(oracle.widen(bits, "bf16"), ref)
 
 
+# ------------------------------------------------------------------ sigmoid routing (MoE kernels §2.2)
+
+def one_token_route(logits, k, bias=None, routing="sigmoid"):
+    """route() on a single token whose logits are given directly (x = [1], W_g = the logits column)."""
+    wg = np.asarray(logits, np.float64)[:, None]
+    return oracle.route(np.ones((1, 1)), wg, k, None if bias is None else np.asarray(bias, np.float64), routing)
+
+
+def test_logistic_matches_scipy_expit_without_overflow():
+    z = np.concatenate([np.linspace(-800, 800, 4001), [-1e300, 1e300, 0.0]])
+    np.testing.assert_allclose(oracle.logistic(z), scipy.special.expit(z), rtol=1e-15, atol=1e-300)
+    assert oracle.logistic(np.array([0.0]))[0] == 0.5
+
+
+def test_sigmoid_routing_without_bias_selects_like_softmax():
+    """sigmoid is strictly increasing, so with no bias it ranks experts exactly as the logits do."""
+    rng = np.random.default_rng(7)
+    x, wg, _ = rand_layer(rng, 60, 12, 16, 4)
+    _, idx_soft, _ = oracle.route(x, wg, 5)
+    _, idx_sig, w_sig = oracle.route(x, wg, 5, None, "sigmoid")
+    np.testing.assert_array_equal(idx_sig, idx_soft)
+    np.testing.assert_allclose(w_sig.sum(1), 1.0, rtol=0, atol=1e-15)
+    assert (w_sig > 0).all()
+
+
+def test_sigmoid_bias_decides_selection_by_hand():
+    """Logits [2, 1, 0, -1], bias +0.6 on expert 2, k = 2. Affinities sigmoid(l) are about
+    [0.881, 0.731, 0.5, 0.269]; with the bias expert 2 scores 1.1 and ranks first, expert 0 second.
+    (Adding the bias to the logit instead, sigmoid(0.6) = 0.646 < 0.731, would keep [0, 1]; a
+    selection that ignores the bias also gives [0, 1].)"""
+    _, idx, w = one_token_route([2.0, 1.0, 0.0, -1.0], 2, [0.0, 0.0, 0.6, 0.0])
+    assert idx.tolist() == [[2, 0]]
+    _, idx0, _ = one_token_route([2.0, 1.0, 0.0, -1.0], 2)
+    assert idx0.tolist() == [[0, 1]]
+    # weights: the unbiased affinities sigmoid(0) = 1/2 and sigmoid(2), normalised: 1/2 is the
+    # smaller share and the two shares sum to one
+    assert w[0, 0] < 0.5 < w[0, 1] and abs(w.sum() - 1.0) < 1e-15
+
+
+def test_sigmoid_bias_leaves_weights_alone():
+    """The bias changes which experts are picked, never their weights ([MoE kernels] §2.2): a bias
+    shifted by a constant, or changed only on experts that stay unselected, gives the same ids and
+    bit-identical weights."""
+    rng = np.random.default_rng(11)
+    x, wg, _ = rand_layer(rng, 40, 10, 12, 4)
+    b = rng.standard_normal(12) * 0.3
+    _, idx, w = oracle.route(x, wg, 3, b, "sigmoid")
+    _, idx2, w2 = oracle.route(x, wg, 3, b + 5.0, "sigmoid")
+    np.testing.assert_array_equal(idx2, idx)
+    np.testing.assert_allclose(w2, w, rtol=1e-15, atol=0)
+    # lower the bias of experts no token selected: nothing changes
+    unused = np.setdiff1d(np.arange(12), np.unique(idx))
+    if unused.size:
+        b3 = b.copy()
+        b3[unused] -= 10.0
+        _, idx3, w3 = oracle.route(x, wg, 3, b3, "sigmoid")
+        np.testing.assert_array_equal(idx3, idx)
+        np.testing.assert_array_equal(w3, w)
+
+
+def test_sigmoid_weights_limits():
+    """Large positive logits saturate every affinity at 1, so the weights tend to 1/k (a softmax
+    would favour the largest logit); for very negative logits sigmoid(l) ~ e^l, so the weights tend
+    to the softmax over the selected logits."""
+    _, idx, w = one_token_route([30.0, 31.0, 32.0, -5.0], 3)
+    assert idx.tolist() == [[2, 1, 0]]
+    np.testing.assert_allclose(w[0], [1 / 3] * 3, rtol=0, atol=1e-12)
+    lg = np.array([-40.0, -37.5, -36.0, -39.0, -45.0])
+    _, idx, w = one_token_route(lg, 3)
+    assert idx.tolist() == [[2, 1, 3]]
+    np.testing.assert_allclose(w[0], scipy.special.softmax(lg[[2, 1, 3]]), rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("E,k", [(5, 2), (8, 3), (7, 7)])
+def test_sigmoid_selection_is_best_subset_by_brute_force(E, k):
+    """The selected set maximises the sum of the biased scores over all k-subsets."""
+    rng = np.random.default_rng(E * 10 + k)
+    for _ in range(20):
+        lg = rng.standard_normal(E) * 2
+        b = rng.standard_normal(E) * 0.2
+        _, idx, _ = one_token_route(lg, k, b)
+        S = 1.0 / (1.0 + np.exp(-lg)) + b
+        best = max(itertools.combinations(range(E), k), key=lambda c: sum(S[list(c)]))
+        assert sorted(idx[0].tolist()) == sorted(best)
+        assert all(S[idx[0][i]] >= S[idx[0][i + 1]] for i in range(k - 1))
+
+
+def test_sigmoid_layer_forward_uses_sigmoid_weights():
+    """A whole layer with sigmoid routing: the output is the weighted sum of the selected experts
+    with the sigmoid weights (the same dense-masked check as the softmax layer)."""
+    rng = np.random.default_rng(3)
+    T, d, E, k, H = 12, 6, 5, 2, 4
+    x, wg, ex = rand_layer(rng, T, d, E, H)
+    b = rng.standard_normal(E) * 0.2
+    r = oracle.layer_forward(x, wg, k, lambda e: ex[e], None, b, "sigmoid")
+    dense = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            e = r["idx"][t, j]
+            dense[t] += r["w"][t, j] * oracle.swiglu(x[t:t + 1], *ex[e])[0]
+    np.testing.assert_allclose(r["out"], dense, rtol=1e-12, atol=1e-12)
+    tok = oracle.layer_forward_tokens(x[3:7], wg, k, lambda e: ex[e], None, b, "sigmoid")
+    np.testing.assert_allclose(tok["out"], r["out"][3:7], rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------------ planted mistakes are caught
 
 def _plant(monkeypatch, name, fn):
@@ -330,15 +435,47 @@ def _perm_reversed(idx, E):
     return c, o, p, inv
 
 
-def _route_bias_weights_only(x, w_router, k, logit_bias=None):
+def _route_bias_weights_only(x, w_router, k, bias=None, routing="softmax"):
     L0 = om.router_logits(x, w_router, None)
     idx = om.select_topk(L0, k)
-    L = om.router_logits(x, w_router, logit_bias)
+    L = om.router_logits(x, w_router, bias)
     return L, idx, om.softmax_selected(L, idx)
+
+
+def _sigmoid_scores_of_biased_logit(L, routing="softmax", bias=None):
+    if routing != "sigmoid":
+        return _SELECTION(L, routing, bias)
+    L = np.asarray(L, np.float64)
+    return om.logistic(L + (0.0 if bias is None else np.asarray(bias)[None, :]))
+
+
+def _sigmoid_scores_without_bias(L, routing="softmax", bias=None):
+    return _SELECTION(L, routing, None)
+
+
+def _sigmoid_weights_with_bias(x, w_router, k, bias=None, routing="softmax"):
+    if routing != "sigmoid":
+        return _ROUTE(x, w_router, k, bias, routing)
+    L = om.router_logits(x, w_router, None)
+    S = om.selection_scores(L, "sigmoid", bias)
+    idx = om.select_topk(S, k)
+    s = np.take_along_axis(S, idx, 1)
+    return L, idx, s / s.sum(1, keepdims=True)
+
+
+def _logistic_sign_flipped(z):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(np.asarray(z, np.float64)))
+
+
+def _sigmoid_weights_softmax(L, idx):
+    return om.softmax_selected(L, idx)
 
 
 _COMBINE = om.combine
 _PERMUTE = om.permute
+_SELECTION = om.selection_scores
+_ROUTE = om.route
 
 MUTATIONS = {
     "silu_as_sigmoid": ("silu", lambda z: 1.0 / (1.0 + np.exp(-np.asarray(z))),
@@ -352,6 +489,14 @@ MUTATIONS = {
     "shared_expert_dropped": ("combine", _combine_no_shared, test_w1_outputs_by_hand),
     "combine_gathers_with_perm_src": ("combine", _combine_with_perm, test_w1_outputs_by_hand),
     "bias_only_in_weights": ("route", _route_bias_weights_only, test_bias_shifts_selection_and_weights),
+    "sigmoid_of_biased_logit": ("selection_scores", _sigmoid_scores_of_biased_logit,
+                                test_sigmoid_bias_decides_selection_by_hand),
+    "sigmoid_selection_ignores_bias": ("selection_scores", _sigmoid_scores_without_bias,
+                                       test_sigmoid_bias_decides_selection_by_hand),
+    "sigmoid_bias_in_weights": ("route", _sigmoid_weights_with_bias, test_sigmoid_bias_leaves_weights_alone),
+    "sigmoid_weights_as_softmax": ("sigmoid_weights_selected", _sigmoid_weights_softmax,
+                                   test_sigmoid_weights_limits),
+    "logistic_sign_flipped": ("logistic", _logistic_sign_flipped, test_logistic_matches_scipy_expit_without_overflow),
 }
 
 
