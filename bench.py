@@ -146,7 +146,7 @@ def cpu_baseline(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8):
     x_bits = host.x[tokens]
     wg_bits = host.w_router
     _, idx, _ = oracle.route(oracle.widen(x_bits, cfg.dtype), oracle.widen(wg_bits, cfg.dtype), cfg.k,
-                             host.logit_bias)
+                             host.router_bias, cfg.routing)
     raw = {int(e): synth.expert_weights_host(cfg, 0, int(e)) for e in np.unique(idx)}   # untimed
     shared_raw = synth.expert_weights_host(cfg, 0, 0, shared=True) if cfg.Hs else None
     expert_fn = lambda e: tuple(oracle.widen(a, cfg.dtype) for a in raw[e])  # noqa: E731
@@ -155,7 +155,7 @@ def cpu_baseline(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8):
     while reps < max_repeats and (reps == 0 or total < min_seconds):
         t0 = time.perf_counter()
         ref = oracle.layer_forward_tokens(oracle.widen(x_bits, cfg.dtype), oracle.widen(wg_bits, cfg.dtype),
-                                          cfg.k, expert_fn, shared_fn, host.logit_bias)
+                                          cfg.k, expert_fn, shared_fn, host.router_bias, cfg.routing)
         total += time.perf_counter() - t0
         reps += 1
     assert ref["out"].shape == (len(tokens), cfg.d)
@@ -217,10 +217,10 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     w_router = up(host.w_router)
-    bias = torch.from_numpy(host.logit_bias).to(dev) if host.logit_bias is not None else None
+    bias = torch.from_numpy(host.router_bias).to(dev) if host.router_bias is not None else None
     xs = [up(host.x)] + [up(synth.normal_host((cfg.T, d), 100 + b, synth.stream_id(synth.K_X), 1.0, cfg.dtype))
                          for b in range(1, N_BATCHES)]
-    shape = moe.make_shape(cfg.T, d, E, cfg.k, H, cfg.Hs, cfg.dtype, layout)
+    shape = moe.make_shape(cfg.T, d, E, cfg.k, H, cfg.Hs, cfg.dtype, layout, cfg.routing)
     ws = moe.allocate_workspace(shape)
     outs = [torch.empty(cfg.T, d, dtype=dt, device=dev) for _ in range(N_BATCHES)]
     counts = [torch.zeros(E, dtype=torch.int32, device=dev) for _ in range(N_BATCHES)]
@@ -305,7 +305,7 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded Philox normal draws; random-init weights of the named layer shape)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
-                   "d_hidden": cfg.H, "d_shared_hidden": cfg.Hs, "zipf_bias": cfg.zipf_s,
+                   "d_hidden": cfg.H, "d_shared_hidden": cfg.Hs, "zipf_bias": cfg.zipf_s, "routing": cfg.routing,
                    "weight_layout": "frag16" if layout == moe.MOE_LAYOUT_FRAG16 else "rowmajor",
                    "parallelism": "single GPU"},
         "roofline": roof,

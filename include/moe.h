@@ -1,7 +1,8 @@
 /*
  * moe.h -- C ABI of the sparse Mixture-of-Experts FFN layer forward on one MI355X (gfx950).
  *
- * One layer forward is: router scoring, top-k selection, softmax over the k selected scores,
+ * One layer forward is: router scoring, top-k selection, weighting of the k selected experts
+ * (softmax over their logits, or their normalised sigmoid scores),
  * dispatch of (token, slot) pairs into expert-contiguous order, the routed SwiGLU experts over
  * their buckets plus an always-on shared expert, and the weighted-sum combine back into token
  * order. Pages this follows:
@@ -64,6 +65,16 @@ typedef enum {
   MOE_LAYOUT_FRAG16 = 1    /* fragment-tiled, see moe_pack_weights */
 } moe_weight_layout;
 
+/* How the router turns logits into the k experts and their weights. */
+typedef enum {
+  MOE_ROUTING_SOFTMAX = 0, /* top-k of the logits (+ logit bias), softmax over the k (overview
+                              article section 2.2) */
+  MOE_ROUTING_SIGMOID = 1  /* top-k of sigmoid(logit) + bias, weights = the selected experts'
+                              sigmoid(logit) normalised to sum 1; the bias steers the selection
+                              only (MoE-kernels page section 2.2, DeepSeek-V3 routing without an
+                              auxiliary loss) */
+} moe_routing;
+
 /* Layer sizes (host pointer). */
 typedef struct {
   int32_t T;               /* tokens in this batch */
@@ -74,6 +85,7 @@ typedef struct {
   int32_t d_shared_hidden; /* Hs, hidden size of the shared expert; 0 = no shared expert */
   int32_t dtype;           /* moe_dtype */
   int32_t weight_layout;   /* moe_weight_layout of the expert weights */
+  int32_t routing;         /* moe_routing */
 } moe_shape;
 
 /*
@@ -96,13 +108,19 @@ const char* moe_status_string(moe_status st);
 
 /*
  * moe_route -- scoring, selection and weighting for every token.
- * Overview article section 2.2 steps 1-3; MoE-kernels page section 4.3 (gate, top-k).
- *   logits[t, e] = sum_i x[t, i] * w_router[e, i] (+ logit_bias[e]), accumulated in float32.
- *   topk_idx[t, 0..k-1] = the k largest logits, ordered by value descending, ties to the lower e.
- *   topk_w[t, j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected (sums to 1).
- * x [T, d] (dtype); w_router [E, d] (dtype); logit_bias [E] float32 or NULL (added before both
- * selection and softmax); logits_out [T, E] float32 or NULL (post-bias logits);
- * topk_idx [T, k] int32 and topk_w [T, k] float32 are required outputs.
+ * Overview article section 2.2 steps 1-3; MoE-kernels page sections 2.2 and 4.3 (gate, top-k).
+ *   logits[t, e] = sum_i x[t, i] * w_router[e, i], accumulated in float32.
+ *   MOE_ROUTING_SOFTMAX: l = logits (+ logit_bias[e]);
+ *     topk_idx[t, 0..k-1] = the k largest l, ordered by value descending, ties to the lower e;
+ *     topk_w[t, j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected (sums to 1).
+ *   MOE_ROUTING_SIGMOID: a_e = sigmoid(logits[t, e]) = 1 / (1 + exp(-logits[t, e]));
+ *     topk_idx[t, 0..k-1] = the k largest a_e + logit_bias[e] (same order and tie rule);
+ *     topk_w[t, j] = a_j / sum_i a_i over the k selected (the bias does not enter the weights).
+ * x [T, d] (dtype); w_router [E, d] (dtype); logit_bias [E] float32 or NULL (softmax: added to
+ * the logits before both selection and softmax; sigmoid: added to the sigmoid scores for the
+ * selection only); logits_out [T, E] float32 or NULL (softmax: the logits with the bias added;
+ * sigmoid: the plain logits); topk_idx [T, k] int32 and topk_w [T, k] float32 are required outputs.
+ * NaN logits rank below every other score.
  */
 moe_status moe_route(const moe_shape* s, const void* x, const void* w_router, const float* logit_bias,
                      float* logits_out, int32_t* topk_idx, float* topk_w, void* workspace, size_t ws_bytes,

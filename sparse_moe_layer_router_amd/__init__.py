@@ -24,6 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_FRAG16 = 0, 1
+MOE_ROUTING_SOFTMAX, MOE_ROUTING_SIGMOID = 0, 1
 STAGES = ["route_logits", "route_topk", "permute_count", "permute_scan", "permute_scatter", "ffn_schedule",
           "ffn_gate_up", "ffn_down", "combine"]
 MOE_NUM_STAGES = len(STAGES)
@@ -32,16 +33,18 @@ MOE_NUM_STAGES = len(STAGES)
 class moe_shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("d_hidden", ctypes.c_int32), ("d_shared_hidden", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("weight_layout", ctypes.c_int32), ("routing", ctypes.c_int32)]
 
 
 def make_shape(T, d_model, n_experts, top_k, d_hidden, d_shared_hidden=0, dtype=MOE_BF16,
-               weight_layout=MOE_LAYOUT_ROWMAJOR) -> moe_shape:
+               weight_layout=MOE_LAYOUT_ROWMAJOR, routing=MOE_ROUTING_SOFTMAX) -> moe_shape:
     if isinstance(dtype, str):
         dtype = {"bf16": MOE_BF16, "f32": MOE_F32}[dtype]
     elif isinstance(dtype, torch.dtype):
         dtype = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[dtype]
-    return moe_shape(T, d_model, n_experts, top_k, d_hidden, d_shared_hidden, dtype, weight_layout)
+    if isinstance(routing, str):
+        routing = {"softmax": MOE_ROUTING_SOFTMAX, "sigmoid": MOE_ROUTING_SIGMOID}[routing]
+    return moe_shape(T, d_model, n_experts, top_k, d_hidden, d_shared_hidden, dtype, weight_layout, routing)
 
 
 class MoeError(RuntimeError):

@@ -10,10 +10,13 @@ namespace moe {
 // ---- routing -------------------------------------------------------------------------------
 hipError_t launch_route_logits(int dtype, const void* x, const void* w_router, const float* bias,
                                float* logits, int T, int E, int d, hipStream_t stream);
-hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
-                             hipStream_t stream);
+// routing rule (moe_routing): softmax over the top-k logits, or sigmoid scores with a selection-only
+// bias (score_bias [E] or NULL; unused by the softmax rule, whose bias is added to the logits)
+enum Routing { kRoutingSoftmax = 0, kRoutingSigmoid = 1 };
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int routing, const float* score_bias,
+                             int32_t* topk_idx, float* topk_w, hipStream_t stream);
 const char* route_logits_kernel_name(int dtype, int T, int E);
-const char* route_topk_kernel_name(int E);
+const char* route_topk_kernel_name(int E, int routing);
 
 // Decode-sized batches (T <= 16 tokens, one per wave of the block; T*k <= 4096 slots): top-k,
 // softmax and the whole dispatch (counts, offsets, perm_src, inv_perm) in one single-block launch
@@ -22,10 +25,10 @@ const char* route_topk_kernel_name(int E);
 constexpr int kSmallTailMaxTokens = 16;
 constexpr int kSmallTailMaxRows = 4096;
 bool route_tail_fused(int T, int k);
-hipError_t launch_route_tail_small(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
-                                   int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
-                                   hipStream_t stream);
-const char* route_tail_small_kernel_name(int E);
+hipError_t launch_route_tail_small(const float* logits, int T, int E, int k, int routing, const float* score_bias,
+                                   int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                                   int32_t* perm_src, int32_t* inv_perm, hipStream_t stream);
+const char* route_tail_small_kernel_name(int E, int routing);
 
 // ---- permutation ---------------------------------------------------------------------------
 // Rows are cut into tiles of `tile` flat slots; `tile_counts` holds [n_tiles, E] int32.

@@ -54,6 +54,7 @@ moe_status check_shape(const moe_shape* s) {
   if ((long long)s->T * s->top_k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (s->d_model % 8 || s->d_hidden % 8 || s->d_shared_hidden % 8) return MOE_ERR_ALIGNMENT;
   if (s->weight_layout != MOE_LAYOUT_ROWMAJOR && s->weight_layout != MOE_LAYOUT_FRAG16) return MOE_ERR_UNSUPPORTED;
+  if (s->routing != MOE_ROUTING_SOFTMAX && s->routing != MOE_ROUTING_SIGMOID) return MOE_ERR_UNSUPPORTED;
   if (s->weight_layout == MOE_LAYOUT_FRAG16) {
     // every expert matrix ([H, d], [d, H], [Hs, d], [d, Hs]) must tile into 16 x 32 blocks
     if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
@@ -108,11 +109,14 @@ char* at(void* base, size_t off) { return (char*)base + off; }
 
 moe_status route_impl(const moe_shape& s, const void* x, const void* w_router, const float* bias, float* logits,
                       int32_t* idx, float* w, const Events& ev, hipStream_t stream) {
+  const bool sig = s.routing == MOE_ROUTING_SIGMOID;
   MOE_MARK(ev, MOE_STAGE_ROUTE_LOGITS, 0);
-  MOE_LAUNCH(moe::launch_route_logits(s.dtype, x, w_router, bias, logits, s.T, s.n_experts, s.d_model, stream));
+  MOE_LAUNCH(moe::launch_route_logits(s.dtype, x, w_router, sig ? nullptr : bias, logits, s.T, s.n_experts,
+                                      s.d_model, stream));
   MOE_MARK(ev, MOE_STAGE_ROUTE_LOGITS, 1);
   MOE_MARK(ev, MOE_STAGE_ROUTE_TOPK, 0);
-  MOE_LAUNCH(moe::launch_route_topk(logits, s.T, s.n_experts, s.top_k, idx, w, stream));
+  MOE_LAUNCH(moe::launch_route_topk(logits, s.T, s.n_experts, s.top_k, s.routing, sig ? bias : nullptr, idx, w,
+                                    stream));
   MOE_MARK(ev, MOE_STAGE_ROUTE_TOPK, 1);
   return MOE_OK;
 }
@@ -225,12 +229,14 @@ moe_status layer_impl(const moe_shape* sp, const void* x, const void* w_router, 
 
   if (moe::route_tail_fused(s.T, s.top_k)) {
     // decode-sized batch: top-k, softmax and the dispatch in one launch after the logits
+    const bool sig = s.routing == MOE_ROUTING_SIGMOID;
     MOE_MARK(ev, MOE_STAGE_ROUTE_LOGITS, 0);
-    MOE_LAUNCH(moe::launch_route_logits(s.dtype, x, w_router, bias, logits, s.T, s.n_experts, s.d_model, stream));
+    MOE_LAUNCH(moe::launch_route_logits(s.dtype, x, w_router, sig ? nullptr : bias, logits, s.T, s.n_experts,
+                                        s.d_model, stream));
     MOE_MARK(ev, MOE_STAGE_ROUTE_LOGITS, 1);
     MOE_MARK(ev, MOE_STAGE_ROUTE_TOPK, 0);
-    MOE_LAUNCH(moe::launch_route_tail_small(logits, s.T, s.n_experts, s.top_k, idx, w, counts, offsets, perm_src,
-                                            inv_perm, stream));
+    MOE_LAUNCH(moe::launch_route_tail_small(logits, s.T, s.n_experts, s.top_k, s.routing, sig ? bias : nullptr, idx,
+                                            w, counts, offsets, perm_src, inv_perm, stream));
     MOE_MARK(ev, MOE_STAGE_ROUTE_TOPK, 1);
     for (int st = MOE_STAGE_PERMUTE_COUNT; st <= MOE_STAGE_PERMUTE_SCATTER; ++st) {
       MOE_MARK(ev, st, 0);
@@ -378,8 +384,8 @@ const char* moe_stage_kernel_name(const moe_shape* s, int stage) {
   switch (stage) {
     case MOE_STAGE_ROUTE_LOGITS: return moe::route_logits_kernel_name(s->dtype, s->T, s->n_experts);
     case MOE_STAGE_ROUTE_TOPK:
-      return moe::route_tail_fused(s->T, s->top_k) ? moe::route_tail_small_kernel_name(s->n_experts)
-                                               : moe::route_topk_kernel_name(s->n_experts);
+      return moe::route_tail_fused(s->T, s->top_k) ? moe::route_tail_small_kernel_name(s->n_experts, s->routing)
+                                               : moe::route_topk_kernel_name(s->n_experts, s->routing);
     case MOE_STAGE_PERMUTE_COUNT: return moe::route_tail_fused(s->T, s->top_k) ? "" : "permute_count_kernel";
     case MOE_STAGE_PERMUTE_SCAN: return moe::route_tail_fused(s->T, s->top_k) ? "" : "permute_scan_kernel";
     case MOE_STAGE_PERMUTE_SCATTER: return moe::route_tail_fused(s->T, s->top_k) ? "" : "permute_scatter_kernel";

@@ -70,22 +70,32 @@ __device__ __forceinline__ int wave_reduce(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Top-k and softmax of one token's logits row by one wave. Writes topk_idx/topk_w of the token
-// (and, when lds_ids is not NULL, a copy of the ids into LDS).
-template <int NPER>
-__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int32_t* __restrict__ idx_out,
-                                           float* __restrict__ w_out, int32_t* lds_ids, int lane) {
-  float v[NPER];
+// Top-k and weights of one token's logits row by one wave. SIG = 0: ranks the logits (any logit
+// bias is already inside them), weights = softmax over the k. SIG = 1: ranks sigmoid(l) + bias[e]
+// (bias may be NULL), weights = the selected sigmoid(l) over their sum. Writes topk_idx/topk_w of
+// the token (and, when lds_ids is not NULL, a copy of the ids into LDS).
+template <int NPER, int SIG>
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, const float* __restrict__ bias,
+                                           int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* lds_ids,
+                                           int lane) {
+  float v[NPER];  // the score that decides the selection
+  float a[NPER];  // sigmoid routing: the unbiased affinity that enters the weights
   uint32_t taken = 0;
 #pragma unroll
   for (int j = 0; j < NPER; ++j) {
     const int e = lane + 64 * j;
     const bool ok = e < E;
     const float val = ok ? row[e] : 0.f;
-    v[j] = (val != val) ? -__builtin_inff() : val;  // NaN orders like -inf so k ids are always chosen
+    const bool nan = val != val;
+    if (SIG) {
+      a[j] = nan ? 0.f : 1.0f / (1.0f + expf(-val));
+      v[j] = nan ? -__builtin_inff() : a[j] + ((bias && ok) ? bias[e] : 0.f);
+    } else {
+      v[j] = nan ? -__builtin_inff() : val;  // NaN orders like -inf so k ids are always chosen
+    }
     if (!ok) taken |= 1u << j;
   }
-  float sel[NPER];  // selected value of slot s = lane + 64*j
+  float sel[NPER];  // weight source of slot s = lane + 64*j: its logit (softmax) or affinity (sigmoid)
 #pragma unroll
   for (int j = 0; j < NPER; ++j) sel[j] = 0.f;
 
@@ -99,22 +109,37 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
     }
     const float m = __int_as_float(wave_reduce<true>(__float_as_int(bv)));
     const int win = wave_reduce<false>((bi != 0x7FFFFFFF && bv == m) ? bi : 0x7FFFFFFF);
+    float src = m;
+    if (SIG) {  // the winner's affinity, from the lane that holds it
+      float mine = 0.f;
+#pragma unroll
+      for (int j = 0; j < NPER; ++j)
+        if (j == (win >> 6)) mine = a[j];
+      src = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), win & 63));
+    }
     if ((win & 63) == lane) taken |= 1u << (win >> 6);
     if ((s & 63) == lane) {
-      sel[s >> 6] = m;  // s >> 6 < NPER because k <= E
+      sel[s >> 6] = src;  // s >> 6 < NPER because k <= E
       idx_out[s] = win;
       if (lds_ids) lds_ids[s] = win;
     }
   }
-  // softmax over the k selected, shifted by the largest (slot 0, held by lane 0)
-  const float mx = __shfl(sel[0], 0, 64);
   float ex[NPER];
   float part = 0.f;
+  if (SIG) {
 #pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    const int s = lane + 64 * j;
-    ex[j] = (s < k) ? expf(sel[j] - mx) : 0.f;
-    part += ex[j];
+    for (int j = 0; j < NPER; ++j) {
+      ex[j] = (lane + 64 * j < k) ? sel[j] : 0.f;
+      part += ex[j];
+    }
+  } else {
+    // softmax over the k selected, shifted by the largest (slot 0, held by lane 0)
+    const float mx = __shfl(sel[0], 0, 64);
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      ex[j] = (lane + 64 * j < k) ? expf(sel[j] - mx) : 0.f;
+      part += ex[j];
+    }
   }
   const float total = wave_sum(part);
 #pragma unroll
@@ -124,13 +149,14 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
   }
 }
 
-template <int NPER>
+template <int NPER, int SIG>
 __global__ void __launch_bounds__(256)
-route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
-                  float* __restrict__ topk_w) {
+route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, const float* __restrict__ bias,
+                  int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_token<NPER>(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, nullptr, lane_id());
+  topk_token<NPER, SIG>(logits + (size_t)t * E, E, k, bias, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, nullptr,
+                        lane_id());
 }
 
 // ------------------------------------------------------------------------------ small batches
@@ -142,9 +168,10 @@ route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t
 constexpr int kTailWaves = 16;
 static_assert(kSmallTailMaxTokens <= kTailWaves, "one token per wave");
 
-template <int NPER>
+template <int NPER, int SIG>
 __global__ void __launch_bounds__(kTailWaves * 64)
-route_tail_small_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
+route_tail_small_kernel(const float* __restrict__ logits, int T, int E, int k, const float* __restrict__ bias,
+                        int32_t* __restrict__ topk_idx,
                         float* __restrict__ topk_w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                         int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_perm) {
   __shared__ int32_t ids[kSmallTailMaxRows];
@@ -152,8 +179,8 @@ route_tail_small_kernel(const float* __restrict__ logits, int T, int E, int k, i
   __shared__ int32_t wave_tot[kTailWaves];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   for (int t = wave; t < T; t += kTailWaves)
-    topk_token<NPER>(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, ids + t * k,
-                     lane);
+    topk_token<NPER, SIG>(logits + (size_t)t * E, E, k, bias, topk_idx + (size_t)t * k, topk_w + (size_t)t * k,
+                          ids + t * k, lane);
   for (int e = threadIdx.x; e < E; e += kTailWaves * 64) cur[e] = 0;
   __syncthreads();
   const int rows = T * k;
@@ -226,21 +253,25 @@ static int nper_of(int E) {
   return n;
 }
 
-#define MOE_NPER_SWITCH(E, F) \
-  switch (nper_of(E)) {       \
-    case 1: F(1); break;      \
-    case 2: F(2); break;      \
-    case 4: F(4); break;      \
-    case 8: F(8); break;      \
-    default: F(16); break;    \
+#define MOE_NPER_SWITCH(E, F, S) \
+  switch (nper_of(E)) {          \
+    case 1: F(1, S); break;      \
+    case 2: F(2, S); break;      \
+    case 4: F(4, S); break;      \
+    case 8: F(8, S); break;      \
+    default: F(16, S); break;    \
   }
 
-hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
-                             hipStream_t stream) {
-#define MOE_TOPK(N)                                                                                               \
-  hipLaunchKernelGGL(route_topk_kernel<N>, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, topk_idx, \
-                     topk_w)
-  MOE_NPER_SWITCH(E, MOE_TOPK)
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int routing, const float* score_bias,
+                             int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+#define MOE_TOPK(N, S)                                                                                 \
+  hipLaunchKernelGGL((route_topk_kernel<N, S>), dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, \
+                     score_bias, topk_idx, topk_w)
+  if (routing == kRoutingSigmoid) {
+    MOE_NPER_SWITCH(E, MOE_TOPK, 1)
+  } else {
+    MOE_NPER_SWITCH(E, MOE_TOPK, 0)
+  }
 #undef MOE_TOPK
   return hipGetLastError();
 }
@@ -252,28 +283,41 @@ const char* route_logits_kernel_name(int dtype, int T, int) {
 
 bool route_tail_fused(int T, int k) { return T <= kSmallTailMaxTokens && (long long)T * k <= kSmallTailMaxRows; }
 
-hipError_t launch_route_tail_small(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
-                                   int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
-                                   hipStream_t stream) {
-#define MOE_TAIL(N)                                                                                             \
-  hipLaunchKernelGGL(route_tail_small_kernel<N>, dim3(1), dim3(kTailWaves * 64), 0, stream, logits, T, E, k, \
-                     topk_idx, topk_w, counts, offsets, perm_src, inv_perm)
-  MOE_NPER_SWITCH(E, MOE_TAIL)
+hipError_t launch_route_tail_small(const float* logits, int T, int E, int k, int routing, const float* score_bias,
+                                   int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                                   int32_t* perm_src, int32_t* inv_perm, hipStream_t stream) {
+#define MOE_TAIL(N, S)                                                                                           \
+  hipLaunchKernelGGL((route_tail_small_kernel<N, S>), dim3(1), dim3(kTailWaves * 64), 0, stream, logits, T, E, k, \
+                     score_bias, topk_idx, topk_w, counts, offsets, perm_src, inv_perm)
+  if (routing == kRoutingSigmoid) {
+    MOE_NPER_SWITCH(E, MOE_TAIL, 1)
+  } else {
+    MOE_NPER_SWITCH(E, MOE_TAIL, 0)
+  }
 #undef MOE_TAIL
   return hipGetLastError();
 }
 
-static const char* const kTopkNames[] = {"route_topk_kernel<1>", "route_topk_kernel<2>", "route_topk_kernel<4>",
-                                         "route_topk_kernel<8>", "route_topk_kernel<16>"};
-static const char* const kTailNames[] = {"route_tail_small_kernel<1>", "route_tail_small_kernel<2>",
-                                         "route_tail_small_kernel<4>", "route_tail_small_kernel<8>",
-                                         "route_tail_small_kernel<16>"};
+static const char* const kTopkNames[2][5] = {
+    {"route_topk_kernel<1, 0>", "route_topk_kernel<2, 0>", "route_topk_kernel<4, 0>", "route_topk_kernel<8, 0>",
+     "route_topk_kernel<16, 0>"},
+    {"route_topk_kernel<1, 1>", "route_topk_kernel<2, 1>", "route_topk_kernel<4, 1>", "route_topk_kernel<8, 1>",
+     "route_topk_kernel<16, 1>"}};
+static const char* const kTailNames[2][5] = {
+    {"route_tail_small_kernel<1, 0>", "route_tail_small_kernel<2, 0>", "route_tail_small_kernel<4, 0>",
+     "route_tail_small_kernel<8, 0>", "route_tail_small_kernel<16, 0>"},
+    {"route_tail_small_kernel<1, 1>", "route_tail_small_kernel<2, 1>", "route_tail_small_kernel<4, 1>",
+     "route_tail_small_kernel<8, 1>", "route_tail_small_kernel<16, 1>"}};
 static int nper_slot(int E) {
   int n = nper_of(E), i = 0;
   while ((1 << i) < n) ++i;
   return i;
 }
-const char* route_topk_kernel_name(int E) { return kTopkNames[nper_slot(E)]; }
-const char* route_tail_small_kernel_name(int E) { return kTailNames[nper_slot(E)]; }
+const char* route_topk_kernel_name(int E, int routing) {
+  return kTopkNames[routing == kRoutingSigmoid ? 1 : 0][nper_slot(E)];
+}
+const char* route_tail_small_kernel_name(int E, int routing) {
+  return kTailNames[routing == kRoutingSigmoid ? 1 : 0][nper_slot(E)];
+}
 
 }  // namespace moe

@@ -9,7 +9,8 @@ filled directly in device memory.
 Shapes follow the configurations the layer is measured on: a tiny fp32 layer, a DeepSeek-V3-shaped
 layer (d_model 7168, 256 routed SwiGLU experts of hidden 2048 plus one shared expert, top-8) at
 T = 8, 256 and 8192 tokens, and a Mixtral-shaped skewed layer (d_model 4096, 8 experts of hidden
-14336, top-2, router logits biased by 2 ln of a Zipf(1.2) law). Weights are N(0, std = 1/sqrt(fan_in)),
+14336, top-2, router logits biased by 2 ln of a Zipf(1.2) law); the decode layer also comes with
+sigmoid routing and a selection-only expert bias N(0, 0.05^2). Weights are N(0, std = 1/sqrt(fan_in)),
 activations N(0, 1).
 """
 
@@ -18,6 +19,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import dataclasses
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -26,7 +28,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
 # stream kinds: stream id = kind * 2**40 + index
-K_X, K_WG, K_GATE, K_UP, K_DOWN, K_SGATE, K_SUP, K_SDOWN, K_REDRAW = range(1, 10)
+K_X, K_WG, K_GATE, K_UP, K_DOWN, K_SGATE, K_SUP, K_SDOWN, K_REDRAW, K_SBIAS = range(1, 11)
 _KSHIFT = 1 << 40
 
 
@@ -116,7 +118,9 @@ class LayerConfig:
     H: int
     Hs: int          # shared-expert hidden size, 0 = none
     dtype: str       # "f32" or "bf16"
-    zipf_s: float | None = None
+    zipf_s: float | None = None          # softmax routing: logit bias 2 ln Zipf(s)
+    routing: str = "softmax"             # "softmax" (top-k of logits, softmax over the k) or "sigmoid"
+    score_bias_std: float | None = None  # sigmoid routing: selection bias b_e ~ N(0, std^2), fp32
     note: str = field(default="", compare=False)
 
 
@@ -131,12 +135,15 @@ CONFIGS = [
                 note="DeepSeek-V3-shaped layer, prefill chunk of 8192, ~256 tokens per expert"),
     LayerConfig("skewed_mixtral_t4096", 4096, 4096, 8, 2, 14336, 0, "bf16", zipf_s=1.2,
                 note="8 experts of hidden 14336, top-2, Zipf(1.2) router bias"),
+    LayerConfig("dsv3_sigmoid_decode_t8", 8, 7168, 256, 8, 2048, 2048, "bf16", routing="sigmoid",
+                score_bias_std=0.05,
+                note="the decode layer with sigmoid routing and a selection-only expert bias"),
 ]
 CONFIG_BY_NAME = {c.name: c for c in CONFIGS}
 
 
 def with_tokens(cfg: LayerConfig, T: int) -> LayerConfig:
-    return LayerConfig(cfg.name, T, cfg.d, cfg.E, cfg.k, cfg.H, cfg.Hs, cfg.dtype, cfg.zipf_s, cfg.note)
+    return dataclasses.replace(cfg, T=T)
 
 
 def zipf_logit_bias(E: int, s: float) -> np.ndarray:
@@ -158,15 +165,24 @@ class HostInputs:
     seed: int
     x: np.ndarray
     w_router: np.ndarray
-    logit_bias: np.ndarray | None
+    logit_bias: np.ndarray | None               # softmax routing: added to the logits
     redraws: dict = field(default_factory=dict)   # token -> attempts used
+    score_bias: np.ndarray | None = None        # sigmoid routing: added to the scores for selection
+
+    @property
+    def router_bias(self) -> np.ndarray | None:
+        """The one per-expert bias vector the layer takes, whichever routing it belongs to."""
+        return self.score_bias if self.cfg.routing == "sigmoid" else self.logit_bias
 
 
 def host_small_inputs(cfg: LayerConfig, seed: int = 0) -> HostInputs:
     x = normal_host((cfg.T, cfg.d), seed, stream_id(K_X), 1.0, cfg.dtype)
     wg = normal_host((cfg.E, cfg.d), seed, stream_id(K_WG), weight_std(cfg.d), cfg.dtype)
     bias = zipf_logit_bias(cfg.E, cfg.zipf_s) if cfg.zipf_s is not None else None
-    return HostInputs(cfg, seed, x, wg, bias)
+    sbias = None
+    if cfg.score_bias_std is not None:
+        sbias = normal_host((cfg.E,), seed, stream_id(K_SBIAS), cfg.score_bias_std, "f32")
+    return HostInputs(cfg, seed, x, wg, bias, score_bias=sbias)
 
 
 def redraw_rows(inp: HostInputs, rows) -> None:

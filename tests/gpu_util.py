@@ -47,7 +47,7 @@ class DeviceLayer:
     @property
     def shape(self):
         c = self.cfg
-        return moe.make_shape(c.T, c.d, c.E, c.k, c.H, c.Hs, c.dtype, self.layout)
+        return moe.make_shape(c.T, c.d, c.E, c.k, c.H, c.Hs, c.dtype, self.layout, c.routing)
 
     def expert_fn(self, cache=True):
         return helpers.expert_fn_host(self.cfg, self.seed, self.stacked_host, cache=cache)
@@ -98,7 +98,7 @@ def make_layer(cfg: synth.LayerConfig, seed: int = 0, screen: bool = True, weigh
         if layout == moe.MOE_LAYOUT_FRAG16:
             weights = packed_weights(weights)
     (g, u, dn), (sg, su, sd), stacked = weights
-    bias = torch.from_numpy(host.logit_bias).cuda() if host.logit_bias is not None else None
+    bias = torch.from_numpy(host.router_bias).cuda() if host.router_bias is not None else None
     return DeviceLayer(cfg, seed, host, to_dev(host.x, cfg.dtype), to_dev(host.w_router, cfg.dtype), bias,
                        g, u, dn, sg, su, sd, stacked, layout)
 
@@ -136,7 +136,9 @@ def tolerance_ok(gpu: np.ndarray, ref: np.ndarray):
 
 
 def oracle_inputs(L: DeviceLayer):
+    """(x, W_g, bias) in float64/float32 as the oracle takes them; the bias is the one the routing
+    rule uses (logit bias for softmax routing, selection bias for sigmoid routing)."""
     c = L.cfg
     x = oracle.widen(L.host.x, c.dtype)
     wg = oracle.widen(L.host.w_router, c.dtype)
-    return x, wg, L.host.logit_bias
+    return x, wg, L.host.router_bias

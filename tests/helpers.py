@@ -11,7 +11,9 @@ MIN_GAP = 1e-4   # tokens whose k-th and (k+1)-th router scores are closer than 
 
 
 def screen_gaps(inp: synth.HostInputs, min_gap: float = MIN_GAP, max_rounds: int = 64) -> int:
-    """Redraw activation rows whose top-k margin (fp64 oracle logits) is below ``min_gap``.
+    """Redraw activation rows whose top-k margin is below ``min_gap``: the margin between the k-th
+    and (k+1)-th fp64 selection scores (the logits with any logit bias for softmax routing; the
+    sigmoid affinities plus the selection bias for sigmoid routing).
 
     Rejection happens per token: a near-tie row is replaced by the next draw of its own redraw
     stream until every token clears the margin. Returns the number of rows redrawn.
@@ -21,7 +23,8 @@ def screen_gaps(inp: synth.HostInputs, min_gap: float = MIN_GAP, max_rounds: int
     redrawn = 0
     for _ in range(max_rounds):
         L = oracle.router_logits(oracle.widen(inp.x, cfg.dtype), wg, inp.logit_bias)
-        bad = np.nonzero(oracle.topk_gap(L, cfg.k) < min_gap)[0]
+        S = oracle.selection_scores(L, cfg.routing, inp.score_bias)
+        bad = np.nonzero(oracle.topk_gap(S, cfg.k) < min_gap)[0]
         if bad.size == 0:
             return redrawn
         synth.redraw_rows(inp, bad)

@@ -76,6 +76,8 @@ def status_of(fn, *a, **k):
     (dict(d_shared_hidden=12), moe.MOE_ERR_ALIGNMENT),
     (dict(dtype=7), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=300_000_000), moe.MOE_ERR_UNSUPPORTED),
+    (dict(routing=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(routing=-1), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_shape_validation(shape, status):
     s = dsv3(**shape)
@@ -129,15 +131,19 @@ def test_status_strings_and_stage_names():
     names = [moe.moe_stage_kernel_name(s, i) for i in range(moe.MOE_NUM_STAGES)]
     assert names[5] == "" and "gate_up" in names[6] and "down" in names[7]     # decode: GEMV, no schedule
     # decode-sized batch: top-k, softmax and dispatch in one launch, the permute stages launch nothing
-    assert names[1] == "route_tail_small_kernel<4>" and names[2:5] == ["", "", ""]
-    assert moe.moe_stage_kernel_name(dsv3(T=16, top_k=256), 1) == "route_tail_small_kernel<4>"   # 4096 slots
-    assert moe.moe_stage_kernel_name(dsv3(T=17), 1) == "route_topk_kernel<4>"
+    assert names[1] == "route_tail_small_kernel<4, 0>" and names[2:5] == ["", "", ""]
+    assert moe.moe_stage_kernel_name(dsv3(T=16, top_k=256), 1) == "route_tail_small_kernel<4, 0>"   # 4096 slots
+    assert moe.moe_stage_kernel_name(dsv3(T=17), 1) == "route_topk_kernel<4, 0>"
     assert moe.moe_stage_kernel_name(dsv3(T=17), 2) == "permute_count_kernel"
-    assert moe.moe_stage_kernel_name(dsv3(T=256), 1) == "route_topk_kernel<4>"
+    assert moe.moe_stage_kernel_name(dsv3(T=256), 1) == "route_topk_kernel<4, 0>"
     names = [moe.moe_stage_kernel_name(dsv3(T=8192), i) for i in range(moe.MOE_NUM_STAGES)]
-    assert names[0] == "grouped_gemm_kernel<2, 0>" and names[1] == "route_topk_kernel<4>"
+    assert names[0] == "grouped_gemm_kernel<2, 0>" and names[1] == "route_topk_kernel<4, 0>"
     assert names[2:5] == ["permute_count_kernel", "permute_scan_kernel", "permute_scatter_kernel"]
     assert names[5] == "gemm_schedule_kernel"
+    sig = moe.MOE_ROUTING_SIGMOID
+    assert moe.moe_stage_kernel_name(dsv3(routing=sig), 1) == "route_tail_small_kernel<4, 1>"
+    assert moe.moe_stage_kernel_name(dsv3(T=4096, routing=sig), 1) == "route_topk_kernel<4, 1>"
+    assert moe.moe_stage_kernel_name(dsv3(T=4096, n_experts=8, top_k=2, routing=sig), 1) == "route_topk_kernel<1, 1>"
     assert names[6] == "grouped_gemm_kernel<0, 0>" and names[7] == "grouped_gemm_kernel<1, 0>"
     packed = dsv3(T=8, weight_layout=moe.MOE_LAYOUT_FRAG16)
     assert moe.moe_stage_kernel_name(packed, 6) == "ffn_gate_up_stream<1, 1>"

@@ -1,12 +1,14 @@
 """HIP path vs the oracle at the full layer sizes the throughput is measured on (needs an MI355X).
 
 DeepSeek-V3-shaped layer (d 7168, 256 routed experts of hidden 2048 + one shared, top-8) at
-T = 8, 256 and 8192, and the Mixtral-shaped skewed layer (d 4096, 8 experts of hidden 14336,
+T = 8, 256 and 8192 (and with sigmoid routing at T = 8 and 4096), and the Mixtral-shaped skewed layer (d 4096, 8 experts of hidden 14336,
 top-2, Zipf router bias) at T = 4096. The 22.5 GB DeepSeek weight set is drawn once in device
 memory; the oracle regenerates on the host exactly the experts it needs. Routing and permutation
 are checked bit-exactly on the GPU logits for every token; outputs are checked for every token at
 T = 8 and for a seeded sample of tokens otherwise (a token's output depends on its row only).
 """
+
+import dataclasses
 
 import numpy as np
 import pytest
@@ -33,7 +35,8 @@ def dsv3_weights():
 
 def sampled_check(L, r, tokens):
     x, wg, b = G.oracle_inputs(L)
-    ref = oracle.layer_forward_tokens(x[tokens], wg, L.cfg.k, L.expert_fn(cache=False), L.shared_fn(), b)
+    ref = oracle.layer_forward_tokens(x[tokens], wg, L.cfg.k, L.expert_fn(cache=False), L.shared_fn(), b,
+                                      L.cfg.routing)
     np.testing.assert_array_equal(np.sort(r.idx.cpu().numpy()[tokens], 1), np.sort(ref["idx"], 1))
     ok, err, bound = G.tolerance_ok(G.to_f64(r.out)[tokens], ref["out"])
     assert ok, (err, bound)
@@ -46,7 +49,7 @@ def sample_tokens(T, n, seed=0):
 
 @pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_FRAG16, moe.MOE_LAYOUT_ROWMAJOR], ids=["frag16", "rowmajor"])
 @pytest.mark.parametrize("name,n_sample", [("dsv3_decode_t8", None), ("dsv3_decode_t256", 12),
-                                           ("dsv3_prefill_t8192", 8)])
+                                           ("dsv3_prefill_t8192", 8), ("dsv3_sigmoid_decode_t8", None)])
 def test_dsv3_layer(name, n_sample, layout, dsv3_weights):
     cfg = synth.CONFIG_BY_NAME[name]
     L = G.make_layer(cfg, weights=dsv3_weights[layout], layout=layout)
@@ -56,6 +59,17 @@ def test_dsv3_layer(name, n_sample, layout, dsv3_weights):
     check_routing_on_gpu_logits(L, r)
     tokens = np.arange(cfg.T) if n_sample is None else sample_tokens(cfg.T, n_sample)
     sampled_check(L, r, tokens)
+
+
+def test_dsv3_sigmoid_layer_router_gemm_size(dsv3_weights):
+    """Sigmoid routing at 4096 tokens: the router GEMM (no bias in its epilogue), the one-wave-per-
+    token top-k and the grouped GEMM experts, on the packed weights."""
+    cfg = dataclasses.replace(synth.CONFIG_BY_NAME["dsv3_sigmoid_decode_t8"], name="dsv3_sigmoid_t4096", T=4096)
+    L = G.make_layer(cfg, weights=dsv3_weights[moe.MOE_LAYOUT_FRAG16], layout=moe.MOE_LAYOUT_FRAG16)
+    r = G.run_layer(L)
+    check_logits_close(L, r)
+    check_routing_on_gpu_logits(L, r)
+    sampled_check(L, r, sample_tokens(cfg.T, 8))
 
 
 @pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_FRAG16, moe.MOE_LAYOUT_ROWMAJOR], ids=["frag16", "rowmajor"])

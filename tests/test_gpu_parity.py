@@ -36,6 +36,12 @@ MID = [
     LayerConfig("gemm_ragged_shared", 600, 264, 16, 2, 200, 136, "bf16"),
     # 2048 tokens: router GEMM too (E = 8 < one N tile), skewed buckets
     LayerConfig("gemm_zipf_router", 2048, 512, 8, 2, 384, 0, "bf16", zipf_s=1.2),
+    # sigmoid routing with a selection-only bias: one-wave-per-token top-k with the grouped GEMM,
+    # the single-block decode tail, float32 without a bias, and the router GEMM
+    LayerConfig("sigmoid_mid_shared", 300, 264, 16, 4, 200, 136, "bf16", routing="sigmoid", score_bias_std=0.05),
+    LayerConfig("sigmoid_small_fused", 12, 128, 64, 6, 64, 32, "bf16", routing="sigmoid", score_bias_std=0.05),
+    LayerConfig("sigmoid_fp32_nobias", 50, 96, 8, 3, 40, 24, "f32", routing="sigmoid"),
+    LayerConfig("sigmoid_gemm_router", 2048, 512, 8, 2, 384, 0, "bf16", routing="sigmoid", score_bias_std=0.05),
 ]
 
 
@@ -43,9 +49,14 @@ def check_routing_on_gpu_logits(L, r):
     """Oracle selection and permutation applied to the GPU's own logits: bit-exact."""
     c = L.cfg
     lg = r.logits.cpu().numpy().astype(np.float64)
-    idx_o = oracle.select_topk(lg, c.k)
+    if c.routing == "sigmoid":
+        idx_o = oracle.select_topk(oracle.selection_scores(lg, "sigmoid", L.host.score_bias), c.k)
+        w_o = oracle.sigmoid_weights_selected(lg, idx_o)
+    else:
+        idx_o = oracle.select_topk(lg, c.k)
+        w_o = oracle.softmax_selected(lg, idx_o)
     np.testing.assert_array_equal(r.idx.cpu().numpy(), idx_o)
-    np.testing.assert_allclose(r.w.cpu().numpy(), oracle.softmax_selected(lg, idx_o), rtol=0, atol=1e-5)
+    np.testing.assert_allclose(r.w.cpu().numpy(), w_o, rtol=0, atol=1e-5)
     counts_o, offsets_o, perm_o, inv_o = oracle.permute(idx_o, c.E)
     np.testing.assert_array_equal(r.counts.cpu().numpy(), counts_o)
     # the permutation entry point on the same ids
@@ -65,7 +76,7 @@ def check_routing_on_gpu_logits(L, r):
 
 def check_logits_close(L, r):
     x, wg, b = G.oracle_inputs(L)
-    lg_o = oracle.router_logits(x, wg, b)
+    lg_o = oracle.router_logits(x, wg, b if L.cfg.routing == "softmax" else None)
     err = np.abs(r.logits.cpu().numpy() - lg_o).max()
     assert err < 1e-4 + 1e-5 * np.abs(lg_o).max(), err
 
@@ -77,7 +88,7 @@ def test_layer_matches_oracle_mid_sizes(cfg):
     check_logits_close(L, r)
     check_routing_on_gpu_logits(L, r)
     x, wg, b = G.oracle_inputs(L)
-    ref = oracle.layer_forward(x, wg, cfg.k, L.expert_fn(), L.shared_fn(), b)
+    ref = oracle.layer_forward(x, wg, cfg.k, L.expert_fn(), L.shared_fn(), b, cfg.routing)
     # gap-screened: the selected sets agree with the oracle's own fp64 routing
     np.testing.assert_array_equal(np.sort(r.idx.cpu().numpy(), 1), np.sort(ref["idx"], 1))
     np.testing.assert_array_equal(r.counts.cpu().numpy(), ref["counts"])
@@ -85,7 +96,7 @@ def test_layer_matches_oracle_mid_sizes(cfg):
     assert ok, (err, bound)
 
 
-@pytest.mark.parametrize("cfg", MID[:3] + MID[-2:], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", MID[:3] + MID[9:11] + MID[-2:], ids=lambda c: c.name)
 def test_entry_points_separately(cfg):
     """moe_route -> moe_permute -> moe_grouped_ffn (routed, then shared as a one-group call) -> moe_combine."""
     L = G.make_layer(cfg)
@@ -113,7 +124,7 @@ def test_entry_points_separately(cfg):
     torch.cuda.synchronize()
 
     x, wg, b = G.oracle_inputs(L)
-    ref = oracle.layer_forward(x, wg, c.k, L.expert_fn(), L.shared_fn(), b)
+    ref = oracle.layer_forward(x, wg, c.k, L.expert_fn(), L.shared_fn(), b, c.routing)
     np.testing.assert_array_equal(np.sort(idx.cpu().numpy(), 1), np.sort(ref["idx"], 1))
     # expert outputs row by row in dispatch order (the dispatch order of the GPU's own routing)
     idx_g = idx.cpu().numpy()
@@ -136,13 +147,14 @@ FUSED = [
     LayerConfig("fused_boundary_4096_slots", 16, 64, 256, 256, 32, 0, "bf16"),
     LayerConfig("fused_k_equals_E", 9, 128, 4, 4, 64, 0, "bf16"),
     LayerConfig("fused_one_token_f32", 1, 64, 8, 3, 32, 0, "f32"),
+    LayerConfig("fused_sigmoid", 16, 256, 256, 8, 64, 0, "bf16", routing="sigmoid", score_bias_std=0.05),
 ]
 
 
 @pytest.mark.parametrize("cfg", FUSED, ids=lambda c: c.name)
 def test_fused_small_batch_dispatch_matches_entry_points(cfg):
     c = cfg
-    s = moe.make_shape(c.T, c.d, c.E, c.k, c.H, c.Hs, c.dtype)
+    s = moe.make_shape(c.T, c.d, c.E, c.k, c.H, c.Hs, c.dtype, routing=c.routing)
     assert moe.moe_stage_kernel_name(s, 1).startswith("route_tail_small_kernel<")
     L = G.make_layer(cfg)
     r = G.run_layer(L)
@@ -214,8 +226,9 @@ def test_route_ties_go_to_lower_index():
     np.testing.assert_array_equal(idx.cpu().numpy(), oracle.select_topk(lg.cpu().numpy().astype(np.float64), k))
 
 
+@pytest.mark.parametrize("routing", ["softmax", "sigmoid"])
 @pytest.mark.parametrize("E", [1, 3, 64, 65, 128, 200, 256, 300, 512, 777, 1024])
-def test_topk_tie_heavy_every_lane_width(E):
+def test_topk_tie_heavy_every_lane_width(E, routing):
     """Router rows drawn from a handful of distinct vectors and biases from a few values, so most
     logits tie exactly; every candidates-per-lane width (E up to 64, 128, 256, 512, 1024), through
     both the one-wave-per-token kernel (T=40) and the single-block decode tail (T=9, via the layer)."""
@@ -227,16 +240,25 @@ def test_topk_tie_heavy_every_lane_width(E):
     for T in (40, 9):
         k = min(E, 9)
         x = torch.randn(T, d, generator=g).to(torch.bfloat16).cuda()
-        s = moe.make_shape(T, d, E, k, 32, 0, "bf16")
+        s = moe.make_shape(T, d, E, k, 32, 0, "bf16", routing=routing)
         idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
         w = torch.empty(T, k, dtype=torch.float32, device="cuda")
         lg = torch.empty(T, E, dtype=torch.float32, device="cuda")
         moe.moe_route(s, x, wr, bias, lg, idx, w, moe.allocate_workspace(s))
         torch.cuda.synchronize()
         lg64 = lg.cpu().numpy().astype(np.float64)
-        idx_o = oracle.select_topk(lg64, k)
+        if routing == "sigmoid":
+            # the selection scores in the kernel's own precision (float32 sigmoid + bias), so that
+            # the exact ties between experts sharing a router row and a bias stay exact
+            a32 = (1.0 / (1.0 + np.exp(-lg.cpu().numpy().astype(np.float32)))).astype(np.float32)
+            S = (a32 + bias.cpu().numpy()).astype(np.float32).astype(np.float64)
+            idx_o = oracle.select_topk(S, k)
+            w_o = oracle.sigmoid_weights_selected(lg64, idx_o)
+        else:
+            idx_o = oracle.select_topk(lg64, k)
+            w_o = oracle.softmax_selected(lg64, idx_o)
         np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
-        np.testing.assert_allclose(w.cpu().numpy(), oracle.softmax_selected(lg64, idx_o), rtol=0, atol=1e-6)
+        np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=0, atol=1e-6)
         if T <= 16:   # the layer's fused tail must select the same ids from the same logits
             wg = torch.zeros(E, 32, d, dtype=torch.bfloat16, device="cuda")
             wd = torch.zeros(E, d, 32, dtype=torch.bfloat16, device="cuda")
@@ -308,7 +330,7 @@ def test_layer_matches_oracle_packed_weights(cfg):
     r = G.run_layer(L)
     check_routing_on_gpu_logits(L, r)
     x, wg, b = G.oracle_inputs(L)
-    ref = oracle.layer_forward(x, wg, cfg.k, L.expert_fn(), L.shared_fn(), b)
+    ref = oracle.layer_forward(x, wg, cfg.k, L.expert_fn(), L.shared_fn(), b, cfg.routing)
     np.testing.assert_array_equal(np.sort(r.idx.cpu().numpy(), 1), np.sort(ref["idx"], 1))
     ok, err, bound = G.tolerance_ok(G.to_f64(r.out), ref["out"])
     assert ok, (err, bound)
