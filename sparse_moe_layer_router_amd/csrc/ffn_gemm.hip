@@ -188,12 +188,17 @@ struct GemmArgs {
   int T, E, d;
 };
 
-template <int MODE, int LAYOUT>
-__global__ void __launch_bounds__(kThreads, 1)
-grouped_gemm_kernel(const GemmArgs ga) {
-  using G = Geo<MODE>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages][G::STAGE];
+// Tile count of a launch: from the router's sizes, or the schedule's running total.
+template <int MODE>
+__device__ __forceinline__ int gemm_total_tiles(const GemmArgs& ga) {
+  if (MODE == kRouter) return ((ga.T + BM - 1) / BM) * ((ga.E + Geo<MODE>::BN - 1) / Geo<MODE>::BN);
+  return ga.sched[ga.p.E + (ga.p.Hs > 0 ? 1 : 0)];
+}
 
+// One output tile t (0 <= t < gemm_total_tiles) through the LDS ring `smem`.
+template <int MODE, int LAYOUT>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8_t (*smem)[Geo<MODE>::STAGE]) {
+  using G = Geo<MODE>;
   const FfnGroups& p = ga.p;
   const int lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave index, 0..7
@@ -205,15 +210,7 @@ grouped_gemm_kernel(const GemmArgs ga) {
   int N = 0, K = 0;      // output columns (weight rows) and reduction length of this group
   const uint16_t* Bp[2] = {nullptr, nullptr};
   {
-    const int L = blockIdx.x;
-    int t;
     if (MODE == kRouter) {
-      const int ntn = (ga.E + G::BN - 1) / G::BN;
-      const int total = ((ga.T + BM - 1) / BM) * ntn;
-      const int per = (total + kXcds - 1) / kXcds;
-      if (L / kXcds >= per) return;
-      t = (L % kXcds) * per + L / kXcds;
-      if (t >= total) return;
       nt = t / ((ga.T + BM - 1) / BM);
       mt = t % ((ga.T + BM - 1) / BM);
       nrows = ga.T;
@@ -222,11 +219,6 @@ grouped_gemm_kernel(const GemmArgs ga) {
       Bp[0] = (const uint16_t*)ga.w;
     } else {
       const int ngroups = p.E + (p.Hs > 0 ? 1 : 0);
-      const int total = ga.sched[ngroups];
-      const int per = (total + kXcds - 1) / kXcds;
-      if (L / kXcds >= per) return;
-      t = (L % kXcds) * per + L / kXcds;
-      if (t >= total) return;
       int lo = 0, hi = ngroups;  // last group with sched[g] <= t
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -460,9 +452,42 @@ grouped_gemm_kernel(const GemmArgs ga) {
     }
 }
 
+// Tiles are numbered expert by expert, N-tile by N-tile, with the M-tiles of one (expert, N-tile)
+// adjacent, and dealt to the 8 XCDs in contiguous ranges (workgroup L runs on XCD L % 8). Each
+// workgroup walks its XCD's range with the stride of the workgroups on that XCD, so a launch of
+// one workgroup per CU is persistent: every round, the workgroups of one XCD take the next block
+// of adjacent tiles together, and the M-tiles that share a weight tile start at the same time and
+// stream it through L2 once. (A launch with a workgroup per tile runs each tile once.)
+template <int MODE, int LAYOUT>
+__global__ void __launch_bounds__(kThreads, 1)
+grouped_gemm_kernel(const GemmArgs ga) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages][Geo<MODE>::STAGE];
+  const int total = gemm_total_tiles<MODE>(ga);
+  const int per = (total + kXcds - 1) / kXcds;
+  const int xcd = (int)blockIdx.x % kXcds, stride = (int)gridDim.x / kXcds;
+  const int end = (xcd + 1) * per < total ? (xcd + 1) * per : total;
+  for (int t = xcd * per + (int)blockIdx.x / kXcds; t < end; t += stride) {
+    if (t >= xcd * per + stride) __syncthreads();  // the previous tile's LDS reads are over
+    gemm_tile<MODE, LAYOUT>(ga, t, smem);
+  }
+}
+
 // ------------------------------------------------------------------------------- launchers
 namespace {
 int round8(long long v) { return (int)((v + kXcds - 1) / kXcds * kXcds); }
+
+// Workgroups of a launch: one per tile up to one per CU (a persistent launch: each workgroup then
+// loops over tiles, see grouped_gemm_kernel), rounded to whole XCD sets.
+int gemm_grid(long long tiles_upper) {
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 0;
+  const long long slots = n_cu >= kXcds ? (long long)(n_cu / kXcds) * kXcds : kXcds;
+#ifdef MOE_GEMM_ONE_TILE_PER_WG
+  return round8(tiles_upper);
+#endif
+  return round8(tiles_upper < slots ? tiles_upper : slots);
+}
 }  // namespace
 
 long long gemm_tiles_upper(const FfnGroups& p, int mode) {
@@ -487,7 +512,7 @@ hipError_t launch_gemm_gate_up(const FfnGroups& p, const int32_t* sched, hipStre
   GemmArgs a{};
   a.p = p;
   a.sched = sched;
-  const dim3 grid(round8(gemm_tiles_upper(p, kGateUp)));
+  const dim3 grid(gemm_grid(gemm_tiles_upper(p, kGateUp)));
   if (p.layout == kFrag16)
     hipLaunchKernelGGL((grouped_gemm_kernel<kGateUp, kFrag16>), grid, dim3(kThreads), 0, stream, a);
   else
@@ -499,7 +524,7 @@ hipError_t launch_gemm_down(const FfnGroups& p, const int32_t* sched, hipStream_
   GemmArgs a{};
   a.p = p;
   a.sched = sched + p.E + 2;
-  const dim3 grid(round8(gemm_tiles_upper(p, kDown)));
+  const dim3 grid(gemm_grid(gemm_tiles_upper(p, kDown)));
   if (p.layout == kFrag16)
     hipLaunchKernelGGL((grouped_gemm_kernel<kDown, kFrag16>), grid, dim3(kThreads), 0, stream, a);
   else
@@ -518,7 +543,7 @@ hipError_t launch_router_gemm(const void* x, const void* w, const float* bias, f
   a.E = E;
   a.d = d;
   const long long tiles = (long long)((T + BM - 1) / BM) * ((E + Geo<kRouter>::BN - 1) / Geo<kRouter>::BN);
-  hipLaunchKernelGGL((grouped_gemm_kernel<kRouter, kRowMajor>), dim3(round8(tiles)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<kRouter, kRowMajor>), dim3(gemm_grid(tiles)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
