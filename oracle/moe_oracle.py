@@ -20,6 +20,11 @@ Sources (the pages this follows):
                   run each expert once over its bucket, convert back to token order, weight, merge).
   [Inference ch.6] "大模型推理优化基础" (LLM-from-scratch ch. 6), roofline section: a gated MLP is
                   up, gate and down matmuls.
+  [Inference ch.6 quant] the same chapter, model-compression part, second route ("make every byte
+                  cheaper"): for memory-bound decode, 1-byte weights halve the bytes read; affine
+                  quantization x_q = round(x / s) + z, x_hat = (x_q - z) * s, with a per-tensor,
+                  per-channel or per-group scale. [MoE overview] §4.3 quantizes expert weights to
+                  INT8 for the same reason.
   [MoE kernels §2.2] the same page, §2.2 (DeepSeek-V3 routing without an auxiliary loss): experts
                   are picked on sigmoid affinities plus a per-expert bias; the weights use the
                   selected experts' sigmoid affinities without the bias, normalised to sum to one;
@@ -51,6 +56,7 @@ __all__ = [
     "widen", "router_logits", "select_topk", "softmax_selected", "route", "permute", "silu",
     "swiglu", "grouped_ffn", "combine", "layer_forward", "layer_forward_tokens", "topk_gap",
     "logistic", "selection_scores", "sigmoid_weights_selected", "ROUTINGS",
+    "quantize", "dequantize", "quantize_rows_int8", "dequantize_rows_int8",
 ]
 
 ROUTINGS = ("softmax", "sigmoid")
@@ -175,6 +181,38 @@ def topk_gap(L: np.ndarray, k: int) -> np.ndarray:
         return np.full(T, np.inf)
     s = -np.sort(-np.asarray(L, np.float64), axis=1)
     return s[:, k - 1] - s[:, k]
+
+
+# ----------------------------------------------------------------------------- weight quantization
+
+def quantize(x, s, z=0):
+    """[Inference ch.6 quant]: x_q = round(x / s) + z (round half to even)."""
+    return np.rint(np.asarray(x, np.float64) / s) + z
+
+
+def dequantize(q, s, z=0):
+    """[Inference ch.6 quant]: x_hat = (x_q - z) * s."""
+    return (np.asarray(q, np.float64) - z) * s
+
+
+def quantize_rows_int8(w: np.ndarray):
+    """Per-output-channel symmetric INT8 of a [..., rows, cols] weight: z = 0 and one scale per
+    row (output channel), s = max|w_row| / 127, codes round(w / s) in [-127, 127]; an all-zero row
+    gets s = 0 and zero codes. The codes are integers decided by floating point, so they are
+    computed in float32 (the precision the weights are stored in and the GPU quantizes in):
+    s = fl32(max / 127), q = rint(fl32(w / s)). Returns (q int8, s float32 [..., rows])."""
+    w32 = np.asarray(w, np.float64).astype(np.float32)
+    m = np.abs(w32).max(axis=-1)
+    s = (m / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = np.rint((w32 / safe[..., None]).astype(np.float32))
+    q = np.where(s[..., None] > 0, np.clip(q, -127, 127), 0)
+    return q.astype(np.int8), s
+
+
+def dequantize_rows_int8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """The float64 weight an INT8 row-scaled matrix stands for: q * s per row."""
+    return dequantize(q, np.asarray(s, np.float64)[..., None])
 
 
 # ----------------------------------------------------------------------------- dispatch

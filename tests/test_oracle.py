@@ -398,6 +398,44 @@ def test_sigmoid_layer_forward_uses_sigmoid_weights():
     np.testing.assert_allclose(tok["out"], r["out"][3:7], rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------------ INT8 weights (Inference ch.6)
+
+def test_quantization_example_from_the_pages():
+    with open(os.path.join(GOLDEN, "quantization_example.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        assert oracle.quantize(c["x"], c["s"], c["z"]) == c["x_q"]
+        assert abs(oracle.dequantize(c["x_q"], c["s"], c["z"]) - c["x_hat"]) < 1e-12
+
+
+def test_int8_rows_round_trip_within_half_a_step():
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal((3, 40, 96)) * rng.uniform(0.01, 10.0, (3, 40, 1))
+    w[1, 7] = 0.0                                      # an all-zero row
+    q, sc = oracle.quantize_rows_int8(w)
+    w32 = w.astype(np.float32).astype(np.float64)
+    err = np.abs(oracle.dequantize_rows_int8(q, sc) - w32)
+    assert (err <= sc.astype(np.float64)[..., None] * (0.5 + 1e-6)).all()
+    nz = sc > 0
+    assert (np.abs(q).max(-1)[nz] == 127).all()        # the largest entry of every row maps to +-127
+    assert sc[1, 7] == 0 and (q[1, 7] == 0).all()
+    assert (np.sign(q) == np.sign(np.rint(w32 / np.where(nz, sc, 1)[..., None]))).all()
+
+
+def test_int8_rows_match_torch_per_channel_quantization():
+    """torch.quantize_per_channel (axis = output channel, zero point 0) gives the same codes, except
+    where w / s sits within float rounding of a half-integer (torch divides in double)."""
+    rng = np.random.default_rng(6)
+    w = rng.standard_normal((64, 128)).astype(np.float32)
+    q, sc = oracle.quantize_rows_int8(w)
+    tq = torch.quantize_per_channel(torch.from_numpy(w), torch.from_numpy(sc.astype(np.float64)),
+                                    torch.zeros(64, dtype=torch.int64), 0, torch.qint8).int_repr().numpy()
+    ratio = w.astype(np.float64) / sc.astype(np.float64)[:, None]
+    near_half = np.abs(np.abs(ratio - np.floor(ratio)) - 0.5) < 1e-4
+    assert (q[~near_half] == tq[~near_half]).all()
+    assert near_half.mean() < 1e-3
+
+
 # ------------------------------------------------------------------ planted mistakes are caught
 
 def _plant(monkeypatch, name, fn):
@@ -472,6 +510,27 @@ def _sigmoid_weights_softmax(L, idx):
     return om.softmax_selected(L, idx)
 
 
+def _quant_rows_div128(w):
+    w32 = np.asarray(w, np.float64).astype(np.float32)
+    sc = (np.abs(w32).max(-1) / np.float32(128.0)).astype(np.float32)
+    q = np.clip(np.rint(w32 / np.where(sc > 0, sc, 1)[..., None]), -127, 127)
+    return q.astype(np.int8), sc
+
+
+def _quant_rows_truncating(w):
+    w32 = np.asarray(w, np.float64).astype(np.float32)
+    sc = (np.abs(w32).max(-1) / np.float32(127.0)).astype(np.float32)
+    q = np.trunc(w32 / np.where(sc > 0, sc, 1)[..., None])
+    return q.astype(np.int8), sc
+
+
+def _quant_cols(w):
+    w32 = np.asarray(w, np.float64).astype(np.float32)
+    sc = (np.abs(w32).max(-2) / np.float32(127.0)).astype(np.float32)
+    q = np.rint(w32 / np.where(sc > 0, sc, 1)[..., None, :])
+    return q.astype(np.int8), (np.abs(w32).max(-1) / np.float32(127.0)).astype(np.float32)
+
+
 _COMBINE = om.combine
 _PERMUTE = om.permute
 _SELECTION = om.selection_scores
@@ -497,6 +556,11 @@ MUTATIONS = {
     "sigmoid_weights_as_softmax": ("sigmoid_weights_selected", _sigmoid_weights_softmax,
                                    test_sigmoid_weights_limits),
     "logistic_sign_flipped": ("logistic", _logistic_sign_flipped, test_logistic_matches_scipy_expit_without_overflow),
+    "int8_scale_over_128": ("quantize_rows_int8", _quant_rows_div128, test_int8_rows_round_trip_within_half_a_step),
+    "int8_truncating": ("quantize_rows_int8", _quant_rows_truncating, test_int8_rows_round_trip_within_half_a_step),
+    "int8_scale_per_column": ("quantize_rows_int8", _quant_cols, test_int8_rows_match_torch_per_channel_quantization),
+    "dequantize_without_zero_point": ("dequantize", lambda q, s, z=0: np.asarray(q, np.float64) * s,
+                                      test_quantization_example_from_the_pages),
 }
 
 
