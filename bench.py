@@ -42,8 +42,9 @@ def parse():
     p.add_argument("--workload", default="dsv3_decode_t8")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=None)
-    p.add_argument("--layout", choices=["frag16", "rowmajor"], default="frag16",
-                   help="expert weight layout (frag16: packed once at load time, before timing)")
+    p.add_argument("--layout", choices=["frag16", "rowmajor", "int8"], default="frag16",
+                   help="expert weight layout (frag16: packed once at load time, before timing; int8: "
+                        "per-row INT8 codes made once from the bf16 weights, before timing)")
     return p.parse_args()
 
 
@@ -81,28 +82,32 @@ class HipEvents:
 
 
 # ------------------------------------------------------------------------------- work accounting
-def alg_bytes_and_flops(cfg, counts_list, es):
+def alg_bytes_and_flops(cfg, counts_list, es, int8=False):
     """Per-stage algorithmic bytes and flops of one step, averaged over the cycled batches.
 
-    Bytes are what the method must move once: each active expert's weights, the shared expert's,
-    the router, x in, out out (plus, per kernel, its own inputs and outputs). Flops are
-    2*T*d*E (router) + 6*rows*d*H (gated MLP) + 6*T*d*Hs."""
+    Bytes are what the method must move once: each active expert's weights (one byte per weight
+    plus a float32 scale per row for INT8 weights), the shared expert's, the router, x in, out out
+    (plus, per kernel, its own inputs and outputs). Flops are 2*T*d*E (router) + 6*rows*d*H (gated
+    MLP) + 6*T*d*Hs."""
     T, d, E, k, H, Hs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.H, cfg.Hs
     rows = T * k
+    wb = 1 if int8 else es
     res = []
     for counts in counts_list:
         n_act = int((counts > 0).sum())
-        gate_up_w = es * (n_act * 2 * H * d + 2 * Hs * d)
-        down_w = es * (n_act * d * H + d * Hs)
+        sc_gu = 4 * (n_act * 2 * H + 2 * Hs) if int8 else 0
+        sc_dn = 4 * (n_act * d + (d if Hs else 0)) if int8 else 0
+        gate_up_w = wb * (n_act * 2 * H * d + 2 * Hs * d) + sc_gu
+        down_w = wb * (n_act * d * H + d * Hs) + sc_dn
         gate_up = gate_up_w + es * T * d + es * (rows * H + T * Hs)              # weights + x + hidden out
         down = down_w + es * (rows * H + T * Hs) + es * (rows + (T if Hs else 0)) * d
-        layer = es * (n_act * 3 * H * d + 3 * Hs * d + E * d) + es * T * d + es * T * d
+        layer = gate_up_w + down_w + es * E * d + es * T * d + es * T * d
         flops_gate_up = 4 * rows * d * H + 4 * T * d * Hs
         flops_down = 2 * rows * d * H + 2 * T * d * Hs
         res.append(dict(n_act=n_act, gate_up=gate_up, down=down, layer=layer,
                         flops_gate_up=flops_gate_up, flops_down=flops_down,
                         flops_layer=2 * T * d * E + 6 * rows * d * H + 6 * T * d * Hs,
-                        unit_gate_up=es * 2 * H * d, unit_down=es * d * H))
+                        unit_gate_up=wb * 2 * H * d, unit_down=wb * d * H))
     avg = {key: sum(r[key] for r in res) / len(res) for key in res[0]}
     return avg
 
@@ -115,9 +120,15 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
+def traffic_path(workload, kernel):
+    """profiles/traffic_<kernel with template arguments>_<workload>.json"""
+    name = "_".join(filter(None, "".join(c if c.isalnum() else " " for c in kernel).split()))
+    return os.path.join(ROOT, "profiles", f"traffic_{name}_{workload}.json")
+
+
 def traffic_for(workload, kernel):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if they match this source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel.split('<')[0]}_{workload}.json")
+    path = traffic_path(workload, kernel)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -128,10 +139,10 @@ def traffic_for(workload, kernel):
 
 
 # ----------------------------------------------------------------------------------- CPU oracle
-def cpu_baseline(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8):
+def cpu_baseline(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8, int8=False):
     """The fp64 oracle on a bounded sample of the same workload (input generation excluded).
 
-    The sample's oracle pass (routing, bf16 -> fp64 widening of the selected experts, SwiGLU,
+    The sample's oracle pass (routing, conversion of the selected experts' stored weights to fp64, SwiGLU,
     combine) is repeated until about ``min_seconds`` of CPU work has been timed."""
     import numpy as np
     import oracle
@@ -149,8 +160,15 @@ def cpu_baseline(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8):
                              host.router_bias, cfg.routing)
     raw = {int(e): synth.expert_weights_host(cfg, 0, int(e)) for e in np.unique(idx)}   # untimed
     shared_raw = synth.expert_weights_host(cfg, 0, 0, shared=True) if cfg.Hs else None
-    expert_fn = lambda e: tuple(oracle.widen(a, cfg.dtype) for a in raw[e])  # noqa: E731
-    shared_fn = (lambda: tuple(oracle.widen(a, cfg.dtype) for a in shared_raw)) if shared_raw else None
+    # stored form of each weight (untimed): the bf16 bits, or per-row INT8 codes and scales
+    store = (lambda a: oracle.quantize_rows_int8(oracle.widen(a, cfg.dtype))) if int8 else (lambda a: a)
+    stored = {e: tuple(store(a) for a in m) for e, m in raw.items()}
+    shared_stored = tuple(store(a) for a in shared_raw) if shared_raw else None
+
+    def weight(a):   # stored form -> the float64 weight the layer uses (timed, like the GPU's loads)
+        return oracle.dequantize_rows_int8(*a) if int8 else oracle.widen(a, cfg.dtype)
+    expert_fn = lambda e: tuple(weight(a) for a in stored[e])  # noqa: E731
+    shared_fn = (lambda: tuple(weight(a) for a in shared_stored)) if shared_stored else None
     reps, total = 0, 0.0
     while reps < max_repeats and (reps == 0 or total < min_seconds):
         t0 = time.perf_counter()
@@ -161,8 +179,9 @@ def cpu_baseline(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8):
     assert ref["out"].shape == (len(tokens), cfg.d)
     return {"value": round(len(tokens) * reps / total, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{len(tokens)} of {cfg.T} tokens of {cfg.name}, {reps} passes in {total:.1f} s (routing, "
-                      f"bf16->fp64 widening of the {len(raw)} selected experts{' + shared' if shared_raw else ''}, "
-                      f"SwiGLU, combine; expert weight generation excluded)"}
+                      f"{'INT8' if int8 else cfg.dtype}->fp64 conversion of the {len(raw)} selected experts"
+                      f"{' + shared' if shared_raw else ''}, SwiGLU, combine; expert weight generation"
+                      f"{' and quantization' if int8 else ''} excluded)"}
 
 
 # ----------------------------------------------------------------------------------------- main
@@ -200,7 +219,19 @@ def main():
                   torch.empty(d, cfg.Hs, dtype=dt, device=dev))
     synth.fill_expert_weights_device(cfg, 0, wgt, wup, wdn, shared)
     layout = moe.MOE_LAYOUT_ROWMAJOR
-    if args.layout == "frag16" and cfg.dtype == "bf16" and cfg.d % 32 == 0 and cfg.H % 32 == 0 and cfg.Hs % 32 == 0:
+    if args.layout == "int8":
+        if cfg.dtype != "bf16" or cfg.d % 64 or cfg.H % 64 or cfg.Hs % 64:
+            print(f"--layout int8 needs a bf16 layer with d, H, Hs multiples of 64 ({cfg.name} is not)",
+                  file=sys.stderr)
+            sys.exit(2)
+        quant = moe.quantize_expert_weights(wgt, wup, wdn, shared)   # one-time preparation, untimed
+        torch.cuda.synchronize()
+        wgt, wup, wdn = quant[:3]
+        shared = tuple(quant[3:]) if shared else None
+        layout = moe.MOE_LAYOUT_INT8_FRAG
+        del quant
+        torch.cuda.empty_cache()
+    elif args.layout == "frag16" and cfg.dtype == "bf16" and cfg.d % 32 == 0 and cfg.H % 32 == 0 and cfg.Hs % 32 == 0:
         # one-time weight preparation (a model load step), outside the timed region
         packed = moe.pack_expert_weights(wgt, wup, wdn, shared)
         torch.cuda.synchronize()
@@ -274,7 +305,7 @@ def main():
     ev.close()
 
     counts_np = [c.cpu().numpy() for c in counts]
-    work = alg_bytes_and_flops(cfg, counts_np, es)
+    work = alg_bytes_and_flops(cfg, counts_np, es, int8=layout == moe.MOE_LAYOUT_INT8_FRAG)
     ms_per_step = elapsed * 1e3 / K
     kname = moe.moe_stage_kernel_name(shape, dom)
     if prefill:
@@ -306,7 +337,8 @@ def main():
         "data": "synthetic (seeded Philox normal draws; random-init weights of the named layer shape)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
                    "d_hidden": cfg.H, "d_shared_hidden": cfg.Hs, "zipf_bias": cfg.zipf_s, "routing": cfg.routing,
-                   "weight_layout": "frag16" if layout == moe.MOE_LAYOUT_FRAG16 else "rowmajor",
+                   "weight_layout": {moe.MOE_LAYOUT_FRAG16: "frag16", moe.MOE_LAYOUT_INT8_FRAG: "int8 per-row",
+                                     moe.MOE_LAYOUT_ROWMAJOR: "rowmajor"}[layout],
                    "parallelism": "single GPU"},
         "roofline": roof,
         "layer": {"alg_bytes": int(work["layer"]), "alg_flops": int(work["flops_layer"]),
@@ -318,7 +350,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         n_tok = args.cpu_sample_tokens or (8 if cfg.E > 8 else 16)
-        line["cpu_baseline"] = cpu_baseline(cfg, host, n_tok)
+        line["cpu_baseline"] = cpu_baseline(cfg, host, n_tok, int8=layout == moe.MOE_LAYOUT_INT8_FRAG)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

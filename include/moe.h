@@ -62,7 +62,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Storage layout of the expert weight matrices (w_gate, w_up, w_down and the shared ones). */
 typedef enum {
   MOE_LAYOUT_ROWMAJOR = 0, /* [out, in] row-major, like a linear layer's weight */
-  MOE_LAYOUT_FRAG16 = 1    /* fragment-tiled, see moe_pack_weights */
+  MOE_LAYOUT_FRAG16 = 1,   /* fragment-tiled, see moe_pack_weights */
+  MOE_LAYOUT_INT8_FRAG = 2 /* INT8 codes with one float32 scale per output row, see
+                              moe_quantize_weights (bf16 layers; experts always run as the
+                              weight-streaming decode kernels) */
 } moe_weight_layout;
 
 /* How the router turns logits into the k experts and their weights. */
@@ -99,6 +102,27 @@ typedef struct {
  * 16-byte aligned. A one-time preparation step (weight load), not part of the layer forward.
  */
 moe_status moe_pack_weights(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols, void* stream);
+
+/*
+ * moe_quantize_weights -- INT8 copy of n_mats row-major bf16 matrices [n_mats, rows, cols] for
+ * MOE_LAYOUT_INT8_FRAG (inference-optimisation chapter, model-compression part, "make every byte
+ * cheaper": x_q = round(x / s) + z; here z = 0 and one scale per output row; overview article
+ * section 4.3: INT8 expert weights). For every row r of every matrix m:
+ *     s[m][r] = max_c |w[m][r][c]| / 127           (float32; 0 for an all-zero row)
+ *     q[m][r][c] = rint(w[m][r][c] / s[m][r])      (float32 division, ties to even, in [-127, 127])
+ * and the layer uses w ~ q * s. dst holds n_mats * rows * cols int8 codes in fragment order
+ * (each 1 KB: a 16-row x 64-column block; lane l = r % 16 + 16 * ((c % 32) / 8) of a wave holds
+ * 8 codes of columns c..c+7 of the block's first 32 columns, then the same 8 of its second 32;
+ * code (r, c) at byte ((r/16) * (cols/64) + c/64) * 1024 + lane * 16 + ((c % 64) / 32) * 8 + c % 8),
+ * followed by the float32 scales [n_mats, rows]. dst needs moe_quantized_weight_bytes() bytes.
+ * rows % 16 == 0, cols % 64 == 0; src and dst 16-byte aligned and not overlapping. A one-time
+ * preparation step (weight load), not part of the layer forward.
+ */
+moe_status moe_quantize_weights(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols,
+                                void* stream);
+
+/* Bytes of an MOE_LAYOUT_INT8_FRAG buffer of n_mats [rows, cols] matrices: codes plus scales. */
+size_t moe_quantized_weight_bytes(int64_t n_mats, int32_t rows, int32_t cols);
 
 /* Bytes of workspace that every entry point below accepts for shape `s` (0 if `s` is invalid). */
 size_t moe_workspace_bytes(const moe_shape* s);

@@ -23,7 +23,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
 MOE_F32, MOE_BF16 = 0, 1
-MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_FRAG16 = 0, 1
+MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_FRAG16, MOE_LAYOUT_INT8_FRAG = 0, 1, 2
 MOE_ROUTING_SOFTMAX, MOE_ROUTING_SIGMOID = 0, 1
 STAGES = ["route_logits", "route_topk", "permute_count", "permute_scan", "permute_scatter", "ffn_schedule",
           "ffn_gate_up", "ffn_down", "combine"]
@@ -66,6 +66,8 @@ _sigs = {
     "moe_layer_forward_timed": (ctypes.c_int, [_S] + [_P] * 15 + [ctypes.c_size_t, _P, _P]),
     "moe_stage_kernel_name": (ctypes.c_char_p, [_S, ctypes.c_int]),
     "moe_pack_weights": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
+    "moe_quantize_weights": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
+    "moe_quantized_weight_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -178,6 +180,28 @@ def pack_expert_weights(w_gate, w_up, w_down, shared=None, stream=None):
         n = 1 if w.dim() == 2 else w.shape[0]
         moe_pack_weights(w, p, n, w.shape[-2], w.shape[-1], stream)
         out.append(p)
+    return out
+
+
+def moe_quantize_weights(src, dst, n_mats, rows, cols, stream=None):
+    """INT8 codes (fragment order) + per-row float32 scales of n_mats bf16 [rows, cols] matrices
+    (MOE_LAYOUT_INT8_FRAG)."""
+    _check("moe_quantize_weights", _lib.moe_quantize_weights(_ptr(src), _ptr(dst), n_mats, rows, cols,
+                                                             _stream(stream)))
+
+
+def moe_quantized_weight_bytes(n_mats, rows, cols) -> int:
+    return int(_lib.moe_quantized_weight_bytes(n_mats, rows, cols))
+
+
+def quantize_expert_weights(w_gate, w_up, w_down, shared=None, stream=None):
+    """INT8 buffers (uint8 tensors) of [E,H,d], [E,H,d], [E,d,H] (and an optional shared triple)."""
+    out = []
+    for w in (w_gate, w_up, w_down) + (tuple(shared) if shared is not None else ()):
+        n = 1 if w.dim() == 2 else w.shape[0]
+        q = torch.empty(moe_quantized_weight_bytes(n, w.shape[-2], w.shape[-1]), dtype=torch.uint8, device=w.device)
+        moe_quantize_weights(w, q, n, w.shape[-2], w.shape[-1], stream)
+        out.append(q)
     return out
 
 

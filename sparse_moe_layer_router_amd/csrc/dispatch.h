@@ -47,7 +47,10 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_perm
                           const void* shared_out, void* out, int T, int k, int d, hipStream_t stream);
 const char* combine_kernel_name(int dtype);
 
-// ---- weight packing (MOE_LAYOUT_FRAG16) --------------------------------------------------------
+// ---- weight packing (MOE_LAYOUT_FRAG16) and INT8 quantization (MOE_LAYOUT_INT8_FRAG) --------------
 hipError_t launch_pack_weights(const void* src, void* dst, long long n_mats, int rows, int cols, hipStream_t stream);
+size_t quantized_weight_bytes(long long n_mats, int rows, int cols);
+hipError_t launch_quantize_weights(const void* src, void* dst, long long n_mats, int rows, int cols,
+                                   hipStream_t stream);
 
 }  // namespace moe

@@ -27,19 +27,31 @@ struct GroupView {
   long long r0;        // first row of the group in the (routed or shared) row space
   int n;               // rows in the group
   int Hg;              // hidden size of the group's expert
-  const uint16_t* wg;  // [Hg, d]
-  const uint16_t* wu;  // [Hg, d]
-  const uint16_t* wd;  // [d, Hg]
+  const void* wg;      // [Hg, d] (bf16, or INT8 codes in the fragment order)
+  const void* wu;      // [Hg, d]
+  const void* wd;      // [d, Hg]
+  const float* sg;     // INT8 weights: per-row scales of wg [Hg], wu [Hg], wd [d]
+  const float* su;
+  const float* sd;
   uint16_t* hid;       // hidden rows of this row space, row stride Hg
   uint16_t* y;         // output rows of this row space, row stride d
   bool routed;
 };
+
+// INT8 expert weights (MOE_LAYOUT_INT8_FRAG): a buffer of n matrices holds n * rows * cols one-byte
+// codes followed by n * rows float32 row scales.
+__device__ __forceinline__ const float* row_scales(const void* codes, long long n_codes) {
+  return (const float*)((const int8_t*)codes + n_codes);
+}
 
 // Group g < E is routed expert g. The shared expert's T rows are cut into chunks of `chunk` rows,
 // one group each (g = E + c): every chunk streams the shared weights once for its own tokens, and
 // the chunks run side by side instead of one group re-streaming the weights for every token tile.
 __device__ __forceinline__ GroupView group_view(const FfnGroups& p, int g, int chunk) {
   GroupView v;
+  const bool q8 = p.layout == kInt8Frag;
+  const size_t eb = q8 ? 1 : 2;  // bytes per weight element
+  v.sg = v.su = v.sd = nullptr;
   if (g < p.E) {
     // clamp to [0, rows] so inconsistent offsets can never address outside the row buffers
     long long a = p.offsets[g], b = p.offsets[g + 1];
@@ -49,9 +61,14 @@ __device__ __forceinline__ GroupView group_view(const FfnGroups& p, int g, int c
     v.n = (int)(b - a);
     v.Hg = p.H;
     const size_t wsz = (size_t)p.H * p.d;
-    v.wg = (const uint16_t*)p.w_gate + (size_t)g * wsz;
-    v.wu = (const uint16_t*)p.w_up + (size_t)g * wsz;
-    v.wd = (const uint16_t*)p.w_down + (size_t)g * wsz;
+    v.wg = (const char*)p.w_gate + (size_t)g * wsz * eb;
+    v.wu = (const char*)p.w_up + (size_t)g * wsz * eb;
+    v.wd = (const char*)p.w_down + (size_t)g * wsz * eb;
+    if (q8) {
+      v.sg = row_scales(p.w_gate, (long long)p.E * wsz) + (size_t)g * p.H;
+      v.su = row_scales(p.w_up, (long long)p.E * wsz) + (size_t)g * p.H;
+      v.sd = row_scales(p.w_down, (long long)p.E * wsz) + (size_t)g * p.d;
+    }
     v.hid = (uint16_t*)p.hid;
     v.y = (uint16_t*)p.y;
     v.routed = true;
@@ -59,9 +76,15 @@ __device__ __forceinline__ GroupView group_view(const FfnGroups& p, int g, int c
     v.r0 = (long long)(g - p.E) * chunk;
     v.n = (int)(p.T - v.r0 < chunk ? p.T - v.r0 : chunk);
     v.Hg = p.Hs;
-    v.wg = (const uint16_t*)p.ws_gate;
-    v.wu = (const uint16_t*)p.ws_up;
-    v.wd = (const uint16_t*)p.ws_down;
+    v.wg = p.ws_gate;
+    v.wu = p.ws_up;
+    v.wd = p.ws_down;
+    if (q8) {
+      const long long wsz = (long long)p.Hs * p.d;
+      v.sg = row_scales(p.ws_gate, wsz);
+      v.su = row_scales(p.ws_up, wsz);
+      v.sd = row_scales(p.ws_down, wsz);
+    }
     v.hid = (uint16_t*)p.hid + (size_t)p.rows * p.H;
     v.y = (uint16_t*)p.y + (size_t)p.rows * p.d;
     v.routed = false;
@@ -80,11 +103,12 @@ __device__ __forceinline__ long long source_row(const FfnGroups& p, const GroupV
 }  // namespace
 
 // Weight fragment source for a wave streaming the 16 rows [r0, r0+16) of a [rows, K] matrix: the
-// lane's 16 bytes of k-step s (32 columns) are at base + s * step.
+// lane's 16 bytes of k-step s (32 columns) are at base + s * step (bf16 elements).
 //   row-major: row r0 + lane%16, columns 8*(lane/16) .. +8 of the step: 16 rows x 64 B per load;
 //   fragment-tiled: block (r0/16, s), lane's 16 bytes: one contiguous 1 KB per load.
 template <int LAYOUT>
-__device__ __forceinline__ const uint16_t* frag_base(const uint16_t* w, int r0, int rows, int K, int lane, int* step) {
+__device__ __forceinline__ const uint16_t* frag_base(const void* wv, int r0, int rows, int K, int lane, int* step) {
+  const uint16_t* w = (const uint16_t*)wv;
   if (LAYOUT == kFrag16) {
     *step = 512;
     return w + (size_t)(r0 / 16) * (K / 32) * 512 + lane * 8;
@@ -92,6 +116,26 @@ __device__ __forceinline__ const uint16_t* frag_base(const uint16_t* w, int r0, 
   *step = 32;
   const int r = (r0 + (lane & 15) < rows) ? r0 + (lane & 15) : rows - 1;  // rows past the matrix: dropped
   return w + (size_t)r * K + (lane >> 4) * 8;
+}
+
+// INT8 fragment order: 1 KB block (r0/16, s2) covers 64 columns, lane's 16 bytes = its A-operand
+// chunk of k-steps 2*s2 and 2*s2+1; base + s2 * 1024 bytes.
+__device__ __forceinline__ const int8_t* q8_base(const void* wv, int r0, int K, int lane) {
+  return (const int8_t*)wv + (size_t)(r0 / 16) * (K / 64) * 1024 + lane * 16;
+}
+
+// Eight int8 codes (two little-endian words) -> the eight bf16 values (exact: |q| <= 127).
+__device__ __forceinline__ u32x4_t i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = i < 2 ? lo : hi;
+    const int b = (i & 1) * 2;  // byte index of the pair's first code
+    const float f0 = (float)((int32_t)(w << (24 - 8 * b)) >> 24);
+    const float f1 = (float)((int32_t)(w << (16 - 8 * b)) >> 24);
+    r[i] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+  }
+  return r;
 }
 
 template <int NTT, int LAYOUT>
@@ -104,9 +148,18 @@ ffn_gate_up_stream(const FfnGroups p) {
   if (h0 >= v.Hg) return;
   const int d = p.d;
   const int ar = lane & 15, kq = lane >> 4;
-  int ws;  // elements between consecutive k-steps of a weight fragment
-  const uint16_t* ag = frag_base<LAYOUT>(v.wg, h0, v.Hg, d, lane, &ws);
-  const uint16_t* au = frag_base<LAYOUT>(v.wu, h0, v.Hg, d, lane, &ws);
+  int ws = 0;  // bf16 layouts: elements between consecutive k-steps of a weight fragment
+  const uint16_t* ag = nullptr;
+  const uint16_t* au = nullptr;
+  const int8_t* qg = nullptr;
+  const int8_t* qu = nullptr;
+  if (LAYOUT == kInt8Frag) {
+    qg = q8_base(v.wg, h0, d, lane);
+    qu = q8_base(v.wu, h0, d, lane);
+  } else {
+    ag = frag_base<LAYOUT>(v.wg, h0, v.Hg, d, lane, &ws);
+    au = frag_base<LAYOUT>(v.wu, h0, v.Hg, d, lane, &ws);
+  }
   const uint16_t* xb = (const uint16_t*)p.x;
 
   for (int tt = 0; tt < v.n; tt += 16 * NTT) {
@@ -124,44 +177,97 @@ ffn_gate_up_stream(const FfnGroups p) {
     for (int j = 0; j < NTT; ++j) { accg[j] = f32x4_t{0, 0, 0, 0}; accu[j] = f32x4_t{0, 0, 0, 0}; }
     const u32x4_t zero = {0, 0, 0, 0};
     int k0 = 0;
-    for (; k0 + 32 * kUnroll <= d; k0 += 32 * kUnroll) {
-      u32x4_t a_g[kUnroll], a_u[kUnroll], b[kUnroll][NTT];
+    if (LAYOUT == kInt8Frag) {
+      // d is a multiple of 64: every load covers two whole k-steps
+      for (; k0 + 32 * kUnroll <= d; k0 += 32 * kUnroll) {
+        u32x4_t r_g[kUnroll / 2], r_u[kUnroll / 2], b[kUnroll][NTT];
 #pragma unroll
-      for (int s = 0; s < kUnroll; ++s) {
-        a_g[s] = ld16_stream(ag + (size_t)(k0 / 32 + s) * ws);
-        a_u[s] = ld16_stream(au + (size_t)(k0 / 32 + s) * ws);
+        for (int s2 = 0; s2 < kUnroll / 2; ++s2) {
+          r_g[s2] = ld16_stream(qg + (size_t)(k0 / 64 + s2) * 1024);
+          r_u[s2] = ld16_stream(qu + (size_t)(k0 / 64 + s2) * 1024);
+        }
+#pragma unroll
+        for (int s = 0; s < kUnroll; ++s)
+#pragma unroll
+          for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bx[j] + k0 + 32 * s) : zero;
+#pragma unroll
+        for (int s2 = 0; s2 < kUnroll / 2; ++s2) {
+          const u32x4_t g0 = i8x8_to_bf16x8(r_g[s2][0], r_g[s2][1]), g1 = i8x8_to_bf16x8(r_g[s2][2], r_g[s2][3]);
+          const u32x4_t u0 = i8x8_to_bf16x8(r_u[s2][0], r_u[s2][1]), u1 = i8x8_to_bf16x8(r_u[s2][2], r_u[s2][3]);
+#pragma unroll
+          for (int j = 0; j < NTT; ++j) {
+            accg[j] = mfma16x16x32(g0, b[2 * s2][j], accg[j]);
+            accu[j] = mfma16x16x32(u0, b[2 * s2][j], accu[j]);
+            accg[j] = mfma16x16x32(g1, b[2 * s2 + 1][j], accg[j]);
+            accu[j] = mfma16x16x32(u1, b[2 * s2 + 1][j], accu[j]);
+          }
+        }
       }
-#pragma unroll
-      for (int s = 0; s < kUnroll; ++s)
-#pragma unroll
-        for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bx[j] + k0 + 32 * s) : zero;
-#pragma unroll
-      for (int s = 0; s < kUnroll; ++s)
+      for (; k0 < d; k0 += 64) {
+        const u32x4_t r_g = ld16_stream(qg + (size_t)(k0 / 64) * 1024);
+        const u32x4_t r_u = ld16_stream(qu + (size_t)(k0 / 64) * 1024);
+        const u32x4_t g0 = i8x8_to_bf16x8(r_g[0], r_g[1]), g1 = i8x8_to_bf16x8(r_g[2], r_g[3]);
+        const u32x4_t u0 = i8x8_to_bf16x8(r_u[0], r_u[1]), u1 = i8x8_to_bf16x8(r_u[2], r_u[3]);
 #pragma unroll
         for (int j = 0; j < NTT; ++j) {
-          accg[j] = mfma16x16x32(a_g[s], b[s][j], accg[j]);
-          accu[j] = mfma16x16x32(a_u[s], b[s][j], accu[j]);
+          const u32x4_t b0 = bok[j] ? ld16(bx[j] + k0) : zero;
+          const u32x4_t b1 = bok[j] ? ld16(bx[j] + k0 + 32) : zero;
+          accg[j] = mfma16x16x32(g0, b0, accg[j]);
+          accu[j] = mfma16x16x32(u0, b0, accu[j]);
+          accg[j] = mfma16x16x32(g1, b1, accg[j]);
+          accu[j] = mfma16x16x32(u1, b1, accu[j]);
         }
-    }
-    for (; k0 < d; k0 += 32) {  // tail: d is a multiple of 8, so a lane's 8-chunk is all in or all out
-      const bool kok = k0 + kq * 8 < d;
-      const u32x4_t a_g = kok ? ld16_stream(ag + (size_t)(k0 / 32) * ws) : zero;
-      const u32x4_t a_u = kok ? ld16_stream(au + (size_t)(k0 / 32) * ws) : zero;
+      }
+    } else {
+      for (; k0 + 32 * kUnroll <= d; k0 += 32 * kUnroll) {
+        u32x4_t a_g[kUnroll], a_u[kUnroll], b[kUnroll][NTT];
 #pragma unroll
-      for (int j = 0; j < NTT; ++j) {
-        const u32x4_t b = (kok && bok[j]) ? ld16(bx[j] + k0) : zero;
-        accg[j] = mfma16x16x32(a_g, b, accg[j]);
-        accu[j] = mfma16x16x32(a_u, b, accu[j]);
+        for (int s = 0; s < kUnroll; ++s) {
+          a_g[s] = ld16_stream(ag + (size_t)(k0 / 32 + s) * ws);
+          a_u[s] = ld16_stream(au + (size_t)(k0 / 32 + s) * ws);
+        }
+#pragma unroll
+        for (int s = 0; s < kUnroll; ++s)
+#pragma unroll
+          for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bx[j] + k0 + 32 * s) : zero;
+#pragma unroll
+        for (int s = 0; s < kUnroll; ++s)
+#pragma unroll
+          for (int j = 0; j < NTT; ++j) {
+            accg[j] = mfma16x16x32(a_g[s], b[s][j], accg[j]);
+            accu[j] = mfma16x16x32(a_u[s], b[s][j], accu[j]);
+          }
+      }
+      for (; k0 < d; k0 += 32) {  // tail: d is a multiple of 8, so a lane's 8-chunk is all in or all out
+        const bool kok = k0 + kq * 8 < d;
+        const u32x4_t a_g = kok ? ld16_stream(ag + (size_t)(k0 / 32) * ws) : zero;
+        const u32x4_t a_u = kok ? ld16_stream(au + (size_t)(k0 / 32) * ws) : zero;
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) {
+          const u32x4_t b = (kok && bok[j]) ? ld16(bx[j] + k0) : zero;
+          accg[j] = mfma16x16x32(a_g, b, accg[j]);
+          accu[j] = mfma16x16x32(a_u, b, accu[j]);
+        }
       }
     }
-    // lane holds rows h0 + kq*4 + {0..3} of token column (lane & 15)
+    // lane holds rows h0 + kq*4 + {0..3} of token column (lane & 15); INT8 rows carry their scale
+    const int h = h0 + kq * 4;
+    f32x4_t sg = {1.f, 1.f, 1.f, 1.f}, su = {1.f, 1.f, 1.f, 1.f};
+    if (LAYOUT == kInt8Frag && h < v.Hg) {
+      sg = *(const f32x4_t*)(v.sg + h);
+      su = *(const f32x4_t*)(v.su + h);
+    }
 #pragma unroll
     for (int j = 0; j < NTT; ++j) {
       const int rr = tt + j * 16 + ar;
-      const int h = h0 + kq * 4;
       if (rr < v.n && h < v.Hg) {
-        uint32_t lo = pack_bf16x2(silu(accg[j][0]) * accu[j][0], silu(accg[j][1]) * accu[j][1]);
-        uint32_t hi = pack_bf16x2(silu(accg[j][2]) * accu[j][2], silu(accg[j][3]) * accu[j][3]);
+        f32x4_t g = accg[j], u = accu[j];
+        if (LAYOUT == kInt8Frag) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { g[e] *= sg[e]; u[e] *= su[e]; }
+        }
+        uint32_t lo = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+        uint32_t hi = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
         *(u32x2_t*)(v.hid + (size_t)(v.r0 + rr) * v.Hg + h) = u32x2_t{lo, hi};
       }
     }
@@ -179,8 +285,13 @@ ffn_down_stream(const FfnGroups p) {
   if (i0 >= d) return;
   const int K = v.Hg;
   const int ar = lane & 15, kq = lane >> 4;
-  int ws;
-  const uint16_t* aw = frag_base<LAYOUT>(v.wd, i0, d, K, lane, &ws);
+  int ws = 0;
+  const uint16_t* aw = nullptr;
+  const int8_t* qw = nullptr;
+  if (LAYOUT == kInt8Frag)
+    qw = q8_base(v.wd, i0, K, lane);
+  else
+    aw = frag_base<LAYOUT>(v.wd, i0, d, K, lane, &ws);
 
   for (int tt = 0; tt < v.n; tt += 16 * NTT) {
     const uint16_t* bh[NTT];
@@ -196,35 +307,72 @@ ffn_down_stream(const FfnGroups p) {
     for (int j = 0; j < NTT; ++j) acc[j] = f32x4_t{0, 0, 0, 0};
     const u32x4_t zero = {0, 0, 0, 0};
     int k0 = 0;
-    for (; k0 + 32 * kUnroll <= K; k0 += 32 * kUnroll) {
-      u32x4_t a[kUnroll], b[kUnroll][NTT];
+    if (LAYOUT == kInt8Frag) {
+      for (; k0 + 32 * kUnroll <= K; k0 += 32 * kUnroll) {
+        u32x4_t r[kUnroll / 2], b[kUnroll][NTT];
 #pragma unroll
-      for (int s = 0; s < kUnroll; ++s) a[s] = ld16_stream(aw + (size_t)(k0 / 32 + s) * ws);
+        for (int s2 = 0; s2 < kUnroll / 2; ++s2) r[s2] = ld16_stream(qw + (size_t)(k0 / 64 + s2) * 1024);
 #pragma unroll
-      for (int s = 0; s < kUnroll; ++s)
+        for (int s = 0; s < kUnroll; ++s)
 #pragma unroll
-        for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bh[j] + k0 + 32 * s) : zero;
+          for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bh[j] + k0 + 32 * s) : zero;
 #pragma unroll
-      for (int s = 0; s < kUnroll; ++s)
+        for (int s2 = 0; s2 < kUnroll / 2; ++s2) {
+          const u32x4_t a0 = i8x8_to_bf16x8(r[s2][0], r[s2][1]), a1 = i8x8_to_bf16x8(r[s2][2], r[s2][3]);
 #pragma unroll
-        for (int j = 0; j < NTT; ++j) acc[j] = mfma16x16x32(a[s], b[s][j], acc[j]);
-    }
-    for (; k0 < K; k0 += 32) {
-      const bool kok = k0 + kq * 8 < K;
-      const u32x4_t a = kok ? ld16_stream(aw + (size_t)(k0 / 32) * ws) : zero;
+          for (int j = 0; j < NTT; ++j) {
+            acc[j] = mfma16x16x32(a0, b[2 * s2][j], acc[j]);
+            acc[j] = mfma16x16x32(a1, b[2 * s2 + 1][j], acc[j]);
+          }
+        }
+      }
+      for (; k0 < K; k0 += 64) {  // K (the hidden size) is a multiple of 64
+        const u32x4_t r = ld16_stream(qw + (size_t)(k0 / 64) * 1024);
+        const u32x4_t a0 = i8x8_to_bf16x8(r[0], r[1]), a1 = i8x8_to_bf16x8(r[2], r[3]);
 #pragma unroll
-      for (int j = 0; j < NTT; ++j) {
-        const u32x4_t b = (kok && bok[j]) ? ld16(bh[j] + k0) : zero;
-        acc[j] = mfma16x16x32(a, b, acc[j]);
+        for (int j = 0; j < NTT; ++j) {
+          acc[j] = mfma16x16x32(a0, bok[j] ? ld16(bh[j] + k0) : zero, acc[j]);
+          acc[j] = mfma16x16x32(a1, bok[j] ? ld16(bh[j] + k0 + 32) : zero, acc[j]);
+        }
+      }
+    } else {
+      for (; k0 + 32 * kUnroll <= K; k0 += 32 * kUnroll) {
+        u32x4_t a[kUnroll], b[kUnroll][NTT];
+#pragma unroll
+        for (int s = 0; s < kUnroll; ++s) a[s] = ld16_stream(aw + (size_t)(k0 / 32 + s) * ws);
+#pragma unroll
+        for (int s = 0; s < kUnroll; ++s)
+#pragma unroll
+          for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bh[j] + k0 + 32 * s) : zero;
+#pragma unroll
+        for (int s = 0; s < kUnroll; ++s)
+#pragma unroll
+          for (int j = 0; j < NTT; ++j) acc[j] = mfma16x16x32(a[s], b[s][j], acc[j]);
+      }
+      for (; k0 < K; k0 += 32) {
+        const bool kok = k0 + kq * 8 < K;
+        const u32x4_t a = kok ? ld16_stream(aw + (size_t)(k0 / 32) * ws) : zero;
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) {
+          const u32x4_t b = (kok && bok[j]) ? ld16(bh[j] + k0) : zero;
+          acc[j] = mfma16x16x32(a, b, acc[j]);
+        }
       }
     }
+    const int i = i0 + kq * 4;
+    f32x4_t sc = {1.f, 1.f, 1.f, 1.f};
+    if (LAYOUT == kInt8Frag && i < d) sc = *(const f32x4_t*)(v.sd + i);
 #pragma unroll
     for (int j = 0; j < NTT; ++j) {
       const int rr = tt + j * 16 + ar;
-      const int i = i0 + kq * 4;
       if (rr < v.n && i < d) {
-        uint32_t lo = pack_bf16x2(acc[j][0], acc[j][1]);
-        uint32_t hi = pack_bf16x2(acc[j][2], acc[j][3]);
+        f32x4_t y = acc[j];
+        if (LAYOUT == kInt8Frag) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] *= sc[e];
+        }
+        uint32_t lo = pack_bf16x2(y[0], y[1]);
+        uint32_t hi = pack_bf16x2(y[2], y[3]);
         *(u32x2_t*)(v.y + (size_t)(v.r0 + rr) * d + i) = u32x2_t{lo, hi};
       }
     }
@@ -314,12 +462,15 @@ long long all_rows(const FfnGroups& g) { return g.rows + (g.Hs > 0 ? g.T : 0); }
 
 FfnPath ffn_path(const FfnGroups& g) {
   if (g.dtype == kF32) return kPathF32;
+  if (g.layout == kInt8Frag) return kPathStream;  // INT8 weights are a decode (weight-streaming) format
   return g.mean_rows_per_group >= kGemmMinRowsPerExpert ? kPathGemm : kPathStream;
 }
 
 hipError_t launch_ffn_gate_up_stream(const FfnGroups& g, hipStream_t stream) {
   dim3 grid((hmax(g) + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
-  if (g.layout == kFrag16)
+  if (g.layout == kInt8Frag)
+    hipLaunchKernelGGL((ffn_gate_up_stream<1, kInt8Frag>), grid, dim3(256), 0, stream, g);
+  else if (g.layout == kFrag16)
     hipLaunchKernelGGL((ffn_gate_up_stream<1, kFrag16>), grid, dim3(256), 0, stream, g);
   else
     hipLaunchKernelGGL((ffn_gate_up_stream<1, kRowMajor>), grid, dim3(256), 0, stream, g);
@@ -328,7 +479,9 @@ hipError_t launch_ffn_gate_up_stream(const FfnGroups& g, hipStream_t stream) {
 
 hipError_t launch_ffn_down_stream(const FfnGroups& g, hipStream_t stream) {
   dim3 grid((g.d + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
-  if (g.layout == kFrag16)
+  if (g.layout == kInt8Frag)
+    hipLaunchKernelGGL((ffn_down_stream<1, kInt8Frag>), grid, dim3(256), 0, stream, g);
+  else if (g.layout == kFrag16)
     hipLaunchKernelGGL((ffn_down_stream<1, kFrag16>), grid, dim3(256), 0, stream, g);
   else
     hipLaunchKernelGGL((ffn_down_stream<1, kRowMajor>), grid, dim3(256), 0, stream, g);
@@ -353,14 +506,18 @@ const char* ffn_schedule_kernel_name(const FfnGroups& g) {
 const char* ffn_gate_up_kernel_name(const FfnGroups& g) {
   switch (ffn_path(g)) {
     case kPathF32: return "ffn_gate_up_f32";
-    case kPathStream: return g.layout == kFrag16 ? "ffn_gate_up_stream<1, 1>" : "ffn_gate_up_stream<1, 0>";
+    case kPathStream:
+      return g.layout == kInt8Frag ? "ffn_gate_up_stream<1, 2>"
+                                   : (g.layout == kFrag16 ? "ffn_gate_up_stream<1, 1>" : "ffn_gate_up_stream<1, 0>");
     default: return g.layout == kFrag16 ? "grouped_gemm_kernel<0, 1>" : "grouped_gemm_kernel<0, 0>";
   }
 }
 const char* ffn_down_kernel_name(const FfnGroups& g) {
   switch (ffn_path(g)) {
     case kPathF32: return "ffn_down_f32";
-    case kPathStream: return g.layout == kFrag16 ? "ffn_down_stream<1, 1>" : "ffn_down_stream<1, 0>";
+    case kPathStream:
+      return g.layout == kInt8Frag ? "ffn_down_stream<1, 2>"
+                                   : (g.layout == kFrag16 ? "ffn_down_stream<1, 1>" : "ffn_down_stream<1, 0>");
     default: return g.layout == kFrag16 ? "grouped_gemm_kernel<1, 1>" : "grouped_gemm_kernel<1, 0>";
   }
 }

@@ -53,12 +53,19 @@ moe_status check_shape(const moe_shape* s) {
   if (s->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
   if ((long long)s->T * s->top_k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (s->d_model % 8 || s->d_hidden % 8 || s->d_shared_hidden % 8) return MOE_ERR_ALIGNMENT;
-  if (s->weight_layout != MOE_LAYOUT_ROWMAJOR && s->weight_layout != MOE_LAYOUT_FRAG16) return MOE_ERR_UNSUPPORTED;
+  if (s->weight_layout != MOE_LAYOUT_ROWMAJOR && s->weight_layout != MOE_LAYOUT_FRAG16 &&
+      s->weight_layout != MOE_LAYOUT_INT8_FRAG)
+    return MOE_ERR_UNSUPPORTED;
   if (s->routing != MOE_ROUTING_SOFTMAX && s->routing != MOE_ROUTING_SIGMOID) return MOE_ERR_UNSUPPORTED;
   if (s->weight_layout == MOE_LAYOUT_FRAG16) {
     // every expert matrix ([H, d], [d, H], [Hs, d], [d, Hs]) must tile into 16 x 32 blocks
     if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (s->d_model % 32 || s->d_hidden % 32 || s->d_shared_hidden % 32) return MOE_ERR_ALIGNMENT;
+  }
+  if (s->weight_layout == MOE_LAYOUT_INT8_FRAG) {
+    // every expert matrix tiles into 16 x 64 blocks of codes
+    if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (s->d_model % 64 || s->d_hidden % 64 || s->d_shared_hidden % 64) return MOE_ERR_ALIGNMENT;
   }
   return MOE_OK;
 }
@@ -289,6 +296,26 @@ moe_status moe_pack_weights(const void* src, void* dst, int64_t n_mats, int32_t 
   if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;  // overlapping buffers
   MOE_LAUNCH(moe::launch_pack_weights(src, dst, n_mats, rows, cols, (hipStream_t)stream));
   return MOE_OK;
+}
+
+moe_status moe_quantize_weights(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols,
+                                void* stream) {
+  if (n_mats < 0 || rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
+  if (rows % 16 || cols % 64) return MOE_ERR_ALIGNMENT;
+  if (n_mats == 0 || rows == 0 || cols == 0) return MOE_OK;
+  MOE_TRY(need(src, 16));
+  MOE_TRY(need(dst, 16));
+  const uintptr_t in = (uintptr_t)n_mats * (uintptr_t)rows * (uintptr_t)cols * 2;
+  const uintptr_t out = moe::quantized_weight_bytes(n_mats, rows, cols);
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + out && b < a + in) return MOE_ERR_INVALID_ARG;  // overlapping buffers
+  MOE_LAUNCH(moe::launch_quantize_weights(src, dst, n_mats, rows, cols, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+size_t moe_quantized_weight_bytes(int64_t n_mats, int32_t rows, int32_t cols) {
+  if (n_mats < 0 || rows < 0 || cols < 0) return 0;
+  return moe::quantized_weight_bytes(n_mats, rows, cols);
 }
 
 moe_status moe_route(const moe_shape* s, const void* x, const void* w_router, const float* logit_bias,

@@ -49,11 +49,15 @@ class DeviceLayer:
         c = self.cfg
         return moe.make_shape(c.T, c.d, c.E, c.k, c.H, c.Hs, c.dtype, self.layout, c.routing)
 
+    @property
+    def int8(self) -> bool:
+        return self.layout == moe.MOE_LAYOUT_INT8_FRAG
+
     def expert_fn(self, cache=True):
-        return helpers.expert_fn_host(self.cfg, self.seed, self.stacked_host, cache=cache)
+        return helpers.expert_fn_host(self.cfg, self.seed, self.stacked_host, cache=cache, int8=self.int8)
 
     def shared_fn(self):
-        return helpers.shared_fn_host(self.cfg, self.seed)
+        return helpers.shared_fn_host(self.cfg, self.seed, int8=self.int8)
 
 
 def make_weights(cfg: synth.LayerConfig, seed: int, host_copy: bool):
@@ -87,6 +91,15 @@ def packed_weights(weights):
     return (tuple(out[:3]), tuple(out[3:]) if sh else (None, None, None), stacked)
 
 
+def int8_weights(weights):
+    """Per-row INT8 copies of the same bf16 weights (MOE_LAYOUT_INT8_FRAG buffers)."""
+    (g, u, dn), shared, stacked = weights
+    sh = tuple(shared) if shared[0] is not None else None
+    out = moe.quantize_expert_weights(g, u, dn, sh)
+    torch.cuda.synchronize()
+    return (tuple(out[:3]), tuple(out[3:]) if sh else (None, None, None), stacked)
+
+
 def make_layer(cfg: synth.LayerConfig, seed: int = 0, screen: bool = True, weights=None,
                layout: int = moe.MOE_LAYOUT_ROWMAJOR) -> DeviceLayer:
     host = synth.host_small_inputs(cfg, seed)
@@ -97,6 +110,8 @@ def make_layer(cfg: synth.LayerConfig, seed: int = 0, screen: bool = True, weigh
         weights = make_weights(cfg, seed, host_copy=small)
         if layout == moe.MOE_LAYOUT_FRAG16:
             weights = packed_weights(weights)
+        elif layout == moe.MOE_LAYOUT_INT8_FRAG:
+            weights = int8_weights(weights)
     (g, u, dn), (sg, su, sd), stacked = weights
     bias = torch.from_numpy(host.router_bias).cuda() if host.router_bias is not None else None
     return DeviceLayer(cfg, seed, host, to_dev(host.x, cfg.dtype), to_dev(host.w_router, cfg.dtype), bias,

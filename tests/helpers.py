@@ -32,8 +32,15 @@ def screen_gaps(inp: synth.HostInputs, min_gap: float = MIN_GAP, max_rounds: int
     raise RuntimeError("gap screening did not converge")
 
 
-def expert_fn_host(cfg: synth.LayerConfig, seed: int, stacked=None, cache: bool = True):
-    """float64 expert weights for the oracle, regenerated on the host from the generator streams.
+def as_oracle_weight(a, dtype: str, int8: bool):
+    """float64 weight the oracle uses: the stored value, or the dequantized INT8 per-row code."""
+    w = oracle.widen(a, dtype)
+    return oracle.dequantize_rows_int8(*oracle.quantize_rows_int8(w)) if int8 else w
+
+
+def expert_fn_host(cfg: synth.LayerConfig, seed: int, stacked=None, cache: bool = True, int8: bool = False):
+    """float64 expert weights for the oracle, regenerated on the host from the generator streams
+    (dequantized from their per-row INT8 codes when ``int8``).
 
     ``cache=False`` regenerates on every call (large layers: one expert in memory at a time)."""
     store = {}
@@ -43,7 +50,7 @@ def expert_fn_host(cfg: synth.LayerConfig, seed: int, stacked=None, cache: bool 
             g, u, dn = (s[e] for s in stacked)
         else:
             g, u, dn = synth.expert_weights_host(cfg, seed, e)
-        return tuple(oracle.widen(a, cfg.dtype) for a in (g, u, dn))
+        return tuple(as_oracle_weight(a, cfg.dtype, int8) for a in (g, u, dn))
 
     def fn(e):
         if not cache:
@@ -55,14 +62,15 @@ def expert_fn_host(cfg: synth.LayerConfig, seed: int, stacked=None, cache: bool 
     return fn
 
 
-def shared_fn_host(cfg: synth.LayerConfig, seed: int):
+def shared_fn_host(cfg: synth.LayerConfig, seed: int, int8: bool = False):
     if cfg.Hs == 0:
         return None
     box = {}
 
     def fn():
         if "w" not in box:
-            box["w"] = tuple(oracle.widen(a, cfg.dtype) for a in synth.expert_weights_host(cfg, seed, 0, shared=True))
+            box["w"] = tuple(as_oracle_weight(a, cfg.dtype, int8)
+                             for a in synth.expert_weights_host(cfg, seed, 0, shared=True))
         return box["w"]
 
     return fn

@@ -150,6 +150,42 @@ def test_status_strings_and_stage_names():
     assert moe.moe_stage_kernel_name(dsv3(top_k=0), 0) == ""
 
 
+@pytest.mark.parametrize("shape,status", [
+    (dict(weight_layout=moe.MOE_LAYOUT_INT8_FRAG), moe.MOE_OK),
+    (dict(weight_layout=moe.MOE_LAYOUT_INT8_FRAG, dtype=moe.MOE_F32), moe.MOE_ERR_UNSUPPORTED),
+    (dict(weight_layout=moe.MOE_LAYOUT_INT8_FRAG, d_model=7200), moe.MOE_ERR_ALIGNMENT),
+    (dict(weight_layout=moe.MOE_LAYOUT_INT8_FRAG, d_hidden=2080), moe.MOE_ERR_ALIGNMENT),
+    (dict(weight_layout=moe.MOE_LAYOUT_INT8_FRAG, d_shared_hidden=2080), moe.MOE_ERR_ALIGNMENT),
+    (dict(weight_layout=3), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_int8_layout_validation(shape, status):
+    s = dsv3(**shape)
+    assert moe.moe_workspace_bytes(s) > 0 if status == moe.MOE_OK else moe.moe_workspace_bytes(s) == 0
+    if status != moe.MOE_OK:
+        assert status_of(moe.moe_layer_forward, s, **layer(s)) == status
+
+
+def test_int8_stage_names_always_stream():
+    q8 = moe.MOE_LAYOUT_INT8_FRAG
+    assert moe.moe_stage_kernel_name(dsv3(weight_layout=q8), 6) == "ffn_gate_up_stream<1, 2>"
+    assert moe.moe_stage_kernel_name(dsv3(weight_layout=q8), 7) == "ffn_down_stream<1, 2>"
+    big = dsv3(T=8192, weight_layout=q8)     # would be the grouped GEMM with bf16 weights
+    assert moe.moe_stage_kernel_name(big, 5) == "" and moe.moe_stage_kernel_name(big, 6) == "ffn_gate_up_stream<1, 2>"
+
+
+def test_quantize_weights_validation():
+    q = moe.moe_quantize_weights
+    assert moe.moe_quantized_weight_bytes(2, 16, 64) == 2 * 16 * 64 + 2 * 16 * 4
+    assert moe.moe_quantized_weight_bytes(-1, 16, 64) == 0
+    assert status_of(q, A, B, 1, 8, 64) == moe.MOE_ERR_ALIGNMENT      # rows % 16
+    assert status_of(q, A, B, 1, 16, 32) == moe.MOE_ERR_ALIGNMENT     # cols % 64
+    assert status_of(q, A, B, -1, 16, 64) == moe.MOE_ERR_INVALID_ARG
+    assert status_of(q, None, B, 1, 16, 64) == moe.MOE_ERR_INVALID_ARG
+    assert status_of(q, A + 8, B, 1, 16, 64) == moe.MOE_ERR_ALIGNMENT
+    assert status_of(q, A, A + 1024, 1, 16, 64) == moe.MOE_ERR_INVALID_ARG   # overlapping
+    assert status_of(q, None, None, 0, 16, 64) == moe.MOE_OK                 # nothing to do
+
+
 def test_empty_batch_accepts_null_tensors():
     s = dsv3(T=0)
     assert status_of(moe.moe_layer_forward, s, **layer(s, x=None, out=None, workspace=None)) == moe.MOE_OK

@@ -28,7 +28,8 @@ pytestmark = pytest.mark.gpu
 def dsv3_weights():
     cfg = synth.CONFIG_BY_NAME["dsv3_decode_t8"]
     w = G.make_weights(cfg, 0, host_copy=False)
-    yield {moe.MOE_LAYOUT_ROWMAJOR: w, moe.MOE_LAYOUT_FRAG16: G.packed_weights(w)}
+    yield {moe.MOE_LAYOUT_ROWMAJOR: w, moe.MOE_LAYOUT_FRAG16: G.packed_weights(w),
+           moe.MOE_LAYOUT_INT8_FRAG: G.int8_weights(w)}
     del w
     torch.cuda.empty_cache()
 
@@ -54,6 +55,18 @@ def test_dsv3_layer(name, n_sample, layout, dsv3_weights):
     cfg = synth.CONFIG_BY_NAME[name]
     L = G.make_layer(cfg, weights=dsv3_weights[layout], layout=layout)
     print(f"[{name}] gap-screen redraws: {sum(L.host.redraws.values())}", flush=True)
+    r = G.run_layer(L)
+    check_logits_close(L, r)
+    check_routing_on_gpu_logits(L, r)
+    tokens = np.arange(cfg.T) if n_sample is None else sample_tokens(cfg.T, n_sample)
+    sampled_check(L, r, tokens)
+
+
+@pytest.mark.parametrize("name,n_sample", [("dsv3_decode_t8", None), ("dsv3_decode_t256", 12)])
+def test_dsv3_layer_int8_weights(name, n_sample, dsv3_weights):
+    """Per-row INT8 expert weights at the decode sizes, against the oracle on the dequantized weights."""
+    cfg = synth.CONFIG_BY_NAME[name]
+    L = G.make_layer(cfg, weights=dsv3_weights[moe.MOE_LAYOUT_INT8_FRAG], layout=moe.MOE_LAYOUT_INT8_FRAG)
     r = G.run_layer(L)
     check_logits_close(L, r)
     check_routing_on_gpu_logits(L, r)
