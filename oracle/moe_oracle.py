@@ -56,7 +56,7 @@ __all__ = [
     "widen", "router_logits", "select_topk", "softmax_selected", "route", "permute", "silu",
     "swiglu", "grouped_ffn", "combine", "layer_forward", "layer_forward_tokens", "topk_gap",
     "logistic", "selection_scores", "sigmoid_weights_selected", "ROUTINGS",
-    "quantize", "dequantize", "quantize_rows_int8", "dequantize_rows_int8",
+    "quantize", "dequantize", "quantize_rows_int8", "dequantize_rows_int8", "load_stats",
 ]
 
 ROUTINGS = ("softmax", "sigmoid")
@@ -245,6 +245,18 @@ def permute(idx: np.ndarray, E: int):
     inv_perm = np.empty(T * k, np.int64)
     inv_perm[perm_src] = np.arange(T * k)
     return counts, offsets, perm_src, inv_perm
+
+
+def load_stats(counts: np.ndarray, T: int, k: int, coef: float = 0.01):
+    """Per-expert load and the balance penalty of the [MoE overview] §4.1 layer code: each expert's
+    share of the T*k assignments, load_e = counts_e / (T k), and
+    aux = coef * sum_e (load_e - 1/E)^2 (coef 0.01 there). Returns (load [E], aux); T = 0 gives
+    zero loads and the penalty of an empty batch, coef * sum_e (1/E)^2 = coef / E."""
+    counts = np.asarray(counts, np.float64)
+    E = counts.shape[0]
+    load = counts / (T * k) if T * k > 0 else np.zeros(E)
+    aux = coef * float(((load - 1.0 / E) ** 2).sum())
+    return load, aux
 
 
 # ----------------------------------------------------------------------------- experts

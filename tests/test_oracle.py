@@ -436,6 +436,35 @@ def test_int8_rows_match_torch_per_channel_quantization():
     assert near_half.mean() < 1e-3
 
 
+# ------------------------------------------------------------------ load statistics (MoE overview §4.1)
+
+def test_load_stats_closed_forms():
+    """Uniform assignment has no penalty; everything on one expert gives coef * (E-1)/E; the loads
+    are the assignment shares and sum to 1."""
+    E, T, k = 8, 16, 2
+    load, aux = oracle.load_stats(np.full(E, T * k // E), T, k)
+    np.testing.assert_allclose(load, 1.0 / E, rtol=0, atol=1e-15)
+    assert aux == 0.0
+    one = np.zeros(E, np.int64)
+    one[3] = T * k
+    load, aux = oracle.load_stats(one, T, k, coef=0.5)
+    assert load[3] == 1.0 and load.sum() == 1.0
+    assert abs(aux - 0.5 * (E - 1) / E) < 1e-15
+
+
+def test_load_stats_from_a_routing():
+    """On a real routing the loads are the assignment shares (brute-force count over the ids)."""
+    rng = np.random.default_rng(9)
+    x, wg, _ = rand_layer(rng, 50, 8, 6, 4)
+    _, idx, _ = oracle.route(x, wg, 2)
+    counts, _, _, _ = oracle.permute(idx, 6)
+    load, aux = oracle.load_stats(counts, 50, 2, coef=0.01)
+    for e in range(6):
+        assert load[e] == sum(1 for t in range(50) for j in range(2) if idx[t, j] == e) / 100
+    assert abs(load.sum() - 1.0) < 1e-15
+    assert abs(aux - 0.01 * sum((load[e] - 1 / 6) ** 2 for e in range(6))) < 1e-15
+
+
 # ------------------------------------------------------------------ planted mistakes are caught
 
 def _plant(monkeypatch, name, fn):
@@ -531,6 +560,11 @@ def _quant_cols(w):
     return q.astype(np.int8), (np.abs(w32).max(-1) / np.float32(127.0)).astype(np.float32)
 
 
+def _load_over_tokens(counts, T, k, coef=0.01):
+    load = np.asarray(counts, np.float64) / T
+    return load, coef * float(((load - 1.0 / len(load)) ** 2).sum())
+
+
 _COMBINE = om.combine
 _PERMUTE = om.permute
 _SELECTION = om.selection_scores
@@ -561,6 +595,7 @@ MUTATIONS = {
     "int8_scale_per_column": ("quantize_rows_int8", _quant_cols, test_int8_rows_match_torch_per_channel_quantization),
     "dequantize_without_zero_point": ("dequantize", lambda q, s, z=0: np.asarray(q, np.float64) * s,
                                       test_quantization_example_from_the_pages),
+    "load_over_tokens_not_slots": ("load_stats", _load_over_tokens, test_load_stats_closed_forms),
 }
 
 
