@@ -165,6 +165,17 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* exp
                        size_t ws_bytes, void* stream);
 
 /*
+ * moe_load_stats -- load statistics of a routing (overview article section 4.1, the layer code's
+ * auxiliary balance loss):
+ *   load_out[e]     = expert_counts[e] / (T * k)                                   float32 [E]
+ *   aux_loss_out[0] = coef * sum_e (load_out[e] - 1/E)^2   (the page uses coef = 0.01) float32 [1]
+ * expert_counts [E] int32 as written by moe_permute / moe_layer_forward; load_out and
+ * aux_loss_out may each be NULL. float32, fixed summation order (deterministic).
+ */
+moe_status moe_load_stats(const moe_shape* s, const int32_t* expert_counts, float coef, float* load_out,
+                          float* aux_loss_out, void* stream);
+
+/*
  * moe_grouped_ffn -- every expert over its own contiguous bucket of rows, in one pass
  * (MoE-kernels page sections 1.2 and 4.2):
  *   for each e and each row r in [expert_offsets[e], expert_offsets[e+1]):

@@ -67,6 +67,7 @@ _sigs = {
     "moe_stage_kernel_name": (ctypes.c_char_p, [_S, ctypes.c_int]),
     "moe_pack_weights": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
     "moe_quantize_weights": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
+    "moe_load_stats": (ctypes.c_int, [_S, _P, ctypes.c_float, _P, _P, _P]),
     "moe_quantized_weight_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
 }
 for _name, (_res, _args) in _sigs.items():
@@ -181,6 +182,12 @@ def pack_expert_weights(w_gate, w_up, w_down, shared=None, stream=None):
         moe_pack_weights(w, p, n, w.shape[-2], w.shape[-1], stream)
         out.append(p)
     return out
+
+
+def moe_load_stats(shape, expert_counts, coef=0.01, load_out=None, aux_loss_out=None, stream=None):
+    """Per-expert load counts/(T*k) and the balance penalty coef * sum (load - 1/E)^2."""
+    _check("moe_load_stats", _lib.moe_load_stats(ctypes.byref(shape), _ptr(expert_counts), coef, _ptr(load_out),
+                                                 _ptr(aux_loss_out), _stream(stream)))
 
 
 def moe_quantize_weights(src, dst, n_mats, rows, cols, stream=None):

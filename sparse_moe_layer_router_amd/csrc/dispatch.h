@@ -42,6 +42,10 @@ hipError_t launch_permute_scatter(const int32_t* topk_idx, long long rows, int E
                                   const int32_t* tile_counts, int32_t* perm_src, int32_t* inv_perm,
                                   hipStream_t stream);
 
+// load statistics: load[e] = counts[e] / slots, aux = coef * sum_e (load[e] - 1/E)^2 (either output may be NULL)
+hipError_t launch_load_stats(const int32_t* counts, int E, long long slots, float coef, float* load, float* aux,
+                             hipStream_t stream);
+
 // ---- combine ---------------------------------------------------------------------------------
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_perm, const float* topk_w,
                           const void* shared_out, void* out, int T, int k, int d, hipStream_t stream);

@@ -298,6 +298,18 @@ moe_status moe_pack_weights(const void* src, void* dst, int64_t n_mats, int32_t 
   return MOE_OK;
 }
 
+moe_status moe_load_stats(const moe_shape* s, const int32_t* expert_counts, float coef, float* load_out,
+                          float* aux_loss_out, void* stream) {
+  MOE_TRY(check_shape(s));
+  if (s->T == 0) return MOE_OK;
+  MOE_TRY(need(expert_counts, 4));
+  MOE_TRY(maybe(load_out, 4));
+  MOE_TRY(maybe(aux_loss_out, 4));
+  MOE_LAUNCH(moe::launch_load_stats(expert_counts, s->n_experts, (long long)s->T * s->top_k, coef, load_out,
+                                    aux_loss_out, (hipStream_t)stream));
+  return MOE_OK;
+}
+
 moe_status moe_quantize_weights(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols,
                                 void* stream) {
   if (n_mats < 0 || rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;

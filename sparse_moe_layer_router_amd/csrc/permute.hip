@@ -121,6 +121,38 @@ permute_scatter_kernel(const int32_t* __restrict__ ids, long long rows, int E, i
   }
 }
 
+// Load statistics of one routing (overview article, section 4.1 layer code): every expert's
+// share of the T*k assignments and the balance penalty coef * sum_e (load_e - 1/E)^2. One block,
+// one expert per thread, the sum in a fixed order (wave butterflies, then the wave totals in order).
+__global__ void __launch_bounds__(1024)
+load_stats_kernel(const int32_t* __restrict__ counts, int E, long long slots, float coef, float* __restrict__ load,
+                  float* __restrict__ aux) {
+  __shared__ float wave_tot[16];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  float sq = 0.f;
+  if (e < E) {
+    const float l = (float)counts[e] / (float)slots;
+    if (load) load[e] = l;
+    const float dl = l - 1.0f / (float)E;
+    sq = dl * dl;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 64);
+  if (lane == 0) wave_tot[wave] = sq;
+  __syncthreads();
+  if (e == 0 && aux) {
+    float t = 0.f;
+    for (int w = 0; w < 16; ++w) t += wave_tot[w];
+    aux[0] = coef * t;
+  }
+}
+
+hipError_t launch_load_stats(const int32_t* counts, int E, long long slots, float coef, float* load, float* aux,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(load_stats_kernel, dim3(1), dim3(1024), 0, stream, counts, E, slots, coef, load, aux);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute_count(const int32_t* ids, long long rows, int E, int tile, int32_t* tile_counts,
                                 hipStream_t stream) {
   int n_tiles = (int)((rows + tile - 1) / tile);

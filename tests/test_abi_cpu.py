@@ -173,6 +173,15 @@ def test_int8_stage_names_always_stream():
     assert moe.moe_stage_kernel_name(big, 5) == "" and moe.moe_stage_kernel_name(big, 6) == "ffn_gate_up_stream<1, 2>"
 
 
+def test_load_stats_validation():
+    s = dsv3()
+    assert status_of(moe.moe_load_stats, s, None, 0.01, A, A) == moe.MOE_ERR_INVALID_ARG
+    assert status_of(moe.moe_load_stats, s, A + 2, 0.01, A, A) == moe.MOE_ERR_ALIGNMENT
+    assert status_of(moe.moe_load_stats, s, A, 0.01, A + 2, A) == moe.MOE_ERR_ALIGNMENT
+    assert status_of(moe.moe_load_stats, dsv3(T=0), None, 0.01, None, None) == moe.MOE_OK
+    assert status_of(moe.moe_load_stats, dsv3(top_k=0), A, 0.01, A, A) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_quantize_weights_validation():
     q = moe.moe_quantize_weights
     assert moe.moe_quantized_weight_bytes(2, 16, 64) == 2 * 16 * 64 + 2 * 16 * 4

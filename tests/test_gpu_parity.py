@@ -272,6 +272,23 @@ def test_topk_tie_heavy_every_lane_width(E, routing):
             np.testing.assert_array_equal(w2.cpu().numpy().view(np.uint32), w.cpu().numpy().view(np.uint32))
 
 
+@pytest.mark.parametrize("cfg", [MID[0], MID[1], MID[6], synth.CONFIGS[0]], ids=lambda c: c.name)
+def test_load_stats_match_oracle(cfg):
+    """Per-expert load and balance penalty of the GPU's own routing, against the oracle's."""
+    L = G.make_layer(cfg)
+    r = G.run_layer(L)
+    load = torch.empty(cfg.E, dtype=torch.float32, device="cuda")
+    aux = torch.empty(1, dtype=torch.float32, device="cuda")
+    moe.moe_load_stats(L.shape, r.counts, 0.01, load, aux)
+    aux2 = torch.empty(1, dtype=torch.float32, device="cuda")
+    moe.moe_load_stats(L.shape, r.counts, 0.01, None, aux2)        # the load output is optional
+    torch.cuda.synchronize()
+    load_o, aux_o = oracle.load_stats(r.counts.cpu().numpy(), cfg.T, cfg.k, 0.01)
+    np.testing.assert_allclose(load.cpu().numpy(), load_o, rtol=1e-6, atol=0)
+    assert abs(aux.item() - aux_o) <= 1e-5 * aux_o + 1e-12, (aux.item(), aux_o)
+    assert aux2.item() == aux.item()
+
+
 def test_deterministic_bitwise():
     L = G.make_layer(MID[0])
     a = G.run_layer(L)
