@@ -7,26 +7,30 @@
 // no expert waits on a separate launch; data-movement page, section 15: once routes are sorted by
 // expert, each expert's weights are loaded once and reused across its whole bucket of tokens.
 //
-// Tiles: BM = 128 rows (tokens) x BN weight rows per B matrix x BK = 32 along K; 512 threads as
-// 2 x 4 waves (two per SIMD), wave (wm, wn) owning rows [64 wm, 64 wm + 64) x BN/4 columns of
-// every B matrix as 32x32x16 MFMA blocks: 8 MFMAs per 16-wide K step from 2 A and 4 B fragments,
-// 128 accumulator registers per wave, which leaves room for double-buffered fragments at two
-// waves per SIMD. Gate and up projections are computed by the same block for the same rows (two B
-// tiles), so SiLU(g)*u is formed in registers and the hidden activation leaves as bf16.
+// Tiles. An expert bucket is cut into M-tiles of up to BM = 320 rows, so a bucket of the prefill
+// regime (about 256 +- 50 rows) is a single M-tile and every weight tile is fetched once per
+// bucket. The tile is BM rows x 256 weight rows (gate/up: 128 gate + 128 up rows for the same
+// hidden columns; down and router: 256 output columns) x BK = 32 along K. 512 threads = 8 waves,
+// two per SIMD, as 2 (M) x 4 (N): wave (wm, wn) owns the 32-row blocks wm, wm + 2, ..., wm + 8
+// (interleaved, so a partly filled tile still splits its rows evenly) and 32 + 32 (gate/up) or
+// 64 columns, as 32x32x16 MFMA blocks: 5 x 2 accumulators of 16 registers. A wave runs only the
+// blocks that hold rows of the tile (a body specialised on that count), so a bucket of 260 rows
+// costs 9 row blocks of MFMA work, not 2 x 256.
 //
 // Operands go straight from global memory into a four-slice LDS ring (global_load_lds, 16 bytes
-// per lane, no register staging), the loads of each slice spread over the MFMAs of the two K steps
-// after the barrier that frees its buffer; waves wait (s_waitcnt vmcnt) only for the slice they
-// need next, with two further slices in flight. Fragments are double-buffered in registers across K steps: while the
-// MFMAs of step j run, the LDS reads of step j+1 are issued between them (scheduling groups pin
-// one read after each of the first MFMAs), so LDS latency hides behind matrix work. The
-// slice barrier sits between the two steps of a slice. A 16-byte-chunk XOR swizzle (activations)
-// and the fragment-tiled weight layout keep fragment reads bank-conflict free.
+// per lane, no register staging; 4 x 36 KB). A slice is 36 load instructions of 1 KB: waves 0-3
+// load the 20 activation groups (16 rows x 64 bytes each, gathered through the permutation),
+// waves 4-7 the 16 weight blocks; each wave's loads for a slice are spread over the MFMAs of the
+// two K steps after the barrier that frees its buffer, and a wave waits (s_waitcnt vmcnt) only
+// for the slice it needs next, with two further slices in flight. Fragments are double-buffered
+// in registers across K steps: while the MFMAs of step j run, the LDS reads of step j+1 are issued
+// between them. A 16-byte-chunk XOR swizzle (activations) and the fragment-tiled weight layout keep
+// fragment reads bank-conflict free.
 //
 // Tile order: tiles are numbered expert by expert, N-tile by N-tile, with the M-tiles of one
 // (expert, N-tile) adjacent. Workgroups are dealt round-robin to the 8 XCDs, so block L runs tile
-// (L % 8) * per_xcd + L / 8: adjacent tiles run at the same time on the same XCD and the second
-// and third M-tiles of a weight tile find it in that XCD's L2 instead of HBM.
+// (L % 8) * per_xcd + L / 8: the N-tiles of one expert run at the same time on the same XCD and
+// share its activation rows in that XCD's L2.
 #include "kernels.h"
 #include "moe_device.h"
 
@@ -34,30 +38,32 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = 128;
 constexpr int BK = 32;
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kWavesM = 2, kWavesN = 4;
 constexpr int kXcds = 8;
-constexpr int kStages = 4;   // LDS ring depth (4 x 40 KB = all 160 KB of LDS): two slices fully in flight
+constexpr int kStages = 4;         // LDS ring depth: two slices in flight while one is consumed
 constexpr int kRowBytes = BK * 2;  // one tile row in LDS: 64 bytes = 4 chunks of 16
 
 enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2 };
 
 template <int MODE> struct Geo {
-  static constexpr int NB = MODE == kGateUp ? 2 : 1;                          // B matrices per tile
-  static constexpr int BN = MODE == kGateUp ? 256 : (MODE == kDown ? 512 : 256);  // rows of each B tile
-  static constexpr int WM = BM / kWavesM;                                      // rows per wave
-  static constexpr int WN = BN / kWavesN;                                     // columns per wave
-  static constexpr int NBLK = WN / 32;                                        // 32-wide MFMA blocks
-  static constexpr int MBLK = WM / 32;                                        // 32-high MFMA blocks
-  static constexpr int A_BYTES = BM * kRowBytes;
-  static constexpr int B_BYTES = NB * BN * kRowBytes;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_LOADS = BM * (BK / 8) / kThreads;         // 16-byte chunks per lane
-  static constexpr int B_LOADS = NB * BN * (BK / 8) / kThreads;
-  static constexpr int LOADS = A_LOADS + B_LOADS;                  // global_load_lds per wave per slice
+  static constexpr int MBW = MODE == kRouter ? 2 : 5;              // 32-row blocks per wave
+  static constexpr int BM = MBW * kWavesM * 32;                    // tile rows: 320 (router 128)
+  static constexpr int NB = MODE == kGateUp ? 2 : 1;               // B matrices per tile
+  static constexpr int BN = MODE == kGateUp ? 128 : 256;           // rows of each B tile
+  static constexpr int BROWS = NB * BN;                            // stacked B rows (256)
+  static constexpr int A_INSTR = BM / 16;                          // 1 KB loads of A per slice
+  static constexpr int B_INSTR = BROWS / 16;                       // 1 KB loads of B per slice
+  static constexpr int INSTR = A_INSTR + B_INSTR;
+  static constexpr int L_HI = (INSTR + kWaves - 1) / kWaves;       // loads per slice, waves < N_HI
+  static constexpr int N_HI = INSTR - kWaves * (L_HI - 1);
+  static constexpr int L_LO = L_HI - 1;                            // loads per slice, other waves
+  static constexpr int SPLIT = (L_HI + 1) / 2;                     // loads issued in part 1
+  static constexpr int A_BYTES = A_INSTR * 1024;
+  static constexpr int STAGE = INSTR * 1024;
+  static_assert(N_HI >= 1 && N_HI <= kWaves, "load split");
 };
 
 // LDS byte offset of 16-byte chunk `chunk` (0..3) of tile row `row`. The XOR key takes four
@@ -67,62 +73,81 @@ template <int MODE> struct Geo {
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 2)) & 3); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + (swz_chunk(row, chunk) << 4); }
 
-// LDS reads of one 16-wide K step: the wave's MBLK A fragments (rows wm*WM + 32*mb + fr) and the
-// NB x NBLK B fragments (rows wn*WN + 32*nb + fr of each B tile), chunk column ch.
-template <class G, int LAYOUT>
-__device__ __forceinline__ void load_frags(u32x4_t (&fa)[G::MBLK], u32x4_t (&fb)[G::NB][G::NBLK], const uint8_t* sa,
-                                           const uint8_t* sb, int wm, int wn, int fr, int ch) {
+// Stacked B row (inside the slice's B region) of the wave's B fragment j for fragment row fr.
+template <int MODE>
+__device__ __forceinline__ int b_row(int j, int wn, int fr) {
+  return MODE == kGateUp ? j * Geo<MODE>::BN + wn * 32 + fr : wn * 64 + j * 32 + fr;
+}
+
+// A fragment i (rows (wm + 2 i) * 32 + fr) and B fragment j of one 16-wide K step, chunk column ch.
+__device__ __forceinline__ u32x4_t read_a(const uint8_t* sa, int i, int wm, int fr, int ch) {
+  return *(const u32x4_t*)(sa + swz((wm + 2 * i) * 32 + fr, ch));
+}
+template <int MODE, int LAYOUT>
+__device__ __forceinline__ u32x4_t read_b(const uint8_t* sb, int j, int wn, int fr, int ch) {
+  const int n = b_row<MODE>(j, wn, fr);
+  if (LAYOUT == kFrag16)  // block n/16 of the stacked tile; lane position (n%16) + 16*chunk
+    return *(const u32x4_t*)(sb + (n / 16) * 1024 + ((n & 15) + 16 * ch) * 16);
+  return *(const u32x4_t*)(sb + swz(n, ch));
+}
+
+// The MFMAs of one 16-wide K step on the fragments in fa / fb, and the LDS reads of the next step
+// into the same registers, each issued right after the last MFMA that needs the value it
+// replaces: B fragment 0 after the NA MFMAs of column block 0, A fragment i after its MFMA with B
+// fragment 1, B fragment 1 last. Every read then has NA MFMAs to land before its first use.
+// `loads` (the step's global-to-LDS loads) comes after the MFMAs of column block 0 in program order.
+template <int MODE, int LAYOUT, int NA, class Loads>
+__device__ __forceinline__ void mma_and_read(f32x16_t (&acc)[NA > 0 ? NA : 1][2], u32x4_t (&fa)[NA > 0 ? NA : 1],
+                                             u32x4_t (&fb)[2], const uint8_t* sa, const uint8_t* sb, int wm,
+                                             int wn, int fr, int ch, Loads&& loads) {
 #pragma unroll
-  for (int mb = 0; mb < G::MBLK; ++mb) fa[mb] = *(const u32x4_t*)(sa + swz(wm * G::WM + mb * 32 + fr, ch));
+  for (int i = 0; i < NA; ++i) acc[i][0] = mfma32x32x16(fa[i], fb[0], acc[i][0]);
+  loads();
+  if (NA > 0) fb[0] = read_b<MODE, LAYOUT>(sb, 0, wn, fr, ch);
 #pragma unroll
-  for (int b = 0; b < G::NB; ++b)
+  for (int i = 0; i < NA; ++i) {
+    acc[i][1] = mfma32x32x16(fa[i], fb[1], acc[i][1]);
+    fa[i] = read_a(sa, i, wm, fr, ch);
+  }
+  if (NA > 0) fb[1] = read_b<MODE, LAYOUT>(sb, 1, wn, fr, ch);
+}
+
+// First reads of a tile (nothing to multiply yet).
+template <int MODE, int LAYOUT, int NA>
+__device__ __forceinline__ void read_all(u32x4_t (&fa)[NA > 0 ? NA : 1], u32x4_t (&fb)[2], const uint8_t* sa,
+                                         const uint8_t* sb, int wm, int wn, int fr, int ch) {
+  if (NA == 0) return;
 #pragma unroll
-    for (int nb = 0; nb < G::NBLK; ++nb) {
-      const int n = wn * G::WN + nb * 32 + fr;   // row inside B matrix b's tile
-      if (LAYOUT == kFrag16)  // block n/16 of matrix b; lane position (n%16) + 16*chunk
-        fb[b][nb] = *(const u32x4_t*)(sb + (b * (G::BN / 16) + n / 16) * 1024 + ((n & 15) + 16 * ch) * 16);
-      else
-        fb[b][nb] = *(const u32x4_t*)(sb + swz(b * G::BN + n, ch));
+  for (int i = 0; i < NA; ++i) fa[i] = read_a(sa, i, wm, fr, ch);
+  fb[0] = read_b<MODE, LAYOUT>(sb, 0, wn, fr, ch);
+  fb[1] = read_b<MODE, LAYOUT>(sb, 1, wn, fr, ch);
+}
+
+// Pin the order of one step's instructions: the NA MFMAs of column block 0 with one
+// global-to-LDS load after each of the first VMEMS of them (loads beyond NA follow), then the read
+// of B fragment 0, then MFMA / A-fragment read pairs, then the read of B fragment 1. The loads
+// come first in program order, so the reads (which the compiler cannot tell apart from the
+// buffers the loads write) stay after them.
+template <int NA, int VMEMS>
+__device__ __forceinline__ void pin_step() {
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
+    if (i < VMEMS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
+  }
+  if (VMEMS > NA) __builtin_amdgcn_sched_group_barrier(0x020, VMEMS > NA ? VMEMS - NA : 0, 0);
+  if (NA > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // read B fragment 0
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // read A fragment i
     }
-}
-
-template <class G>
-__device__ __forceinline__ void mma_step(f32x16_t (&acc)[G::NB][G::MBLK][G::NBLK], const u32x4_t (&fa)[G::MBLK],
-                                         const u32x4_t (&fb)[G::NB][G::NBLK]) {
-#pragma unroll
-  for (int b = 0; b < G::NB; ++b)
-#pragma unroll
-    for (int nb = 0; nb < G::NBLK; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < G::MBLK; ++mb) acc[b][mb][nb] = mfma32x32x16(fa[mb], fb[b][nb], acc[b][mb][nb]);
-}
-
-// Pin the order of the instructions just emitted: MFMA, LDS read, MFMA, LDS read, ... and then the
-// remaining MFMAs, so each LDS read issues under an MFMA instead of in a block before them.
-template <int MFMAS, int READS>
-__device__ __forceinline__ void interleave_mfma_lds() {
-  static_assert(READS <= MFMAS, "one LDS read after each of the first READS MFMAs");
-#pragma unroll
-  for (int i = 0; i < READS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-  }
-  if (MFMAS > READS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
-}
-
-// The same with VMEMS global-to-LDS loads after each of the last VMEMS MFMAs. The loads write LDS
-// that the compiler cannot tell apart from the buffer being read, so they stay after the reads
-// (their program order): MFMA, read, ..., MFMA, read, load, ..., MFMA, load.
-template <int MFMAS, int READS, int VMEMS>
-__device__ __forceinline__ void interleave_mfma_lds_vmem() {
-  static_assert(READS <= MFMAS && VMEMS <= MFMAS, "at most one read and one load after each MFMA");
-#pragma unroll
-  for (int i = 0; i < MFMAS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // one MFMA
-    if (i < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);           // one LDS read
-    if (i >= MFMAS - VMEMS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // read B fragment 1
   }
 }
+
+template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 }  // namespace
 
@@ -152,9 +177,8 @@ gemm_schedule_kernel(const FfnGroups p, int32_t* __restrict__ sched_gu, int32_t*
         n = p.T;
         Hg = p.Hs;
       }
-      const int mt = (int)((n + BM - 1) / BM);
-      a = mt * ((Hg + Geo<kGateUp>::BN - 1) / Geo<kGateUp>::BN);
-      b = mt * ((p.d + Geo<kDown>::BN - 1) / Geo<kDown>::BN);
+      a = (int)((n + Geo<kGateUp>::BM - 1) / Geo<kGateUp>::BM) * ((Hg + Geo<kGateUp>::BN - 1) / Geo<kGateUp>::BN);
+      b = (int)((n + Geo<kDown>::BM - 1) / Geo<kDown>::BM) * ((p.d + Geo<kDown>::BN - 1) / Geo<kDown>::BN);
     }
     int32_t ia = a, ib = b;
 #pragma unroll
@@ -188,11 +212,162 @@ struct GemmArgs {
   int T, E, d;
 };
 
+// Everything one tile's main loop needs, set up once per tile.
+template <int MODE>
+struct TileCtx {
+  int g;                  // group (expert; E = shared expert)
+  long long r0;           // first row of the tile in its group's row space (group row base + m0)
+  int rows;               // valid rows in the tile (1..BM)
+  int n0, N, K, nk;       // first output column, output columns, reduction length, K slices
+  int first;              // first load slot of this wave
+  const uint16_t* src[Geo<MODE>::L_HI];  // per load: lane's source at K slice 0
+  int kc[Geo<MODE>::L_HI];               // per load: element offset of the lane's chunk in a slice
+  int stride[Geo<MODE>::L_HI];           // per load: elements to advance per K slice (wave-uniform)
+};
+
 // Tile count of a launch: from the router's sizes, or the schedule's running total.
 template <int MODE>
 __device__ __forceinline__ int gemm_total_tiles(const GemmArgs& ga) {
-  if (MODE == kRouter) return ((ga.T + BM - 1) / BM) * ((ga.E + Geo<MODE>::BN - 1) / Geo<MODE>::BN);
+  if (MODE == kRouter) return ((ga.T + Geo<MODE>::BM - 1) / Geo<MODE>::BM) * ((ga.E + Geo<MODE>::BN - 1) / Geo<MODE>::BN);
   return ga.sched[ga.p.E + (ga.p.Hs > 0 ? 1 : 0)];
+}
+
+// Main loop and epilogue of one tile for a wave that owns NA active row blocks and issues L loads
+// per slice.
+template <int MODE, int LAYOUT, int NA, int L>
+__device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE>& c,
+                                          uint8_t (*smem)[Geo<MODE>::STAGE], int wv) {
+  using G = Geo<MODE>;
+  constexpr int NAF = NA > 0 ? NA : 1;
+  const int lane = lane_id();
+  const int K = c.K, nk = c.nk;
+  typedef __attribute__((address_space(3))) void lds_t;
+
+  // Loads j in [j0, j1) of slice kt into ring buffer `buf`. A slice index past the end is clamped
+  // to the last slice: such loads fill a buffer that is never read again, which keeps the number
+  // of loads per slice fixed for the vmcnt arithmetic below.
+  auto issue = [&](int kt, int buf, int j0, int j1) {
+    const int kcl = kt < nk ? kt : nk - 1;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      if (i < j0 || i >= j1) continue;
+      const int k = kcl * BK + c.kc[i];
+      const uint16_t* s = c.src[i] + (k < K ? (size_t)kcl * c.stride[i] + c.kc[i] : 0);  // past K: zeroed later
+      __builtin_amdgcn_global_load_lds((const void*)s, (lds_t*)(smem[buf] + (c.first + i) * 1024), 16, 0, 0);
+    }
+  };
+  // chunks past K in the last slice: write zeros over what the loads brought in
+  auto zero_tail = [&](int kt, int buf) {
+    const u32x4_t zero = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      if (kt * BK + c.kc[i] >= K) *(u32x4_t*)(smem[buf] + (c.first + i) * 1024 + lane * 16) = zero;
+  };
+
+  f32x16_t acc[NAF][2];
+#pragma unroll
+  for (int i = 0; i < NAF; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int fr = lane & 31, fh = lane >> 5;   // fragment row / k-half of this lane
+  const int wm = wv / kWavesN, wn = wv % kWavesN;
+
+  // Ring protocol (S = kStages). The loads of slice s go to buffer s % S and are issued in two
+  // parts spread over the MFMAs: part 1 (loads [0, P1)) during step 1 of slice s-S, part 2 (the
+  // rest) during step 0 of slice s-S+1, both after the barrier that ends every wave's reads of
+  // slice s-S, the previous tenant of the buffer. Before step 1 of slice kt a wave waits for its
+  // loads of slice kt+1: slices kt+2 .. kt+S-1 have been issued in full by then and loads complete
+  // in issue order, so vmcnt((S-2) * L) leaves exactly those outstanding. The barrier that follows
+  // makes every wave's part of slice kt+1 visible. Slices past the end are clamped copies of the
+  // last one (see issue); in the last step the buffer of slice kt+1 (free: its previous tenant was
+  // slice kt+1-S) takes them, since the current buffer may still be read by waves that are behind
+  // and no barrier follows.
+  constexpr int S = kStages;
+  static_assert(S >= 3, "the issue schedule below needs a ring of at least 3 slices");
+  constexpr int P1 = G::SPLIT < L ? G::SPLIT : L;
+  constexpr int kAhead = (S - 2) * L;   // loads allowed in flight when slice kt+1 must land
+  static_assert(kAhead + P1 < 64, "vmcnt holds 6 bits");
+  auto arrive = [&](int kt) {
+    wait_vmcnt<kAhead>();
+    if (kt == nk - 1 && (K % BK)) zero_tail(kt, kt % S);  // its loads have all landed here
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  static_assert(BK / 16 == 2, "the loop below is written for two K steps per slice");
+  u32x4_t fa[NAF], fb[2];
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) issue(i, i, 0, L);
+  issue(S - 1, S - 1, 0, P1);
+  wait_vmcnt<kAhead + P1>();
+  if (nk == 1 && (K % BK)) zero_tail(0, 0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  read_all<MODE, LAYOUT, NA>(fa, fb, smem[0], smem[0] + G::A_BYTES, wm, wn, fr, fh);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt % S;
+    // step 0 of slice kt: multiply while reading step 1 (chunks 2, 3 of the same slice) and issuing
+    // part 2 of slice kt+S-1
+    mma_and_read<MODE, LAYOUT, NA>(acc, fa, fb, smem[buf], smem[buf] + G::A_BYTES, wm, wn, fr, 2 + fh,
+                                   [&] { issue(kt + S - 1, (kt + S - 1) % S, P1, L); });
+    pin_step<NA, L - P1>();
+    // step 1 of slice kt: multiply while reading step 0 of slice kt+1 and issuing part 1 of slice
+    // kt+S into this slice's buffer (after the last slice the reads re-read the current buffer and
+    // are never used)
+    if (kt + 1 < nk) arrive(kt + 1);
+    const int nbuf = kt + 1 < nk ? (kt + 1) % S : buf;
+    const int lbuf = kt + 1 < nk ? buf : (kt + 1) % S;
+    mma_and_read<MODE, LAYOUT, NA>(acc, fa, fb, smem[nbuf], smem[nbuf] + G::A_BYTES, wm, wn, fr, fh,
+                                   [&] { issue(kt + S, lbuf, 0, P1); });
+    pin_step<NA, P1>();
+  }
+  wait_vmcnt<0>();  // no load may still write LDS when the tile ends
+
+  // ---- epilogue: lane holds column fr of each 32x32 block, rows (e/4)*8 + fh*4 + e%4 ---------
+  // The lane index is re-read through an opaque move so that no output address is computed
+  // before the main loop (hoisted addresses would stay live in registers across it).
+  int elane = lane;
+  asm volatile("" : "+v"(elane));
+  const int efr = elane & 31, efh = elane >> 5;
+  const FfnGroups& p = ga.p;
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+#pragma unroll
+    for (int j = 0; j < (MODE == kGateUp ? 1 : 2); ++j) {
+      const int n = c.n0 + (MODE == kGateUp ? wn * 32 : wn * 64 + j * 32) + efr;
+      if (n >= c.N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = (wm + 2 * i) * 32 + (e >> 2) * 8 + efh * 4 + (e & 3);
+        if (row >= c.rows) continue;
+        if (MODE == kGateUp) {
+          const float gv = acc[i][0][e], uv = acc[i][1][e];
+          uint16_t* hid = (uint16_t*)p.hid + (c.g < p.E ? 0 : (size_t)p.rows * p.H);
+          hid[(size_t)(c.r0 + row) * c.N + n] = (uint16_t)f32_to_bf16(silu(gv) * uv);
+        } else if (MODE == kDown) {
+          uint16_t* y = (uint16_t*)p.y + (c.g < p.E ? 0 : (size_t)p.rows * p.d);
+          y[(size_t)(c.r0 + row) * c.N + n] = (uint16_t)f32_to_bf16(acc[i][j][e]);
+        } else {
+          ga.logits[(size_t)(c.r0 + row) * c.N + n] = acc[i][j][e] + (ga.bias ? ga.bias[n] : 0.f);
+        }
+      }
+    }
+  }
+}
+
+// The body specialised on the wave's active row-block count.
+template <int MODE, int LAYOUT, int L>
+__device__ __forceinline__ void tile_body_na(const GemmArgs& ga, const TileCtx<MODE>& c,
+                                             uint8_t (*smem)[Geo<MODE>::STAGE], int wv, int na) {
+  switch (na) {
+    case 0: tile_body<MODE, LAYOUT, 0, L>(ga, c, smem, wv); break;
+    case 1: tile_body<MODE, LAYOUT, 1, L>(ga, c, smem, wv); break;
+    case 2: tile_body<MODE, LAYOUT, 2, L>(ga, c, smem, wv); break;
+    case 3: if constexpr (Geo<MODE>::MBW >= 3) tile_body<MODE, LAYOUT, 3, L>(ga, c, smem, wv); break;
+    case 4: if constexpr (Geo<MODE>::MBW >= 4) tile_body<MODE, LAYOUT, 4, L>(ga, c, smem, wv); break;
+    default: if constexpr (Geo<MODE>::MBW >= 5) tile_body<MODE, LAYOUT, 5, L>(ga, c, smem, wv); break;
+  }
 }
 
 // One output tile t (0 <= t < gemm_total_tiles) through the LDS ring `smem`.
@@ -204,252 +379,128 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave index, 0..7
 
   // ---- which tile --------------------------------------------------------------------------
-  int g = 0, mt = 0, nt = 0;
-  long long r0 = 0;      // first row of the group in its row space
+  TileCtx<MODE> c;
+  int mt = 0, nt = 0;
+  long long gr0 = 0;     // first row of the group in its row space
   int nrows = 0;         // rows in the group
-  int N = 0, K = 0;      // output columns (weight rows) and reduction length of this group
   const uint16_t* Bp[2] = {nullptr, nullptr};
-  {
-    if (MODE == kRouter) {
-      nt = t / ((ga.T + BM - 1) / BM);
-      mt = t % ((ga.T + BM - 1) / BM);
-      nrows = ga.T;
-      N = ga.E;
-      K = ga.d;
-      Bp[0] = (const uint16_t*)ga.w;
+  c.g = 0;
+  if (MODE == kRouter) {
+    const int mtiles = (ga.T + G::BM - 1) / G::BM;
+    nt = t / mtiles;
+    mt = t % mtiles;
+    nrows = ga.T;
+    c.N = ga.E;
+    c.K = ga.d;
+    Bp[0] = (const uint16_t*)ga.w;
+  } else {
+    const int ngroups = p.E + (p.Hs > 0 ? 1 : 0);
+    int lo = 0, hi = ngroups;  // last group with sched[g] <= t
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ga.sched[mid] <= t) lo = mid; else hi = mid;
+    }
+    c.g = lo;
+    int Hg;
+    if (c.g < p.E) {
+      long long a = p.offsets[c.g], b = p.offsets[c.g + 1];
+      a = a < 0 ? 0 : (a > p.rows ? p.rows : a);
+      b = b < a ? a : (b > p.rows ? p.rows : b);
+      gr0 = a;
+      nrows = (int)(b - a);
+      Hg = p.H;
     } else {
-      const int ngroups = p.E + (p.Hs > 0 ? 1 : 0);
-      int lo = 0, hi = ngroups;  // last group with sched[g] <= t
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (ga.sched[mid] <= t) lo = mid; else hi = mid;
-      }
-      g = lo;
-      int Hg;
-      if (g < p.E) {
-        long long a = p.offsets[g], b = p.offsets[g + 1];
-        a = a < 0 ? 0 : (a > p.rows ? p.rows : a);
-        b = b < a ? a : (b > p.rows ? p.rows : b);
-        r0 = a;
-        nrows = (int)(b - a);
-        Hg = p.H;
-      } else {
-        r0 = 0;
-        nrows = p.T;
-        Hg = p.Hs;
-      }
-      const int mtiles = (nrows + BM - 1) / BM;
-      const int local = t - ga.sched[g];
-      nt = local / mtiles;
-      mt = local % mtiles;
-      const size_t wsz = (size_t)p.H * p.d;
-      if (MODE == kGateUp) {
-        N = Hg;
-        K = p.d;
-        Bp[0] = g < p.E ? (const uint16_t*)p.w_gate + (size_t)g * wsz : (const uint16_t*)p.ws_gate;
-        Bp[1] = g < p.E ? (const uint16_t*)p.w_up + (size_t)g * wsz : (const uint16_t*)p.ws_up;
-      } else {
-        N = p.d;
-        K = Hg;
-        Bp[0] = g < p.E ? (const uint16_t*)p.w_down + (size_t)g * wsz : (const uint16_t*)p.ws_down;
-      }
+      gr0 = 0;
+      nrows = p.T;
+      Hg = p.Hs;
+    }
+    const int mtiles = (nrows + G::BM - 1) / G::BM;
+    const int local = t - ga.sched[c.g];
+    nt = local / mtiles;
+    mt = local % mtiles;
+    const size_t wsz = (size_t)p.H * p.d;
+    if (MODE == kGateUp) {
+      c.N = Hg;
+      c.K = p.d;
+      Bp[0] = c.g < p.E ? (const uint16_t*)p.w_gate + (size_t)c.g * wsz : (const uint16_t*)p.ws_gate;
+      Bp[1] = c.g < p.E ? (const uint16_t*)p.w_up + (size_t)c.g * wsz : (const uint16_t*)p.ws_up;
+    } else {
+      c.N = p.d;
+      c.K = Hg;
+      Bp[0] = c.g < p.E ? (const uint16_t*)p.w_down + (size_t)c.g * wsz : (const uint16_t*)p.ws_down;
     }
   }
-  const int m0 = mt * BM, n0 = nt * G::BN;
+  const int m0 = mt * G::BM;
+  c.rows = nrows - m0 < G::BM ? nrows - m0 : G::BM;
+  c.r0 = gr0 + m0;
+  c.n0 = nt * G::BN;
+  c.nk = (c.K + BK - 1) / BK;
 
-  // ---- per-lane global sources -----------------------------------------------------------------
-  // A slice holds BM*4 chunks of A and NB*BN*4 chunks of B (4 chunks of 16 bytes per 32-wide row).
-  // Wave w fills chunk positions [w*BM*4/8, (w+1)*BM*4/8) of A and the matching share of the stacked
-  // B tiles, 64 consecutive positions per instruction (lane l -> position base + l). Position p
-  // holds row p/4, physical chunk p%4, i.e. logical chunk swz_chunk(row, p%4): the lane loads that
-  // logical chunk of that row.
+  // ---- this wave's loads: slots [first, first + L) of the slice's INSTR 1 KB loads -------------
+  // Slot s < A_INSTR: A rows [16 s, 16 s + 16), lane l -> row 16 s + l/4, physical chunk l%4 (the
+  // logical chunk swz_chunk(row, l%4) of that row). Slot s >= A_INSTR: B block q = s - A_INSTR;
+  // fragment-tiled: one contiguous 16 x 32 block of weight band n0/16 + q % (BN/16) of matrix
+  // q / (BN/16); row-major: stacked B rows [16 q, 16 q + 16) like A. Slot s lands at LDS byte s * 1024
+  // of the slice (A rows first, then the stacked B tiles).
+  const bool hi_wave = wv < G::N_HI;
+  c.first = hi_wave ? wv * G::L_HI : G::N_HI * G::L_HI + (wv - G::N_HI) * G::L_LO;
+  const int nload = hi_wave ? G::L_HI : G::L_LO;
   const int phys = lane & 3;
-  const uint16_t* a_src[G::A_LOADS];
-  const uint16_t* b_src[G::B_LOADS];
-  int a_kc[G::A_LOADS], b_kc[G::B_LOADS];     // element offset of the lane's chunk inside a K slice
 #pragma unroll
-  for (int i = 0; i < G::A_LOADS; ++i) {
-    const int row = wv * (BM / kWaves) + i * 16 + (lane >> 2);
-    a_kc[i] = swz_chunk(row, phys) * 8;
-    int rr = m0 + row;
-    rr = rr < nrows ? rr : (nrows > 0 ? nrows - 1 : 0);  // rows past the bucket: any valid row, never stored
-    long long src;
-    if (MODE == kRouter) {
-      src = rr;
-      a_src[i] = (const uint16_t*)ga.x + (size_t)src * K;
-    } else if (MODE == kGateUp) {
-      if (g < p.E) {
-        src = p.perm_src ? (long long)(p.perm_src[r0 + rr] / p.k) : r0 + rr;
-        const long long lim = p.perm_src ? (long long)p.T : p.rows;
-        src = src < 0 ? 0 : (src >= lim ? lim - 1 : src);
-      } else {
-        src = rr;
-      }
-      a_src[i] = (const uint16_t*)p.x + (size_t)src * K;
-    } else {
-      const uint16_t* hid = (const uint16_t*)p.hid + (g < p.E ? 0 : (size_t)p.rows * p.H);
-      a_src[i] = hid + (size_t)(r0 + rr) * K;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < G::B_LOADS; ++i) {
-    if (LAYOUT == kFrag16) {
-      // one 16 x 32 block (1 KB, contiguous in the packed weight) per instruction: block q of the
-      // stacked B tiles is band n0/16 + q % (BN/16) of matrix q / (BN/16)
-      const int q = wv * G::B_LOADS + i;
-      const int b = q / (G::BN / 16);
-      int band = n0 / 16 + q % (G::BN / 16);
-      band = band < N / 16 ? band : N / 16 - 1;  // bands past N: any valid band, never stored
-      b_kc[i] = 0;
-      b_src[i] = Bp[b] + (size_t)band * (K / 32) * 512 + lane * 8;
-    } else {
-      const int row = wv * (G::NB * G::BN / kWaves) + i * 16 + (lane >> 2);   // stacked rows of the B tiles
-      b_kc[i] = swz_chunk(row, phys) * 8;
-      const int b = row / G::BN;
-      int n = n0 + (row % G::BN);
-      n = n < N ? n : N - 1;                     // rows past N: any valid row, never stored
-      b_src[i] = Bp[b] + (size_t)n * K;
-    }
-  }
-
-  const int nk = (K + BK - 1) / BK;  // K slices
-  typedef __attribute__((address_space(3))) void lds_t;
-  // LDS byte offsets (wave-uniform) of this wave's instruction i inside a slice
-  auto a_dst = [&](int i) { return (wv * (BM / kWaves) + i * 16) * kRowBytes; };
-  auto b_dst = [&](int i) {
-    return LAYOUT == kFrag16 ? G::A_BYTES + (wv * G::B_LOADS + i) * 1024
-                             : G::A_BYTES + (wv * (G::NB * G::BN / kWaves) + i * 16) * kRowBytes;
-  };
-  // Loads j in [J0, J1) of slice kt (A loads first, then B loads) into ring buffer `buf`. A slice
-  // index past the end is clamped to the last slice: such loads fill a buffer that is never read
-  // again, which keeps the number of loads per slice fixed for the vmcnt arithmetic below.
-  auto issue = [&](int kt, int buf, int j0, int j1) {
-    const int kc = kt < nk ? kt : nk - 1;
-    const int k0 = kc * BK;
-#pragma unroll
-    for (int i = 0; i < G::A_LOADS; ++i) {
-      if (i < j0 || i >= j1) continue;
-      const int k = k0 + a_kc[i];
-      const uint16_t* src = a_src[i] + (k < K ? k : 0);    // out-of-range chunks are zeroed after landing
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_t*)(smem[buf] + a_dst(i)), 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < G::B_LOADS; ++i) {
-      if (G::A_LOADS + i < j0 || G::A_LOADS + i >= j1) continue;
-      const uint16_t* src;
-      if (LAYOUT == kFrag16) {
-        src = b_src[i] + (size_t)kc * 512;  // K is a multiple of 32 in this layout: no tail
-      } else {
-        const int k = k0 + b_kc[i];
-        src = b_src[i] + (k < K ? k : 0);
-      }
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_t*)(smem[buf] + b_dst(i)), 16, 0, 0);
-    }
-  };
-  // chunks past K in the last slice: write zeros over what the loads brought in
-  auto zero_tail = [&](int kt, int buf) {
-    const int k0 = kt * BK;
-    const u32x4_t zero = {0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < G::A_LOADS; ++i)
-      if (k0 + a_kc[i] >= K) *(u32x4_t*)(smem[buf] + a_dst(i) + lane * 16) = zero;
-    if (LAYOUT != kFrag16) {
-#pragma unroll
-      for (int i = 0; i < G::B_LOADS; ++i)
-        if (k0 + b_kc[i] >= K) *(u32x4_t*)(smem[buf] + b_dst(i) + lane * 16) = zero;
-    }
-  };
-
-  f32x16_t acc[G::NB][G::MBLK][G::NBLK];
-#pragma unroll
-  for (int b = 0; b < G::NB; ++b)
-#pragma unroll
-    for (int mb = 0; mb < G::MBLK; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < G::NBLK; ++nb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[b][mb][nb][e] = 0.f;
-
-  const int fr = lane & 31, fh = lane >> 5;   // fragment row / k-half of this lane
-  const int wm = wv / kWavesN, wn = wv % kWavesN;
-  constexpr int kMfmas = G::NB * G::NBLK * G::MBLK;          // per K step
-  constexpr int kReads = G::MBLK + G::NB * G::NBLK;          // per K step
-
-  // Ring protocol (S = kStages). The loads of slice s go to buffer s % S and are issued in two
-  // parts spread over the MFMAs: part 1 (loads [0, kSplit)) during step 1 of slice s-S, part 2
-  // (the rest) during step 0 of slice s-S+1, both after the barrier that ends every wave's reads
-  // of slice s-S, the previous tenant of the buffer. Spreading them keeps the vector-memory issue
-  // queue from stalling all waves at once right after the barrier. Before step 1 of slice kt a
-  // wave waits for its loads of slice kt+1: slices kt+2 .. kt+S-1 have been issued in full by
-  // then and loads complete in issue order, so vmcnt((S-2) * LOADS) leaves exactly those
-  // outstanding. The barrier that follows makes every wave's part of slice kt+1 visible.
-  // Slices past the end are clamped copies of the last one (see issue); in the last step the
-  // buffer of slice kt+1 (free: its previous tenant was slice kt+1-S) takes them, since the
-  // current buffer may still be read by waves that are behind and no barrier follows.
-  constexpr int S = kStages;
-  static_assert(S >= 3, "the issue schedule below needs a ring of at least 3 slices");
-  constexpr int kSplit = (G::LOADS + 1) / 2;
-  constexpr int kAhead = (S - 2) * G::LOADS;   // loads allowed in flight when slice kt+1 must land
-  static_assert(kAhead + kSplit < 64, "vmcnt holds 6 bits");
-  auto arrive = [&](int kt) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAhead) : "memory");
-    if (kt == nk - 1 && (K % BK)) zero_tail(kt, kt % S);  // its loads have all landed here
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
-
-  static_assert(BK / 16 == 2, "the loop below is written for two K steps per slice");
-  u32x4_t fa0[G::MBLK], fb0[G::NB][G::NBLK], fa1[G::MBLK], fb1[G::NB][G::NBLK];
-#pragma unroll
-  for (int i = 0; i < S - 1; ++i) issue(i, i, 0, G::LOADS);
-  issue(S - 1, S - 1, 0, kSplit);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAhead + kSplit) : "memory");
-  if (nk == 1 && (K % BK)) zero_tail(0, 0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  load_frags<G, LAYOUT>(fa0, fb0, smem[0], smem[0] + G::A_BYTES, wm, wn, fr, fh);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt % S;
-    // step 0 of slice kt: multiply fragments 0 while reading step 1 into fragments 1 and issuing
-    // part 2 of slice kt+S-1
-    mma_step<G>(acc, fa0, fb0);
-    load_frags<G, LAYOUT>(fa1, fb1, smem[buf], smem[buf] + G::A_BYTES, wm, wn, fr, 2 + fh);
-    issue(kt + S - 1, (kt + S - 1) % S, kSplit, G::LOADS);
-    interleave_mfma_lds_vmem<kMfmas, kReads, G::LOADS - kSplit>();
-    // step 1 of slice kt: multiply fragments 1 while reading step 0 of slice kt+1 into fragments 0
-    // and issuing part 1 of slice kt+S into this slice's buffer (after the last slice the reads
-    // re-read the current buffer and are never used)
-    if (kt + 1 < nk) arrive(kt + 1);
-    const int nbuf = kt + 1 < nk ? (kt + 1) % S : buf;
-    const int lbuf = kt + 1 < nk ? buf : (kt + 1) % S;
-    mma_step<G>(acc, fa1, fb1);
-    load_frags<G, LAYOUT>(fa0, fb0, smem[nbuf], smem[nbuf] + G::A_BYTES, wm, wn, fr, fh);
-    issue(kt + S, lbuf, 0, kSplit);
-    interleave_mfma_lds_vmem<kMfmas, kReads, kSplit>();
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still write LDS when the block exits
-
-  // ---- epilogue: lane holds column n = fr of each 32x32 block, rows (e/4)*8 + fh*4 + e%4 --------
-#pragma unroll
-  for (int mb = 0; mb < G::MBLK; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < G::NBLK; ++nb) {
-      const int n = n0 + wn * G::WN + nb * 32 + fr;
-      if (n >= N) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * G::WM + mb * 32 + (e >> 2) * 8 + fh * 4 + (e & 3);
-        if (row >= nrows) continue;
-        if (MODE == kGateUp) {
-          const float gv = acc[0][mb][nb][e], uv = acc[1][mb][nb][e];
-          uint16_t* hid = (uint16_t*)p.hid + (g < p.E ? 0 : (size_t)p.rows * p.H);
-          hid[(size_t)(r0 + row) * N + n] = (uint16_t)f32_to_bf16(silu(gv) * uv);
-        } else if (MODE == kDown) {
-          uint16_t* y = (uint16_t*)p.y + (g < p.E ? 0 : (size_t)p.rows * p.d);
-          y[(size_t)(r0 + row) * N + n] = (uint16_t)f32_to_bf16(acc[0][mb][nb][e]);
+  for (int i = 0; i < G::L_HI; ++i) {
+    const int s = c.first + (i < nload ? i : 0);
+    if (s < G::A_INSTR) {
+      const int row = s * 16 + (lane >> 2);
+      c.kc[i] = swz_chunk(row, phys) * 8;
+      c.stride[i] = BK;
+      int rr = m0 + row;
+      rr = rr < nrows ? rr : (nrows > 0 ? nrows - 1 : 0);  // rows past the tile: any valid row, never stored
+      long long src;
+      if (MODE == kRouter) {
+        c.src[i] = (const uint16_t*)ga.x + (size_t)rr * c.K;
+      } else if (MODE == kGateUp) {
+        if (c.g < p.E) {
+          src = p.perm_src ? (long long)(p.perm_src[gr0 + rr] / p.k) : gr0 + rr;
+          const long long lim = p.perm_src ? (long long)p.T : p.rows;
+          src = src < 0 ? 0 : (src >= lim ? lim - 1 : src);
         } else {
-          ga.logits[(size_t)row * N + n] = acc[0][mb][nb][e] + (ga.bias ? ga.bias[n] : 0.f);
+          src = rr;
         }
+        c.src[i] = (const uint16_t*)p.x + (size_t)src * c.K;
+      } else {
+        const uint16_t* hid = (const uint16_t*)p.hid + (c.g < p.E ? 0 : (size_t)p.rows * p.H);
+        c.src[i] = hid + (size_t)(gr0 + rr) * c.K;
+      }
+    } else {
+      const int q = s - G::A_INSTR;
+      if (LAYOUT == kFrag16) {
+        const int b = q / (G::BN / 16);
+        int band = c.n0 / 16 + q % (G::BN / 16);
+        band = band < c.N / 16 ? band : c.N / 16 - 1;  // bands past N: any valid band, never stored
+        c.kc[i] = 0;
+        c.stride[i] = 512;                              // K is a multiple of 32 in this layout: no tail
+        c.src[i] = Bp[b] + (size_t)band * (c.K / 32) * 512 + lane * 8;
+      } else {
+        const int srow = q * 16 + (lane >> 2);          // stacked row of the B tiles
+        c.kc[i] = swz_chunk(srow, phys) * 8;
+        c.stride[i] = BK;
+        const int b = srow / G::BN;
+        int n = c.n0 + (srow % G::BN);
+        n = n < c.N ? n : c.N - 1;                      // rows past N: any valid row, never stored
+        c.src[i] = Bp[b] + (size_t)n * c.K;
       }
     }
+  }
+
+  // ---- active row blocks of this wave: blocks wm, wm + 2, ... below ceil(rows / 32) --------------
+  const int nbt = (c.rows + 31) / 32;
+  const int wm = wv / kWavesN;
+  int na = nbt > wm ? (nbt - wm + 1) / 2 : 0;
+  na = na < G::MBW ? na : G::MBW;
+  if (hi_wave)
+    tile_body_na<MODE, LAYOUT, G::L_HI>(ga, c, smem, wv, na);
+  else if constexpr (G::L_LO != G::L_HI && G::N_HI < kWaves)
+    tile_body_na<MODE, LAYOUT, G::L_LO>(ga, c, smem, wv, na);
 }
 
 // Tiles are numbered expert by expert, N-tile by N-tile, with the M-tiles of one (expert, N-tile)
@@ -475,16 +526,16 @@ namespace {
 int round8(long long v) { return (int)((v + kXcds - 1) / kXcds * kXcds); }
 
 // Workgroups of a launch: one per tile (rounded to whole XCD sets). The hardware then starts the
-// tiles of each XCD in order as CUs free up, so the M-tiles that share a weight tile start
-// together and stream it through L2 once. A persistent launch (one workgroup per CU, each walking
-// its XCD's range) measured the same time but let those M-tiles drift apart: 29.6 GB fetched from
-// the fabric per gate/up launch at T=8192 instead of 24 GB.
+// tiles of each XCD in order as CUs free up, so the tiles that share activation rows start
+// together and stream them through L2 once.
 int gemm_grid(long long tiles_upper) { return round8(tiles_upper); }
 }  // namespace
 
 long long gemm_tiles_upper(const FfnGroups& p, int mode) {
-  const long long mt_routed = p.rows / BM + p.E;  // each group adds at most one partial tile
-  const long long mt_shared = p.Hs > 0 ? (p.T + BM - 1) / BM : 0;
+  constexpr int bm = Geo<kGateUp>::BM;
+  static_assert(Geo<kGateUp>::BM == Geo<kDown>::BM, "one M-tiling for both passes");
+  const long long mt_routed = p.rows / bm + p.E;  // each group adds at most one partial tile
+  const long long mt_shared = p.Hs > 0 ? (p.T + bm - 1) / bm : 0;
   if (mode == kGateUp) {
     const int bn = Geo<kGateUp>::BN;
     return mt_routed * ((p.H + bn - 1) / bn) + mt_shared * ((p.Hs + bn - 1) / bn);
@@ -534,7 +585,8 @@ hipError_t launch_router_gemm(const void* x, const void* w, const float* bias, f
   a.T = T;
   a.E = E;
   a.d = d;
-  const long long tiles = (long long)((T + BM - 1) / BM) * ((E + Geo<kRouter>::BN - 1) / Geo<kRouter>::BN);
+  using G = Geo<kRouter>;
+  const long long tiles = (long long)((T + G::BM - 1) / G::BM) * ((E + G::BN - 1) / G::BN);
   hipLaunchKernelGGL((grouped_gemm_kernel<kRouter, kRowMajor>), dim3(gemm_grid(tiles)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
