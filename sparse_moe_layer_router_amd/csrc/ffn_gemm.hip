@@ -49,8 +49,8 @@ constexpr int kRowBytes = BK * 2;  // one tile row in LDS: 64 bytes = 4 chunks o
 enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2 };
 
 template <int MODE> struct Geo {
-  static constexpr int MBW = MODE == kRouter ? 2 : 5;              // 32-row blocks per wave
-  static constexpr int BM = MBW * kWavesM * 32;                    // tile rows: 320 (router 128)
+  static constexpr int MBW = MODE == kRouter ? 1 : 5;              // 32-row blocks per wave
+  static constexpr int BM = MBW * kWavesM * 32;                    // tile rows: 320 (router 64)
   static constexpr int NB = MODE == kGateUp ? 2 : 1;               // B matrices per tile
   static constexpr int BN = MODE == kGateUp ? 128 : 256;           // rows of each B tile
   static constexpr int BROWS = NB * BN;                            // stacked B rows (256)
@@ -80,8 +80,13 @@ __device__ __forceinline__ int b_row(int j, int wn, int fr) {
 }
 
 // A fragment i (rows (wm + 2 i) * 32 + fr) and B fragment j of one 16-wide K step, chunk column ch.
+// The down pass holds A (the hidden activations) as packed 16 x 32 blocks, one per 16-row band;
+// gate/up and the router hold gathered rows.
+template <int MODE>
 __device__ __forceinline__ u32x4_t read_a(const uint8_t* sa, int i, int wm, int fr, int ch) {
-  return *(const u32x4_t*)(sa + swz((wm + 2 * i) * 32 + fr, ch));
+  const int r = (wm + 2 * i) * 32 + fr;
+  if (MODE == kDown) return *(const u32x4_t*)(sa + (r / 16) * 1024 + ((r & 15) + 16 * ch) * 16);
+  return *(const u32x4_t*)(sa + swz(r, ch));
 }
 template <int MODE, int LAYOUT>
 __device__ __forceinline__ u32x4_t read_b(const uint8_t* sb, int j, int wn, int fr, int ch) {
@@ -107,7 +112,7 @@ __device__ __forceinline__ void mma_and_read(f32x16_t (&acc)[NA > 0 ? NA : 1][2]
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     acc[i][1] = mfma32x32x16(fa[i], fb[1], acc[i][1]);
-    fa[i] = read_a(sa, i, wm, fr, ch);
+    fa[i] = read_a<MODE>(sa, i, wm, fr, ch);
   }
   if (NA > 0) fb[1] = read_b<MODE, LAYOUT>(sb, 1, wn, fr, ch);
 }
@@ -118,7 +123,7 @@ __device__ __forceinline__ void read_all(u32x4_t (&fa)[NA > 0 ? NA : 1], u32x4_t
                                          const uint8_t* sb, int wm, int wn, int fr, int ch) {
   if (NA == 0) return;
 #pragma unroll
-  for (int i = 0; i < NA; ++i) fa[i] = read_a(sa, i, wm, fr, ch);
+  for (int i = 0; i < NA; ++i) fa[i] = read_a<MODE>(sa, i, wm, fr, ch);
   fb[0] = read_b<MODE, LAYOUT>(sb, 0, wn, fr, ch);
   fb[1] = read_b<MODE, LAYOUT>(sb, 1, wn, fr, ch);
 }
@@ -147,56 +152,76 @@ __device__ __forceinline__ void pin_step() {
   }
 }
 
+// One zero kilobyte: the source of packed A blocks past the end of a group.
+__device__ __attribute__((aligned(16))) const uint32_t g_zero_block[256] = {0};
+
 template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 }  // namespace
 
 // ------------------------------------------------------------------------------- schedule
+// Rows of group g (routed groups clamp their offsets into [0, rows]; the shared group has T).
+__device__ __forceinline__ long long group_rows(const FfnGroups& p, int g, long long* first) {
+  if (g < p.E) {
+    long long lo = p.offsets[g], hi = p.offsets[g + 1];
+    lo = lo < 0 ? 0 : (lo > p.rows ? p.rows : lo);
+    hi = hi < lo ? lo : (hi > p.rows ? p.rows : hi);
+    if (first) *first = lo;
+    return hi - lo;
+  }
+  if (first) *first = 0;
+  return p.T;
+}
+
 // One block: for every group, m-tiles = ceil(rows / BM); tiles = m-tiles * n-tiles of that group.
-// Writes exclusive prefix sums for the gate/up pass (sched_gu) and the down pass (sched_dn),
-// 1024 groups per round with the running total carried between rounds.
+// Writes exclusive prefix sums for the gate/up pass (sched_gu) and the down pass (sched_dn), and
+// the first 16-row band of every routed group in the packed activations (pband: ceil(rows / 16)
+// bands per group), 1024 groups per round with the running totals carried between rounds.
 __global__ void __launch_bounds__(1024)
-gemm_schedule_kernel(const FfnGroups p, int32_t* __restrict__ sched_gu, int32_t* __restrict__ sched_dn) {
-  __shared__ int32_t wtot_gu[16], wtot_dn[16];
+gemm_schedule_kernel(const FfnGroups p, int32_t* __restrict__ sched_gu, int32_t* __restrict__ sched_dn,
+                     int32_t* __restrict__ pband) {
+  __shared__ int32_t wtot[3][16];
   const int ngroups = p.E + (p.Hs > 0 ? 1 : 0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int32_t carry_a = 0, carry_b = 0;
+  int32_t carry[3] = {0, 0, 0};
   for (int base = 0; base < ngroups; base += 1024) {
     const int g = base + (int)threadIdx.x;
-    int32_t a = 0, b = 0;
+    int32_t v[3] = {0, 0, 0};
     if (g < ngroups) {
-      long long n;
-      int Hg;
-      if (g < p.E) {
-        long long lo = p.offsets[g], hi = p.offsets[g + 1];
-        lo = lo < 0 ? 0 : (lo > p.rows ? p.rows : lo);
-        hi = hi < lo ? lo : (hi > p.rows ? p.rows : hi);
-        n = hi - lo;
-        Hg = p.H;
-      } else {
-        n = p.T;
-        Hg = p.Hs;
-      }
-      a = (int)((n + Geo<kGateUp>::BM - 1) / Geo<kGateUp>::BM) * ((Hg + Geo<kGateUp>::BN - 1) / Geo<kGateUp>::BN);
-      b = (int)((n + Geo<kDown>::BM - 1) / Geo<kDown>::BM) * ((p.d + Geo<kDown>::BN - 1) / Geo<kDown>::BN);
+      const long long n = group_rows(p, g, nullptr);
+      const int Hg = g < p.E ? p.H : p.Hs;
+      v[0] = (int)((n + Geo<kGateUp>::BM - 1) / Geo<kGateUp>::BM) * ((Hg + Geo<kGateUp>::BN - 1) / Geo<kGateUp>::BN);
+      v[1] = (int)((n + Geo<kDown>::BM - 1) / Geo<kDown>::BM) * ((p.d + Geo<kDown>::BN - 1) / Geo<kDown>::BN);
+      v[2] = g < p.E ? (int)((n + 15) / 16) : 0;
     }
-    int32_t ia = a, ib = b;
+    int32_t inc[3] = {v[0], v[1], v[2]};
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int32_t oa = __shfl_up(ia, off, 64), ob = __shfl_up(ib, off, 64);
-      if (lane >= off) { ia += oa; ib += ob; }
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const int32_t o = __shfl_up(inc[q], off, 64);
+        if (lane >= off) inc[q] += o;
+      }
     }
-    if (lane == 63) { wtot_gu[wave] = ia; wtot_dn[wave] = ib; }
+    if (lane == 63)
+      for (int q = 0; q < 3; ++q) wtot[q][wave] = inc[q];
     __syncthreads();
-    int32_t ba = carry_a, bb = carry_b;
-    for (int w = 0; w < wave; ++w) { ba += wtot_gu[w]; bb += wtot_dn[w]; }
+    int32_t ex[3] = {carry[0], carry[1], carry[2]};
+    for (int w = 0; w < wave; ++w)
+      for (int q = 0; q < 3; ++q) ex[q] += wtot[q][w];
     if (g < ngroups) {
-      sched_gu[g] = ba + ia - a;
-      sched_dn[g] = bb + ib - b;
-      if (g == ngroups - 1) { sched_gu[ngroups] = ba + ia; sched_dn[ngroups] = bb + ib; }
+      sched_gu[g] = ex[0] + inc[0] - v[0];
+      sched_dn[g] = ex[1] + inc[1] - v[1];
+      pband[g] = ex[2] + inc[2] - v[2];
+      if (g == ngroups - 1) {
+        sched_gu[ngroups] = ex[0] + inc[0];
+        sched_dn[ngroups] = ex[1] + inc[1];
+        pband[ngroups] = ex[2] + inc[2];
+      }
     }
-    for (int w = 0; w < 16; ++w) { carry_a += wtot_gu[w]; carry_b += wtot_dn[w]; }
-    __syncthreads();  // wtot_* are rewritten in the next round
+    for (int w = 0; w < 16; ++w)
+      for (int q = 0; q < 3; ++q) carry[q] += wtot[q][w];
+    __syncthreads();  // wtot is rewritten in the next round
   }
 }
 
@@ -204,6 +229,7 @@ gemm_schedule_kernel(const FfnGroups p, int32_t* __restrict__ sched_gu, int32_t*
 struct GemmArgs {
   FfnGroups p;
   const int32_t* sched;   // [ngroups + 1] (kGateUp / kDown); unused for the router
+  const int32_t* pband;   // [E + 1] first packed band of every routed group (kGateUp / kDown)
   // router mode
   const void* x;          // [T, d]
   const void* w;          // [E, d]
@@ -217,6 +243,7 @@ template <int MODE>
 struct TileCtx {
   int g;                  // group (expert; E = shared expert)
   long long r0;           // first row of the tile in its group's row space (group row base + m0)
+  long long pr0;          // first packed row of the tile (expert passes: group band * 16 + m0)
   int rows;               // valid rows in the tile (1..BM)
   int n0, N, K, nk;       // first output column, output columns, reduction length, K slices
   int first;              // first load slot of this wave
@@ -331,20 +358,24 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   asm volatile("" : "+v"(elane));
   const int efr = elane & 31, efh = elane >> 5;
   const FfnGroups& p = ga.p;
+  // gate/up: the hidden activation goes to the packed layout the down pass reads (columns padded
+  // to a multiple of 32 with zeros; the shared group's region follows the routed one)
+  const int np = (int)gemm_pad32(c.N);
+  uint16_t* hid = (uint16_t*)p.hid + (c.g < p.E ? 0 : (size_t)p.rbands * 16 * gemm_pad32(p.H));
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
 #pragma unroll
     for (int j = 0; j < (MODE == kGateUp ? 1 : 2); ++j) {
       const int n = c.n0 + (MODE == kGateUp ? wn * 32 : wn * 64 + j * 32) + efr;
-      if (n >= c.N) continue;
+      if (n >= (MODE == kGateUp ? np : c.N)) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = (wm + 2 * i) * 32 + (e >> 2) * 8 + efh * 4 + (e & 3);
         if (row >= c.rows) continue;
         if (MODE == kGateUp) {
           const float gv = acc[i][0][e], uv = acc[i][1][e];
-          uint16_t* hid = (uint16_t*)p.hid + (c.g < p.E ? 0 : (size_t)p.rows * p.H);
-          hid[(size_t)(c.r0 + row) * c.N + n] = (uint16_t)f32_to_bf16(silu(gv) * uv);
+          hid[frag16_offset((size_t)(c.pr0 + row), (size_t)n, (size_t)np)] =
+              n < c.N ? (uint16_t)f32_to_bf16(silu(gv) * uv) : (uint16_t)0;
         } else if (MODE == kDown) {
           uint16_t* y = (uint16_t*)p.y + (c.g < p.E ? 0 : (size_t)p.rows * p.d);
           y[(size_t)(c.r0 + row) * c.N + n] = (uint16_t)f32_to_bf16(acc[i][j][e]);
@@ -395,12 +426,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
     Bp[0] = (const uint16_t*)ga.w;
   } else {
     const int ngroups = p.E + (p.Hs > 0 ? 1 : 0);
-    int lo = 0, hi = ngroups;  // last group with sched[g] <= t
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (ga.sched[mid] <= t) lo = mid; else hi = mid;
+    // The group of tile t is the last g with sched[g] <= t, i.e. (sched is non-decreasing and
+    // sched[0] = 0) the number of g in [0, ngroups) with sched[g] <= t, minus one: the wave counts
+    // them with independent loads (one memory latency, not one per bisection step).
+    int cnt = 0;
+    for (int b = 0; b < ngroups; b += 256) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int gi = b + q * 64 + lane;
+        cnt += (gi < ngroups && ga.sched[gi] <= t) ? 1 : 0;
+      }
     }
-    c.g = lo;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    c.g = __builtin_amdgcn_readfirstlane(cnt) - 1;
     int Hg;
     if (c.g < p.E) {
       long long a = p.offsets[c.g], b = p.offsets[c.g + 1];
@@ -435,6 +474,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
   c.r0 = gr0 + m0;
   c.n0 = nt * G::BN;
   c.nk = (c.K + BK - 1) / BK;
+  // expert passes: the hidden activations of the tile are packed bands band0 + m0/16 + s of its
+  // group's region (written by gate/up, read by down)
+  const long long band0 = MODE == kRouter ? 0 : (c.g < p.E ? (long long)ga.pband[c.g] : 0);
+  const int gbands = (nrows + 15) / 16;
+  c.pr0 = band0 * 16 + m0;
+  const uint16_t* abase =
+      MODE == kDown ? (const uint16_t*)p.hid + (c.g < p.E ? 0 : (size_t)p.rbands * 16 * gemm_pad32(p.H)) : nullptr;
 
   // ---- this wave's loads: slots [first, first + L) of the slice's INSTR 1 KB loads -------------
   // Slot s < A_INSTR: A rows [16 s, 16 s + 16), lane l -> row 16 s + l/4, physical chunk l%4 (the
@@ -449,7 +495,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
 #pragma unroll
   for (int i = 0; i < G::L_HI; ++i) {
     const int s = c.first + (i < nload ? i : 0);
-    if (s < G::A_INSTR) {
+    if (s < G::A_INSTR && MODE != kDown) {
       const int row = s * 16 + (lane >> 2);
       c.kc[i] = swz_chunk(row, phys) * 8;
       c.stride[i] = BK;
@@ -457,19 +503,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
       rr = rr < nrows ? rr : (nrows > 0 ? nrows - 1 : 0);  // rows past the tile: any valid row, never stored
       long long src;
       if (MODE == kRouter) {
-        c.src[i] = (const uint16_t*)ga.x + (size_t)rr * c.K;
-      } else if (MODE == kGateUp) {
-        if (c.g < p.E) {
-          src = p.perm_src ? (long long)(p.perm_src[gr0 + rr] / p.k) : gr0 + rr;
-          const long long lim = p.perm_src ? (long long)p.T : p.rows;
-          src = src < 0 ? 0 : (src >= lim ? lim - 1 : src);
-        } else {
-          src = rr;
-        }
-        c.src[i] = (const uint16_t*)p.x + (size_t)src * c.K;
+        src = rr;
+      } else if (c.g < p.E) {
+        src = p.perm_src ? (long long)(p.perm_src[gr0 + rr] / p.k) : gr0 + rr;
+        const long long lim = p.perm_src ? (long long)p.T : p.rows;
+        src = src < 0 ? 0 : (src >= lim ? lim - 1 : src);
       } else {
-        const uint16_t* hid = (const uint16_t*)p.hid + (c.g < p.E ? 0 : (size_t)p.rows * p.H);
-        c.src[i] = hid + (size_t)(gr0 + rr) * c.K;
+        src = rr;
+      }
+      c.src[i] = (const uint16_t*)(MODE == kRouter ? ga.x : p.x) + (size_t)src * c.K;
+    } else if (s < G::A_INSTR) {
+      // packed A: one contiguous 1 KB block per slice; bands past the group read zeros
+      const int bl = m0 / 16 + s;
+      c.kc[i] = 0;
+      if (bl < gbands) {
+        c.stride[i] = 512;
+        c.src[i] = abase + (size_t)(band0 + bl) * (c.nk * 512) + lane * 8;
+      } else {
+        c.stride[i] = 0;
+        c.src[i] = (const uint16_t*)g_zero_block + lane * 8;
       }
     } else {
       const int q = s - G::A_INSTR;
@@ -544,17 +596,21 @@ long long gemm_tiles_upper(const FfnGroups& p, int mode) {
   return (mt_routed + mt_shared) * ((p.d + bn - 1) / bn);
 }
 
-size_t gemm_schedule_ints(int E) { return 2 * (size_t)(E + 2); }
+// [sched_gu | sched_dn | pband], E + 2 ints each
+size_t gemm_schedule_ints(int E) { return 3 * (size_t)(E + 2); }
 
 hipError_t launch_gemm_schedule(const FfnGroups& p, int32_t* sched, hipStream_t stream) {
-  hipLaunchKernelGGL(gemm_schedule_kernel, dim3(1), dim3(1024), 0, stream, p, sched, sched + p.E + 2);
+  hipLaunchKernelGGL(gemm_schedule_kernel, dim3(1), dim3(1024), 0, stream, p, sched, sched + p.E + 2,
+                     sched + 2 * (p.E + 2));
   return hipGetLastError();
 }
+
 
 hipError_t launch_gemm_gate_up(const FfnGroups& p, const int32_t* sched, hipStream_t stream) {
   GemmArgs a{};
   a.p = p;
   a.sched = sched;
+  a.pband = sched + 2 * (p.E + 2);
   const dim3 grid(gemm_grid(gemm_tiles_upper(p, kGateUp)));
   if (p.layout == kFrag16)
     hipLaunchKernelGGL((grouped_gemm_kernel<kGateUp, kFrag16>), grid, dim3(kThreads), 0, stream, a);
@@ -567,6 +623,7 @@ hipError_t launch_gemm_down(const FfnGroups& p, const int32_t* sched, hipStream_
   GemmArgs a{};
   a.p = p;
   a.sched = sched + p.E + 2;
+  a.pband = sched + 2 * (p.E + 2);
   const dim3 grid(gemm_grid(gemm_tiles_upper(p, kDown)));
   if (p.layout == kFrag16)
     hipLaunchKernelGGL((grouped_gemm_kernel<kDown, kFrag16>), grid, dim3(kThreads), 0, stream, a);

@@ -47,10 +47,23 @@ struct FfnGroups {
   const void* ws_up;           // [Hs, d]
   const void* ws_down;         // [d, Hs]
   // outputs
-  void* hid;                   // routed hidden [rows, H], then shared hidden [T, Hs] (dtype)
+  void* hid;                   // hidden activations (dtype): routed [rows, H], then shared [T, Hs]; on the
+                               // grouped-GEMM path in the packed layout described below instead
   void* y;                     // routed outputs [rows, d], then shared outputs [T, d] (dtype)
   float mean_rows_per_group;   // host-side regime hint (T*k / E)
+  long long rbands;            // grouped-GEMM path: routed band capacity of the packed hidden activations
 };
+
+// Grouped-GEMM path: the hidden activations are packed into 16-row x 32-column blocks
+// (frag16_offset order, columns padded to a multiple of 32 with zeros), the layout the down pass
+// loads as contiguous kilobytes. Every routed group starts on a 16-row band: group g owns bands
+// [pband[g], pband[g] + ceil(n_g / 16)) of the routed region, which holds `rbands` bands; the
+// shared group's T rows follow in a region of their own.
+__host__ __device__ inline long long gemm_pad32(long long v) { return (v + 31) / 32 * 32; }
+__host__ __device__ inline long long gemm_routed_bands(long long rows, int E) { return (rows + 15) / 16 + E; }
+__host__ __device__ inline long long gemm_hid_elems(long long rows, int E, int T, int H, int Hs) {
+  return gemm_routed_bands(rows, E) * 16 * gemm_pad32(H) + (Hs > 0 ? (long long)(T + 15) / 16 * 16 * gemm_pad32(Hs) : 0);
+}
 
 // Which kernels run the experts, chosen from shapes only (no device data):
 //   kPathF32    float32 layers: plain VALU kernels;
@@ -65,7 +78,8 @@ hipError_t launch_ffn_down_stream(const FfnGroups& g, hipStream_t stream);
 hipError_t launch_ffn_gate_up_f32(const FfnGroups& g, hipStream_t stream);
 hipError_t launch_ffn_down_f32(const FfnGroups& g, hipStream_t stream);
 
-// grouped GEMM: `sched` holds gemm_schedule_ints(E) int32 (tile prefix sums of both passes)
+// grouped GEMM: `sched` holds gemm_schedule_ints(E) int32 (tile prefix sums of both passes and the
+// routed groups' first bands of the packed hidden activations)
 size_t gemm_schedule_ints(int E);
 hipError_t launch_gemm_schedule(const FfnGroups& g, int32_t* sched, hipStream_t stream);
 hipError_t launch_gemm_gate_up(const FfnGroups& g, const int32_t* sched, hipStream_t stream);

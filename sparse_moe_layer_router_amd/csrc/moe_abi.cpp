@@ -36,7 +36,18 @@ Layout layout_of(const moe_shape& s) {
   L.inv_perm = take(rows * 4);
   L.tile_counts = take(moe::permute_scratch_bytes((long long)rows, (int)E));
   L.sched = take(moe::gemm_schedule_ints((int)E) * 4);
-  L.hid = take((rows * H + (Hs ? T * Hs : 0)) * es);
+  // the grouped-GEMM path keeps its hidden activations in the packed layout
+  moe::FfnGroups shape_only{};
+  shape_only.dtype = s.dtype;
+  shape_only.layout = s.weight_layout;
+  shape_only.mean_rows_per_group = (float)((double)s.T * s.top_k / s.n_experts);
+  const bool gemm = moe::ffn_path(shape_only) == moe::kPathGemm;
+  size_t hid_elems = rows * H + (Hs ? T * Hs : 0);
+  if (gemm) {
+    const size_t packed = (size_t)moe::gemm_hid_elems((long long)rows, (int)E, (int)T, (int)H, (int)Hs);
+    hid_elems = packed > hid_elems ? packed : hid_elems;
+  }
+  L.hid = take(hid_elems * es);
   L.y = take((rows + (Hs ? T : 0)) * d * es);
   L.total = off;
   return L;
@@ -169,13 +180,16 @@ moe::FfnGroups groups_for(const moe_shape& s, const void* x, const int32_t* perm
   g.hid = hid;
   g.y = y;
   g.mean_rows_per_group = (float)((double)s.T * s.top_k / s.n_experts);
+  g.rbands = moe::gemm_routed_bands(g.rows, g.E);
   return g;
 }
 
 moe_status ffn_impl(const moe::FfnGroups& g, int32_t* sched, const Events& ev, hipStream_t stream) {
   const moe::FfnPath path = moe::ffn_path(g);
   MOE_MARK(ev, MOE_STAGE_FFN_SCHEDULE, 0);
-  if (path == moe::kPathGemm) MOE_LAUNCH(moe::launch_gemm_schedule(g, sched, stream));
+  if (path == moe::kPathGemm) {
+    MOE_LAUNCH(moe::launch_gemm_schedule(g, sched, stream));
+  }
   MOE_MARK(ev, MOE_STAGE_FFN_SCHEDULE, 1);
   MOE_MARK(ev, MOE_STAGE_FFN_GATE_UP, 0);
   switch (path) {
