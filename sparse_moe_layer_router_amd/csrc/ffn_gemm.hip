@@ -106,12 +106,12 @@ __device__ __forceinline__ void mma_and_read(f32x16_t (&acc)[NA > 0 ? NA : 1][2]
                                              u32x4_t (&fb)[2], const uint8_t* sa, const uint8_t* sb, int wm,
                                              int wn, int fr, int ch, Loads&& loads) {
 #pragma unroll
-  for (int i = 0; i < NA; ++i) acc[i][0] = mfma32x32x16(fa[i], fb[0], acc[i][0]);
+  for (int i = 0; i < NA; ++i) acc[i][0] = mfma32x32x16(fb[0], fa[i], acc[i][0]);
   loads();
   if (NA > 0) fb[0] = read_b<MODE, LAYOUT>(sb, 0, wn, fr, ch);
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    acc[i][1] = mfma32x32x16(fa[i], fb[1], acc[i][1]);
+    acc[i][1] = mfma32x32x16(fb[1], fa[i], acc[i][1]);
     fa[i] = read_a<MODE>(sa, i, wm, fr, ch);
   }
   if (NA > 0) fb[1] = read_b<MODE, LAYOUT>(sb, 1, wn, fr, ch);
@@ -351,7 +351,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   }
   wait_vmcnt<0>();  // no load may still write LDS when the tile ends
 
-  // ---- epilogue: lane holds column fr of each 32x32 block, rows (e/4)*8 + fh*4 + e%4 ---------
+  // ---- epilogue ----------------------------------------------------------------------------------
+  // The MFMAs take the weights as their first operand, so each 32x32 block holds the transposed
+  // product: lane l has output row fr = l % 32 of the block and, for q = 0..3, the four
+  // consecutive output columns 8 q + 4 fh .. + 3 (e = 4 q .. 4 q + 3), one 8-byte store each.
   // The lane index is re-read through an opaque move so that no output address is computed
   // before the main loop (hoisted addresses would stay live in registers across it).
   int elane = lane;
@@ -362,25 +365,35 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   // to a multiple of 32 with zeros; the shared group's region follows the routed one)
   const int np = (int)gemm_pad32(c.N);
   uint16_t* hid = (uint16_t*)p.hid + (c.g < p.E ? 0 : (size_t)p.rbands * 16 * gemm_pad32(p.H));
+  uint16_t* y = (uint16_t*)p.y + (c.g < p.E ? 0 : (size_t)p.rows * p.d);
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
+    const int row = (wm + 2 * i) * 32 + efr;
+    if (row >= c.rows) continue;
 #pragma unroll
     for (int j = 0; j < (MODE == kGateUp ? 1 : 2); ++j) {
-      const int n = c.n0 + (MODE == kGateUp ? wn * 32 : wn * 64 + j * 32) + efr;
-      if (n >= (MODE == kGateUp ? np : c.N)) continue;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = (wm + 2 * i) * 32 + (e >> 2) * 8 + efh * 4 + (e & 3);
-        if (row >= c.rows) continue;
+      for (int q = 0; q < 4; ++q) {
+        const int n = c.n0 + (MODE == kGateUp ? wn * 32 : wn * 64 + j * 32) + q * 8 + efh * 4;  // 4 columns
         if (MODE == kGateUp) {
-          const float gv = acc[i][0][e], uv = acc[i][1][e];
-          hid[frag16_offset((size_t)(c.pr0 + row), (size_t)n, (size_t)np)] =
-              n < c.N ? (uint16_t)f32_to_bf16(silu(gv) * uv) : (uint16_t)0;
+          if (n >= np) continue;  // N, np and n are multiples of 4: the four columns are all in or all out
+          u32x2_t v = {0u, 0u};
+          if (n < c.N)
+            v = u32x2_t{pack_bf16x2(silu(acc[i][0][4 * q]) * acc[i][1][4 * q],
+                                    silu(acc[i][0][4 * q + 1]) * acc[i][1][4 * q + 1]),
+                        pack_bf16x2(silu(acc[i][0][4 * q + 2]) * acc[i][1][4 * q + 2],
+                                    silu(acc[i][0][4 * q + 3]) * acc[i][1][4 * q + 3])};
+          *(u32x2_t*)(hid + frag16_offset((size_t)(c.pr0 + row), (size_t)n, (size_t)np)) = v;
         } else if (MODE == kDown) {
-          uint16_t* y = (uint16_t*)p.y + (c.g < p.E ? 0 : (size_t)p.rows * p.d);
-          y[(size_t)(c.r0 + row) * c.N + n] = (uint16_t)f32_to_bf16(acc[i][j][e]);
+          if (n >= c.N) continue;
+          *(u32x2_t*)(y + (size_t)(c.r0 + row) * c.N + n) =
+              u32x2_t{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                      pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
         } else {
-          ga.logits[(size_t)(c.r0 + row) * c.N + n] = acc[i][j][e] + (ga.bias ? ga.bias[n] : 0.f);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (n + t < c.N)
+              ga.logits[(size_t)(c.r0 + row) * c.N + n + t] = acc[i][j][4 * q + t] + (ga.bias ? ga.bias[n + t] : 0.f);
         }
       }
     }
