@@ -366,6 +366,46 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   const int np = (int)gemm_pad32(c.N);
   uint16_t* hid = (uint16_t*)p.hid + (c.g < p.E ? 0 : (size_t)p.rbands * 16 * gemm_pad32(p.H));
   uint16_t* y = (uint16_t*)p.y + (c.g < p.E ? 0 : (size_t)p.rows * p.d);
+  if constexpr (MODE == kDown) {
+    // Output rows are 512-byte segments of y: stage each half of the tile (160 rows x 256
+    // columns, 80 KB) in LDS, then store it with 16-byte stores, a row per 32 lanes. In LDS a
+    // row's 16-byte chunk c sits at chunk c ^ (row % 32), so the 32 rows a store instruction of the
+    // accumulators touches fall in distinct banks.
+    static_assert(G::MBW == 5 && G::BN == 256 && 160 * 512 <= kStages * G::STAGE, "staging layout");
+    uint8_t* lt = &smem[0][0];
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));  // (as for the lane index above)
+    __syncthreads();  // every wave's reads of the ring are over (its loads have landed above)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int b = wm + 2 * i;
+        if (b / 5 != h) continue;
+        const int rl = (b - 5 * h) * 32 + efr;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nl = wn * 64 + j * 32 + q * 8 + efh * 4;
+            *(u32x2_t*)(lt + rl * 512 + (((nl >> 3) ^ (rl & 31)) << 4) + (nl & 4) * 2) =
+                u32x2_t{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                        pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+          }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 160 * 32 / kThreads; ++k) {
+        const int idx = k * kThreads + tid;
+        const int rl = idx >> 5, ch = idx & 31;
+        const int row = 160 * h + rl, n = c.n0 + ch * 8;
+        if (row < c.rows && n < c.N)
+          *(u32x4_t*)(y + (size_t)(c.r0 + row) * c.N + n) = *(const u32x4_t*)(lt + rl * 512 + ((ch ^ (rl & 31)) << 4));
+      }
+      __syncthreads();
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int row = (wm + 2 * i) * 32 + efr;
