@@ -273,6 +273,12 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   // Loads j in [j0, j1) of slice kt into ring buffer `buf`. A slice index past the end is clamped
   // to the last slice: such loads fill a buffer that is never read again, which keeps the number
   // of loads per slice fixed for the vmcnt arithmetic below.
+  // Cache policy of this wave's loads. In the expert passes the waves with L_LO loads fetch only
+  // weight blocks, which (a bucket being one M-tile) no other workgroup reads again: they load with
+  // the non-temporal hint (policy bit NT = 2), leaving L2 to the activation rows that every N-tile
+  // of the expert shares.
+  constexpr int kAux = (MODE != kRouter && L == G::L_LO && G::L_LO != G::L_HI) ? 2 : 0;
+  static_assert(MODE == kRouter || G::N_HI * G::L_HI == G::A_INSTR, "the L_LO waves load weights only");
   auto issue = [&](int kt, int buf, int j0, int j1) {
     const int kcl = kt < nk ? kt : nk - 1;
 #pragma unroll
@@ -280,7 +286,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
       if (i < j0 || i >= j1) continue;
       const int k = kcl * BK + c.kc[i];
       const uint16_t* s = c.src[i] + (k < K ? (size_t)kcl * c.stride[i] + c.kc[i] : 0);  // past K: zeroed later
-      __builtin_amdgcn_global_load_lds((const void*)s, (lds_t*)(smem[buf] + (c.first + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)s, (lds_t*)(smem[buf] + (c.first + i) * 1024), 16, 0, kAux);
     }
   };
   // chunks past K in the last slice: write zeros over what the loads brought in

@@ -16,17 +16,16 @@ namespace moe {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-// float -> bfloat16, round to nearest, ties to even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// float -> bfloat16, round to nearest, ties to even, NaN stays NaN (quiet), denormals kept: the
+// gfx950 conversion instruction (v_cvt_pk_bf16_f32), two values per instruction.
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_hw_t){lo, hi}, bf16x2_hw_t));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xFFFFu; }
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *(const u32x4_t*)p; }
 
@@ -52,7 +51,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU(z) = z * sigmoid(z). The hardware reciprocal (about 1 ulp) replaces the IEEE division: the
+// result is rounded to bf16 or summed in fp32 next, and the division's correction sequence made
+// the GEMM epilogue several times longer. 1 + exp(-z) >= 1, and its reciprocal is 0 when it
+// overflows (z below about -88), so the result is -0 there, as the division gives.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (MOE_WAVE - 1)); }
 
