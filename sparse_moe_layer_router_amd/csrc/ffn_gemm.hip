@@ -28,9 +28,10 @@
 // fragment reads bank-conflict free.
 //
 // Tile order: tiles are numbered expert by expert, N-tile by N-tile, with the M-tiles of one
-// (expert, N-tile) adjacent. Workgroups are dealt round-robin to the 8 XCDs, so block L runs tile
-// (L % 8) * per_xcd + L / 8: the N-tiles of one expert run at the same time on the same XCD and
-// share its activation rows in that XCD's L2.
+// (expert, N-tile) adjacent, and each XCD takes a contiguous range of that order, the ranges cut
+// by the schedule kernel so that they hold equal work. Workgroups are dealt round-robin to the 8
+// XCDs, so block L runs the (L / 8)-th tile of XCD L % 8's range: the N-tiles of one expert run at
+// the same time on the same XCD and share its activation rows in that XCD's L2.
 #include "kernels.h"
 #include "moe_device.h"
 
@@ -43,6 +44,7 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kWavesM = 2, kWavesN = 4;
 constexpr int kXcds = 8;
+constexpr int kCusPerXcd = 32;
 constexpr int kStages = 4;         // LDS ring depth: two slices in flight while one is consumed
 constexpr int kRowBytes = BK * 2;  // one tile row in LDS: 64 bytes = 4 chunks of 16
 
@@ -173,55 +175,124 @@ __device__ __forceinline__ long long group_rows(const FfnGroups& p, int g, long 
   return p.T;
 }
 
-// One block: for every group, m-tiles = ceil(rows / BM); tiles = m-tiles * n-tiles of that group.
-// Writes exclusive prefix sums for the gate/up pass (sched_gu) and the down pass (sched_dn), and
+// One block. For every group: m-tiles = ceil(rows / BM), tiles = m-tiles * n-tiles; writes the
+// exclusive prefix sums of the tiles of the gate/up pass (sched_gu) and the down pass (sched_dn), and
 // the first 16-row band of every routed group in the packed activations (pband: ceil(rows / 16)
 // bands per group), 1024 groups per round with the running totals carried between rounds.
+//
+// It also cuts each pass's tile sequence into kXcds contiguous ranges of about equal work (xb_gu,
+// xb_dn: kXcds + 1 bounds), one per XCD: with equal tile counts the XCD holding the shared expert's
+// full tiles would get the most work and every other XCD would wait for it. The work of an M-tile
+// with b 32-row blocks is modelled, in units of about 128 cycles, as 2 ceil(b / 2) + 3 per K slice
+// (the busiest wave runs ceil(b / 2) blocks; the loads, barriers and reads of a slice cost about
+// three units whatever b is) plus 192 for its set-up and epilogue. A bound falls between two M-tiles
+// of the group that holds it. With fewer than four tiles per CU the ranges stay equal in count:
+// there a range's time is set by how many rounds of tiles its CUs run, not by the sum of its work.
+// With more than 1024 groups a first pass over them finds the totals; the last pass writes
+// everything.
+__device__ __forceinline__ long long tile_work(long long blocks, long long nk) {
+  return (2 * ((blocks + 1) / 2) + 3) * nk + 192;
+}
+
 __global__ void __launch_bounds__(1024)
 gemm_schedule_kernel(const FfnGroups p, int32_t* __restrict__ sched_gu, int32_t* __restrict__ sched_dn,
-                     int32_t* __restrict__ pband) {
-  __shared__ int32_t wtot[3][16];
+                     int32_t* __restrict__ pband, int32_t* __restrict__ xb_gu, int32_t* __restrict__ xb_dn) {
+  constexpr int kQ = 5;  // per group: gate/up tiles, down tiles, bands, gate/up work, down work
+  constexpr int BM = Geo<kGateUp>::BM;
+  static_assert(Geo<kDown>::BM == BM, "one M-tiling for both passes");
+  __shared__ long long wtot[kQ][16];
   const int ngroups = p.E + (p.Hs > 0 ? 1 : 0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int32_t carry[3] = {0, 0, 0};
-  for (int base = 0; base < ngroups; base += 1024) {
-    const int g = base + (int)threadIdx.x;
-    int32_t v[3] = {0, 0, 0};
-    if (g < ngroups) {
-      const long long n = group_rows(p, g, nullptr);
-      const int Hg = g < p.E ? p.H : p.Hs;
-      v[0] = (int)((n + Geo<kGateUp>::BM - 1) / Geo<kGateUp>::BM) * ((Hg + Geo<kGateUp>::BN - 1) / Geo<kGateUp>::BN);
-      v[1] = (int)((n + Geo<kDown>::BM - 1) / Geo<kDown>::BM) * ((p.d + Geo<kDown>::BN - 1) / Geo<kDown>::BN);
-      v[2] = g < p.E ? (int)((n + 15) / 16) : 0;
-    }
-    int32_t inc[3] = {v[0], v[1], v[2]};
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const int32_t o = __shfl_up(inc[q], off, 64);
-        if (lane >= off) inc[q] += o;
+  long long total[kQ] = {0, 0, 0, 0, 0};
+  const bool one_round = ngroups <= 1024;  // then the totals are known after the round's scan
+  for (int pass = one_round ? 1 : 0; pass < 2; ++pass) {
+    long long carry[kQ] = {0, 0, 0, 0, 0};
+    for (int base = 0; base < ngroups; base += 1024) {
+      const int g = base + (int)threadIdx.x;
+      long long v[kQ] = {0, 0, 0, 0, 0};
+      long long mt = 0, ntg = 0, ntd = 0, nkg = 0, nkd = 0;
+      if (g < ngroups) {
+        const long long n = group_rows(p, g, nullptr);
+        const int Hg = g < p.E ? p.H : p.Hs;
+        mt = (n + BM - 1) / BM;
+        ntg = (Hg + Geo<kGateUp>::BN - 1) / Geo<kGateUp>::BN;
+        ntd = (p.d + Geo<kDown>::BN - 1) / Geo<kDown>::BN;
+        nkg = (p.d + BK - 1) / BK;
+        nkd = (Hg + BK - 1) / BK;
+        const long long b_last = mt > 0 ? (n - (mt - 1) * BM + 31) / 32 : 0;  // blocks of the last M-tile
+        v[0] = mt * ntg;
+        v[1] = mt * ntd;
+        v[2] = g < p.E ? (n + 15) / 16 : 0;
+        v[3] = mt > 0 ? ntg * ((mt - 1) * tile_work(BM / 32, nkg) + tile_work(b_last, nkg)) : 0;
+        v[4] = mt > 0 ? ntd * ((mt - 1) * tile_work(BM / 32, nkd) + tile_work(b_last, nkd)) : 0;
       }
-    }
-    if (lane == 63)
-      for (int q = 0; q < 3; ++q) wtot[q][wave] = inc[q];
-    __syncthreads();
-    int32_t ex[3] = {carry[0], carry[1], carry[2]};
-    for (int w = 0; w < wave; ++w)
-      for (int q = 0; q < 3; ++q) ex[q] += wtot[q][w];
-    if (g < ngroups) {
-      sched_gu[g] = ex[0] + inc[0] - v[0];
-      sched_dn[g] = ex[1] + inc[1] - v[1];
-      pband[g] = ex[2] + inc[2] - v[2];
-      if (g == ngroups - 1) {
-        sched_gu[ngroups] = ex[0] + inc[0];
-        sched_dn[ngroups] = ex[1] + inc[1];
-        pband[ngroups] = ex[2] + inc[2];
+      long long inc[kQ];
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) inc[q] = v[q];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+          const long long o = __shfl_up(inc[q], off, 64);
+          if (lane >= off) inc[q] += o;
+        }
       }
+      if (lane == 63)
+        for (int q = 0; q < kQ; ++q) wtot[q][wave] = inc[q];
+      __syncthreads();
+      if (one_round)
+        for (int w = 0; w < 16; ++w)
+          for (int q = 0; q < kQ; ++q) total[q] += wtot[q][w];
+      long long ex[kQ];
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) ex[q] = carry[q] + inc[q] - v[q];
+      for (int w = 0; w < wave; ++w)
+        for (int q = 0; q < kQ; ++q) ex[q] += wtot[q][w];
+      if (pass == 1 && g < ngroups) {
+        sched_gu[g] = (int32_t)ex[0];
+        sched_dn[g] = (int32_t)ex[1];
+        pband[g] = (int32_t)ex[2];
+        if (g == ngroups - 1) {
+          sched_gu[ngroups] = (int32_t)(ex[0] + v[0]);
+          sched_dn[ngroups] = (int32_t)(ex[1] + v[1]);
+          pband[ngroups] = (int32_t)(ex[2] + v[2]);
+        }
+        // XCD bounds inside this group: target work x * total / kXcds in [ex, ex + v), placed after
+        // N-tile k and, within it, after the nearest M-tile
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const long long w0 = ex[3 + q], wg = v[3 + q], nt = q == 0 ? ntg : ntd;
+          const long long per_nt = wg / (nt > 0 ? nt : 1);  // work of one N-tile (all its M-tiles)
+          const long long per_m = tile_work(BM / 32, q == 0 ? nkg : nkd);
+          if (total[q] < kXcds * kCusPerXcd * 4) continue;  // equal counts (below)
+          for (int x = 1; x < kXcds; ++x) {
+            const long long target = total[3 + q] * x / kXcds;
+            if (wg > 0 && target >= w0 && target < w0 + wg) {
+              const long long k = (target - w0) / per_nt;   // < nt
+              long long m = (target - w0 - k * per_nt + per_m / 2) / per_m;
+              m = m < mt ? m : mt;
+              (q == 0 ? xb_gu : xb_dn)[x] = (int32_t)(ex[q] + k * mt + m);
+            }
+          }
+        }
+      }
+      for (int w = 0; w < 16; ++w)
+        for (int q = 0; q < kQ; ++q) carry[q] += wtot[q][w];
+      __syncthreads();  // wtot is rewritten in the next round
     }
-    for (int w = 0; w < 16; ++w)
-      for (int q = 0; q < 3; ++q) carry[q] += wtot[q][w];
-    __syncthreads();  // wtot is rewritten in the next round
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) total[q] = carry[q];  // the same in every thread
+  }
+  if (threadIdx.x == 0) {
+    xb_gu[0] = 0;
+    xb_dn[0] = 0;
+    xb_gu[kXcds] = (int32_t)total[0];
+    xb_dn[kXcds] = (int32_t)total[1];
+    for (int x = 1; x < kXcds; ++x) {  // equal counts, or no work: nobody else writes a bound
+      const long long eg = (total[0] + kXcds - 1) / kXcds * x, ed = (total[1] + kXcds - 1) / kXcds * x;
+      if (total[0] < kXcds * kCusPerXcd * 4 || total[3] == 0) xb_gu[x] = (int32_t)(eg < total[0] ? eg : total[0]);
+      if (total[1] < kXcds * kCusPerXcd * 4 || total[4] == 0) xb_dn[x] = (int32_t)(ed < total[1] ? ed : total[1]);
+    }
   }
 }
 
@@ -230,6 +301,7 @@ struct GemmArgs {
   FfnGroups p;
   const int32_t* sched;   // [ngroups + 1] (kGateUp / kDown); unused for the router
   const int32_t* pband;   // [E + 1] first packed band of every routed group (kGateUp / kDown)
+  const int32_t* xb;      // [kXcds + 1] tile ranges of the XCDs (kGateUp / kDown)
   // router mode
   const void* x;          // [T, d]
   const void* w;          // [E, d]
@@ -615,19 +687,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
 }
 
 // Tiles are numbered expert by expert, N-tile by N-tile, with the M-tiles of one (expert, N-tile)
-// adjacent, and dealt to the 8 XCDs in contiguous ranges (workgroup L runs on XCD L % 8).
-// Workgroup L takes tile (L % 8) * per + L / 8 and then every (gridDim / 8)-th tile after it in
-// its XCD's range: with one workgroup per tile (the launch used) that is exactly one tile.
+// adjacent; XCD x takes the contiguous range [xb[x], xb[x + 1]) that the schedule balanced by work
+// (the router: equal ranges). Workgroup L runs on XCD L % 8 and takes the (L / 8)-th tile of its
+// XCD's range, then every (gridDim / 8)-th after it: with at least as many workgroups per XCD as
+// tiles in its range that is one tile, and the surplus workgroups exit at once.
 template <int MODE, int LAYOUT>
 __global__ void __launch_bounds__(kThreads, 1)
 grouped_gemm_kernel(const GemmArgs ga) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages][Geo<MODE>::STAGE];
   const int total = gemm_total_tiles<MODE>(ga);
-  const int per = (total + kXcds - 1) / kXcds;
   const int xcd = (int)blockIdx.x % kXcds, stride = (int)gridDim.x / kXcds;
-  const int end = (xcd + 1) * per < total ? (xcd + 1) * per : total;
-  for (int t = xcd * per + (int)blockIdx.x / kXcds; t < end; t += stride) {
-    if (t >= xcd * per + stride) __syncthreads();  // the previous tile's LDS reads are over
+  int lo, hi;
+  if (MODE == kRouter) {
+    const int per = (total + kXcds - 1) / kXcds;
+    lo = xcd * per;
+    hi = lo + per;
+  } else {
+    lo = ga.xb[xcd];
+    hi = ga.xb[xcd + 1];
+  }
+  lo = lo < 0 ? 0 : (lo > total ? total : lo);   // whatever the bounds hold, only tiles in [0, total)
+  hi = hi < lo ? lo : (hi > total ? total : hi);
+  for (int t = lo + (int)blockIdx.x / kXcds; t < hi; t += stride) {
+    if (t >= lo + stride) __syncthreads();  // the previous tile's LDS reads are over
     gemm_tile<MODE, LAYOUT>(ga, t, smem);
   }
 }
@@ -655,12 +737,13 @@ long long gemm_tiles_upper(const FfnGroups& p, int mode) {
   return (mt_routed + mt_shared) * ((p.d + bn - 1) / bn);
 }
 
-// [sched_gu | sched_dn | pband], E + 2 ints each
-size_t gemm_schedule_ints(int E) { return 3 * (size_t)(E + 2); }
+// [sched_gu | sched_dn | pband] (E + 2 ints each), then [xb_gu | xb_dn] (kXcds + 1 each)
+size_t gemm_schedule_ints(int E) { return 3 * (size_t)(E + 2) + 2 * (kXcds + 1); }
 
 hipError_t launch_gemm_schedule(const FfnGroups& p, int32_t* sched, hipStream_t stream) {
+  int32_t* xb = sched + 3 * (p.E + 2);
   hipLaunchKernelGGL(gemm_schedule_kernel, dim3(1), dim3(1024), 0, stream, p, sched, sched + p.E + 2,
-                     sched + 2 * (p.E + 2));
+                     sched + 2 * (p.E + 2), xb, xb + kXcds + 1);
   return hipGetLastError();
 }
 
@@ -670,6 +753,7 @@ hipError_t launch_gemm_gate_up(const FfnGroups& p, const int32_t* sched, hipStre
   a.p = p;
   a.sched = sched;
   a.pband = sched + 2 * (p.E + 2);
+  a.xb = sched + 3 * (p.E + 2);
   const dim3 grid(gemm_grid(gemm_tiles_upper(p, kGateUp)));
   if (p.layout == kFrag16)
     hipLaunchKernelGGL((grouped_gemm_kernel<kGateUp, kFrag16>), grid, dim3(kThreads), 0, stream, a);
@@ -683,6 +767,7 @@ hipError_t launch_gemm_down(const FfnGroups& p, const int32_t* sched, hipStream_
   a.p = p;
   a.sched = sched + p.E + 2;
   a.pband = sched + 2 * (p.E + 2);
+  a.xb = sched + 3 * (p.E + 2) + kXcds + 1;
   const dim3 grid(gemm_grid(gemm_tiles_upper(p, kDown)));
   if (p.layout == kFrag16)
     hipLaunchKernelGGL((grouped_gemm_kernel<kDown, kFrag16>), grid, dim3(kThreads), 0, stream, a);

@@ -78,8 +78,8 @@ hipError_t launch_ffn_down_stream(const FfnGroups& g, hipStream_t stream);
 hipError_t launch_ffn_gate_up_f32(const FfnGroups& g, hipStream_t stream);
 hipError_t launch_ffn_down_f32(const FfnGroups& g, hipStream_t stream);
 
-// grouped GEMM: `sched` holds gemm_schedule_ints(E) int32 (tile prefix sums of both passes and the
-// routed groups' first bands of the packed hidden activations)
+// grouped GEMM: `sched` holds gemm_schedule_ints(E) int32 (tile prefix sums of both passes, the
+// routed groups' first bands of the packed hidden activations, and each pass's per-XCD tile ranges)
 size_t gemm_schedule_ints(int E);
 hipError_t launch_gemm_schedule(const FfnGroups& g, int32_t* sched, hipStream_t stream);
 hipError_t launch_gemm_gate_up(const FfnGroups& g, const int32_t* sched, hipStream_t stream);

@@ -36,6 +36,9 @@ MID = [
     LayerConfig("gemm_ragged_shared", 600, 264, 16, 2, 200, 136, "bf16"),
     # 2048 tokens: router GEMM too (E = 8 < one N tile), skewed buckets
     LayerConfig("gemm_zipf_router", 2048, 512, 8, 2, 384, 0, "bf16", zipf_s=1.2),
+    # 1024 routed experts + the shared one: more than 1024 groups (two-round tile schedule) and more
+    # than 1024 tiles per pass (XCD ranges balanced by work); the router GEMM over four N tiles
+    LayerConfig("gemm_many_groups", 16384, 64, 1024, 2, 32, 32, "bf16"),
     # sigmoid routing with a selection-only bias: one-wave-per-token top-k with the grouped GEMM,
     # the single-block decode tail, float32 without a bias, and the router GEMM
     LayerConfig("sigmoid_mid_shared", 300, 264, 16, 4, 200, 136, "bf16", routing="sigmoid", score_bias_std=0.05),
