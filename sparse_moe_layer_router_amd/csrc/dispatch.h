@@ -49,7 +49,7 @@ hipError_t launch_load_stats(const int32_t* counts, int E, long long slots, floa
 // ---- combine ---------------------------------------------------------------------------------
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_perm, const float* topk_w,
                           const void* shared_out, void* out, int T, int k, int d, hipStream_t stream);
-const char* combine_kernel_name(int dtype);
+const char* combine_kernel_name(int dtype, int k);
 
 // ---- weight packing (MOE_LAYOUT_FRAG16) and INT8 quantization (MOE_LAYOUT_INT8_FRAG) --------------
 hipError_t launch_pack_weights(const void* src, void* dst, long long n_mats, int rows, int cols, hipStream_t stream);

@@ -445,7 +445,7 @@ const char* moe_stage_kernel_name(const moe_shape* s, int stage) {
     case MOE_STAGE_FFN_SCHEDULE: return moe::ffn_schedule_kernel_name(g);
     case MOE_STAGE_FFN_GATE_UP: return moe::ffn_gate_up_kernel_name(g);
     case MOE_STAGE_FFN_DOWN: return moe::ffn_down_kernel_name(g);
-    case MOE_STAGE_COMBINE: return moe::combine_kernel_name(s->dtype);
+    case MOE_STAGE_COMBINE: return moe::combine_kernel_name(s->dtype, s->top_k);
   }
   return "";
 }

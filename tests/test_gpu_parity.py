@@ -29,6 +29,7 @@ MID = [
     LayerConfig("mid_fp32_shared", 50, 96, 8, 3, 40, 24, "f32"),
     LayerConfig("single_expert_k1", 5, 64, 1, 1, 32, 0, "bf16"),
     LayerConfig("k_equals_E", 20, 128, 4, 4, 64, 32, "bf16"),
+    LayerConfig("k12_wide_topk", 40, 128, 32, 12, 64, 32, "bf16"),  # combine with more than 8 slots
     LayerConfig("one_token", 1, 256, 32, 8, 128, 64, "bf16"),
     LayerConfig("wide_E1024", 40, 64, 1024, 2, 16, 0, "bf16"),
     synth.CONFIGS[0],
