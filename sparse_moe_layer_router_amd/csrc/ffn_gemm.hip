@@ -22,10 +22,10 @@
 // load the 20 activation groups (16 rows x 64 bytes each, gathered through the permutation),
 // waves 4-7 the 16 weight blocks; each wave's loads for a slice are spread over the MFMAs of the
 // two K steps after the barrier that frees its buffer, and a wave waits (s_waitcnt vmcnt) only
-// for the slice it needs next, with two further slices in flight. Fragments are double-buffered
-// in registers across K steps: while the MFMAs of step j run, the LDS reads of step j+1 are issued
-// between them. A 16-byte-chunk XOR swizzle (activations) and the fragment-tiled weight layout keep
-// fragment reads bank-conflict free.
+// for the slice it needs next, with two further slices in flight. Fragments live in one set of
+// registers: while the MFMAs of step j run, each LDS read of step j+1 is issued right after the
+// last MFMA that needs the register it overwrites. A 16-byte-chunk XOR swizzle (activations) and
+// the fragment-tiled weight layout keep fragment reads bank-conflict free.
 //
 // Tile order: tiles are numbered expert by expert, N-tile by N-tile, with the M-tiles of one
 // (expert, N-tile) adjacent, and each XCD takes a contiguous range of that order, the ranges cut
@@ -101,22 +101,37 @@ __device__ __forceinline__ u32x4_t read_b(const uint8_t* sb, int j, int wn, int 
 // The MFMAs of one 16-wide K step on the fragments in fa / fb, and the LDS reads of the next step
 // into the same registers, each issued right after the last MFMA that needs the value it
 // replaces: B fragment 0 after the NA MFMAs of column block 0, A fragment i after its MFMA with B
-// fragment 1, B fragment 1 last. Every read then has NA MFMAs to land before its first use.
-// `loads` (the step's global-to-LDS loads) comes after the MFMAs of column block 0 in program order.
-template <int MODE, int LAYOUT, int NA, class Loads>
+// fragment 1, B fragment 1 last. The NV global-to-LDS loads of the step (load(j), j < NV) follow the
+// first MFMAs of column block 0, one after each. Scheduling fences keep exactly this order: left
+// to itself the compiler gathers the reads after the last MFMA, and every read's latency then
+// shows at the start of the next step.
+template <int MODE, int LAYOUT, int NA, int NV, class Load>
 __device__ __forceinline__ void mma_and_read(f32x16_t (&acc)[NA > 0 ? NA : 1][2], u32x4_t (&fa)[NA > 0 ? NA : 1],
                                              u32x4_t (&fb)[2], const uint8_t* sa, const uint8_t* sb, int wm,
-                                             int wn, int fr, int ch, Loads&& loads) {
+                                             int wn, int fr, int ch, Load&& load) {
 #pragma unroll
-  for (int i = 0; i < NA; ++i) acc[i][0] = mfma32x32x16(fb[0], fa[i], acc[i][0]);
-  loads();
+  for (int i = 0; i < NA; ++i) {
+    acc[i][0] = mfma32x32x16(fb[0], fa[i], acc[i][0]);
+    if (i < NV) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int j = NA; j < NV; ++j) load(j);
+  __builtin_amdgcn_sched_barrier(0);
   if (NA > 0) fb[0] = read_b<MODE, LAYOUT>(sb, 0, wn, fr, ch);
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
     acc[i][1] = mfma32x32x16(fb[1], fa[i], acc[i][1]);
+    __builtin_amdgcn_sched_barrier(0);
     fa[i] = read_a<MODE>(sa, i, wm, fr, ch);
   }
+  __builtin_amdgcn_sched_barrier(0);
   if (NA > 0) fb[1] = read_b<MODE, LAYOUT>(sb, 1, wn, fr, ch);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // First reads of a tile (nothing to multiply yet).
@@ -124,40 +139,25 @@ template <int MODE, int LAYOUT, int NA>
 __device__ __forceinline__ void read_all(u32x4_t (&fa)[NA > 0 ? NA : 1], u32x4_t (&fb)[2], const uint8_t* sa,
                                          const uint8_t* sb, int wm, int wn, int fr, int ch) {
   if (NA == 0) return;
+  fb[0] = read_b<MODE, LAYOUT>(sb, 0, wn, fr, ch);
 #pragma unroll
   for (int i = 0; i < NA; ++i) fa[i] = read_a<MODE>(sa, i, wm, fr, ch);
-  fb[0] = read_b<MODE, LAYOUT>(sb, 0, wn, fr, ch);
   fb[1] = read_b<MODE, LAYOUT>(sb, 1, wn, fr, ch);
-}
-
-// Pin the order of one step's instructions: the NA MFMAs of column block 0 with one
-// global-to-LDS load after each of the first VMEMS of them (loads beyond NA follow), then the read
-// of B fragment 0, then MFMA / A-fragment read pairs, then the read of B fragment 1. The loads
-// come first in program order, so the reads (which the compiler cannot tell apart from the
-// buffers the loads write) stay after them.
-template <int NA, int VMEMS>
-__device__ __forceinline__ void pin_step() {
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
-    if (i < VMEMS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
-  }
-  if (VMEMS > NA) __builtin_amdgcn_sched_group_barrier(0x020, VMEMS > NA ? VMEMS - NA : 0, 0);
-  if (NA > 0) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // read B fragment 0
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // read A fragment i
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // read B fragment 1
-  }
 }
 
 // One zero kilobyte: the source of packed A blocks past the end of a group.
 __device__ __attribute__((aligned(16))) const uint32_t g_zero_block[256] = {0};
 
-template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// s_waitcnt through the builtin, so that the compiler's own wait insertion knows what has landed
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; a field at its maximum waits
+// for nothing).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+// Workgroup barrier with no fence: the waits the ring needs come before it, explicitly.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 }  // namespace
 
@@ -357,7 +357,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
     for (int i = 0; i < L; ++i) {
       if (i < j0 || i >= j1) continue;
       const int k = kcl * BK + c.kc[i];
-      const uint16_t* s = c.src[i] + (k < K ? (size_t)kcl * c.stride[i] + c.kc[i] : 0);  // past K: zeroed later
+      const uint16_t* s = c.src[i] + (LAYOUT == kFrag16 || k < K ? (size_t)kcl * c.stride[i] + c.kc[i] : 0);  // past K: zeroed later
       __builtin_amdgcn_global_load_lds((const void*)s, (lds_t*)(smem[buf] + (c.first + i) * 1024), 16, 0, kAux);
     }
   };
@@ -397,8 +397,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   static_assert(kAhead + P1 < 64, "vmcnt holds 6 bits");
   auto arrive = [&](int kt) {
     wait_vmcnt<kAhead>();
-    if (kt == nk - 1 && (K % BK)) zero_tail(kt, kt % S);  // its loads have all landed here
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (LAYOUT != kFrag16 && kt == nk - 1 && (K % BK)) zero_tail(kt, kt % S);  // its loads have all landed here
+    wait_lgkmcnt0();
+    lds_barrier();
   };
 
   static_assert(BK / 16 == 2, "the loop below is written for two K steps per slice");
@@ -407,26 +408,37 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   for (int i = 0; i < S - 1; ++i) issue(i, i, 0, L);
   issue(S - 1, S - 1, 0, P1);
   wait_vmcnt<kAhead + P1>();
-  if (nk == 1 && (K % BK)) zero_tail(0, 0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (LAYOUT != kFrag16 && nk == 1 && (K % BK)) zero_tail(0, 0);
+  wait_lgkmcnt0();
+  lds_barrier();
   read_all<MODE, LAYOUT, NA>(fa, fb, smem[0], smem[0] + G::A_BYTES, wm, wn, fr, fh);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt % S;
-    // step 0 of slice kt: multiply while reading step 1 (chunks 2, 3 of the same slice) and issuing
-    // part 2 of slice kt+S-1
-    mma_and_read<MODE, LAYOUT, NA>(acc, fa, fb, smem[buf], smem[buf] + G::A_BYTES, wm, wn, fr, 2 + fh,
-                                   [&] { issue(kt + S - 1, (kt + S - 1) % S, P1, L); });
-    pin_step<NA, L - P1>();
-    // step 1 of slice kt: multiply while reading step 0 of slice kt+1 and issuing part 1 of slice
-    // kt+S into this slice's buffer (after the last slice the reads re-read the current buffer and
-    // are never used)
-    if (kt + 1 < nk) arrive(kt + 1);
-    const int nbuf = kt + 1 < nk ? (kt + 1) % S : buf;
-    const int lbuf = kt + 1 < nk ? buf : (kt + 1) % S;
-    mma_and_read<MODE, LAYOUT, NA>(acc, fa, fb, smem[nbuf], smem[nbuf] + G::A_BYTES, wm, wn, fr, fh,
-                                   [&] { issue(kt + S, lbuf, 0, P1); });
-    pin_step<NA, P1>();
+  // Step 0 of slice kt (S0) multiplies while reading step 1 (chunks 2, 3 of the same slice) and
+  // issuing part 2 of slice kt+S-1; step 1 (S1) multiplies while reading step 0 of slice kt+1 and
+  // issuing part 1 of slice kt+S into slice kt's buffer. The loop runs S1(kt) S0(kt+1) arrive(kt+2),
+  // so that its body is one straight block that closes right after a barrier, where no LDS read is
+  // in flight (the last two steps are peeled off, with no barrier). The last slice's S1 re-reads the
+  // current buffer (the values are never used) and sends its loads to the next buffer, since waves
+  // that are behind may still read the current one and no barrier follows.
+  auto s0 = [&](int kt) {
+    mma_and_read<MODE, LAYOUT, NA, L - P1>(acc, fa, fb, smem[kt % S], smem[kt % S] + G::A_BYTES, wm, wn, fr,
+                                           2 + fh, [&](int j) { issue(kt + S - 1, (kt + S - 1) % S, P1 + j, P1 + j + 1); });
+  };
+  auto s1 = [&](int kt, int rbuf, int lbuf) {
+    mma_and_read<MODE, LAYOUT, NA, P1>(acc, fa, fb, smem[rbuf], smem[rbuf] + G::A_BYTES, wm, wn, fr, fh,
+                                       [&](int j) { issue(kt + S, lbuf, j, j + 1); });
+  };
+  s0(0);
+  if (nk > 1) arrive(1);
+  for (int kt = 0; kt + 2 < nk; ++kt) {
+    s1(kt, (kt + 1) % S, kt % S);
+    s0(kt + 1);
+    arrive(kt + 2);
   }
+  if (nk > 1) {
+    s1(nk - 2, (nk - 1) % S, (nk - 2) % S);
+    s0(nk - 1);
+  }
+  s1(nk - 1, (nk - 1) % S, nk % S);
   wait_vmcnt<0>();  // no load may still write LDS when the tile ends
 
   // ---- epilogue ----------------------------------------------------------------------------------
