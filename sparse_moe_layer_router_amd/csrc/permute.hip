@@ -48,19 +48,26 @@ permute_count_kernel(const int32_t* __restrict__ ids, long long rows, int E, int
 }
 
 // One block of 1024 threads (one expert each): column scan over tiles, then a block-wide exclusive
-// scan over experts of the totals.
+// scan over experts of the totals. The tile counts are read 16 tiles at a time before any of them
+// is written back, so a column costs n_tiles / 16 memory round trips, not n_tiles.
 __global__ void __launch_bounds__(1024)
 permute_scan_kernel(int32_t* __restrict__ tile_counts, int n_tiles, int E, int32_t* __restrict__ counts,
                     int32_t* __restrict__ offsets) {
   __shared__ int32_t wave_tot[16];
   const int e = threadIdx.x;
   const int lane = e & 63, wave = e >> 6;
+  constexpr int kChunk = 16;
   int32_t total = 0;
   if (e < E) {
-    for (int b = 0; b < n_tiles; ++b) {
-      int32_t c = tile_counts[(size_t)b * E + e];
-      tile_counts[(size_t)b * E + e] = total;  // exclusive within the expert, offset added below
-      total += c;
+    for (int b0 = 0; b0 < n_tiles; b0 += kChunk) {
+      int32_t c[kChunk];
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) c[j] = b0 + j < n_tiles ? tile_counts[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        if (b0 + j < n_tiles) tile_counts[(size_t)(b0 + j) * E + e] = total;  // exclusive within the expert
+        total += c[j];
+      }
     }
   }
   // inclusive scan of `total` across the 1024 threads: within waves, then across waves
@@ -79,7 +86,14 @@ permute_scan_kernel(int32_t* __restrict__ tile_counts, int n_tiles, int E, int32
     if (counts) counts[e] = total;
     offsets[e] = excl;
     if (e == E - 1) offsets[E] = excl + total;
-    for (int b = 0; b < n_tiles; ++b) tile_counts[(size_t)b * E + e] += excl;
+    for (int b0 = 0; b0 < n_tiles; b0 += kChunk) {
+      int32_t c[kChunk];
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) c[j] = b0 + j < n_tiles ? tile_counts[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j)
+        if (b0 + j < n_tiles) tile_counts[(size_t)(b0 + j) * E + e] = c[j] + excl;
+    }
   }
 }
 
