@@ -10,6 +10,9 @@
 
 namespace moe {
 
+// Largest expert count the kernels handle (the C ABI rejects more).
+constexpr int kMaxExperts = 1024;
+
 enum Dtype { kF32 = 0, kBF16 = 1 };
 
 // ---- grouped SwiGLU experts ------------------------------------------------------------------

@@ -61,7 +61,7 @@ moe_status check_shape(const moe_shape* s) {
   if (s->T < 0 || s->d_model < 1 || s->n_experts < 1 || s->top_k < 1 || s->d_hidden < 1 || s->d_shared_hidden < 0)
     return MOE_ERR_INVALID_ARG;
   if (s->top_k > s->n_experts) return MOE_ERR_INVALID_ARG;
-  if (s->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
+  if (s->n_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if ((long long)s->T * s->top_k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (s->d_model % 8 || s->d_hidden % 8 || s->d_shared_hidden % 8) return MOE_ERR_ALIGNMENT;
   if (s->weight_layout != MOE_LAYOUT_ROWMAJOR && s->weight_layout != MOE_LAYOUT_FRAG16 &&

@@ -16,8 +16,6 @@
 
 namespace moe {
 
-constexpr int kMaxExperts = 1024;
-
 int permute_tile_size(long long rows) {
   long long tile = 1024;
   while ((rows + tile - 1) / tile > 1024) tile *= 2;  // at most 1024 tiles
