@@ -40,6 +40,9 @@ MID = [
     # 1024 routed experts + the shared one: more than 1024 groups (two-round tile schedule) and more
     # than 1024 tiles per pass (XCD ranges balanced by work); the router GEMM over four N tiles
     LayerConfig("gemm_many_groups", 16384, 64, 1024, 2, 32, 32, "bf16"),
+    # skewed buckets of several M-tiles each and more than 1024 gate/up tiles (XCD ranges balanced
+    # by work, bounds falling between the M-tiles of one N-tile)
+    LayerConfig("gemm_balanced_zipf", 4096, 512, 8, 2, 4608, 0, "bf16", zipf_s=1.2),
     # sigmoid routing with a selection-only bias: one-wave-per-token top-k with the grouped GEMM,
     # the single-block decode tail, float32 without a bias, and the router GEMM
     LayerConfig("sigmoid_mid_shared", 300, 264, 16, 4, 200, 136, "bf16", routing="sigmoid", score_bias_std=0.05),
@@ -47,6 +50,14 @@ MID = [
     LayerConfig("sigmoid_fp32_nobias", 50, 96, 8, 3, 40, 24, "f32", routing="sigmoid"),
     LayerConfig("sigmoid_gemm_router", 2048, 512, 8, 2, 384, 0, "bf16", routing="sigmoid", score_bias_std=0.05),
 ]
+
+
+MID_BY_NAME = {c.name: c for c in MID}
+
+
+def pick(*names):
+    """Configs of MID by name (a missing name fails at collection)."""
+    return [MID_BY_NAME[n] for n in names]
 
 
 def check_routing_on_gpu_logits(L, r):
@@ -100,7 +111,9 @@ def test_layer_matches_oracle_mid_sizes(cfg):
     assert ok, (err, bound)
 
 
-@pytest.mark.parametrize("cfg", MID[:3] + MID[9:11] + MID[-2:], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", pick("mid_ragged_shared", "mid_zipf_bias", "mid_fp32_shared", "gemm_ragged_shared",
+                                      "gemm_zipf_router", "gemm_many_groups", "sigmoid_mid_shared",
+                                      "sigmoid_fp32_nobias", "sigmoid_gemm_router"), ids=lambda c: c.name)
 def test_entry_points_separately(cfg):
     """moe_route -> moe_permute -> moe_grouped_ffn (routed, then shared as a one-group call) -> moe_combine."""
     L = G.make_layer(cfg)
@@ -276,7 +289,8 @@ def test_topk_tie_heavy_every_lane_width(E, routing):
             np.testing.assert_array_equal(w2.cpu().numpy().view(np.uint32), w.cpu().numpy().view(np.uint32))
 
 
-@pytest.mark.parametrize("cfg", [MID[0], MID[1], MID[6], synth.CONFIGS[0]], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", pick("mid_ragged_shared", "mid_zipf_bias", "wide_E1024") + [synth.CONFIGS[0]],
+                         ids=lambda c: c.name)
 def test_load_stats_match_oracle(cfg):
     """Per-expert load and balance penalty of the GPU's own routing, against the oracle's."""
     L = G.make_layer(cfg)
