@@ -22,6 +22,12 @@ namespace {
 
 constexpr int kRowsPerBlock = 64;   // 4 waves x 16 weight rows
 constexpr int kUnroll = 8;          // k-steps of 32 issued back to back (8 KB per matrix per wave)
+// 16-token tiles a weight fragment is applied to in one pass (NTT): a group of n rows streams its
+// weights ceil(n / (16 NTT)) times, and the shared expert is cut into chunks of 16 NTT rows. With
+// more than 16 tokens, bf16 weights take NTT = 2 (at a decode batch of 256 that halves the shared
+// expert's passes: -2.4% for the layer), at a register cost that still leaves two to three waves per
+// SIMD. With 16 tokens or fewer there is one chunk either way, and the INT8 kernels lose more to
+// the lower occupancy than they gain: NTT = 1. Four tiles cost too much occupancy everywhere.
 
 struct GroupView {
   long long r0;        // first row of the group in the (routed or shared) row space
@@ -454,8 +460,12 @@ ffn_down_f32(const FfnGroups p) {
 
 // --------------------------------------------------------------------------------- launchers
 namespace {
-// routed groups + one group per 16-row chunk of the shared expert (NTT = 1)
-int groups_of(const FfnGroups& g) { return g.E + (g.Hs > 0 ? (g.T + 15) / 16 : 0); }
+int stream_ntt(const FfnGroups& g) { return g.layout != kInt8Frag && g.T > 16 ? 2 : 1; }
+// routed groups + one group per 16 NTT-row chunk of the shared expert
+int groups_of(const FfnGroups& g) {
+  const int c = 16 * stream_ntt(g);
+  return g.E + (g.Hs > 0 ? (g.T + c - 1) / c : 0);
+}
 int hmax(const FfnGroups& g) { return g.H > g.Hs ? g.H : g.Hs; }
 long long all_rows(const FfnGroups& g) { return g.rows + (g.Hs > 0 ? g.T : 0); }
 }  // namespace
@@ -468,10 +478,15 @@ FfnPath ffn_path(const FfnGroups& g) {
 
 hipError_t launch_ffn_gate_up_stream(const FfnGroups& g, hipStream_t stream) {
   dim3 grid((hmax(g) + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
+  const bool two = stream_ntt(g) == 2;
   if (g.layout == kInt8Frag)
     hipLaunchKernelGGL((ffn_gate_up_stream<1, kInt8Frag>), grid, dim3(256), 0, stream, g);
+  else if (g.layout == kFrag16 && two)
+    hipLaunchKernelGGL((ffn_gate_up_stream<2, kFrag16>), grid, dim3(256), 0, stream, g);
   else if (g.layout == kFrag16)
     hipLaunchKernelGGL((ffn_gate_up_stream<1, kFrag16>), grid, dim3(256), 0, stream, g);
+  else if (two)
+    hipLaunchKernelGGL((ffn_gate_up_stream<2, kRowMajor>), grid, dim3(256), 0, stream, g);
   else
     hipLaunchKernelGGL((ffn_gate_up_stream<1, kRowMajor>), grid, dim3(256), 0, stream, g);
   return hipGetLastError();
@@ -479,10 +494,15 @@ hipError_t launch_ffn_gate_up_stream(const FfnGroups& g, hipStream_t stream) {
 
 hipError_t launch_ffn_down_stream(const FfnGroups& g, hipStream_t stream) {
   dim3 grid((g.d + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
+  const bool two = stream_ntt(g) == 2;
   if (g.layout == kInt8Frag)
     hipLaunchKernelGGL((ffn_down_stream<1, kInt8Frag>), grid, dim3(256), 0, stream, g);
+  else if (g.layout == kFrag16 && two)
+    hipLaunchKernelGGL((ffn_down_stream<2, kFrag16>), grid, dim3(256), 0, stream, g);
   else if (g.layout == kFrag16)
     hipLaunchKernelGGL((ffn_down_stream<1, kFrag16>), grid, dim3(256), 0, stream, g);
+  else if (two)
+    hipLaunchKernelGGL((ffn_down_stream<2, kRowMajor>), grid, dim3(256), 0, stream, g);
   else
     hipLaunchKernelGGL((ffn_down_stream<1, kRowMajor>), grid, dim3(256), 0, stream, g);
   return hipGetLastError();
@@ -507,8 +527,9 @@ const char* ffn_gate_up_kernel_name(const FfnGroups& g) {
   switch (ffn_path(g)) {
     case kPathF32: return "ffn_gate_up_f32";
     case kPathStream:
-      return g.layout == kInt8Frag ? "ffn_gate_up_stream<1, 2>"
-                                   : (g.layout == kFrag16 ? "ffn_gate_up_stream<1, 1>" : "ffn_gate_up_stream<1, 0>");
+      if (g.layout == kInt8Frag) return "ffn_gate_up_stream<1, 2>";
+      if (stream_ntt(g) == 2) return g.layout == kFrag16 ? "ffn_gate_up_stream<2, 1>" : "ffn_gate_up_stream<2, 0>";
+      return g.layout == kFrag16 ? "ffn_gate_up_stream<1, 1>" : "ffn_gate_up_stream<1, 0>";
     default: return g.layout == kFrag16 ? "grouped_gemm_kernel<0, 1>" : "grouped_gemm_kernel<0, 0>";
   }
 }
@@ -516,8 +537,9 @@ const char* ffn_down_kernel_name(const FfnGroups& g) {
   switch (ffn_path(g)) {
     case kPathF32: return "ffn_down_f32";
     case kPathStream:
-      return g.layout == kInt8Frag ? "ffn_down_stream<1, 2>"
-                                   : (g.layout == kFrag16 ? "ffn_down_stream<1, 1>" : "ffn_down_stream<1, 0>");
+      if (g.layout == kInt8Frag) return "ffn_down_stream<1, 2>";
+      if (stream_ntt(g) == 2) return g.layout == kFrag16 ? "ffn_down_stream<2, 1>" : "ffn_down_stream<2, 0>";
+      return g.layout == kFrag16 ? "ffn_down_stream<1, 1>" : "ffn_down_stream<1, 0>";
     default: return g.layout == kFrag16 ? "grouped_gemm_kernel<1, 1>" : "grouped_gemm_kernel<1, 0>";
   }
 }
