@@ -90,6 +90,8 @@ hipError_t launch_gemm_down(const FfnGroups& g, const int32_t* sched, hipStream_
 
 // dense router GEMM (bf16, large T): logits = x . w^T + bias
 constexpr int kRouterGemmMinTokens = 2048;
+// bf16 router logits: one wave per (token, expert) up to this many tokens, MFMA tiles of 16 x 16 above
+constexpr int kRouterValuMaxTokens = 16;
 hipError_t launch_router_gemm(const void* x, const void* w, const float* bias, float* logits, int T, int E, int d,
                               hipStream_t stream);
 

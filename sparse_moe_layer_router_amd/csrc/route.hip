@@ -43,6 +43,63 @@ route_logits_valu(const void* __restrict__ x, const void* __restrict__ w, const 
   if (lane == 0) logits[(size_t)t * E + e] = acc + (bias ? bias[e] : 0.f);
 }
 
+// bf16: one block of four waves per tile of 16 experts x 16 tokens, as 16x16x32 MFMAs over d
+// (A = 16 router rows, B = 16 token rows, lane l reading row l % 16 at k-chunk l / 16 of each
+// 32-wide step, 16 bytes per lane). Every router row and token row is read once per tile, not once
+// per (token, expert) pair. The four waves take consecutive quarters of the 32-wide k-steps and
+// their partial sums are added in wave order through LDS (fixed order: the result does not depend
+// on timing). Rows past E repeat a valid row and tokens past T read zeros; neither is stored. Lane
+// l ends with experts 4 (l / 16) + i, i < 4, of token l % 16.
+__global__ void __launch_bounds__(256)
+route_logits_mfma(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias,
+                  float* __restrict__ logits, int T, int E, int d) {
+  constexpr int kU = 8;  // k-steps loaded back to back
+  __shared__ f32x4_t part[3][64];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+  const int ar = lane & 15, kq = lane >> 4;
+  const int er = e0 + ar < E ? e0 + ar : E - 1;
+  const bool tok = t0 + ar < T;
+  const uint16_t* wa = w + (size_t)er * d + kq * 8;
+  const uint16_t* xb = x + (size_t)(tok ? t0 + ar : 0) * d + kq * 8;
+  const int nk = (d + 31) / 32, per = (nk + 3) / 4;
+  const int kb = wave * per * 32, ke = (wave + 1) * per * 32 < d ? (wave + 1) * per * 32 : d;
+  const u32x4_t zero = {0, 0, 0, 0};
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  int k0 = kb;
+  for (; k0 + 32 * kU <= ke; k0 += 32 * kU) {
+    u32x4_t a[kU], b[kU];
+#pragma unroll
+    for (int s = 0; s < kU; ++s) a[s] = ld16(wa + k0 + 32 * s);
+#pragma unroll
+    for (int s = 0; s < kU; ++s) b[s] = tok ? ld16(xb + k0 + 32 * s) : zero;
+#pragma unroll
+    for (int s = 0; s < kU; ++s) acc = mfma16x16x32(a[s], b[s], acc);
+  }
+  for (; k0 < ke; k0 += 32) {  // d is a multiple of 8: a lane's 8-element chunk is all in or all out
+    const bool kok = k0 + kq * 8 < d;
+    const u32x4_t a = kok ? ld16(wa + k0) : zero;
+    const u32x4_t b = (kok && tok) ? ld16(xb + k0) : zero;
+    acc = mfma16x16x32(a, b, acc);
+  }
+  if (wave > 0) part[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const f32x4_t p = part[q][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += p[i];
+  }
+  const int t = t0 + ar;
+  if (t >= T) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + kq * 4 + i;
+    if (e < E) logits[(size_t)t * E + e] = acc[i] + (bias ? bias[e] : 0.f);
+  }
+}
+
 // ------------------------------------------------------------------------------------- top-k
 // One wave per token. Lane l holds logits l, l+64, ... (NPER = ceil(E/64) <= 16 per lane). Each of
 // the k rounds takes the lane-local best not yet taken, then the wave's largest value (a DPP
@@ -238,6 +295,11 @@ route_tail_small_kernel(const float* __restrict__ logits, int T, int E, int k, c
 hipError_t launch_route_logits(int dtype, const void* x, const void* w_router, const float* bias, float* logits,
                                int T, int E, int d, hipStream_t stream) {
   if (dtype == kBF16 && T >= kRouterGemmMinTokens) return launch_router_gemm(x, w_router, bias, logits, T, E, d, stream);
+  if (dtype == kBF16 && T > kRouterValuMaxTokens) {
+    hipLaunchKernelGGL(route_logits_mfma, dim3((E + 15) / 16, (T + 15) / 16), dim3(256), 0, stream,
+                       (const uint16_t*)x, (const uint16_t*)w_router, bias, logits, T, E, d);
+    return hipGetLastError();
+  }
   dim3 grid(T, (E + 3) / 4), block(256);
   if (dtype == kBF16)
     hipLaunchKernelGGL(route_logits_valu<kBF16>, grid, block, 0, stream, x, w_router, bias, logits, T, E, d);
@@ -278,6 +340,7 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int routi
 
 const char* route_logits_kernel_name(int dtype, int T, int) {
   if (dtype == kBF16 && T >= kRouterGemmMinTokens) return "grouped_gemm_kernel<2, 0>";
+  if (dtype == kBF16 && T > kRouterValuMaxTokens) return "route_logits_mfma";
   return dtype == kBF16 ? "route_logits_valu<1>" : "route_logits_valu<0>";
 }
 

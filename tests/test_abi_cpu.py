@@ -147,6 +147,10 @@ def test_status_strings_and_stage_names():
     assert names[6] == "grouped_gemm_kernel<0, 0>" and names[7] == "grouped_gemm_kernel<1, 0>"
     packed = dsv3(T=8, weight_layout=moe.MOE_LAYOUT_FRAG16)
     assert moe.moe_stage_kernel_name(packed, 6) == "ffn_gate_up_stream<1, 1>"
+    # router logits: one wave per (token, expert) up to 16 tokens, MFMA tiles up to 2047, the GEMM after
+    assert moe.moe_stage_kernel_name(dsv3(T=16), 0) == "route_logits_valu<1>"
+    assert moe.moe_stage_kernel_name(dsv3(T=256), 0) == "route_logits_mfma"
+    assert moe.moe_stage_kernel_name(dsv3(T=2048), 0) == "grouped_gemm_kernel<2, 0>"
     # more than 16 tokens, bf16: two token tiles per pass over the weights (NTT = 2)
     assert moe.moe_stage_kernel_name(dsv3(T=256, weight_layout=moe.MOE_LAYOUT_FRAG16), 6) == "ffn_gate_up_stream<2, 1>"
     assert moe.moe_stage_kernel_name(dsv3(T=256, weight_layout=moe.MOE_LAYOUT_FRAG16), 7) == "ffn_down_stream<2, 1>"
