@@ -21,6 +21,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import statistics
 import os
 import sys
 import time
@@ -286,6 +287,22 @@ def main():
         durs = [ev_all.elapsed_ms(2 * n_st * i + 2 * s, 2 * n_st * i + 2 * s + 1) for i in range(n_prof)]
         stage_ms[moe.STAGES[s]] = sum(durs) / n_prof
     ev_all.close()
+    # Per-step distribution of the whole layer: an untimed pass with one event pair per step (at the
+    # first stage's start and the last stage's end), for mean, standard deviation and median.
+    n_dist = min(K, 30)
+    ev_d = HipEvents(2 * n_dist)
+    slots_d = [(ctypes.c_void_p * (2 * n_st))() for _ in range(n_dist)]
+    for i in range(n_dist):
+        slots_d[i][0] = ev_d.ev[2 * i]
+        slots_d[i][2 * n_st - 1] = ev_d.ev[2 * i + 1]
+    for i in range(n_dist):
+        step(i, ctypes.cast(slots_d[i], ctypes.POINTER(ctypes.c_void_p)))
+    torch.cuda.synchronize()
+    step_ms = [ev_d.elapsed_ms(2 * i, 2 * i + 1) for i in range(n_dist)]
+    ev_d.close()
+    step_dist = {"mean": round(statistics.mean(step_ms), 4), "std": round(statistics.pstdev(step_ms), 4),
+                 "median": round(statistics.median(step_ms), 4), "steps": n_dist}
+
     dominant = max(("ffn_gate_up", "ffn_down"), key=lambda s_: stage_ms[s_])
     dom = moe.STAGES.index(dominant)
 
@@ -346,6 +363,7 @@ def main():
                   "tflops": round(work["flops_layer"] / (ms_per_step * 1e-3) / 1e12, 2),
                   "active_experts_mean": work["n_act"]},
         "stage_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},   # untimed pass, events on every stage
+        "step_ms_events": step_dist,   # untimed pass, events around each whole layer call
         "setup_s": round(t_setup, 1),
     }
     if not args.no_cpu_baseline:
