@@ -33,6 +33,7 @@ METRIC = "MoE-layer tokens/s; achieved HBM TB/s (decode) and MFMA util (prefill)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 N_BATCHES = 4                   # distinct token batches cycled through the steps
+FLUSH_BYTES = 1 << 30          # cache-evicting copy between the steps of the distribution pass
 
 
 def parse():
@@ -58,6 +59,7 @@ class HipEvents:
         self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.ev = (ctypes.c_void_p * n)()
         for i in range(n):
             h = ctypes.c_void_p()
@@ -65,6 +67,11 @@ class HipEvents:
             if rc != 0:
                 raise RuntimeError(f"hipEventCreate failed ({rc})")
             self.ev[i] = h
+
+    def record(self, i, stream):
+        rc = self.lib.hipEventRecord(self.ev[i], ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def array(self, start, count):
         return ctypes.cast(ctypes.byref(self.ev, start * ctypes.sizeof(ctypes.c_void_p)),
@@ -287,21 +294,34 @@ def main():
         durs = [ev_all.elapsed_ms(2 * n_st * i + 2 * s, 2 * n_st * i + 2 * s + 1) for i in range(n_prof)]
         stage_ms[moe.STAGES[s]] = sum(durs) / n_prof
     ev_all.close()
-    # Per-step distribution of the whole layer: an untimed pass with one event pair per step (at the
-    # first stage's start and the last stage's end), for mean, standard deviation and median.
-    n_dist = min(K, 30)
-    ev_d = HipEvents(2 * n_dist)
+    # Per-step distribution of the whole layer: an untimed pass of 30 steps with one event pair per
+    # step (at the first stage's start and the last stage's end), for mean, standard deviation and
+    # median. Between steps, outside the event pairs, a 1 GiB device-to-device copy evicts L2 and
+    # the 256 MB Infinity Cache, so every step starts cold; the copies, timed with their own events,
+    # also give a measured large-copy HBM bandwidth.
+    n_dist = 30
+    flush_src = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+    ev_d = HipEvents(4 * n_dist)
     slots_d = [(ctypes.c_void_p * (2 * n_st))() for _ in range(n_dist)]
     for i in range(n_dist):
         slots_d[i][0] = ev_d.ev[2 * i]
         slots_d[i][2 * n_st - 1] = ev_d.ev[2 * i + 1]
+    torch.cuda.synchronize()
     for i in range(n_dist):
+        ev_d.record(2 * n_dist + 2 * i, stream.cuda_stream)
+        flush_dst.copy_(flush_src)
+        ev_d.record(2 * n_dist + 2 * i + 1, stream.cuda_stream)
         step(i, ctypes.cast(slots_d[i], ctypes.POINTER(ctypes.c_void_p)))
     torch.cuda.synchronize()
     step_ms = [ev_d.elapsed_ms(2 * i, 2 * i + 1) for i in range(n_dist)]
+    copy_ms = statistics.median(ev_d.elapsed_ms(2 * n_dist + 2 * i, 2 * n_dist + 2 * i + 1) for i in range(n_dist))
     ev_d.close()
+    del flush_src, flush_dst
+    copy_GBps = 2 * FLUSH_BYTES / (copy_ms * 1e-3) / 1e9   # read + write
     step_dist = {"mean": round(statistics.mean(step_ms), 4), "std": round(statistics.pstdev(step_ms), 4),
-                 "median": round(statistics.median(step_ms), 4), "steps": n_dist}
+                 "median": round(statistics.median(step_ms), 4), "steps": n_dist,
+                 "between_steps": "1 GiB device copy (L2 and Infinity Cache evicted)"}
 
     dominant = max(("ffn_gate_up", "ffn_down"), key=lambda s_: stage_ms[s_])
     dom = moe.STAGES.index(dominant)
@@ -338,6 +358,9 @@ def main():
     roof["kernel"] = kname
     roof["kernel_ms"] = round(kms, 4)
     roof["traffic"] = traffic_for(cfg.name, kname)
+    if roof["bound"] == "hbm":   # the same kernel against the large-copy bandwidth measured above
+        roof["measured_copy_GBps"] = round(copy_GBps, 1)
+        roof["frac_of_measured_copy"] = round(achieved / copy_GBps, 4)
 
     line = {
         "metric": METRIC,
@@ -363,7 +386,7 @@ def main():
                   "tflops": round(work["flops_layer"] / (ms_per_step * 1e-3) / 1e12, 2),
                   "active_experts_mean": work["n_act"]},
         "stage_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},   # untimed pass, events on every stage
-        "step_ms_events": step_dist,   # untimed pass, events around each whole layer call
+        "step_ms_events": step_dist,   # untimed pass, cold caches, events around each whole layer call
         "setup_s": round(t_setup, 1),
     }
     if not args.no_cpu_baseline:
