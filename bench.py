@@ -208,7 +208,7 @@ def main():
 
     cfg = synth.CONFIG_BY_NAME[args.workload]
     prefill = cfg.T * cfg.k / cfg.E > 32
-    K = args.steps if args.steps is not None else (20 if prefill else 50)
+    K = args.steps if args.steps is not None else (30 if prefill else 50)
     W = args.warmup if args.warmup is not None else 5
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
