@@ -43,12 +43,18 @@ Readings where the pages are silent or garbled (each is also listed in the design doc
   * gate = softmax over the K selected raw logits, temperature 1 ([MoE overview] §2.2 step 3).
   * expert = SwiGLU: h = SiLU(x W_gate^T) * (x W_up^T), y = h W_down^T, SiLU(z) = z * sigmoid(z)
     (standard definition; the pages name the three matrices but never define the activation).
+  * GELU expert ([MoE overview] §4.1 layer code, the optional two-layer variant): y = GELU(x W1^T
+    + b1) W2^T + b2, both linears with a bias, GELU(z) = z * Phi(z) with Phi the standard normal
+    CDF (the exact form, the default of the linear-GELU-linear block the listing builds; the
+    page does not define GELU itself), no shared expert.
   * top-K order: value descending, ties to the lower expert index.
   * permutation: rows sorted by (expert, token), i.e. flat position t*k+j ascending inside each
     expert; offsets are exclusive with E+1 entries.
 """
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -57,6 +63,7 @@ __all__ = [
     "swiglu", "grouped_ffn", "combine", "layer_forward", "layer_forward_tokens", "topk_gap",
     "logistic", "selection_scores", "sigmoid_weights_selected", "ROUTINGS",
     "quantize", "dequantize", "quantize_rows_int8", "dequantize_rows_int8", "load_stats",
+    "gelu", "gelu_mlp", "grouped_ffn_gelu", "layer_forward_gelu",
 ]
 
 ROUTINGS = ("softmax", "sigmoid")
@@ -279,6 +286,41 @@ def swiglu(X: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarr
     return (silu(G) * U) @ np.asarray(w_down, np.float64).T
 
 
+_erfc = np.frompyfunc(math.erfc, 1, 1)
+
+
+def gelu(z: np.ndarray) -> np.ndarray:
+    """GELU, exact form: z * Phi(z), with Phi(z) = erfc(-z / sqrt 2) / 2 (the C library's erfc;
+    the same as (1 + erf(z / sqrt 2)) / 2 without its cancellation for negative z)."""
+    z = np.asarray(z, np.float64)
+    return z * _erfc(-z / math.sqrt(2.0)).astype(np.float64) / 2.0
+
+
+def gelu_mlp(X: np.ndarray, w1: np.ndarray, b1, w2: np.ndarray, b2) -> np.ndarray:
+    """The two-layer expert of the [MoE overview] §4.1 layer code: Linear(d -> H), GELU,
+    Linear(H -> d), each linear with a bias (None = zero). Weights are [out, in]."""
+    X = np.asarray(X, np.float64)
+    Z = X @ np.asarray(w1, np.float64).T
+    if b1 is not None:
+        Z = Z + np.asarray(b1, np.float64)[None, :]
+    Y = gelu(Z) @ np.asarray(w2, np.float64).T
+    if b2 is not None:
+        Y = Y + np.asarray(b2, np.float64)[None, :]
+    return Y
+
+
+def grouped_ffn_gelu(x_rows: np.ndarray, offsets: np.ndarray, expert_fn) -> np.ndarray:
+    """``grouped_ffn`` with the GELU expert: ``expert_fn(e)`` returns float64 (W1 [H,d], b1 [H] or
+    None, W2 [d,H], b2 [d] or None)."""
+    x_rows = np.asarray(x_rows, np.float64)
+    y = np.zeros_like(x_rows)
+    for e in range(len(offsets) - 1):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            y[a:b] = gelu_mlp(x_rows[a:b], *expert_fn(e))
+    return y
+
+
 def grouped_ffn(x_rows: np.ndarray, offsets: np.ndarray, expert_fn) -> np.ndarray:
     """Every expert over its own contiguous bucket of rows; empty buckets do no work.
 
@@ -352,3 +394,20 @@ def layer_forward_tokens(x_rows, w_router, k, expert_fn, shared_fn=None, bias=No
         g, u, dn = expert_fn(int(e))
         out[t_sel] += w[t_sel, j_sel][:, None] * swiglu(x_rows[t_sel], g, u, dn)
     return dict(logits=L, idx=idx, w=w, out=out)
+
+
+def layer_forward_gelu(x, w_router, k, expert_fn, bias=None, routing="softmax"):
+    """The layer of the [MoE overview] §4.1 code with its two-layer GELU experts: routing, dispatch,
+    ``grouped_ffn_gelu`` and the weighted combine, no shared expert. ``expert_fn(e)`` as in
+    ``grouped_ffn_gelu``; ``bias`` and ``routing`` as in ``route`` (the listing's biased router
+    linear is the logit bias of softmax routing)."""
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    E = np.asarray(w_router).shape[0]
+    L, idx, w = route(x, w_router, k, bias, routing)
+    counts, offsets, perm_src, inv_perm = permute(idx, E)
+    x_rows = x[perm_src // k] if T else np.zeros((0, x.shape[1]))
+    y_perm = grouped_ffn_gelu(x_rows, offsets, expert_fn)
+    out = combine(y_perm, inv_perm, w, None)
+    return dict(logits=L, idx=idx, w=w, counts=counts, offsets=offsets, perm_src=perm_src,
+                inv_perm=inv_perm, y_perm=y_perm, out=out)

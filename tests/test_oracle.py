@@ -465,6 +465,99 @@ def test_load_stats_from_a_routing():
     assert abs(aux - 0.01 * sum((load[e] - 1 / 6) ** 2 for e in range(6))) < 1e-15
 
 
+# ------------------------------------------------------------------ GELU expert variant
+
+def test_gelu_known_values():
+    """GELU(z) = z Phi(z): Phi(0) = 1/2, Phi(1) and Phi(2) from the standard normal table; GELU(z) -
+    GELU(-z) = z (as Phi(z) + Phi(-z) = 1); against scipy's normal CDF and torch's exact GELU."""
+    assert oracle.gelu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(oracle.gelu(np.array([1.0, -1.0, 2.0])),
+                               [0.8413447460685429, -0.15865525393145707, 2 * 0.9772498680518208], rtol=1e-15)
+    z = np.linspace(-7, 7, 57)
+    np.testing.assert_allclose(oracle.gelu(z) - oracle.gelu(-z), z, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(oracle.gelu(z), z * scipy.special.ndtr(z), rtol=1e-14, atol=1e-300)
+    ref = torch.nn.functional.gelu(torch.from_numpy(z), approximate="none").numpy()
+    np.testing.assert_allclose(oracle.gelu(z), ref, rtol=1e-14, atol=1e-15)   # torch's 1 + erf cancels for z << 0
+
+
+def test_gelu_mlp_by_hand():
+    """Two rows through a 3 -> 2 -> 3 expert with both biases, in plain Python."""
+    X = [[0.5, -1.0, 2.0], [1.5, 0.25, -0.75]]
+    w1 = [[0.2, -0.4, 0.1], [-0.3, 0.5, 0.6]]
+    b1 = [0.05, -0.1]
+    w2 = [[1.0, -2.0], [0.5, 0.25], [-1.5, 0.75]]
+    b2 = [0.3, -0.2, 0.1]
+    got = oracle.gelu_mlp(np.array(X), np.array(w1), np.array(b1), np.array(w2), np.array(b2))
+    for r in range(2):
+        h = []
+        for o in range(2):
+            z = sum(X[r][i] * w1[o][i] for i in range(3)) + b1[o]
+            h.append(z * 0.5 * (1 + math.erf(z / math.sqrt(2))))
+        for o in range(3):
+            assert abs(got[r, o] - (sum(h[i] * w2[o][i] for i in range(2)) + b2[o])) < 1e-14
+
+
+def _gelu_experts(E, d, H, seed):
+    rng = np.random.default_rng(seed)
+    return [(rng.standard_normal((H, d)) / math.sqrt(d), rng.standard_normal(H) * 0.1,
+             rng.standard_normal((d, H)) / math.sqrt(H), rng.standard_normal(d) * 0.1) for _ in range(E)]
+
+
+def test_gelu_single_expert_layer_is_torch_linear_gelu_linear():
+    """E = k = 1: the layer is the listing's expert block itself (weight 1), built from torch modules."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((9, 6))
+    (w1, b1, w2, b2), = _gelu_experts(1, 6, 10, 6)
+    r = oracle.layer_forward_gelu(x, rng.standard_normal((1, 6)), 1, lambda e: (w1, b1, w2, b2))
+    blk = torch.nn.Sequential(torch.nn.Linear(6, 10), torch.nn.GELU(), torch.nn.Linear(10, 6)).double()
+    with torch.no_grad():
+        blk[0].weight.copy_(torch.from_numpy(w1)); blk[0].bias.copy_(torch.from_numpy(b1))
+        blk[2].weight.copy_(torch.from_numpy(w2)); blk[2].bias.copy_(torch.from_numpy(b2))
+        ref = blk(torch.from_numpy(x)).numpy()
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_gelu_layer_is_the_weighted_sum_over_the_selected_experts():
+    """Every token: sum over its k selected experts of weight x expert(x_t), experts from torch modules."""
+    rng = np.random.default_rng(7)
+    T, d, E, k, H = 13, 8, 5, 2, 12
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((E, d))
+    b = rng.standard_normal(E) * 0.3
+    ex = _gelu_experts(E, d, H, 8)
+    r = oracle.layer_forward_gelu(x, wg, k, lambda e: ex[e], b)
+    mods = []
+    for (w1, b1, w2, b2) in ex:
+        m = torch.nn.Sequential(torch.nn.Linear(d, H), torch.nn.GELU(), torch.nn.Linear(H, d)).double()
+        with torch.no_grad():
+            m[0].weight.copy_(torch.from_numpy(w1)); m[0].bias.copy_(torch.from_numpy(b1))
+            m[2].weight.copy_(torch.from_numpy(w2)); m[2].bias.copy_(torch.from_numpy(b2))
+        mods.append(m)
+    L = x @ wg.T + b
+    for t in range(T):
+        top = sorted(range(E), key=lambda e: (-L[t, e], e))[:k]
+        w = np.exp(L[t, top] - L[t, top].max())
+        w /= w.sum()
+        with torch.no_grad():
+            ref = sum(w[j] * mods[e](torch.from_numpy(x[t:t + 1])).numpy()[0] for j, e in enumerate(top))
+        np.testing.assert_allclose(r["out"][t], ref, rtol=1e-12, atol=1e-13)
+
+
+def _gelu_tanh(z):
+    z = np.asarray(z, np.float64)
+    return 0.5 * z * (1 + np.tanh(math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3)))
+
+
+def _gelu_mlp_without_b2(X, w1, b1, w2, b2):
+    return _GELU_MLP(X, w1, b1, w2, None)
+
+
+def _gelu_mlp_bias_after_activation(X, w1, b1, w2, b2):
+    X = np.asarray(X, np.float64)
+    H = om.gelu(X @ np.asarray(w1).T) + (0 if b1 is None else np.asarray(b1)[None, :])
+    return H @ np.asarray(w2).T + (0 if b2 is None else np.asarray(b2)[None, :])
+
+
 # ------------------------------------------------------------------ planted mistakes are caught
 
 def _plant(monkeypatch, name, fn):
@@ -566,6 +659,7 @@ def _load_over_tokens(counts, T, k, coef=0.01):
 
 
 _COMBINE = om.combine
+_GELU_MLP = om.gelu_mlp
 _PERMUTE = om.permute
 _SELECTION = om.selection_scores
 _ROUTE = om.route
@@ -596,6 +690,11 @@ MUTATIONS = {
     "dequantize_without_zero_point": ("dequantize", lambda q, s, z=0: np.asarray(q, np.float64) * s,
                                       test_quantization_example_from_the_pages),
     "load_over_tokens_not_slots": ("load_stats", _load_over_tokens, test_load_stats_closed_forms),
+    "gelu_tanh_approximation": ("gelu", _gelu_tanh, test_gelu_known_values),
+    "gelu_as_silu": ("gelu", lambda z: om.silu(z), test_gelu_known_values),
+    "gelu_expert_drops_output_bias": ("gelu_mlp", _gelu_mlp_without_b2,
+                                      test_gelu_single_expert_layer_is_torch_linear_gelu_linear),
+    "gelu_expert_bias_after_activation": ("gelu_mlp", _gelu_mlp_bias_after_activation, test_gelu_mlp_by_hand),
 }
 
 
