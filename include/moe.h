@@ -192,6 +192,30 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* x, const int32_t* per
                            const void* w_down, void* y, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * moe_grouped_ffn_gelu -- moe_grouped_ffn with the two-layer GELU expert of the overview
+ * article's layer code (section 4.1: Linear(d -> H), GELU, Linear(H -> d), each linear with a bias)
+ * in place of SwiGLU:
+ *   for each e and each row r in [expert_offsets[e], expert_offsets[e+1]):
+ *     src = perm_src ? perm_src[r] / k : r
+ *     h = GELU(w1[e] . x[src] + b1[e]),  GELU(z) = z * Phi(z) = z * erfc(-z / sqrt 2) / 2
+ *     y[r] = w2[e] . h + b2[e]
+ * bfloat16 layers only and weight_layout MOE_LAYOUT_ROWMAJOR or MOE_LAYOUT_FRAG16 (otherwise
+ * MOE_ERR_UNSUPPORTED). w1 [E, H, d] and w2 [E, d, H] are stored like w_gate and w_down; b1 [E, H]
+ * and b2 [E, d] are float32, or NULL for a zero bias. d_shared_hidden is ignored (routed experts
+ * only). The hidden activations live in the workspace (moe_workspace_bytes() of the same shape). A
+ * layer with these experts is moe_route, moe_permute, moe_grouped_ffn_gelu and moe_combine with
+ * shared_out NULL. Accumulation in float32; h is rounded to bfloat16 before the second linear and
+ * y once. Experts run as weight-streaming kernels at every batch size (the form decode needs).
+ */
+moe_status moe_grouped_ffn_gelu(const moe_shape* s, const void* x, const int32_t* perm_src,
+                                const int32_t* expert_offsets, const void* w1, const float* b1, const void* w2,
+                                const float* b2, void* y, void* workspace, size_t ws_bytes, void* stream);
+
+/* Kernel of one layer of moe_grouped_ffn_gelu for this shape (layer 0: the first linear and GELU,
+ * 1: the second linear), as the profiler names it; "" for an invalid shape or layer. */
+const char* moe_gelu_kernel_name(const moe_shape* s, int layer);
+
+/*
  * moe_combine -- back to token order and weighted merge (overview article section 2.2 step 4;
  * MoE-kernels page section 1.1: the shared expert's output is added for every token):
  *   out[t] = shared_out[t] + sum_{j<k} topk_w[t, j] * y_perm[inv_perm[t*k + j]]

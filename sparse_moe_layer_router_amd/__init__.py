@@ -62,6 +62,8 @@ _sigs = {
     "moe_permute": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_grouped_ffn": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_combine": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
+    "moe_grouped_ffn_gelu": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_gelu_kernel_name": (ctypes.c_char_p, [_S, ctypes.c_int]),
     "moe_layer_forward": (ctypes.c_int, [_S] + [_P] * 15 + [ctypes.c_size_t, _P]),
     "moe_layer_forward_timed": (ctypes.c_int, [_S] + [_P] * 15 + [ctypes.c_size_t, _P, _P]),
     "moe_stage_kernel_name": (ctypes.c_char_p, [_S, ctypes.c_int]),
@@ -136,6 +138,38 @@ def moe_grouped_ffn(shape, x, perm_src, expert_offsets, w_gate, w_up, w_down, y,
     _check("moe_grouped_ffn", _lib.moe_grouped_ffn(ctypes.byref(shape), _ptr(x), _ptr(perm_src),
                                                    _ptr(expert_offsets), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                                    _ptr(y), ws, nb, _stream(stream)))
+
+
+def moe_grouped_ffn_gelu(shape, x, perm_src, expert_offsets, w1, b1, w2, b2, y, workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check("moe_grouped_ffn_gelu", _lib.moe_grouped_ffn_gelu(ctypes.byref(shape), _ptr(x), _ptr(perm_src),
+                                                             _ptr(expert_offsets), _ptr(w1), _ptr(b1), _ptr(w2),
+                                                             _ptr(b2), _ptr(y), ws, nb, _stream(stream)))
+
+
+def gelu_layer_buffers(shape, device="cuda"):
+    """Intermediates of a layer with GELU experts: routing, dispatch and expert outputs, and the
+    workspace (hidden activations, logits, permutation scratch)."""
+    T, k, E, d = shape.T, shape.top_k, shape.n_experts, shape.d_model
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(idx=torch.empty(T, k, **i32), w=torch.empty(T, k, dtype=torch.float32, device=device),
+                counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32), perm_src=torch.empty(T * k, **i32),
+                inv_perm=torch.empty(T * k, **i32), y=torch.empty(T * k, d, dtype=torch.bfloat16, device=device),
+                workspace=allocate_workspace(shape, device))
+
+
+def moe_layer_forward_gelu(shape, x, w_router, logit_bias, w1, b1, w2, b2, out, buffers, stream=None):
+    """A layer with the two-layer GELU experts: moe_route, moe_permute, moe_grouped_ffn_gelu and
+    moe_combine (no shared expert) on `buffers` from gelu_layer_buffers."""
+    b = buffers
+    moe_route(shape, x, w_router, logit_bias, None, b["idx"], b["w"], b["workspace"], stream)
+    moe_permute(shape, b["idx"], b["counts"], b["offsets"], b["perm_src"], b["inv_perm"], b["workspace"], stream)
+    moe_grouped_ffn_gelu(shape, x, b["perm_src"], b["offsets"], w1, b1, w2, b2, b["y"], b["workspace"], stream)
+    moe_combine(shape, b["y"], b["inv_perm"], b["w"], None, out, stream)
+
+
+def moe_gelu_kernel_name(shape, layer: int) -> str:
+    return _lib.moe_gelu_kernel_name(ctypes.byref(shape), layer).decode()
 
 
 def moe_combine(shape, y_perm, inv_perm, topk_w, shared_out, out, stream=None):

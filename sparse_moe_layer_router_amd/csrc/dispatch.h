@@ -51,6 +51,28 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* inv_perm
                           const void* shared_out, void* out, int T, int k, int d, hipStream_t stream);
 const char* combine_kernel_name(int dtype, int k);
 
+// ---- two-layer GELU experts (bf16; row-major or fragment-tiled weights) ----------------------
+// Routed groups 0..E-1 take rows [offsets[g], offsets[g+1]) of the dispatched order (source token
+// perm_src[r] / k, or row r of x when perm_src is NULL). hid[r] = GELU(W1[g] x + b1[g]) (bf16,
+// [rows, H] row-major), y[r] = W2[g] hid[r] + b2[g] (bf16, [rows, d]); a NULL bias is zero.
+struct GeluGroups {
+  int layout;              // kRowMajor or kFrag16
+  int d, E, k, H, T;
+  long long rows;          // T*k
+  const int32_t* offsets;  // [E+1]
+  const int32_t* perm_src; // [rows] or NULL
+  const void* x;           // [T, d] (or [rows, d] when perm_src is NULL)
+  const void* w1;          // [E, H, d]
+  const float* b1;         // [E, H] or NULL
+  const void* w2;          // [E, d, H]
+  const float* b2;         // [E, d] or NULL
+  void* hid;               // [rows, H]
+  void* y;                 // [rows, d]
+};
+hipError_t launch_gelu_up(const GeluGroups& g, hipStream_t stream);
+hipError_t launch_gelu_down(const GeluGroups& g, hipStream_t stream);
+const char* gelu_kernel_name(const GeluGroups& g, bool up);
+
 // ---- weight packing (MOE_LAYOUT_FRAG16) and INT8 quantization (MOE_LAYOUT_INT8_FRAG) --------------
 hipError_t launch_pack_weights(const void* src, void* dst, long long n_mats, int rows, int cols, hipStream_t stream);
 size_t quantized_weight_bytes(long long n_mats, int rows, int cols);

@@ -184,6 +184,29 @@ moe::FfnGroups groups_for(const moe_shape& s, const void* x, const int32_t* perm
   return g;
 }
 
+moe::GeluGroups gelu_groups_for(const moe_shape& s, const void* x, const int32_t* perm_src, const int32_t* offsets,
+                                const void* w1, const float* b1, const void* w2, const float* b2, void* hid,
+                                void* y) {
+  moe::GeluGroups g{};
+  g.layout = s.weight_layout;
+  g.d = s.d_model;
+  g.E = s.n_experts;
+  g.k = s.top_k;
+  g.H = s.d_hidden;
+  g.T = s.T;
+  g.rows = (long long)s.T * s.top_k;
+  g.offsets = offsets;
+  g.perm_src = perm_src;
+  g.x = x;
+  g.w1 = w1;
+  g.b1 = b1;
+  g.w2 = w2;
+  g.b2 = b2;
+  g.hid = hid;
+  g.y = y;
+  return g;
+}
+
 moe_status ffn_impl(const moe::FfnGroups& g, int32_t* sched, const Events& ev, hipStream_t stream) {
   const moe::FfnPath path = moe::ffn_path(g);
   MOE_MARK(ev, MOE_STAGE_FFN_SCHEDULE, 0);
@@ -395,6 +418,37 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* x, const int32_t* per
   const moe::FfnGroups g = groups_for(routed, x, perm_src, expert_offsets, w_gate, w_up, w_down, nullptr, nullptr,
                                       nullptr, at(workspace, L.hid), y);
   return ffn_impl(g, (int32_t*)at(workspace, L.sched), Events{nullptr, nullptr}, (hipStream_t)stream);
+}
+
+moe_status moe_grouped_ffn_gelu(const moe_shape* s, const void* x, const int32_t* perm_src,
+                                const int32_t* expert_offsets, const void* w1, const float* b1, const void* w2,
+                                const float* b2, void* y, void* workspace, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_shape(s));
+  if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->weight_layout != MOE_LAYOUT_ROWMAJOR && s->weight_layout != MOE_LAYOUT_FRAG16) return MOE_ERR_UNSUPPORTED;
+  if (s->T == 0) return MOE_OK;
+  MOE_TRY(need(x, 16));
+  MOE_TRY(maybe(perm_src, 4));
+  MOE_TRY(need(expert_offsets, 4));
+  MOE_TRY(need(w1, 16));
+  MOE_TRY(maybe(b1, 4));
+  MOE_TRY(need(w2, 16));
+  MOE_TRY(maybe(b2, 4));
+  MOE_TRY(need(y, 16));
+  MOE_TRY(check_workspace(*s, workspace, ws_bytes));
+  const moe::GeluGroups g = gelu_groups_for(*s, x, perm_src, expert_offsets, w1, b1, w2, b2,
+                                            at(workspace, layout_of(*s).hid), y);
+  MOE_LAUNCH(moe::launch_gelu_up(g, (hipStream_t)stream));
+  MOE_LAUNCH(moe::launch_gelu_down(g, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+const char* moe_gelu_kernel_name(const moe_shape* s, int layer) {
+  if (check_shape(s) != MOE_OK || s->dtype != MOE_BF16 || (layer != 0 && layer != 1)) return "";
+  if (s->weight_layout != MOE_LAYOUT_ROWMAJOR && s->weight_layout != MOE_LAYOUT_FRAG16) return "";
+  const moe::GeluGroups g = gelu_groups_for(*s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                            nullptr, nullptr);
+  return moe::gelu_kernel_name(g, layer == 0);
 }
 
 moe_status moe_combine(const moe_shape* s, const void* y_perm, const int32_t* inv_perm, const float* topk_w,

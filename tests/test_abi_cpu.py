@@ -234,3 +234,38 @@ def test_pack_weights_validation():
     assert status_of(moe.moe_pack_weights, A + 8, B, 2, 32, 64) == moe.MOE_ERR_ALIGNMENT
     assert status_of(moe.moe_pack_weights, A, B, 0, 32, 64) == moe.MOE_OK
     assert status_of(moe.moe_pack_weights, A, B, -1, 32, 64) == moe.MOE_ERR_INVALID_ARG
+
+
+def gelu_args(**over):
+    args = dict(x=A, perm_src=A, expert_offsets=A, w1=A, b1=None, w2=A, b2=None, y=B, workspace=(A, 1 << 40),
+                stream=0)
+    args.update(over)
+    return args
+
+
+@pytest.mark.parametrize("shape,over,status", [
+    (dict(dtype=moe.MOE_F32), {}, moe.MOE_ERR_UNSUPPORTED),
+    (dict(weight_layout=moe.MOE_LAYOUT_INT8_FRAG), {}, moe.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=0), {}, moe.MOE_ERR_INVALID_ARG),
+    ({}, dict(w1=None), moe.MOE_ERR_INVALID_ARG),
+    ({}, dict(w2=A + 8), moe.MOE_ERR_ALIGNMENT),
+    ({}, dict(b1=A + 2), moe.MOE_ERR_ALIGNMENT),
+    ({}, dict(b2=A + 1), moe.MOE_ERR_ALIGNMENT),
+    ({}, dict(expert_offsets=None), moe.MOE_ERR_INVALID_ARG),
+    ({}, dict(y=None), moe.MOE_ERR_INVALID_ARG),
+    ({}, dict(workspace=None), moe.MOE_ERR_WORKSPACE),
+    ({}, dict(workspace=(A, 1024)), moe.MOE_ERR_WORKSPACE),
+    (dict(T=0), dict(x=None, perm_src=None, expert_offsets=None, w1=None, w2=None, y=None, workspace=None), moe.MOE_OK),
+])
+def test_gelu_ffn_validation(shape, over, status):
+    s = dsv3(**dict(dict(d_shared_hidden=0), **shape))
+    assert status_of(moe.moe_grouped_ffn_gelu, s, **gelu_args(**over)) == status
+
+
+def test_gelu_kernel_names():
+    assert moe.moe_gelu_kernel_name(dsv3(d_shared_hidden=0), 0) == "ffn_gelu_stream<1, 0, true>"
+    assert moe.moe_gelu_kernel_name(dsv3(T=256, weight_layout=moe.MOE_LAYOUT_FRAG16), 1) == \
+        "ffn_gelu_stream<2, 1, false>"
+    assert moe.moe_gelu_kernel_name(dsv3(), 2) == ""
+    assert moe.moe_gelu_kernel_name(dsv3(dtype=moe.MOE_F32), 0) == ""
+    assert moe.moe_gelu_kernel_name(dsv3(weight_layout=moe.MOE_LAYOUT_INT8_FRAG), 0) == ""
