@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--workload", default="dsv3_decode_t8")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=None)
+    p.add_argument("--expert", choices=["swiglu", "gelu"], default="swiglu",
+                   help="expert form: SwiGLU (with the shared expert), or the two-layer GELU expert with "
+                        "biased linears (moe_grouped_ffn_gelu; no shared expert)")
     p.add_argument("--layout", choices=["frag16", "rowmajor", "int8"], default="frag16",
                    help="expert weight layout (frag16: packed once at load time, before timing; int8: "
                         "per-row INT8 codes made once from the bf16 weights, before timing)")
@@ -192,6 +195,172 @@ def cpu_baseline(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8, int8=Fals
                       f"{' and quantization' if int8 else ''} excluded)"}
 
 
+# ------------------------------------------------------------------------ GELU expert variant
+def gelu_alg_bytes(cfg, counts_list):
+    """Algorithmic bytes of moe_grouped_ffn_gelu per call, averaged over the cycled batches: the
+    active experts' W1 and W2 (bf16) and biases (fp32), x read, hidden rows written and read, expert
+    rows written."""
+    T, d, H, k = cfg.T, cfg.d, cfg.H, cfg.k
+    rows = T * k
+    tot = 0
+    for counts in counts_list:
+        n_act = int((counts > 0).sum())
+        tot += n_act * (2 * 2 * H * d + 4 * (H + d)) + 2 * T * d + 2 * 2 * rows * H + 2 * rows * d
+    return tot / len(counts_list)
+
+
+def cpu_baseline_gelu(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8):
+    """The fp64 oracle of the GELU-expert layer on a bounded sample of tokens (weight generation
+    excluded; the bf16 -> fp64 conversion of the selected experts is timed)."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = None
+    E, H, d = cfg.E, cfg.H, cfg.d
+    rng = np.random.default_rng(1)
+    tokens = np.sort(rng.choice(cfg.T, size=min(n_tokens, cfg.T), replace=False))
+    x = oracle.widen(host.x[tokens], cfg.dtype)
+    wg = oracle.widen(host.w_router, cfg.dtype)
+    _, idx, _ = oracle.route(x, wg, cfg.k, host.router_bias, cfg.routing)
+    sid = lambda i: synth.stream_id(synth.K_GELU, i)  # noqa: E731
+    raw = {int(e): (synth.normal_host((H, d), 0, sid(0), 1.0 / np.sqrt(d), "bf16", first=int(e) * H * d),
+                    synth.normal_host((H,), 0, sid(2), 0.1, "f32", first=int(e) * H),
+                    synth.normal_host((d, H), 0, sid(1), 1.0 / np.sqrt(H), "bf16", first=int(e) * d * H),
+                    synth.normal_host((d,), 0, sid(3), 0.1, "f32", first=int(e) * d))
+           for e in np.unique(idx)}   # untimed
+    expert_fn = lambda e: (oracle.widen(raw[e][0], "bf16"), raw[e][1].astype(np.float64),  # noqa: E731
+                           oracle.widen(raw[e][2], "bf16"), raw[e][3].astype(np.float64))
+    reps, total = 0, 0.0
+    while reps < max_repeats and (reps == 0 or total < min_seconds):
+        t0 = time.perf_counter()
+        ref = oracle.layer_forward_gelu(x, wg, cfg.k, expert_fn, host.router_bias, cfg.routing)
+        total += time.perf_counter() - t0
+        reps += 1
+    assert ref["out"].shape == (len(tokens), d)
+    return {"value": round(len(tokens) * reps / total, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(tokens)} of {cfg.T} tokens of {cfg.name} with GELU experts, {reps} passes in "
+                      f"{total:.1f} s (routing, bf16->fp64 conversion of the {len(raw)} selected experts, "
+                      f"GELU experts, combine; expert weight generation excluded)"}
+
+
+def main_gelu(args, cfg, K, W):
+    """The layer with two-layer GELU experts: moe_route, moe_permute, moe_grouped_ffn_gelu and
+    moe_combine per step; the timed steps carry hipEvents around the expert stage (its two kernels)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import sparse_moe_layer_router_amd as moe
+
+    if cfg.dtype != "bf16" or args.layout == "int8":
+        print("--expert gelu runs bf16 layers with row-major or fragment-tiled weights", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    E, H, d = cfg.E, cfg.H, cfg.d
+    t_setup = time.perf_counter()
+    w1 = torch.empty(E, H, d, dtype=torch.bfloat16, device=dev)
+    w2 = torch.empty(E, d, H, dtype=torch.bfloat16, device=dev)
+    b1 = torch.empty(E, H, dtype=torch.float32, device=dev)
+    b2 = torch.empty(E, d, dtype=torch.float32, device=dev)
+    for i, (t, std) in enumerate(((w1, 1.0 / np.sqrt(d)), (w2, 1.0 / np.sqrt(H)), (b1, 0.1), (b2, 0.1))):
+        synth.normal_device(t, 0, synth.stream_id(synth.K_GELU, i), std)
+    layout = moe.MOE_LAYOUT_ROWMAJOR
+    if args.layout == "frag16" and d % 32 == 0 and H % 32 == 0:
+        p1, p2 = torch.empty_like(w1), torch.empty_like(w2)
+        moe.moe_pack_weights(w1, p1, E, H, d)
+        moe.moe_pack_weights(w2, p2, E, d, H)
+        torch.cuda.synchronize()
+        w1, w2, layout = p1, p2, moe.MOE_LAYOUT_FRAG16
+        torch.cuda.empty_cache()
+    host = synth.host_small_inputs(cfg, 0)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    w_router = up(host.w_router)
+    bias = torch.from_numpy(host.router_bias).to(dev) if host.router_bias is not None else None
+    xs = [up(host.x)] + [up(synth.normal_host((cfg.T, d), 100 + b, synth.stream_id(synth.K_X), 1.0, "bf16"))
+                         for b in range(1, N_BATCHES)]
+    shape = moe.make_shape(cfg.T, d, E, cfg.k, H, 0, "bf16", layout, cfg.routing)
+    bufs = [moe.gelu_layer_buffers(shape, dev) for _ in range(N_BATCHES)]
+    outs = [torch.empty(cfg.T, d, dtype=torch.bfloat16, device=dev) for _ in range(N_BATCHES)]
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    def step(i, ev=None, e0=0):
+        bf, x = bufs[i % N_BATCHES], xs[i % N_BATCHES]
+        moe.moe_route(shape, x, w_router, bias, None, bf["idx"], bf["w"], bf["workspace"], stream)
+        moe.moe_permute(shape, bf["idx"], bf["counts"], bf["offsets"], bf["perm_src"], bf["inv_perm"],
+                        bf["workspace"], stream)
+        if ev is not None:
+            ev.record(e0, stream.cuda_stream)
+        moe.moe_grouped_ffn_gelu(shape, x, bf["perm_src"], bf["offsets"], w1, b1, w2, b2, bf["y"],
+                                 bf["workspace"], stream)
+        if ev is not None:
+            ev.record(e0 + 1, stream.cuda_stream)
+        moe.moe_combine(shape, bf["y"], bf["inv_perm"], bf["w"], None, outs[i % N_BATCHES], stream)
+
+    for i in range(max(W, N_BATCHES)):
+        step(i)
+    torch.cuda.synchronize()
+    # per-step distribution (cold caches: a 1 GiB evicting copy between steps, outside the events)
+    n_dist = 30
+    flush_src = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+    ev_d = HipEvents(2 * n_dist)
+    for i in range(n_dist):
+        flush_dst.copy_(flush_src)
+        ev_d.record(2 * i, stream.cuda_stream)
+        step(i)
+        ev_d.record(2 * i + 1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    step_ms = [ev_d.elapsed_ms(2 * i, 2 * i + 1) for i in range(n_dist)]
+    ev_d.close()
+    del flush_src, flush_dst
+    # timed steps: events around the expert stage only
+    ev = HipEvents(2 * K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, ev, 2 * i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ffn_ms = sum(ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)) / K
+    ev.close()
+    counts_np = [bf["counts"].cpu().numpy() for bf in bufs]
+    byt = gelu_alg_bytes(cfg, counts_np)
+    achieved = byt / (ffn_ms * 1e-3) / 1e9
+    kname = moe.moe_gelu_kernel_name(shape, 0) + " + " + moe.moe_gelu_kernel_name(shape, 1)
+    ms_per_step = elapsed * 1e3 / K
+    line = {
+        "metric": METRIC, "value": round(cfg.T * K / elapsed, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Philox normal draws; random-init weights of the named layer shape)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": d, "n_experts": E, "top_k": cfg.k, "d_hidden": H,
+                   "d_shared_hidden": 0, "expert": "gelu (two linears with bias)", "routing": cfg.routing,
+                   "weight_layout": "frag16" if layout == moe.MOE_LAYOUT_FRAG16 else "rowmajor",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "kernel": kname, "kernel_ms": round(ffn_ms, 4),
+                     "traffic": traffic_for(cfg.name + "_gelu", kname)},
+        "layer": {"ffn_alg_bytes": int(byt), "active_experts_mean": float(np.mean([(c > 0).sum() for c in counts_np]))},
+        "step_ms_events": {"mean": round(statistics.mean(step_ms), 4), "std": round(statistics.pstdev(step_ms), 4),
+                           "median": round(statistics.median(step_ms), 4), "steps": n_dist,
+                           "between_steps": "1 GiB device copy (L2 and Infinity Cache evicted)"},
+        "setup_s": round(t_setup, 1),
+    }
+    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_gelu(
+        cfg, host, args.cpu_sample_tokens or (8 if cfg.E > 8 else 16))
+    print(json.dumps(line), flush=True)
+
+
 # ----------------------------------------------------------------------------------------- main
 def main():
     args = parse()
@@ -210,6 +379,8 @@ def main():
     prefill = cfg.T * cfg.k / cfg.E > 32
     K = args.steps if args.steps is not None else (30 if prefill else 50)
     W = args.warmup if args.warmup is not None else 5
+    if args.expert == "gelu":
+        return main_gelu(args, cfg, K, W)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dt = {"bf16": torch.bfloat16, "f32": torch.float32}[cfg.dtype]

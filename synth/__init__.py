@@ -29,6 +29,7 @@ LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
 # stream kinds: stream id = kind * 2**40 + index
 K_X, K_WG, K_GATE, K_UP, K_DOWN, K_SGATE, K_SUP, K_SDOWN, K_REDRAW, K_SBIAS = range(1, 11)
+K_GELU = 16   # GELU expert variant: index 0 W1 [E, H, d], 1 W2 [E, d, H], 2 b1 [E, H], 3 b2 [E, d]
 _KSHIFT = 1 << 40
 
 

@@ -20,8 +20,6 @@ import sparse_moe_layer_router_amd as moe
 
 pytestmark = pytest.mark.gpu
 
-K_GELU = 16   # stream kind of the GELU expert weights (clear of the kinds synth uses)
-
 CONFIGS = [
     synth.LayerConfig("gelu_decode", 8, 256, 16, 4, 128, 0, "bf16"),
     synth.LayerConfig("gelu_ragged", 300, 264, 16, 2, 200, 0, "bf16"),          # d % 32 and H % 16 != 0
@@ -35,10 +33,10 @@ CASES = [(c, moe.MOE_LAYOUT_ROWMAJOR) for c in CONFIGS] + \
 def gelu_weights(cfg, seed, with_bias=True):
     """Host copies (bf16 bits / float32) of W1, b1, W2, b2."""
     E, H, d = cfg.E, cfg.H, cfg.d
-    w1 = synth.normal_host((E, H, d), seed, synth.stream_id(K_GELU, 0), 1.0 / np.sqrt(d), "bf16")
-    w2 = synth.normal_host((E, d, H), seed, synth.stream_id(K_GELU, 1), 1.0 / np.sqrt(H), "bf16")
-    b1 = synth.normal_host((E, H), seed, synth.stream_id(K_GELU, 2), 0.1, "f32") if with_bias else None
-    b2 = synth.normal_host((E, d), seed, synth.stream_id(K_GELU, 3), 0.1, "f32") if with_bias else None
+    w1 = synth.normal_host((E, H, d), seed, synth.stream_id(synth.K_GELU, 0), 1.0 / np.sqrt(d), "bf16")
+    w2 = synth.normal_host((E, d, H), seed, synth.stream_id(synth.K_GELU, 1), 1.0 / np.sqrt(H), "bf16")
+    b1 = synth.normal_host((E, H), seed, synth.stream_id(synth.K_GELU, 2), 0.1, "f32") if with_bias else None
+    b2 = synth.normal_host((E, d), seed, synth.stream_id(synth.K_GELU, 3), 0.1, "f32") if with_bias else None
     return w1, b1, w2, b2
 
 
@@ -99,7 +97,7 @@ def test_gelu_ffn_on_given_rows_without_bias(layout):
     w1, b1, w2, b2 = device_weights(cfg, hw, layout)
     counts = np.array([0, 17, 1, 0, 22, 0])
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    rows = synth.normal_host((cfg.T, cfg.d), 7, synth.stream_id(K_GELU, 9), 1.0, "bf16")
+    rows = synth.normal_host((cfg.T, cfg.d), 7, synth.stream_id(synth.K_GELU, 9), 1.0, "bf16")
     s = shape_of(cfg, layout)
     y = torch.full((cfg.T, cfg.d), float("nan"), dtype=torch.bfloat16, device="cuda")
     moe.moe_grouped_ffn_gelu(s, G.to_dev(rows, "bf16"), None, torch.from_numpy(offsets).cuda(), w1, b1, w2, b2, y,
