@@ -80,3 +80,21 @@ def test_traffic_summary_is_ignored_once_its_sources_change(tmp_path, monkeypatc
     assert bench.traffic_for("w", kernel.replace("<1, 2>", "<2, 2>")) is None   # another kernel: no file
     src.write_text("__global__ void k() { /* changed */ }\n")
     assert bench.traffic_for("w", kernel) is None
+
+
+def test_gelu_expert_stage_bytes():
+    """W1 and W2 of every active expert (bf16) with their fp32 biases, x read once, the hidden rows
+    written and read back, the expert rows written."""
+    cfg = synth.CONFIG_BY_NAME["dsv3_decode_t256"]
+    T, d, E, k, H = cfg.T, cfg.d, cfg.E, cfg.k, cfg.H
+    counts = np.ones(E, dtype=np.int64)
+    counts[:6] = 0
+    want = (E - 6) * (2 * H * d * 2 + 4 * (H + d)) + 2 * T * d + 2 * (2 * T * k * H) + 2 * T * k * d
+    assert bench.gelu_alg_bytes(cfg, [counts]) == want
+
+
+def test_gelu_bench_refuses_int8_weights_before_touching_a_device():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--expert", "gelu", "--layout", "int8"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    assert "--expert gelu" in r.stderr
