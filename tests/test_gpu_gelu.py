@@ -125,3 +125,46 @@ def test_gelu_layer_is_deterministic_and_empty_batch_is_a_no_op():
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
     s0 = moe.make_shape(0, cfg.d, cfg.E, cfg.k, cfg.H, 0, "bf16", moe.MOE_LAYOUT_FRAG16)
     moe.moe_grouped_ffn_gelu(s0, None, None, None, None, None, None, None, None, None)
+
+
+@pytest.mark.parametrize("name,n_sample", [("dsv3_decode_t8", None), ("dsv3_decode_t256", 6)])
+def test_gelu_layer_full_decode_size(name, n_sample):
+    """The DeepSeek-V3-shaped decode layer with GELU experts (d 7168, 256 experts of hidden 2048,
+    top-8, no shared expert), fragment-tiled weights drawn in device memory as the benchmark does;
+    the oracle regenerates on the host only the experts the checked tokens select."""
+    base = synth.CONFIG_BY_NAME[name]
+    cfg = synth.LayerConfig(name + "_gelu", base.T, base.d, base.E, base.k, base.H, 0, "bf16")
+    E, H, d = cfg.E, cfg.H, cfg.d
+    host = synth.host_small_inputs(cfg, 0)
+    helpers.screen_gaps(host)
+    w = [torch.empty(E, H, d, dtype=torch.bfloat16, device="cuda"), torch.empty(E, d, H, dtype=torch.bfloat16, device="cuda"),
+         torch.empty(E, H, dtype=torch.float32, device="cuda"), torch.empty(E, d, dtype=torch.float32, device="cuda")]
+    for i, (t, std) in enumerate(zip(w, (1.0 / np.sqrt(d), 1.0 / np.sqrt(H), 0.1, 0.1))):
+        synth.normal_device(t, 0, synth.stream_id(synth.K_GELU, i), std)
+    p1, p2 = torch.empty_like(w[0]), torch.empty_like(w[1])
+    moe.moe_pack_weights(w[0], p1, E, H, d)
+    moe.moe_pack_weights(w[1], p2, E, d, H)
+    del w[:2]
+    b1, b2 = w
+    s = shape_of(cfg, moe.MOE_LAYOUT_FRAG16)
+    buf = moe.gelu_layer_buffers(s)
+    out = torch.empty(cfg.T, d, dtype=torch.bfloat16, device="cuda")
+    moe.moe_layer_forward_gelu(s, G.to_dev(host.x, "bf16"), G.to_dev(host.w_router, "bf16"), None, p1, b1, p2, b2,
+                               out, buf)
+    torch.cuda.synchronize()
+    del p1, p2
+    tokens = np.arange(cfg.T) if n_sample is None else \
+        np.unique(np.concatenate([[0, cfg.T - 1], np.random.default_rng(0).choice(cfg.T, n_sample - 2, replace=False)]))
+    sid = lambda i: synth.stream_id(synth.K_GELU, i)  # noqa: E731
+
+    def expert(e):
+        return (oracle.widen(synth.normal_host((H, d), 0, sid(0), 1.0 / np.sqrt(d), "bf16", first=e * H * d), "bf16"),
+                synth.normal_host((H,), 0, sid(2), 0.1, "f32", first=e * H).astype(np.float64),
+                oracle.widen(synth.normal_host((d, H), 0, sid(1), 1.0 / np.sqrt(H), "bf16", first=e * d * H), "bf16"),
+                synth.normal_host((d,), 0, sid(3), 0.1, "f32", first=e * d).astype(np.float64))
+
+    ref = oracle.layer_forward_gelu(oracle.widen(host.x[tokens], "bf16"), oracle.widen(host.w_router, "bf16"), cfg.k,
+                                    expert, None, cfg.routing)
+    np.testing.assert_array_equal(np.sort(buf["idx"].cpu().numpy()[tokens], 1), np.sort(ref["idx"], 1))
+    ok, err, bound = G.tolerance_ok(G.to_f64(out)[tokens], ref["out"])
+    assert ok, (err, bound)
