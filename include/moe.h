@@ -144,7 +144,10 @@ const char* moe_status_string(moe_status st);
  * the logits before both selection and softmax; sigmoid: added to the sigmoid scores for the
  * selection only); logits_out [T, E] float32 or NULL (softmax: the logits with the bias added;
  * sigmoid: the plain logits); topk_idx [T, k] int32 and topk_w [T, k] float32 are required outputs.
- * NaN logits rank below every other score.
+ * Scores are compared as floats with a NaN score taken as -inf, so every token gets k distinct ids
+ * in [0, E) whatever the logits hold (a NaN ties with -inf, and the tie goes to the lower id).
+ * Softmax weights of selected -inf or NaN scores are 0 while at least one selected score is
+ * finite; with none finite the weights are unspecified.
  */
 moe_status moe_route(const moe_shape* s, const void* x, const void* w_router, const float* logit_bias,
                      float* logits_out, int32_t* topk_idx, float* topk_w, void* workspace, size_t ws_bytes,

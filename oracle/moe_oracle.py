@@ -60,7 +60,8 @@ import numpy as np
 
 __all__ = [
     "widen", "router_logits", "select_topk", "softmax_selected", "route", "permute", "silu",
-    "swiglu", "grouped_ffn", "combine", "layer_forward", "layer_forward_tokens", "topk_gap",
+    "swiglu", "grouped_ffn", "combine", "layer_forward", "layer_forward_tokens", "layer_forward_tokens_many",
+    "topk_gap",
     "logistic", "selection_scores", "sigmoid_weights_selected", "ROUTINGS",
     "quantize", "dequantize", "quantize_rows_int8", "dequantize_rows_int8", "load_stats",
     "gelu", "gelu_mlp", "grouped_ffn_gelu", "layer_forward_gelu",
@@ -205,9 +206,11 @@ def dequantize(q, s, z=0):
 def quantize_rows_int8(w: np.ndarray):
     """Per-output-channel symmetric INT8 of a [..., rows, cols] weight: z = 0 and one scale per
     row (output channel), s = max|w_row| / 127, codes round(w / s) in [-127, 127]; an all-zero row
-    gets s = 0 and zero codes. The codes are integers decided by floating point, so they are
-    computed in float32 (the precision the weights are stored in and the GPU quantizes in):
-    s = fl32(max / 127), q = rint(fl32(w / s)). Returns (q int8, s float32 [..., rows])."""
+    gets s = 0 and zero codes. The codes are integers decided by floating point, and the pages fix
+    no precision for that decision; the weights are stored in bf16 and the GPU kernel quantizes in
+    float32, so the oracle takes the same decision in float32 (fl32 = rounding to float32):
+    s = fl32(max / 127), q = rint(fl32(w / s)). The dequantized weight q * s that the layer uses
+    is then exact in float64. Returns (q int8, s float32 [..., rows])."""
     w32 = np.asarray(w, np.float64).astype(np.float32)
     m = np.abs(w32).max(axis=-1)
     s = (m / np.float32(127.0)).astype(np.float32)
@@ -394,6 +397,33 @@ def layer_forward_tokens(x_rows, w_router, k, expert_fn, shared_fn=None, bias=No
         g, u, dn = expert_fn(int(e))
         out[t_sel] += w[t_sel, j_sel][:, None] * swiglu(x_rows[t_sel], g, u, dn)
     return dict(logits=L, idx=idx, w=w, out=out)
+
+
+def layer_forward_tokens_many(cases, expert_fn, shared_fn=None):
+    """``layer_forward_tokens`` for several token samples that share the expert weights (each with
+    its own router weight, k, bias and routing rule), visiting every expert once for all of them:
+    on the CPU the expert weights, not the rows, are the cost. ``cases`` is a list of
+    (x_rows, w_router, k, bias, routing); returns one dict (logits, idx, w, out) per case, each
+    equal to what ``layer_forward_tokens`` gives for that case on its own."""
+    res = []
+    for x_rows, w_router, k, bias, routing in cases:
+        x_rows = np.asarray(x_rows, np.float64)
+        L, idx, w = route(x_rows, w_router, k, bias, routing)
+        res.append(dict(logits=L, idx=idx, w=w, out=np.zeros_like(x_rows), x=x_rows))
+    if shared_fn is not None and any(r["x"].shape[0] for r in res):
+        sw = shared_fn()
+        for r in res:
+            r["out"] += swiglu(r["x"], *sw)
+    experts = sorted(set().union(*(set(np.unique(r["idx"]).tolist()) for r in res))) if res else []
+    for e in experts:
+        g, u, dn = expert_fn(int(e))
+        for r in res:
+            t_sel, j_sel = np.nonzero(r["idx"] == e)
+            if t_sel.size:
+                r["out"][t_sel] += r["w"][t_sel, j_sel][:, None] * swiglu(r["x"][t_sel], g, u, dn)
+    for r in res:
+        del r["x"]
+    return res
 
 
 def layer_forward_gelu(x, w_router, k, expert_fn, bias=None, routing="softmax"):

@@ -8,6 +8,23 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+def _keep_freed_memory_mapped():
+    """The oracle checks of the full-size layers widen one expert's weights at a time to float64
+    (hundreds of MB). glibc serves such blocks with fresh mmap pages and returns them on free, so
+    every expert pays the page faults again, several times the cost of its arithmetic. Serving them
+    from the heap and never trimming it keeps the pages (the peak stays what one expert needs)."""
+    try:
+        import ctypes
+        libc = ctypes.CDLL("libc.so.6")
+        libc.mallopt(-3, 1 << 30)          # M_MMAP_THRESHOLD: blocks below 1 GiB come from the heap
+        libc.mallopt(-1, (1 << 62) - 1)    # M_TRIM_THRESHOLD: never hand the heap top back
+    except (OSError, AttributeError):     # pragma: no cover - not glibc
+        pass
+
+
+_keep_freed_memory_mapped()
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs a real MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: full-size cases (minutes)")

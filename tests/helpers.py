@@ -8,6 +8,7 @@ import oracle
 import synth
 
 MIN_GAP = 1e-4   # tokens whose k-th and (k+1)-th router scores are closer than this are redrawn
+M_TILE_ROWS = 320  # rows of one M-tile of the grouped GEMM
 
 
 def screen_gaps(inp: synth.HostInputs, min_gap: float = MIN_GAP, max_rounds: int = 64) -> int:
@@ -74,3 +75,46 @@ def shared_fn_host(cfg: synth.LayerConfig, seed: int, int8: bool = False):
         return box["w"]
 
     return fn
+
+
+def structural_tokens(idx, T, Hs, n_random=8, seed=0):
+    """The first and last token of every M-tile of every expert bucket (a bucket lists the tokens
+    that chose the expert in increasing order) and of the shared expert's rows (token order), plus
+    ``n_random`` seeded tokens."""
+    idx = np.asarray(idx)
+    toks = set()
+    for e in np.unique(idx):
+        t_e = np.nonzero((idx == e).any(axis=1))[0]
+        for m0 in range(0, len(t_e), M_TILE_ROWS):
+            toks.update((int(t_e[m0]), int(t_e[min(m0 + M_TILE_ROWS, len(t_e)) - 1])))
+    if Hs:
+        for m0 in range(0, T, M_TILE_ROWS):
+            toks.update((m0, min(m0 + M_TILE_ROWS, T) - 1))
+    rng = np.random.default_rng(seed)
+    toks.update(int(t) for t in rng.choice(T, size=min(n_random, T), replace=False))
+    return np.array(sorted(toks), dtype=np.int64)
+
+
+def assert_tile_edges_covered(idx, counts, tokens, T, Hs):
+    """Every expert with rows (by the GPU's counts) has the first and last row of each of its
+    M-tiles among the checked tokens, and so has every M-tile of the shared expert's rows."""
+    idx, counts = np.asarray(idx), np.asarray(counts)
+    chosen = set(np.asarray(tokens).tolist())
+    missing = []
+    for e in np.nonzero(counts)[0]:
+        t_e = np.nonzero((idx == e).any(axis=1))[0]
+        assert len(t_e) == counts[e], (e, len(t_e), counts[e])
+        for m0 in range(0, int(counts[e]), M_TILE_ROWS):
+            for r in (m0, min(m0 + M_TILE_ROWS, int(counts[e])) - 1):
+                if int(t_e[r]) not in chosen:
+                    missing.append((int(e), r))
+    if Hs:
+        for m0 in range(0, T, M_TILE_ROWS):
+            for r in (m0, min(m0 + M_TILE_ROWS, T) - 1):
+                if r not in chosen:
+                    missing.append(("shared", r))
+    assert not missing, missing[:10]
+    n_tiles = sum((int(c) + M_TILE_ROWS - 1) // M_TILE_ROWS for c in counts) + (
+        (T + M_TILE_ROWS - 1) // M_TILE_ROWS if Hs else 0)
+    print(f"  checked tokens {len(chosen)} cover both edges of all {n_tiles} M-tiles "
+          f"({int((counts > 0).sum())} experts{' + shared' if Hs else ''})", flush=True)

@@ -1,12 +1,18 @@
 """HIP path vs the oracle at the full layer sizes the throughput is measured on (needs an MI355X).
 
 DeepSeek-V3-shaped layer (d 7168, 256 routed experts of hidden 2048 + one shared, top-8) at
-T = 8, 256 and 8192 (and with sigmoid routing at T = 8 and 4096), and the Mixtral-shaped skewed layer (d 4096, 8 experts of hidden 14336,
-top-2, Zipf router bias) at T = 4096. The 22.5 GB DeepSeek weight set is drawn once in device
-memory; the oracle regenerates on the host exactly the experts it needs. Routing and permutation
-are checked bit-exactly on the GPU logits for every token; outputs are checked for every token at
-T = 8 and for a seeded sample of tokens otherwise (a token's output depends on its row only); where
-the grouped GEMM runs, the sample also holds the tokens at the edges of the largest expert buckets.
+T = 8, 256 and 8192 (and with sigmoid routing at T = 8 and 4096), and the Mixtral-shaped skewed
+layer (d 4096, 8 experts of hidden 14336, top-2, Zipf router bias) at T = 4096. The 22.5 GB
+DeepSeek weight set is drawn once in device memory; the oracle regenerates on the host exactly the
+experts it needs, once for all cases that share them.
+
+Routing and permutation are checked bit-exactly on the GPU logits for every token. Outputs are
+checked for every token at T = 8 and 256. Where the grouped GEMM runs (T >= 2048), the checked
+tokens are chosen by the GEMM's structure: the first and the last row of every M-tile (320 rows) of
+every expert bucket and of the shared expert's rows, plus a seeded random sample. Every tile of the
+grouped GEMM (each (group, N-tile, M-tile), whichever XCD range holds it) then produces at least
+two checked rows, at its ragged edges; the test asserts that coverage from the GPU's own counts.
+A token's output depends on its own row only, so the oracle computes just those rows.
 """
 
 import dataclasses
@@ -18,108 +24,161 @@ import torch
 import oracle
 import synth
 from tests import gpu_util as G
+from tests.helpers import M_TILE_ROWS, assert_tile_edges_covered, structural_tokens
 from tests.test_gpu_parity import check_logits_close, check_routing_on_gpu_logits
 
 import sparse_moe_layer_router_amd as moe
 
 pytestmark = pytest.mark.gpu
 
+GEMM_MIN_TOKENS = 2048  # DeepSeek-shaped layers above this many tokens run the grouped GEMM
+LAYOUTS = {"frag16": moe.MOE_LAYOUT_FRAG16, "rowmajor": moe.MOE_LAYOUT_ROWMAJOR}
+
+
+def tokens_for(cfg, idx):
+    if cfg.T < GEMM_MIN_TOKENS:
+        return np.arange(cfg.T)
+    return structural_tokens(idx, cfg.T, cfg.Hs)
+
+
+def run_cases(cases, weights_for):
+    """Run every (config, layout) case on the GPU and keep what the checks need."""
+    runs = {}
+    for cfg, lname in cases:
+        key = f"{cfg.name}-{lname}"
+        print(f"[{key}] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} H={cfg.H} Hs={cfg.Hs} routing={cfg.routing} "
+              f"moe_layer_forward", flush=True)
+        L = G.make_layer(cfg, weights=weights_for(lname), layout=LAYOUTS[lname])
+        r = G.run_layer(L)
+        idx = r.idx.cpu().numpy()
+        tokens = tokens_for(cfg, idx)
+        rows = G.to_f64(r.out[torch.from_numpy(tokens).to(r.out.device)])
+        runs[key] = dict(cfg=cfg, L=L, r=r, idx=idx, counts=r.counts.cpu().numpy(), tokens=tokens,
+                         out=rows, redraws=sum(L.host.redraws.values()))
+        r.out = None   # the checked rows are kept on the host
+    return runs
+
+
+def attach_oracle(runs, expert_fn, shared_fn):
+    """One oracle pass over the experts for all runs: runs of the same workload share their inputs,
+    so the union of their checked tokens is computed once."""
+    by_name = {}
+    for key, run in runs.items():
+        by_name.setdefault(run["cfg"].name, []).append(key)
+    names = sorted(by_name)
+    toks = {n: np.unique(np.concatenate([runs[k]["tokens"] for k in by_name[n]])) for n in names}
+    cases = []
+    for n in names:
+        L = runs[by_name[n][0]]["L"]
+        x, wg, b = G.oracle_inputs(L)
+        cases.append((x[toks[n]], wg, L.cfg.k, b, L.cfg.routing))
+    seen = []
+
+    def expert_fn_progress(e):   # a line every 32 experts: the weights are regenerated on the host
+        seen.append(e)
+        if len(seen) % 32 == 0:
+            print(f"  oracle: {len(seen)} experts", flush=True)
+        return expert_fn(e)
+
+    refs = oracle.layer_forward_tokens_many(cases, expert_fn_progress, shared_fn)
+    for n, ref in zip(names, refs):
+        for key in by_name[n]:
+            pos = np.searchsorted(toks[n], runs[key]["tokens"])
+            runs[key]["ref_idx"] = ref["idx"][pos]
+            runs[key]["ref_out"] = ref["out"][pos]
+
+
+DSV3 = synth.CONFIG_BY_NAME["dsv3_decode_t8"]
+DSV3_CASES = [(synth.CONFIG_BY_NAME[n], lay)
+              for n in ("dsv3_decode_t8", "dsv3_decode_t256", "dsv3_prefill_t8192", "dsv3_sigmoid_decode_t8")
+              for lay in ("frag16", "rowmajor")]
+DSV3_CASES.append((dataclasses.replace(synth.CONFIG_BY_NAME["dsv3_sigmoid_decode_t8"], name="dsv3_sigmoid_t4096",
+                                       T=4096), "frag16"))
+DSV3_IDS = [f"{c.name}-{lay}" for c, lay in DSV3_CASES]
+
 
 @pytest.fixture(scope="module")
 def dsv3_weights():
-    cfg = synth.CONFIG_BY_NAME["dsv3_decode_t8"]
-    w = G.make_weights(cfg, 0, host_copy=False)
-    yield {moe.MOE_LAYOUT_ROWMAJOR: w, moe.MOE_LAYOUT_FRAG16: G.packed_weights(w),
-           moe.MOE_LAYOUT_INT8_FRAG: G.int8_weights(w)}
+    w = G.make_weights(DSV3, 0, host_copy=False)
+    yield {"rowmajor": w, "frag16": G.packed_weights(w), "int8": G.int8_weights(w)}
     del w
     torch.cuda.empty_cache()
 
 
-def sampled_check(L, r, tokens):
-    x, wg, b = G.oracle_inputs(L)
-    ref = oracle.layer_forward_tokens(x[tokens], wg, L.cfg.k, L.expert_fn(cache=False), L.shared_fn(), b,
-                                      L.cfg.routing)
-    np.testing.assert_array_equal(np.sort(r.idx.cpu().numpy()[tokens], 1), np.sort(ref["idx"], 1))
-    ok, err, bound = G.tolerance_ok(G.to_f64(r.out)[tokens], ref["out"])
+@pytest.fixture(scope="module")
+def dsv3_runs(dsv3_weights):
+    runs = run_cases(DSV3_CASES, lambda lname: dsv3_weights[lname])
+    print("[dsv3] oracle pass over the selected experts of every case", flush=True)
+    L0 = next(iter(runs.values()))["L"]
+    attach_oracle(runs, L0.expert_fn(cache=False), L0.shared_fn())
+    yield runs
+    runs.clear()
+    torch.cuda.empty_cache()
+
+
+def check_run(run):
+    cfg, L, r = run["cfg"], run["L"], run["r"]
+    print(f"[{cfg.name}] gap-screen redraws: {run['redraws']}", flush=True)
+    check_logits_close(L, r)
+    check_routing_on_gpu_logits(L, r)
+    if cfg.T >= GEMM_MIN_TOKENS:
+        assert_tile_edges_covered(run["idx"], run["counts"], run["tokens"], cfg.T, cfg.Hs)
+    np.testing.assert_array_equal(np.sort(run["idx"][run["tokens"]], 1), np.sort(run["ref_idx"], 1))
+    ok, err, bound = G.tolerance_ok(run["out"], run["ref_out"])
     assert ok, (err, bound)
 
 
-def sample_tokens(T, n, seed=0):
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=n - 2, replace=False)]))
-
-
-def bucket_edge_tokens(idx, n_buckets=3, tile_rows=320):
-    """Tokens whose rows sit at the ragged edges of the largest expert buckets of the grouped GEMM
-    (its M-tiles hold 320 rows): each bucket's last row and, where the bucket is longer than one
-    M-tile, the first and last rows of its second M-tile. A bucket lists its tokens in increasing
-    order, so a token's row in it is the number of smaller tokens that chose the same expert."""
-    idx = np.asarray(idx)
-    counts = np.bincount(idx.ravel(), minlength=int(idx.max()) + 1)
-    toks = []
-    for e in np.argsort(-counts, kind="stable")[:n_buckets]:
-        t_e = np.nonzero((idx == e).any(axis=1))[0]
-        toks.append(t_e[-1])
-        if len(t_e) > tile_rows:
-            toks += [t_e[tile_rows], t_e[min(2 * tile_rows, len(t_e)) - 1]]
-    return np.unique(np.asarray(toks, dtype=np.int64))
-
-
-def gemm_sample(T, n, idx):
-    """A seeded sample of tokens plus the bucket-edge tokens of the GPU's routing."""
-    return np.union1d(sample_tokens(T, n), bucket_edge_tokens(idx.cpu().numpy()))
-
-
-@pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_FRAG16, moe.MOE_LAYOUT_ROWMAJOR], ids=["frag16", "rowmajor"])
-@pytest.mark.parametrize("name,n_sample", [("dsv3_decode_t8", None), ("dsv3_decode_t256", 12),
-                                           ("dsv3_prefill_t8192", 8), ("dsv3_sigmoid_decode_t8", None)])
-def test_dsv3_layer(name, n_sample, layout, dsv3_weights):
-    cfg = synth.CONFIG_BY_NAME[name]
-    L = G.make_layer(cfg, weights=dsv3_weights[layout], layout=layout)
-    print(f"[{name}] gap-screen redraws: {sum(L.host.redraws.values())}", flush=True)
-    r = G.run_layer(L)
-    check_logits_close(L, r)
-    check_routing_on_gpu_logits(L, r)
-    if n_sample is None:
-        tokens = np.arange(cfg.T)
-    elif cfg.T >= 2048:   # grouped GEMM experts: also the rows at the bucket edges
-        tokens = gemm_sample(cfg.T, n_sample, r.idx)
-    else:
-        tokens = sample_tokens(cfg.T, n_sample)
-    sampled_check(L, r, tokens)
+@pytest.mark.timeout(1200)   # the first test also runs the shared fixture: every case + one oracle pass
+@pytest.mark.parametrize("case", DSV3_IDS)
+def test_dsv3_layer(case, dsv3_runs):
+    check_run(dsv3_runs[case])
 
 
 @pytest.mark.parametrize("name,n_sample", [("dsv3_decode_t8", None), ("dsv3_decode_t256", 12)])
 def test_dsv3_layer_int8_weights(name, n_sample, dsv3_weights):
     """Per-row INT8 expert weights at the decode sizes, against the oracle on the dequantized weights."""
     cfg = synth.CONFIG_BY_NAME[name]
-    L = G.make_layer(cfg, weights=dsv3_weights[moe.MOE_LAYOUT_INT8_FRAG], layout=moe.MOE_LAYOUT_INT8_FRAG)
+    print(f"[{name}-int8] moe_layer_forward", flush=True)
+    L = G.make_layer(cfg, weights=dsv3_weights["int8"], layout=moe.MOE_LAYOUT_INT8_FRAG)
     r = G.run_layer(L)
     check_logits_close(L, r)
     check_routing_on_gpu_logits(L, r)
-    tokens = np.arange(cfg.T) if n_sample is None else sample_tokens(cfg.T, n_sample)
-    sampled_check(L, r, tokens)
+    if n_sample is None:
+        tokens = np.arange(cfg.T)
+    else:
+        rng = np.random.default_rng(0)
+        tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, size=n_sample - 2, replace=False)]))
+    x, wg, b = G.oracle_inputs(L)
+    ref = oracle.layer_forward_tokens(x[tokens], wg, cfg.k, L.expert_fn(cache=False), L.shared_fn(), b,
+                                      cfg.routing)
+    np.testing.assert_array_equal(np.sort(r.idx.cpu().numpy()[tokens], 1), np.sort(ref["idx"], 1))
+    ok, err, bound = G.tolerance_ok(G.to_f64(r.out)[tokens], ref["out"])
+    assert ok, (err, bound)
 
 
-def test_dsv3_sigmoid_layer_router_gemm_size(dsv3_weights):
-    """Sigmoid routing at 4096 tokens: the router GEMM (no bias in its epilogue), the one-wave-per-
-    token top-k and the grouped GEMM experts, on the packed weights."""
-    cfg = dataclasses.replace(synth.CONFIG_BY_NAME["dsv3_sigmoid_decode_t8"], name="dsv3_sigmoid_t4096", T=4096)
-    L = G.make_layer(cfg, weights=dsv3_weights[moe.MOE_LAYOUT_FRAG16], layout=moe.MOE_LAYOUT_FRAG16)
-    r = G.run_layer(L)
-    check_logits_close(L, r)
-    check_routing_on_gpu_logits(L, r)
-    sampled_check(L, r, gemm_sample(cfg.T, 8, r.idx))
+SKEWED = synth.CONFIG_BY_NAME["skewed_mixtral_t4096"]
 
 
-@pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_FRAG16, moe.MOE_LAYOUT_ROWMAJOR], ids=["frag16", "rowmajor"])
-def test_skewed_mixtral_layer(layout):
-    cfg = synth.CONFIG_BY_NAME["skewed_mixtral_t4096"]
-    L = G.make_layer(cfg, layout=layout)
-    r = G.run_layer(L)
-    counts = r.counts.cpu().numpy()
+@pytest.fixture(scope="module")
+def skewed_runs():
+    w = G.make_weights(SKEWED, 0, host_copy=False)
+    weights = {"rowmajor": w, "frag16": G.packed_weights(w)}
+    runs = run_cases([(SKEWED, lay) for lay in ("frag16", "rowmajor")], lambda lname: weights[lname])
+    print("[skewed] oracle pass over the 8 experts", flush=True)
+    L0 = next(iter(runs.values()))["L"]
+    attach_oracle(runs, L0.expert_fn(cache=False), L0.shared_fn())
+    yield runs, weights
+    runs.clear()
+    del weights, w
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("layout", ["frag16", "rowmajor"])
+def test_skewed_mixtral_layer(layout, skewed_runs):
+    runs, _ = skewed_runs
+    run = runs[f"{SKEWED.name}-{layout}"]
+    counts = run["counts"]
     print(f"[skewed] expert counts {counts.tolist()}", flush=True)
-    assert counts[0] > 0.4 * cfg.T * cfg.k       # the Zipf head expert is the straggler
-    check_logits_close(L, r)
-    check_routing_on_gpu_logits(L, r)
-    sampled_check(L, r, gemm_sample(cfg.T, 8, r.idx))
+    assert counts[0] > 0.4 * SKEWED.T * SKEWED.k       # the Zipf head expert is the straggler
+    check_run(run)

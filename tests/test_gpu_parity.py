@@ -243,6 +243,42 @@ def test_route_ties_go_to_lower_index():
     np.testing.assert_array_equal(idx.cpu().numpy(), oracle.select_topk(lg.cpu().numpy().astype(np.float64), k))
 
 
+@pytest.mark.parametrize("T", [8, 40])   # the fused decode tail (T <= 16) and the one-wave-per-token kernel
+def test_route_nan_and_inf_scores(T):
+    """Logit biases holding NaN and -inf, through the whole layer: a NaN score orders like -inf
+    (ties to the lower id), every token still gets k distinct ids, the selected -inf / NaN scores
+    get weight 0 and the output stays finite. The ids equal the oracle's selection on the GPU's
+    logits with NaN read as -inf."""
+    d, E, k = 64, 16, 12
+    x = torch.randn(T, d, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16).cuda()
+    wr = (torch.randn(E, d, generator=torch.Generator().manual_seed(3)) / 8).to(torch.bfloat16).cuda()
+    bias = torch.zeros(E, dtype=torch.float32)
+    bias[[0, 7, 12]] = -float("inf")
+    bias[[3, 9, 14]] = float("nan")        # 10 finite scores: 2 of the 6 others are selected
+    bias = bias.cuda()
+    H = 64
+    s = moe.make_shape(T, d, E, k, H, 0, "bf16")
+    gen = torch.Generator().manual_seed(4)
+    wgt, wup = ((torch.randn(E, H, d, generator=gen) / 8).to(torch.bfloat16).cuda() for _ in range(2))
+    wdn = (torch.randn(E, d, H, generator=gen) / 8).to(torch.bfloat16).cuda()
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    lg = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    out = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    moe.moe_layer_forward(s, x, wr, bias, wgt, wup, wdn, None, None, None, out, idx, w, None, lg,
+                          moe.allocate_workspace(s))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    ids, wt, L = idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy().astype(np.float64)
+    assert np.isnan(L[:, [3, 9, 14]]).all() and np.isneginf(L[:, [0, 7, 12]]).all()
+    assert all(len(set(r)) == k for r in ids.tolist()) and ids.min() >= 0 and ids.max() < E
+    assert (ids[:, 10:] == [0, 3]).all()    # the two lowest ids of the -inf / NaN group
+    Ln = np.where(np.isnan(L), -np.inf, L)
+    np.testing.assert_array_equal(ids, oracle.select_topk(Ln, k))
+    np.testing.assert_allclose(wt, oracle.softmax_selected(Ln, ids), rtol=0, atol=1e-5)
+    assert (wt[:, 10:] == 0).all()
+
+
 @pytest.mark.parametrize("routing", ["softmax", "sigmoid"])
 @pytest.mark.parametrize("E", [1, 3, 64, 65, 128, 200, 256, 300, 512, 777, 1024])
 def test_topk_tie_heavy_every_lane_width(E, routing):

@@ -135,6 +135,48 @@ def test_topk_matches_torch_topk_and_is_monotone_invariant():
     np.testing.assert_array_equal(idx, oracle.select_topk(scipy.special.softmax(L, axis=1), 8))
 
 
+def test_topk_gap_by_hand():
+    """The screening margin is the k-th largest score minus the (k+1)-th largest, per token.
+    Row [3, 2, 1.5, 0]: k=1 -> 3-2 = 1, k=2 -> 2-1.5 = 0.5, k=3 -> 1.5-0 = 1.5. Row [3, 1, 2, 2]
+    (unsorted, with a tie inside): k=1 -> 1, k=2 -> 0 (a tie at the cut), k=3 -> 2-1 = 1. With
+    k = E nothing is left unselected, so no tie can change the selection: the margin is infinite."""
+    L = np.array([[3.0, 2.0, 1.5, 0.0], [3.0, 1.0, 2.0, 2.0]])
+    np.testing.assert_array_equal(oracle.topk_gap(L, 1), [1.0, 1.0])
+    np.testing.assert_array_equal(oracle.topk_gap(L, 2), [0.5, 0.0])
+    np.testing.assert_array_equal(oracle.topk_gap(L, 3), [1.5, 1.0])
+    assert np.all(np.isinf(oracle.topk_gap(L, 4))) and np.all(oracle.topk_gap(L, 4) > 0)
+    # negative scores and a single token
+    np.testing.assert_array_equal(oracle.topk_gap(np.array([[-4.0, -1.0, -2.5]]), 1), [1.5])
+
+
+def test_topk_gap_is_the_smallest_selected_minus_largest_unselected():
+    """Brute force: for the selected set K (the k largest), the margin equals
+    min_{i in K} s_i - max_{j not in K} s_j, and a permutation of the experts leaves it unchanged."""
+    rng = np.random.default_rng(21)
+    S = rng.standard_normal((50, 9))
+    for k in range(1, 9):
+        gap = oracle.topk_gap(S, k)
+        for t in range(S.shape[0]):
+            sel = set(oracle.select_topk(S[t:t + 1], k)[0].tolist())
+            lo = min(S[t, i] for i in sel)
+            hi = max(S[t, j] for j in range(9) if j not in sel)
+            assert gap[t] == lo - hi
+        perm = rng.permutation(9)
+        np.testing.assert_array_equal(oracle.topk_gap(S[:, perm], k), gap)
+    assert (oracle.topk_gap(S, 3) > 0).all()
+
+
+def test_topk_gap_on_sigmoid_selection_scores():
+    """Sigmoid routing screens on the scores that decide its selection, sigmoid(l) + b. Logits all
+    zero and bias [0.3, 0.1, 0.2, 0]: scores [0.8, 0.6, 0.7, 0.5], so k = 2 leaves a margin of
+    0.7 - 0.6 = 0.1; without the bias every score is 0.5 and the margin is 0."""
+    L = np.zeros((1, 4))
+    b = np.array([0.3, 0.1, 0.2, 0.0])
+    gap = oracle.topk_gap(oracle.selection_scores(L, "sigmoid", b), 2)
+    np.testing.assert_allclose(gap, [0.1], rtol=0, atol=1e-15)
+    assert oracle.topk_gap(oracle.selection_scores(L, "sigmoid", None), 2)[0] == 0.0
+
+
 def test_softmax_over_k_is_renormalised_full_softmax():
     rng = np.random.default_rng(5)
     L = rng.standard_normal((40, 16)) * 3
@@ -280,6 +322,36 @@ def test_token_sampled_forward_matches_full_forward():
     part = oracle.layer_forward_tokens(x[rows], wg, 3, lambda e: ex[e], lambda: sh)
     np.testing.assert_allclose(part["out"], full["out"][rows], rtol=1e-12, atol=1e-13)
     np.testing.assert_array_equal(part["idx"], full["idx"][rows])
+
+
+def test_token_sets_sharing_experts_match_separate_full_forwards():
+    """Several token samples with their own routers, k, biases and routing rules, run with one visit
+    per expert, give for each sample what its own full layer gives on those rows."""
+    rng = np.random.default_rng(8)
+    E, d, H = 8, 12, 10
+    x1, wg1, ex = screened(rng, 14, d, E, 3, H)
+    x2, wg2, _ = screened(rng, 9, d, E, 2, H)
+    x3 = rng.standard_normal((6, d))
+    wg3 = rng.standard_normal((E, d)) / math.sqrt(d)
+    b3 = rng.standard_normal(E) * 0.05
+    sh = (rng.standard_normal((7, d)), rng.standard_normal((7, d)), rng.standard_normal((d, 7)))
+    visits = []
+
+    def efn(e):
+        visits.append(e)
+        return ex[e]
+
+    cases = [(x1[[0, 5, 13]], wg1, 3, None, "softmax"), (x2, wg2, 2, None, "softmax"),
+             (x3, wg3, 4, b3, "sigmoid"), (x1[:0], wg1, 3, None, "softmax")]
+    many = oracle.layer_forward_tokens_many(cases, efn, lambda: sh)
+    assert len(visits) == len(set(visits))      # each expert generated once
+    full = [oracle.layer_forward(x1, wg1, 3, lambda e: ex[e], lambda: sh)["out"][[0, 5, 13]],
+            oracle.layer_forward(x2, wg2, 2, lambda e: ex[e], lambda: sh)["out"],
+            oracle.layer_forward(x3, wg3, 4, lambda e: ex[e], lambda: sh, b3, "sigmoid")["out"],
+            np.zeros((0, d))]
+    for r, f in zip(many, full):
+        np.testing.assert_allclose(r["out"], f, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(many[2]["idx"], oracle.route(x3, wg3, 4, b3, "sigmoid")[1])
 
 
 def test_empty_batch():
@@ -653,6 +725,27 @@ def _quant_cols(w):
     return q.astype(np.int8), (np.abs(w32).max(-1) / np.float32(127.0)).astype(np.float32)
 
 
+def _gap_one_past(L, k):
+    """Margin measured one place too far down: (k+1)-th minus (k+2)-th score."""
+    s = -np.sort(-np.asarray(L, np.float64), axis=1)
+    out = np.full(s.shape[0], np.inf)
+    if k + 1 < s.shape[1]:
+        out = s[:, k] - s[:, k + 1]
+    return out
+
+
+def _gap_one_short(L, k):
+    """Margin measured one place too high: (k-1)-th minus k-th score (the first gap for k = 1)."""
+    s = -np.sort(-np.asarray(L, np.float64), axis=1)
+    if k >= s.shape[1]:
+        return np.full(s.shape[0], np.inf)
+    return s[:, max(k - 2, 0)] - s[:, max(k - 1, 1)]
+
+
+def _gap_always_inf(L, k):
+    return np.full(np.asarray(L).shape[0], np.inf)
+
+
 def _load_over_tokens(counts, T, k, coef=0.01):
     load = np.asarray(counts, np.float64) / T
     return load, coef * float(((load - 1.0 / len(load)) ** 2).sum())
@@ -690,6 +783,9 @@ MUTATIONS = {
     "dequantize_without_zero_point": ("dequantize", lambda q, s, z=0: np.asarray(q, np.float64) * s,
                                       test_quantization_example_from_the_pages),
     "load_over_tokens_not_slots": ("load_stats", _load_over_tokens, test_load_stats_closed_forms),
+    "topk_gap_one_place_too_far": ("topk_gap", _gap_one_past, test_topk_gap_by_hand),
+    "topk_gap_one_place_too_high": ("topk_gap", _gap_one_short, test_topk_gap_by_hand),
+    "topk_gap_never_rejects": ("topk_gap", _gap_always_inf, test_topk_gap_is_the_smallest_selected_minus_largest_unselected),
     "gelu_tanh_approximation": ("gelu", _gelu_tanh, test_gelu_known_values),
     "gelu_as_silu": ("gelu", lambda z: om.silu(z), test_gelu_known_values),
     "gelu_expert_drops_output_bias": ("gelu_mlp", _gelu_mlp_without_b2,
