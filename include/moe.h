@@ -54,7 +54,8 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = 2, /* dtype or size outside the supported range */
   MOE_ERR_ALIGNMENT = 3,   /* d_model / hidden sizes or pointers not aligned as required */
   MOE_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than moe_workspace_bytes() */
-  MOE_ERR_HIP = 5          /* a kernel launch or event record failed */
+  MOE_ERR_HIP = 5,         /* a kernel launch or event record failed */
+  MOE_ERR_TOO_LARGE = 6    /* the shape needs more than moe_layer_forward_noalloc's fixed scratch */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -240,6 +241,25 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* w_ro
                              const void* w_shared_gate, const void* w_shared_up, const void* w_shared_down,
                              void* out, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
                              float* logits_out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_layer_forward_noalloc -- moe_layer_forward with no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. The intermediates live in a fixed device array of MOE_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per GPU, held until the process ends; the call itself allocates and
+ * frees nothing. Shapes whose moe_workspace_bytes() exceed that size return MOE_ERR_TOO_LARGE
+ * (64 MiB holds the DeepSeek-V3-shaped decode layer up to T = 401 tokens). The current device must
+ * be the device of `stream` (else MOE_ERR_INVALID_ARG); the first call on a device looks up that
+ * device's address of the array, so make it outside stream capture. Every call on one GPU uses the
+ * same array and leaves its contents behind: calls that overlap on one GPU (other streams, other
+ * threads) race, so serialize them. Arguments and results otherwise as moe_layer_forward.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_layer_forward_noalloc(const moe_shape* s, const void* x, const void* w_router,
+                                     const float* logit_bias, const void* w_gate, const void* w_up,
+                                     const void* w_down, const void* w_shared_gate, const void* w_shared_up,
+                                     const void* w_shared_down, void* out, int32_t* topk_idx_out,
+                                     float* topk_w_out, int32_t* counts_out, float* logits_out, void* stream);
 
 /*
  * Kernel stages of moe_layer_forward, for per-kernel timing. moe_layer_forward_timed() is

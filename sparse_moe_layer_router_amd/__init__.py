@@ -21,7 +21,9 @@ if not os.path.exists(LIB_PATH):
                       "(hipcc, gfx950). There is no CPU fallback.")
 _lib = ctypes.CDLL(LIB_PATH)
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
+(MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
+ MOE_ERR_TOO_LARGE) = range(7)
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20   # fixed device scratch of moe_layer_forward_noalloc
 MOE_F32, MOE_BF16 = 0, 1
 MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_FRAG16, MOE_LAYOUT_INT8_FRAG = 0, 1, 2
 MOE_ROUTING_SOFTMAX, MOE_ROUTING_SIGMOID = 0, 1
@@ -66,6 +68,7 @@ _sigs = {
     "moe_gelu_kernel_name": (ctypes.c_char_p, [_S, ctypes.c_int]),
     "moe_layer_forward": (ctypes.c_int, [_S] + [_P] * 15 + [ctypes.c_size_t, _P]),
     "moe_layer_forward_timed": (ctypes.c_int, [_S] + [_P] * 15 + [ctypes.c_size_t, _P, _P]),
+    "moe_layer_forward_noalloc": (ctypes.c_int, [_S] + [_P] * 15),   # 14 tensors + the stream
     "moe_stage_kernel_name": (ctypes.c_char_p, [_S, ctypes.c_int]),
     "moe_pack_weights": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
     "moe_quantize_weights": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
@@ -191,6 +194,16 @@ def moe_layer_forward(shape, x, w_router, logit_bias, w_gate, w_up, w_down, w_sh
     _check("moe_layer_forward", _lib.moe_layer_forward(*_layer_args(
         shape, x, w_router, logit_bias, w_gate, w_up, w_down, w_shared_gate, w_shared_up, w_shared_down, out,
         topk_idx_out, topk_w_out, counts_out, logits_out, workspace, stream)))
+
+
+def moe_layer_forward_noalloc(shape, x, w_router, logit_bias, w_gate, w_up, w_down, w_shared_gate, w_shared_up,
+                              w_shared_down, out, topk_idx_out=None, topk_w_out=None, counts_out=None,
+                              logits_out=None, stream=None):
+    """moe_layer_forward on the library's fixed per-GPU scratch: no workspace argument."""
+    _check("moe_layer_forward_noalloc", _lib.moe_layer_forward_noalloc(
+        ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        _ptr(w_shared_gate), _ptr(w_shared_up), _ptr(w_shared_down), _ptr(out), _ptr(topk_idx_out),
+        _ptr(topk_w_out), _ptr(counts_out), _ptr(logits_out), _stream(stream)))
 
 
 def moe_layer_forward_timed(shape, x, w_router, logit_bias, w_gate, w_up, w_down, w_shared_gate, w_shared_up,

@@ -318,6 +318,7 @@ const char* moe_status_string(moe_status st) {
     case MOE_ERR_ALIGNMENT: return "misaligned size or pointer";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_TOO_LARGE: return "shape needs more than the fixed no-allocation scratch";
   }
   return "unknown status";
 }

@@ -269,3 +269,18 @@ def test_gelu_kernel_names():
     assert moe.moe_gelu_kernel_name(dsv3(), 2) == ""
     assert moe.moe_gelu_kernel_name(dsv3(dtype=moe.MOE_F32), 0) == ""
     assert moe.moe_gelu_kernel_name(dsv3(weight_layout=moe.MOE_LAYOUT_INT8_FRAG), 0) == ""
+
+
+def test_noalloc_validation():
+    """The no-allocation layer refuses shapes beyond its fixed scratch and invalid shapes before
+    touching a device, and returns at once for an empty batch."""
+    big = dsv3(T=8192, weight_layout=moe.MOE_LAYOUT_FRAG16)
+    assert moe.moe_workspace_bytes(big) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    args = dict(layer(big))
+    del args["workspace"]
+    assert status_of(moe.moe_layer_forward_noalloc, big, **args) == moe.MOE_ERR_TOO_LARGE
+    assert moe.moe_workspace_bytes(dsv3(T=401)) <= moe.MOE_NOALLOC_SCRATCH_BYTES < moe.moe_workspace_bytes(dsv3(T=402))
+    assert status_of(moe.moe_layer_forward_noalloc, dsv3(top_k=300), **args) == moe.MOE_ERR_INVALID_ARG
+    empty = {k: None for k in args if k != "stream"}
+    assert status_of(moe.moe_layer_forward_noalloc, dsv3(T=0), **empty, stream=0) == moe.MOE_OK
+    assert "no-allocation" in moe.moe_status_string(moe.MOE_ERR_TOO_LARGE)
