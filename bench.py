@@ -12,7 +12,12 @@ each timed step, and its algorithmic bytes or flops per launch), the per-stage b
 untimed pass with events around every stage), and the CPU oracle timed on a bounded sample of the
 same workload on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+The default workload is the DeepSeek-V3-shaped prefill chunk (T = 8192, the compute-bound half of
+the metric, against the bf16 MFMA peak). The same run then measures the same layer and weights at
+the decode sizes T = 8 and T = 256 (the HBM-bound half) and carries them under "decode".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode]
+                       [--no-cpu-baseline] [--layout frag16|rowmajor|int8] [--expert swiglu|gelu]
 """
 
 from __future__ import annotations
@@ -41,8 +46,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
-    p.add_argument("--workload", default="dsv3_decode_t8")
+    p.add_argument("--workload", default="dsv3_prefill_t8192")
+    p.add_argument("--no-decode", action="store_true",
+                   help="skip the decode sub-records (the same layer at T = 8 and 256) of a prefill run")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ceilings", action="store_true", help="skip the measured read and MFMA ceilings")
+    p.add_argument("--ceilings", action="store_true",
+                   help="only measure the read-stream, copy and MFMA ceilings of this GPU (one JSON line)")
     p.add_argument("--cpu-sample-tokens", type=int, default=None)
     p.add_argument("--expert", choices=["swiglu", "gelu"], default="swiglu",
                    help="expert form: SwiGLU (with the shared expert), or the two-layer GELU expert with "
@@ -189,6 +199,7 @@ def cpu_baseline(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8, int8=Fals
         reps += 1
     assert ref["out"].shape == (len(tokens), cfg.d)
     return {"value": round(len(tokens) * reps / total, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sampled": True, "sample_tokens": int(len(tokens)), "workload_tokens": cfg.T,
             "sample": f"{len(tokens)} of {cfg.T} tokens of {cfg.name}, {reps} passes in {total:.1f} s (routing, "
                       f"{'INT8' if int8 else cfg.dtype}->fp64 conversion of the {len(raw)} selected experts"
                       f"{' + shared' if shared_raw else ''}, SwiGLU, combine; expert weight generation"
@@ -242,6 +253,7 @@ def cpu_baseline_gelu(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8):
         reps += 1
     assert ref["out"].shape == (len(tokens), d)
     return {"value": round(len(tokens) * reps / total, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sampled": True, "sample_tokens": int(len(tokens)), "workload_tokens": cfg.T,
             "sample": f"{len(tokens)} of {cfg.T} tokens of {cfg.name} with GELU experts, {reps} passes in "
                       f"{total:.1f} s (routing, bf16->fp64 conversion of the {len(raw)} selected experts, "
                       f"GELU experts, combine; expert weight generation excluded)"}
@@ -361,33 +373,71 @@ def main_gelu(args, cfg, K, W):
     print(json.dumps(line), flush=True)
 
 
-# ----------------------------------------------------------------------------------------- main
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (expert-parallel "
-              "all-to-all is out of scope); run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+# ------------------------------------------------------------------------------- measured roofs
+def measure_ceilings(dev, read_gib=4, mfma_iters=40000, reps=7):
+    """What this GPU sustains, from the library's probes (include/moe_calib.h), timed with HIP
+    events on the launch stream (medians over ``reps``): a streaming read of a ``read_gib`` GiB
+    buffer with and without the non-temporal hint, a device copy (read + write), and a register-only
+    bf16 MFMA loop, two waves per SIMD, on random and on constant operands, with the shader clock
+    each ran at (from the counters each wave reads at its start and end)."""
     import torch
-
-    import synth
     import sparse_moe_layer_router_amd as moe
 
-    cfg = synth.CONFIG_BY_NAME[args.workload]
-    prefill = cfg.T * cfg.k / cfg.E > 32
-    K = args.steps if args.steps is not None else (30 if prefill else 50)
-    W = args.warmup if args.warmup is not None else 5
-    if args.expert == "gelu":
-        return main_gelu(args, cfg, K, W)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[cfg.dtype]
-    es = 2 if cfg.dtype == "bf16" else 4
+    stream = torch.cuda.current_stream(dev)
+    nbytes = read_gib << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).random_()
+    sink_r = torch.empty(moe.MOE_CALIB_READ_BLOCKS, dtype=torch.int32, device=dev)
+    ev = HipEvents(2 * reps)
 
-    t_setup = time.perf_counter()
-    # weights: drawn directly in device memory (same generator streams as the host oracle)
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        for i in range(reps):
+            ev.record(2 * i, stream.cuda_stream)
+            fn()
+            ev.record(2 * i + 1, stream.cuda_stream)
+        torch.cuda.synchronize()
+        return statistics.median(ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps))
+
+    out = {}
+    for nt in (True, False):
+        ms = timed(lambda: moe.moe_calib_read_stream(buf, sink_r, nt, stream))
+        out["read_nontemporal_GBps" if nt else "read_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    half = buf[: buf.numel() // 2]
+    dst = torch.empty_like(half)
+    ms = timed(lambda: dst.copy_(half))
+    out["copy_GBps"] = round(2 * half.numel() * 4 / (ms * 1e-3) / 1e9, 1)   # read + write
+    del buf, half, dst
+    n_ops = moe.MOE_CALIB_MFMA_BLOCKS * 512 * 16
+    sink_m = torch.empty(moe.MOE_CALIB_MFMA_BLOCKS, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(moe.MOE_CALIB_MFMA_BLOCKS * 8 * 4, dtype=torch.int64, device=dev)
+    flops = moe.MOE_CALIB_MFMA_BLOCKS * 8 * mfma_iters * 8 * 32768
+    gen = torch.Generator(device=dev).manual_seed(0)
+    for name, ops in (("random", torch.randn(n_ops, generator=gen, device=dev).to(torch.bfloat16)),
+                      ("constant", torch.ones(n_ops, dtype=torch.bfloat16, device=dev))):
+        ms = timed(lambda: moe.moe_calib_mfma(ops, mfma_iters, sink_m, clocks, stream))
+        c = clocks.view(-1, 4).cpu().double()
+        ghz = ((c[:, 2] - c[:, 0]) / (c[:, 3] - c[:, 1]) * 0.1).median().item()   # real-time counter: 100 MHz
+        out[f"mfma_bf16_{name}_TFLOPs"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        out[f"mfma_bf16_{name}_clock_GHz"] = round(ghz, 3)
+    ev.close()
+    out["note"] = (f"read/copy: {read_gib} GiB; MFMA: {moe.MOE_CALIB_MFMA_BLOCKS} workgroups x 8 waves, "
+                   f"{mfma_iters} x 8 32x32x16 bf16 MFMAs per wave; medians of {reps} event-timed runs")
+    torch.cuda.empty_cache()
+    return out
+
+
+# ----------------------------------------------------------------------------------------- main
+DECODE_SUBRECORDS = ("dsv3_decode_t8", "dsv3_decode_t256")   # same layer and weights as the prefill chunk
+
+
+def make_weights(args, cfg, dev):
+    """Expert weights of ``cfg`` drawn in device memory and, before any timing, put in the layout the
+    bench runs (fragment-tiled or per-row INT8): one-time preparation, like a model load."""
+    import torch
+    import synth
+    import sparse_moe_layer_router_amd as moe
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[cfg.dtype]
     E, H, d = cfg.E, cfg.H, cfg.d
     wgt = torch.empty(E, H, d, dtype=dt, device=dev)
     wup = torch.empty(E, H, d, dtype=dt, device=dev)
@@ -403,7 +453,7 @@ def main():
             print(f"--layout int8 needs a bf16 layer with d, H, Hs multiples of 64 ({cfg.name} is not)",
                   file=sys.stderr)
             sys.exit(2)
-        quant = moe.quantize_expert_weights(wgt, wup, wdn, shared)   # one-time preparation, untimed
+        quant = moe.quantize_expert_weights(wgt, wup, wdn, shared)
         torch.cuda.synchronize()
         wgt, wup, wdn = quant[:3]
         shared = tuple(quant[3:]) if shared else None
@@ -411,7 +461,6 @@ def main():
         del quant
         torch.cuda.empty_cache()
     elif args.layout == "frag16" and cfg.dtype == "bf16" and cfg.d % 32 == 0 and cfg.H % 32 == 0 and cfg.Hs % 32 == 0:
-        # one-time weight preparation (a model load step), outside the timed region
         packed = moe.pack_expert_weights(wgt, wup, wdn, shared)
         torch.cuda.synchronize()
         wgt, wup, wdn = packed[:3]
@@ -419,6 +468,24 @@ def main():
         layout = moe.MOE_LAYOUT_FRAG16
         del packed
         torch.cuda.empty_cache()
+    return (wgt, wup, wdn, shared), layout
+
+
+def run_layer_bench(cfg, K, W, weights, layout, dev):
+    """One workload on resident weights: warm-up, a per-stage event pass, a cold-cache distribution
+    pass, then K timed steps with events around the dominant kernel only. Returns the measurement
+    (without the CPU baseline) and the host inputs."""
+    import numpy as np
+    import torch
+
+    import synth
+    import sparse_moe_layer_router_amd as moe
+
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[cfg.dtype]
+    es = 2 if cfg.dtype == "bf16" else 4
+    prefill = cfg.T * cfg.k / cfg.E > 32
+    wgt, wup, wdn, shared = weights
+    d, E = cfg.d, cfg.E
     host = synth.host_small_inputs(cfg, 0)
 
     def up(a):
@@ -430,14 +497,13 @@ def main():
     bias = torch.from_numpy(host.router_bias).to(dev) if host.router_bias is not None else None
     xs = [up(host.x)] + [up(synth.normal_host((cfg.T, d), 100 + b, synth.stream_id(synth.K_X), 1.0, cfg.dtype))
                          for b in range(1, N_BATCHES)]
-    shape = moe.make_shape(cfg.T, d, E, cfg.k, H, cfg.Hs, cfg.dtype, layout, cfg.routing)
+    shape = moe.make_shape(cfg.T, d, E, cfg.k, cfg.H, cfg.Hs, cfg.dtype, layout, cfg.routing)
     ws = moe.allocate_workspace(shape)
     outs = [torch.empty(cfg.T, d, dtype=dt, device=dev) for _ in range(N_BATCHES)]
     counts = [torch.zeros(E, dtype=torch.int32, device=dev) for _ in range(N_BATCHES)]
     sg, su, sd = shared if shared else (None, None, None)
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
-    t_setup = time.perf_counter() - t_setup
 
     def step(i, events=None):
         b = i % N_BATCHES
@@ -532,20 +598,21 @@ def main():
     if roof["bound"] == "hbm":   # the same kernel against the large-copy bandwidth measured above
         roof["measured_copy_GBps"] = round(copy_GBps, 1)
         roof["frac_of_measured_copy"] = round(achieved / copy_GBps, 4)
+    # both expert kernels from the per-stage pass, against the roofline of the regime
+    kernels = {}
+    for st_, wkey, fkey in (("ffn_gate_up", "gate_up", "flops_gate_up"), ("ffn_down", "down", "flops_down")):
+        ms_ = stage_ms[st_]
+        kernels[st_] = {"kernel": moe.moe_stage_kernel_name(shape, moe.STAGES.index(st_)), "ms": round(ms_, 4),
+                        "TFLOPs": round(work[fkey] / (ms_ * 1e-3) / 1e12, 2),
+                        "GBps": round(work[wkey] / (ms_ * 1e-3) / 1e9, 1)}
+        kernels[st_]["frac"] = round(kernels[st_]["TFLOPs"] / BF16_PEAK_TFLOPS if prefill
+                                     else kernels[st_]["GBps"] / HBM_PEAK_GBPS, 4)
 
-    line = {
-        "metric": METRIC,
+    rec = {
         "value": round(cfg.T * K / elapsed, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
         "steps": K,
         "warmup": W,
         "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg.dtype,
-        "data": "synthetic (seeded Philox normal draws; random-init weights of the named layer shape)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
                    "d_hidden": cfg.H, "d_shared_hidden": cfg.Hs, "zipf_bias": cfg.zipf_s, "routing": cfg.routing,
                    "weight_layout": {moe.MOE_LAYOUT_FRAG16: "frag16", moe.MOE_LAYOUT_INT8_FRAG: "int8 per-row",
@@ -555,14 +622,87 @@ def main():
         "layer": {"alg_bytes": int(work["layer"]), "alg_flops": int(work["flops_layer"]),
                   "hbm_GBps": round(work["layer"] / (ms_per_step * 1e-3) / 1e9, 1),
                   "tflops": round(work["flops_layer"] / (ms_per_step * 1e-3) / 1e12, 2),
-                  "active_experts_mean": work["n_act"]},
+                  "active_experts_mean": work["n_act"], "expert_kernels": kernels},
         "stage_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},   # untimed pass, events on every stage
         "step_ms_events": step_dist,   # untimed pass, cold caches, events around each whole layer call
-        "setup_s": round(t_setup, 1),
     }
+    del ws, outs, xs
+    torch.cuda.empty_cache()
+    return rec, host
+
+
+def sub_record(rec):
+    """The decode figures carried next to the headline: step time, tokens/s and the dominant
+    kernel against the HBM roofline (with its counter traffic when the summary is current)."""
+    r = rec["roofline"]
+    return {"workload": rec["config"]["workload"], "T": rec["config"]["T"], "steps": rec["steps"],
+            "ms_per_step": rec["ms_per_step"], "tokens_per_s": rec["value"], "kernel": r["kernel"],
+            "kernel_ms": r["kernel_ms"], "bound": r["bound"], "achieved": r["achieved"], "unit": r["unit"],
+            "frac": r["frac"], "traffic": r["traffic"], "layer_hbm_GBps": rec["layer"]["hbm_GBps"],
+            "step_ms_events": rec["step_ms_events"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (expert-parallel "
+              "all-to-all is out of scope); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+
+    if args.ceilings:
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        print(json.dumps({"ceilings": measure_ceilings(dev)}), flush=True)
+        return
+    cfg = synth.CONFIG_BY_NAME[args.workload]
+    prefill = cfg.T * cfg.k / cfg.E > 32
+    K = args.steps if args.steps is not None else (30 if prefill else 50)
+    W = args.warmup if args.warmup is not None else 5
+    if args.expert == "gelu":
+        return main_gelu(args, cfg, K, W)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_setup = time.perf_counter()
+    weights, layout = make_weights(args, cfg, dev)
+    t_setup = time.perf_counter() - t_setup
+    rec, host = run_layer_bench(cfg, K, W, weights, layout, dev)
+    line = {"metric": METRIC, "value": rec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+            "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": cfg.dtype,
+            "data": "synthetic (seeded Philox normal draws; random-init weights of the named layer shape)"}
+    line.update({k_: rec[k_] for k_ in ("config", "roofline", "layer", "stage_ms", "step_ms_events")})
+    line["setup_s"] = round(t_setup, 1)
+    # The decode half of the metric, on the same weights: the DeepSeek-V3-shaped layer at T = 8 and 256.
+    same_layer = lambda c: (c.d, c.E, c.k, c.H, c.Hs, c.dtype, c.routing) == (  # noqa: E731
+        cfg.d, cfg.E, cfg.k, cfg.H, cfg.Hs, cfg.dtype, cfg.routing)
+    if not args.no_decode:
+        subs = {}
+        for name in DECODE_SUBRECORDS:
+            c = synth.CONFIG_BY_NAME[name]
+            if name != cfg.name and same_layer(c):
+                subs[name] = sub_record(run_layer_bench(c, 50, 5, weights, layout, dev)[0])
+        if subs:
+            line["decode"] = subs
+    if not args.no_ceilings:   # measured after the layer runs, so they do not disturb them
+        ceil = measure_ceilings(dev)
+        line["ceilings"] = ceil
+        rf = line["roofline"]
+        if rf["bound"] == "mfma":
+            rf["measured_mfma_random_TFLOPs"] = ceil["mfma_bf16_random_TFLOPs"]
+            rf["frac_of_measured_mfma"] = round(rf["achieved"] / ceil["mfma_bf16_random_TFLOPs"], 4)
+        else:
+            rf["measured_read_GBps"] = ceil["read_nontemporal_GBps"]
+            rf["frac_of_measured_read"] = round(rf["achieved"] / ceil["read_nontemporal_GBps"], 4)
+        for sub in line.get("decode", {}).values():
+            sub["frac_of_measured_read"] = round(sub["achieved"] / ceil["read_nontemporal_GBps"], 4)
     if not args.no_cpu_baseline:
         n_tok = args.cpu_sample_tokens or (8 if cfg.E > 8 else 16)
-        line["cpu_baseline"] = cpu_baseline(cfg, host, n_tok, int8=layout == moe.MOE_LAYOUT_INT8_FRAG)
+        line["cpu_baseline"] = cpu_baseline(cfg, host, n_tok, int8=args.layout == "int8")
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

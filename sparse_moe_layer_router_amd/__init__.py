@@ -24,6 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 (MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
  MOE_ERR_TOO_LARGE) = range(7)
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20   # fixed device scratch of moe_layer_forward_noalloc
+MOE_CALIB_READ_BLOCKS, MOE_CALIB_MFMA_BLOCKS = 2048, 256   # workgroups (sink entries) of the probes
 MOE_F32, MOE_BF16 = 0, 1
 MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_FRAG16, MOE_LAYOUT_INT8_FRAG = 0, 1, 2
 MOE_ROUTING_SOFTMAX, MOE_ROUTING_SIGMOID = 0, 1
@@ -74,6 +75,9 @@ _sigs = {
     "moe_quantize_weights": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
     "moe_load_stats": (ctypes.c_int, [_S, _P, ctypes.c_float, _P, _P, _P]),
     "moe_quantized_weight_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
+    # measurement probes (include/moe_calib.h)
+    "moe_calib_read_stream": (ctypes.c_int, [_P, ctypes.c_size_t, _P, ctypes.c_int, _P]),
+    "moe_calib_mfma": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -261,3 +265,16 @@ def quantize_expert_weights(w_gate, w_up, w_down, shared=None, stream=None):
 
 def moe_stage_kernel_name(shape, stage: int) -> str:
     return _lib.moe_stage_kernel_name(ctypes.byref(shape), stage).decode()
+
+
+def moe_calib_read_stream(buf, sink, nontemporal=True, stream=None):
+    """Read all of ``buf`` once (16-byte loads); sink: MOE_CALIB_READ_BLOCKS uint32 (int32 tensor)."""
+    _check("moe_calib_read_stream", _lib.moe_calib_read_stream(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(bool(nontemporal)), _stream(stream)))
+
+
+def moe_calib_mfma(operands, iters, sink, clocks=None, stream=None):
+    """bf16 MFMA loop on ``operands`` (MOE_CALIB_MFMA_BLOCKS * 512 * 16 bf16); sink: float32
+    [MOE_CALIB_MFMA_BLOCKS]; clocks: int64 [MOE_CALIB_MFMA_BLOCKS * 8 * 4] or None."""
+    _check("moe_calib_mfma", _lib.moe_calib_mfma(_ptr(operands), int(iters), _ptr(sink), _ptr(clocks),
+                                                 _stream(stream)))

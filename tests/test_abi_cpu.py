@@ -19,7 +19,8 @@ B = 0x200000
 
 
 def header_functions():
-    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    inc = os.path.join(ROOT, "include")
+    src = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
 
@@ -284,3 +285,20 @@ def test_noalloc_validation():
     empty = {k: None for k in args if k != "stream"}
     assert status_of(moe.moe_layer_forward_noalloc, dsv3(T=0), **empty, stream=0) == moe.MOE_OK
     assert "no-allocation" in moe.moe_status_string(moe.MOE_ERR_TOO_LARGE)
+
+
+def test_calib_probe_validation():
+    """The measurement probes refuse bad arguments on the host (no GPU here: a valid call would
+    reach the launch and report MOE_ERR_HIP)."""
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    lib.moe_calib_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_void_p]
+    lib.moe_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    assert lib.moe_calib_read_stream(A, 0, B, 1, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_read_stream(None, 1024, B, 1, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_read_stream(A, 1000, B, 1, None) == moe.MOE_ERR_ALIGNMENT
+    assert lib.moe_calib_read_stream(A + 8, 1024, B, 1, None) == moe.MOE_ERR_ALIGNMENT
+    assert lib.moe_calib_mfma(A, 0, B, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_mfma(A + 4, 10, B, None, None) == moe.MOE_ERR_ALIGNMENT
+    assert lib.moe_calib_mfma(A, 10, B, B + 4, None) == moe.MOE_ERR_ALIGNMENT
