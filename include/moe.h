@@ -209,14 +209,17 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* x, const int32_t* per
  * only). The hidden activations live in the workspace (moe_workspace_bytes() of the same shape). A
  * layer with these experts is moe_route, moe_permute, moe_grouped_ffn_gelu and moe_combine with
  * shared_out NULL. Accumulation in float32; h is rounded to bfloat16 before the second linear and
- * y once. Experts run as weight-streaming kernels at every batch size (the form decode needs).
+ * y once. Like moe_grouped_ffn, the experts run as weight-streaming kernels when the buckets are
+ * small (fewer than 32 rows per expert on average: decode) and as the tiled grouped GEMM otherwise
+ * (prefill), with the biases and the GELU applied in the GEMM's epilogues.
  */
 moe_status moe_grouped_ffn_gelu(const moe_shape* s, const void* x, const int32_t* perm_src,
                                 const int32_t* expert_offsets, const void* w1, const float* b1, const void* w2,
                                 const float* b2, void* y, void* workspace, size_t ws_bytes, void* stream);
 
 /* Kernel of one layer of moe_grouped_ffn_gelu for this shape (layer 0: the first linear and GELU,
- * 1: the second linear), as the profiler names it; "" for an invalid shape or layer. */
+ * 1: the second linear), as the profiler names it; "" for an invalid shape or layer. On the grouped
+ * GEMM path a third, small launch (gemm_schedule_kernel) precedes them. */
 const char* moe_gelu_kernel_name(const moe_shape* s, int layer);
 
 /*

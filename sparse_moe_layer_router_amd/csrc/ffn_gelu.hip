@@ -11,9 +11,9 @@
 // layer gathers x rows through perm_src and stores GELU(acc + b1) as bf16 hidden rows [rows, H];
 // the second reads those rows and stores acc + b2 as bf16 output rows [rows, d]. Accumulation is
 // fp32 inside the MFMA; the bias is added in fp32 before the activation and the single rounding.
-// The form runs at every batch size: a bucket of n rows streams its expert's weights ceil(n / 16 NTT)
-// times, so large buckets pay for it (the variant is a decode-regime form; the tiled grouped GEMM
-// serves SwiGLU experts only).
+// A bucket of n rows streams its expert's weights ceil(n / 16 NTT) times, so this is the decode-regime
+// form; layers with many rows per expert run the tiled grouped GEMM instead (ffn_gemm.hip, GELU
+// modes).
 #include "dispatch.h"
 #include "moe_device.h"
 

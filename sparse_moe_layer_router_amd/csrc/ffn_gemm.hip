@@ -7,6 +7,11 @@
 // no expert waits on a separate launch; data-movement page, section 15: once routes are sorted by
 // expert, each expert's weights are loaded once and reused across its whole bucket of tokens.
 //
+// The same kernel runs the two-layer GELU expert (overview article, section 4.1 layer code:
+// Linear(d -> H) with a bias, GELU, Linear(H -> d) with a bias) when its buckets are large: the first
+// pass multiplies by W1 alone (256 hidden columns per tile) and its epilogue stores GELU(acc + b1) in
+// the packed hidden layout; the second is the down pass with b2 added before the output rounding.
+//
 // Tiles. An expert bucket is cut into M-tiles of up to BM = 320 rows, so a bucket of the prefill
 // regime (about 256 +- 50 rows) is a single M-tile and every weight tile is fetched once per
 // bucket. The tile is BM rows x 256 weight rows (gate/up: 128 gate + 128 up rows for the same
@@ -48,7 +53,15 @@ constexpr int kCusPerXcd = 32;
 constexpr int kStages = 4;         // LDS ring depth: two slices in flight while one is consumed
 constexpr int kRowBytes = BK * 2;  // one tile row in LDS: 64 bytes = 4 chunks of 16
 
-enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2 };
+enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2, kGeluUp = 3, kGeluDown = 4 };
+
+// The first pass of an expert (gathered token rows times the up-projection weights) and the second
+// (packed hidden activations times the down-projection weights).
+constexpr bool first_pass(int mode) { return mode == kGateUp || mode == kGeluUp; }
+constexpr bool packed_a(int mode) { return mode == kDown || mode == kGeluDown; }
+
+// exact GELU, z * Phi(z) = z * erfc(-z / sqrt 2) / 2
+__device__ __forceinline__ float gelu_exact(float z) { return 0.5f * z * erfcf(-0.70710678118654752f * z); }
 
 template <int MODE> struct Geo {
   static constexpr int MBW = MODE == kRouter ? 1 : 5;              // 32-row blocks per wave
@@ -87,7 +100,7 @@ __device__ __forceinline__ int b_row(int j, int wn, int fr) {
 template <int MODE>
 __device__ __forceinline__ u32x4_t read_a(const uint8_t* sa, int i, int wm, int fr, int ch) {
   const int r = (wm + 2 * i) * 32 + fr;
-  if (MODE == kDown) return *(const u32x4_t*)(sa + (r / 16) * 1024 + ((r & 15) + 16 * ch) * 16);
+  if (packed_a(MODE)) return *(const u32x4_t*)(sa + (r / 16) * 1024 + ((r & 15) + 16 * ch) * 16);
   return *(const u32x4_t*)(sa + swz(r, ch));
 }
 template <int MODE, int LAYOUT>
@@ -215,7 +228,8 @@ gemm_schedule_kernel(const FfnGroups p, int32_t* __restrict__ sched_gu, int32_t*
         const long long n = group_rows(p, g, nullptr);
         const int Hg = g < p.E ? p.H : p.Hs;
         mt = (n + BM - 1) / BM;
-        ntg = (Hg + Geo<kGateUp>::BN - 1) / Geo<kGateUp>::BN;
+        const int bn_up = p.gelu ? Geo<kGeluUp>::BN : Geo<kGateUp>::BN;  // 256 weight rows per tile either way
+        ntg = (Hg + bn_up - 1) / bn_up;
         ntd = (p.d + Geo<kDown>::BN - 1) / Geo<kDown>::BN;
         nkg = (p.d + BK - 1) / BK;
         nkd = (Hg + BK - 1) / BK;
@@ -456,11 +470,13 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   const int np = (int)gemm_pad32(c.N);
   uint16_t* hid = (uint16_t*)p.hid + (c.g < p.E ? 0 : (size_t)p.rbands * 16 * gemm_pad32(p.H));
   uint16_t* y = (uint16_t*)p.y + (c.g < p.E ? 0 : (size_t)p.rows * p.d);
-  if constexpr (MODE == kDown) {
+  if constexpr (packed_a(MODE)) {
     // Output rows are 512-byte segments of y: stage each half of the tile (160 rows x 256
     // columns, 80 KB) in LDS, then store it with 16-byte stores, a row per 32 lanes. In LDS a
     // row's 16-byte chunk c sits at chunk c ^ (row % 32), so the 32 rows a store instruction of the
-    // accumulators touches fall in distinct banks.
+    // accumulators touches fall in distinct banks. The GELU expert's second linear adds its bias
+    // (fp32) before the rounding.
+    const float* b2 = MODE == kGeluDown && p.b2 ? p.b2 + (size_t)c.g * p.d : nullptr;
     static_assert(G::MBW == 5 && G::BN == 256 && 160 * 512 <= kStages * G::STAGE, "staging layout");
     uint8_t* lt = &smem[0][0];
     int tid = (int)threadIdx.x;
@@ -478,9 +494,13 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int nl = wn * 64 + j * 32 + q * 8 + efh * 4;
+            float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            if (MODE == kGeluDown && b2 && c.n0 + nl < c.N) {  // N is a multiple of 8: 4 columns all in or all out
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] += b2[c.n0 + nl + e];
+            }
             *(u32x2_t*)(lt + rl * 512 + (((nl >> 3) ^ (rl & 31)) << 4) + (nl & 4) * 2) =
-                u32x2_t{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                        pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+                u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           }
       }
       __syncthreads();
@@ -513,6 +533,17 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
                                     silu(acc[i][0][4 * q + 1]) * acc[i][1][4 * q + 1]),
                         pack_bf16x2(silu(acc[i][0][4 * q + 2]) * acc[i][1][4 * q + 2],
                                     silu(acc[i][0][4 * q + 3]) * acc[i][1][4 * q + 3])};
+          *(u32x2_t*)(hid + frag16_offset((size_t)(c.pr0 + row), (size_t)n, (size_t)np)) = v;
+        } else if (MODE == kGeluUp) {
+          if (n >= np) continue;  // (as for gate/up)
+          u32x2_t v = {0u, 0u};
+          if (n < c.N) {
+            const float* b1 = p.b1 ? p.b1 + (size_t)c.g * p.H + n : nullptr;
+            float z[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] = gelu_exact(acc[i][j][4 * q + e] + (b1 ? b1[e] : 0.f));
+            v = u32x2_t{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+          }
           *(u32x2_t*)(hid + frag16_offset((size_t)(c.pr0 + row), (size_t)n, (size_t)np)) = v;
         } else if (MODE == kDown) {
           if (n >= c.N) continue;
@@ -601,11 +632,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
     nt = local / mtiles;
     mt = local % mtiles;
     const size_t wsz = (size_t)p.H * p.d;
-    if (MODE == kGateUp) {
+    if (first_pass(MODE)) {  // gate/up, or the GELU expert's W1 (held in w_gate)
       c.N = Hg;
       c.K = p.d;
       Bp[0] = c.g < p.E ? (const uint16_t*)p.w_gate + (size_t)c.g * wsz : (const uint16_t*)p.ws_gate;
-      Bp[1] = c.g < p.E ? (const uint16_t*)p.w_up + (size_t)c.g * wsz : (const uint16_t*)p.ws_up;
+      if (MODE == kGateUp)
+        Bp[1] = c.g < p.E ? (const uint16_t*)p.w_up + (size_t)c.g * wsz : (const uint16_t*)p.ws_up;
     } else {
       c.N = p.d;
       c.K = Hg;
@@ -623,7 +655,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
   const int gbands = (nrows + 15) / 16;
   c.pr0 = band0 * 16 + m0;
   const uint16_t* abase =
-      MODE == kDown ? (const uint16_t*)p.hid + (c.g < p.E ? 0 : (size_t)p.rbands * 16 * gemm_pad32(p.H)) : nullptr;
+      packed_a(MODE) ? (const uint16_t*)p.hid + (c.g < p.E ? 0 : (size_t)p.rbands * 16 * gemm_pad32(p.H)) : nullptr;
 
   // ---- this wave's loads: slots [first, first + L) of the slice's INSTR 1 KB loads -------------
   // Slot s < A_INSTR: A rows [16 s, 16 s + 16), lane l -> row 16 s + l/4, physical chunk l%4 (the
@@ -638,7 +670,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
 #pragma unroll
   for (int i = 0; i < G::L_HI; ++i) {
     const int s = c.first + (i < nload ? i : 0);
-    if (s < G::A_INSTR && MODE != kDown) {
+    if (s < G::A_INSTR && !packed_a(MODE)) {
       const int row = s * 16 + (lane >> 2);
       c.kc[i] = swz_chunk(row, phys) * 8;
       c.stride[i] = BK;
@@ -742,7 +774,7 @@ long long gemm_tiles_upper(const FfnGroups& p, int mode) {
   const long long mt_routed = p.rows / bm + p.E;  // each group adds at most one partial tile
   const long long mt_shared = p.Hs > 0 ? (p.T + bm - 1) / bm : 0;
   if (mode == kGateUp) {
-    const int bn = Geo<kGateUp>::BN;
+    const int bn = p.gelu ? Geo<kGeluUp>::BN : Geo<kGateUp>::BN;
     return mt_routed * ((p.H + bn - 1) / bn) + mt_shared * ((p.Hs + bn - 1) / bn);
   }
   const int bn = Geo<kDown>::BN;
@@ -767,7 +799,11 @@ hipError_t launch_gemm_gate_up(const FfnGroups& p, const int32_t* sched, hipStre
   a.pband = sched + 2 * (p.E + 2);
   a.xb = sched + 3 * (p.E + 2);
   const dim3 grid(gemm_grid(gemm_tiles_upper(p, kGateUp)));
-  if (p.layout == kFrag16)
+  if (p.gelu && p.layout == kFrag16)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kGeluUp, kFrag16>), grid, dim3(kThreads), 0, stream, a);
+  else if (p.gelu)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kGeluUp, kRowMajor>), grid, dim3(kThreads), 0, stream, a);
+  else if (p.layout == kFrag16)
     hipLaunchKernelGGL((grouped_gemm_kernel<kGateUp, kFrag16>), grid, dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((grouped_gemm_kernel<kGateUp, kRowMajor>), grid, dim3(kThreads), 0, stream, a);
@@ -781,7 +817,11 @@ hipError_t launch_gemm_down(const FfnGroups& p, const int32_t* sched, hipStream_
   a.pband = sched + 2 * (p.E + 2);
   a.xb = sched + 3 * (p.E + 2) + kXcds + 1;
   const dim3 grid(gemm_grid(gemm_tiles_upper(p, kDown)));
-  if (p.layout == kFrag16)
+  if (p.gelu && p.layout == kFrag16)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kGeluDown, kFrag16>), grid, dim3(kThreads), 0, stream, a);
+  else if (p.gelu)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kGeluDown, kRowMajor>), grid, dim3(kThreads), 0, stream, a);
+  else if (p.layout == kFrag16)
     hipLaunchKernelGGL((grouped_gemm_kernel<kDown, kFrag16>), grid, dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((grouped_gemm_kernel<kDown, kRowMajor>), grid, dim3(kThreads), 0, stream, a);

@@ -530,7 +530,9 @@ const char* ffn_gate_up_kernel_name(const FfnGroups& g) {
       if (g.layout == kInt8Frag) return "ffn_gate_up_stream<1, 2>";
       if (stream_ntt(g) == 2) return g.layout == kFrag16 ? "ffn_gate_up_stream<2, 1>" : "ffn_gate_up_stream<2, 0>";
       return g.layout == kFrag16 ? "ffn_gate_up_stream<1, 1>" : "ffn_gate_up_stream<1, 0>";
-    default: return g.layout == kFrag16 ? "grouped_gemm_kernel<0, 1>" : "grouped_gemm_kernel<0, 0>";
+    default:
+      if (g.gelu) return g.layout == kFrag16 ? "grouped_gemm_kernel<3, 1>" : "grouped_gemm_kernel<3, 0>";
+      return g.layout == kFrag16 ? "grouped_gemm_kernel<0, 1>" : "grouped_gemm_kernel<0, 0>";
   }
 }
 const char* ffn_down_kernel_name(const FfnGroups& g) {
@@ -540,7 +542,9 @@ const char* ffn_down_kernel_name(const FfnGroups& g) {
       if (g.layout == kInt8Frag) return "ffn_down_stream<1, 2>";
       if (stream_ntt(g) == 2) return g.layout == kFrag16 ? "ffn_down_stream<2, 1>" : "ffn_down_stream<2, 0>";
       return g.layout == kFrag16 ? "ffn_down_stream<1, 1>" : "ffn_down_stream<1, 0>";
-    default: return g.layout == kFrag16 ? "grouped_gemm_kernel<1, 1>" : "grouped_gemm_kernel<1, 0>";
+    default:
+      if (g.gelu) return g.layout == kFrag16 ? "grouped_gemm_kernel<4, 1>" : "grouped_gemm_kernel<4, 0>";
+      return g.layout == kFrag16 ? "grouped_gemm_kernel<1, 1>" : "grouped_gemm_kernel<1, 0>";
   }
 }
 

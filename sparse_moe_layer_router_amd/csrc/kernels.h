@@ -55,6 +55,11 @@ struct FfnGroups {
   void* y;                     // routed outputs [rows, d], then shared outputs [T, d] (dtype)
   float mean_rows_per_group;   // host-side regime hint (T*k / E)
   long long rbands;            // grouped-GEMM path: routed band capacity of the packed hidden activations
+  // Two-layer GELU experts on the grouped-GEMM path (gelu = 1): w_gate holds W1 [E, H, d], w_down
+  // W2 [E, d, H], w_up is unused, Hs = 0; hid = GELU(W1 x + b1), y = W2 hid + b2 (a NULL bias is zero)
+  int gelu;
+  const float* b1;             // [E, H] or NULL
+  const float* b2;             // [E, d] or NULL
 };
 
 // Grouped-GEMM path: the hidden activations are packed into 16-row x 32-column blocks

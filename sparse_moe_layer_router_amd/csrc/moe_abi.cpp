@@ -207,6 +207,18 @@ moe::GeluGroups gelu_groups_for(const moe_shape& s, const void* x, const int32_t
   return g;
 }
 
+// The GELU experts as grouped-GEMM groups: W1 in the gate slot, W2 in the down slot, no shared expert.
+moe::FfnGroups gelu_gemm_groups(const moe_shape& s, const void* x, const int32_t* perm_src, const int32_t* offsets,
+                                const void* w1, const float* b1, const void* w2, const float* b2, void* hid, void* y) {
+  moe_shape routed = s;
+  routed.d_shared_hidden = 0;
+  moe::FfnGroups g = groups_for(routed, x, perm_src, offsets, w1, nullptr, w2, nullptr, nullptr, nullptr, hid, y);
+  g.gelu = 1;
+  g.b1 = b1;
+  g.b2 = b2;
+  return g;
+}
+
 moe_status ffn_impl(const moe::FfnGroups& g, int32_t* sched, const Events& ev, hipStream_t stream) {
   const moe::FfnPath path = moe::ffn_path(g);
   MOE_MARK(ev, MOE_STAGE_FFN_SCHEDULE, 0);
@@ -437,8 +449,11 @@ moe_status moe_grouped_ffn_gelu(const moe_shape* s, const void* x, const int32_t
   MOE_TRY(maybe(b2, 4));
   MOE_TRY(need(y, 16));
   MOE_TRY(check_workspace(*s, workspace, ws_bytes));
-  const moe::GeluGroups g = gelu_groups_for(*s, x, perm_src, expert_offsets, w1, b1, w2, b2,
-                                            at(workspace, layout_of(*s).hid), y);
+  const Layout L = layout_of(*s);
+  const moe::FfnGroups fg = gelu_gemm_groups(*s, x, perm_src, expert_offsets, w1, b1, w2, b2, at(workspace, L.hid), y);
+  if (moe::ffn_path(fg) == moe::kPathGemm)  // many rows per expert: the tiled grouped GEMM
+    return ffn_impl(fg, (int32_t*)at(workspace, L.sched), Events{nullptr, nullptr}, (hipStream_t)stream);
+  const moe::GeluGroups g = gelu_groups_for(*s, x, perm_src, expert_offsets, w1, b1, w2, b2, at(workspace, L.hid), y);
   MOE_LAUNCH(moe::launch_gelu_up(g, (hipStream_t)stream));
   MOE_LAUNCH(moe::launch_gelu_down(g, (hipStream_t)stream));
   return MOE_OK;
@@ -447,6 +462,10 @@ moe_status moe_grouped_ffn_gelu(const moe_shape* s, const void* x, const int32_t
 const char* moe_gelu_kernel_name(const moe_shape* s, int layer) {
   if (check_shape(s) != MOE_OK || s->dtype != MOE_BF16 || (layer != 0 && layer != 1)) return "";
   if (s->weight_layout != MOE_LAYOUT_ROWMAJOR && s->weight_layout != MOE_LAYOUT_FRAG16) return "";
+  const moe::FfnGroups fg = gelu_gemm_groups(*s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                             nullptr, nullptr);
+  if (moe::ffn_path(fg) == moe::kPathGemm)
+    return layer == 0 ? moe::ffn_gate_up_kernel_name(fg) : moe::ffn_down_kernel_name(fg);
   const moe::GeluGroups g = gelu_groups_for(*s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                             nullptr, nullptr);
   return moe::gelu_kernel_name(g, layer == 0);

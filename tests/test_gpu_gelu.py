@@ -25,6 +25,9 @@ CONFIGS = [
     synth.LayerConfig("gelu_ragged", 300, 264, 16, 2, 200, 0, "bf16"),          # d % 32 and H % 16 != 0
     synth.LayerConfig("gelu_many_rows", 2048, 512, 8, 2, 384, 0, "bf16", zipf_s=1.2),
     synth.LayerConfig("gelu_sigmoid", 40, 128, 32, 6, 64, 0, "bf16", routing="sigmoid", score_bias_std=0.05),
+    # grouped-GEMM path with many groups: ~256 rows per expert (one M-tile, some spilling into a
+    # second), partial N-tiles of both passes (H = 192 < 256)
+    synth.LayerConfig("gelu_gemm_groups", 4096, 256, 64, 4, 192, 0, "bf16"),
 ]
 CASES = [(c, moe.MOE_LAYOUT_ROWMAJOR) for c in CONFIGS] + \
         [(c, moe.MOE_LAYOUT_FRAG16) for c in CONFIGS if c.d % 32 == 0 and c.H % 32 == 0]
@@ -127,11 +130,15 @@ def test_gelu_layer_is_deterministic_and_empty_batch_is_a_no_op():
     moe.moe_grouped_ffn_gelu(s0, None, None, None, None, None, None, None, None, None)
 
 
-@pytest.mark.parametrize("name,n_sample", [("dsv3_decode_t8", None), ("dsv3_decode_t256", 6)])
-def test_gelu_layer_full_decode_size(name, n_sample):
-    """The DeepSeek-V3-shaped decode layer with GELU experts (d 7168, 256 experts of hidden 2048,
-    top-8, no shared expert), fragment-tiled weights drawn in device memory as the benchmark does;
-    the oracle regenerates on the host only the experts the checked tokens select."""
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,n_sample", [("dsv3_decode_t8", None), ("dsv3_decode_t256", 6),
+                                           ("dsv3_prefill_t8192", "structural")])
+def test_gelu_layer_full_size(name, n_sample):
+    """The DeepSeek-V3-shaped layer with GELU experts (d 7168, 256 experts of hidden 2048, top-8,
+    no shared expert) at the decode sizes (weight streaming) and the prefill chunk (grouped GEMM),
+    fragment-tiled weights drawn in device memory as the benchmark does; the oracle regenerates on
+    the host only the experts the checked tokens select. At the prefill size the checked tokens hold
+    the first and last row of every M-tile of every expert bucket."""
     base = synth.CONFIG_BY_NAME[name]
     cfg = synth.LayerConfig(name + "_gelu", base.T, base.d, base.E, base.k, base.H, 0, "bf16")
     E, H, d = cfg.E, cfg.H, cfg.d
@@ -153,11 +160,25 @@ def test_gelu_layer_full_decode_size(name, n_sample):
                                out, buf)
     torch.cuda.synchronize()
     del p1, p2
-    tokens = np.arange(cfg.T) if n_sample is None else \
-        np.unique(np.concatenate([[0, cfg.T - 1], np.random.default_rng(0).choice(cfg.T, n_sample - 2, replace=False)]))
+    if n_sample is None:
+        tokens = np.arange(cfg.T)
+    elif n_sample == "structural":
+        idx, counts = buf["idx"].cpu().numpy(), buf["counts"].cpu().numpy()
+        tokens = helpers.structural_tokens(idx, cfg.T, 0)
+        helpers.assert_tile_edges_covered(idx, counts, tokens, cfg.T, 0)
+    else:
+        tokens = np.unique(np.concatenate([[0, cfg.T - 1], np.random.default_rng(0).choice(cfg.T, n_sample - 2,
+                                                                                            replace=False)]))
+    print(f"[{cfg.name}] kernels {moe.moe_gelu_kernel_name(s, 0)} + {moe.moe_gelu_kernel_name(s, 1)}; "
+          f"{len(tokens)} checked tokens", flush=True)
     sid = lambda i: synth.stream_id(synth.K_GELU, i)  # noqa: E731
 
+    seen = []
+
     def expert(e):
+        seen.append(e)
+        if len(seen) % 32 == 0:
+            print(f"  oracle: {len(seen)} experts", flush=True)
         return (oracle.widen(synth.normal_host((H, d), 0, sid(0), 1.0 / np.sqrt(d), "bf16", first=e * H * d), "bf16"),
                 synth.normal_host((H,), 0, sid(2), 0.1, "f32", first=e * H).astype(np.float64),
                 oracle.widen(synth.normal_host((d, H), 0, sid(1), 1.0 / np.sqrt(H), "bf16", first=e * d * H), "bf16"),
