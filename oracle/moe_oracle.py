@@ -64,6 +64,7 @@ __all__ = [
     "topk_gap",
     "logistic", "selection_scores", "sigmoid_weights_selected", "ROUTINGS",
     "quantize", "dequantize", "quantize_rows_int8", "dequantize_rows_int8", "load_stats",
+    "E4M3_MAX", "fp8_e4m3_decode", "fp8_e4m3_encode", "quantize_rows_fp8", "dequantize_rows_fp8",
     "gelu", "gelu_mlp", "grouped_ffn_gelu", "layer_forward_gelu",
 ]
 
@@ -223,6 +224,65 @@ def quantize_rows_int8(w: np.ndarray):
 def dequantize_rows_int8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     """The float64 weight an INT8 row-scaled matrix stands for: q * s per row."""
     return dequantize(q, np.asarray(s, np.float64)[..., None])
+
+
+# FP8 weights ([Inference ch.6 quant]: any 1-byte code halves the bytes decode reads; the pages name
+# no FP8 format, so the reading is the OCP 8-bit floating-point format E4M3 in its "fn" variant:
+# 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities, and the
+# pattern S.1111.111 reserved for NaN, so the largest finite magnitude is 1.75 * 2^8 = 448).
+
+E4M3_MAX = 448.0
+
+
+def fp8_e4m3_decode(code: np.ndarray) -> np.ndarray:
+    """Value of each E4M3 code (uint8) as float64: (-1)^s (1 + m/8) 2^(e-7) for e > 0, (-1)^s m 2^-9
+    for e = 0 (subnormals); NaN for the reserved pattern."""
+    c = np.asarray(code, np.uint8).astype(np.int64)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def fp8_e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Code (uint8) of the E4M3 value nearest to each float32 input, ties to the even code;
+    magnitudes of 464 and above (past the midpoint between 448 and the 480 the format does not
+    have) saturate to 448. The sign bit is the input's (-0.0 gives 0x80). Every step below is exact
+    in float64 for float32 inputs, so the rounding is decided on the exact value."""
+    x = np.asarray(x, np.float32).astype(np.float64)
+    sign = np.signbit(x).astype(np.int64) << 7
+    a = np.abs(x)
+    sub = np.rint(np.minimum(a, 1.0) * 512.0)        # subnormal grid 2^-9; 8 is 2^-6, the first normal
+    frac, ex = np.frexp(np.where(a > 0, a, 1.0))     # a = frac 2^ex, frac in [0.5, 1)
+    e = ex - 1 + 7                                   # biased exponent of a = (1 + m/8) 2^(ex-1)
+    m = np.rint((2.0 * frac - 1.0) * 8.0)            # 0 .. 8
+    carry = m == 8.0
+    e = e + carry
+    m = np.where(carry, 0.0, m)
+    normal = (e.astype(np.int64) << 3) | m.astype(np.int64)
+    code = np.where(a >= 464.0, 0x7E, np.where(a < 2.0 ** -6, sub.astype(np.int64), normal))
+    return (code | sign).astype(np.uint8)
+
+
+def quantize_rows_fp8(w: np.ndarray):
+    """Per-output-channel FP8 (E4M3) of a [..., rows, cols] weight: one scale per row,
+    s = max|w_row| / 448, codes E4M3(w / s), so each row's largest magnitude maps to 448; an
+    all-zero row gets s = 0 and zero codes. The pages fix no precision for the division; as for the
+    INT8 codes the decision is taken in float32, the precision the GPU kernel quantizes in:
+    s = fl32(max / 448), code = E4M3(fl32(w / s)). Returns (codes uint8, s float32 [..., rows])."""
+    w32 = np.asarray(w, np.float64).astype(np.float32)
+    mx = np.abs(w32).max(axis=-1)
+    s = (mx / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    codes = fp8_e4m3_encode((w32 / safe[..., None]).astype(np.float32))
+    codes = np.where(s[..., None] > 0, codes, np.uint8(0)).astype(np.uint8)
+    return codes, s
+
+
+def dequantize_rows_fp8(codes: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """The float64 weight an FP8 row-scaled matrix stands for: E4M3 value * s per row."""
+    return fp8_e4m3_decode(codes) * np.asarray(s, np.float64)[..., None]
 
 
 # ----------------------------------------------------------------------------- dispatch

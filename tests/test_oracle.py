@@ -510,6 +510,74 @@ def test_int8_rows_match_torch_per_channel_quantization():
 
 # ------------------------------------------------------------------ load statistics (MoE overview §4.1)
 
+# ------------------------------------------------------------------ FP8 (E4M3) weights
+
+def test_fp8_e4m3_codes_by_hand():
+    """Codes from the format's definition (sign, 4 exponent bits with bias 7, 3 mantissa bits):
+    1 = 2^0 -> e 7 -> 0x38; 0.5 -> 0x30; 1.125 = 1 + 1/8 -> 0x39; 3.5 = 1.75 * 2 -> 0x46; 240 = 1.875 * 2^7
+    -> 0x77; 448 = 1.75 * 2^8 -> 0x7E (largest finite); 2^-6 -> 0x08 (smallest normal); 2^-9 -> 0x01
+    (smallest subnormal); 7 * 2^-9 -> 0x07; the sign is the top bit (-0.0 -> 0x80)."""
+    x = [1.0, -1.0, 0.5, 1.125, 3.5, 240.0, 448.0, -448.0, 2.0 ** -6, 2.0 ** -9, 7 * 2.0 ** -9, 0.0, -0.0]
+    want = [0x38, 0xB8, 0x30, 0x39, 0x46, 0x77, 0x7E, 0xFE, 0x08, 0x01, 0x07, 0x00, 0x80]
+    assert oracle.fp8_e4m3_encode(np.array(x, np.float32)).tolist() == want
+    np.testing.assert_array_equal(oracle.fp8_e4m3_decode(np.array(want, np.uint8)), x)
+    assert np.isnan(oracle.fp8_e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def test_fp8_e4m3_rounding_ties_and_saturation():
+    """Nearest value, ties to the even code: 1.0625 lies midway between 1 (0x38) and 1.125 (0x39) and
+    goes to 0x38; 1.1875 between 0x39 and 0x3A goes to 0x3A; 1.05 is nearer 1 than 1.125; on the
+    subnormal grid 1.5 * 2^-9 goes
+    to 0x02 and 7.5 * 2^-9 to 0x08 (= 2^-6). Past 448 the nearest finite value is 448 up to the midpoint
+    464 with the absent 480; at and above it the code saturates to 448 as well."""
+    x = np.array([1.0625, 1.1875, 1.05, 1.5 * 2.0 ** -9, 7.5 * 2.0 ** -9, 460.0, 464.0, 1e30, -500.0], np.float32)
+    assert oracle.fp8_e4m3_encode(x).tolist() == [0x38, 0x3A, 0x38, 0x02, 0x08, 0x7E, 0x7E, 0x7E, 0xFE]
+
+
+def test_fp8_e4m3_is_the_nearest_code_by_brute_force():
+    """Every finite code decodes and re-encodes to itself, and for random float32 inputs within range
+    the code is the finite code of least distance (ties to the even code), found by trying all 253."""
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    vals = oracle.fp8_e4m3_decode(codes)
+    np.testing.assert_array_equal(oracle.fp8_e4m3_encode(vals.astype(np.float32)), codes)
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(4000) * np.exp2(rng.uniform(-12, 9, 4000))).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    got = oracle.fp8_e4m3_encode(x)
+    pos = codes[codes < 0x80]
+    pv = oracle.fp8_e4m3_decode(pos)
+    for xi, gi in zip(x.astype(np.float64), got):
+        d = np.abs(pv - abs(xi))
+        best = pos[d == d.min()]
+        best = best[best % 2 == 0] if len(best) > 1 else best      # a tie goes to the even code
+        assert (gi & 0x7F) == best[0] and (gi >> 7) == (xi < 0 or (xi == 0 and np.signbit(xi)))
+
+
+def test_fp8_e4m3_matches_torch_float8_e4m3fn():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal(20000) * np.exp2(rng.uniform(-14, 9, 20000))).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    t = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.fp8_e4m3_encode(x), t)
+
+
+def test_fp8_rows_map_each_row_maximum_to_448_and_stay_within_half_a_step():
+    rng = np.random.default_rng(6)
+    w = rng.standard_normal((3, 40, 96)) * rng.uniform(1e-3, 5, (3, 40, 1))
+    w[1, 7] = 0.0
+    codes, s = oracle.quantize_rows_fp8(w)
+    assert s.dtype == np.float32 and codes.dtype == np.uint8 and s[1, 7] == 0 and (codes[1, 7] == 0).all()
+    nz = s > 0
+    amax = np.abs(oracle.fp8_e4m3_decode(codes)).max(-1)
+    assert (amax[nz] == 448.0).all()
+    w32 = w.astype(np.float32).astype(np.float64)
+    back = oracle.dequantize_rows_fp8(codes, s)
+    x = w32 / np.where(s > 0, s, 1)[..., None]
+    # half a step of the E4M3 grid at |x|: 2^(floor(log2|x|) - 4) for normals, 2^-10 for subnormals
+    half = np.where(np.abs(x) < 2.0 ** -6, 2.0 ** -10, np.exp2(np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -6))) - 4))
+    assert (np.abs(back - w32) <= half * s[..., None] * (1 + 1e-6) + 1e-30).all()
+
+
 def test_load_stats_closed_forms():
     """Uniform assignment has no penalty; everything on one expert gives coef * (E-1)/E; the loads
     are the assignment shares and sum to 1."""
@@ -746,6 +814,35 @@ def _gap_always_inf(L, k):
     return np.full(np.asarray(L).shape[0], np.inf)
 
 
+def _e4m3_truncating(x):
+    x = np.asarray(x, np.float32).astype(np.float64)
+    a = np.abs(x)
+    frac, ex = np.frexp(np.where(a > 0, a, 1.0))
+    code = np.where(a < 2.0 ** -6, np.floor(a * 512.0), ((ex + 6) * 8 + np.floor((2 * frac - 1) * 8)))
+    code = np.where(a >= 448, 0x7E, code).astype(np.int64) | (np.signbit(x).astype(np.int64) << 7)
+    return code.astype(np.uint8)
+
+
+def _e4m3_decode_bias8(code):
+    c = np.asarray(code, np.uint8).astype(np.int64)
+    e, m = (c >> 3) & 15, (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -10, (1 + m / 8) * np.exp2(e - 8.0))
+    return np.where(c & 0x80, -mag, mag)
+
+
+def _e4m3_decode_no_subnormals(code):
+    c = np.asarray(code, np.uint8).astype(np.int64)
+    e, m = (c >> 3) & 15, (c & 7).astype(np.float64)
+    mag = (1 + m / 8) * np.exp2(e - 7.0)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def _fp8_rows_scale_127(w):
+    w32 = np.asarray(w, np.float64).astype(np.float32)
+    sc = (np.abs(w32).max(-1) / np.float32(127.0)).astype(np.float32)
+    return om.fp8_e4m3_encode((w32 / np.where(sc > 0, sc, 1)[..., None]).astype(np.float32)), sc
+
+
 def _load_over_tokens(counts, T, k, coef=0.01):
     load = np.asarray(counts, np.float64) / T
     return load, coef * float(((load - 1.0 / len(load)) ** 2).sum())
@@ -783,6 +880,11 @@ MUTATIONS = {
     "dequantize_without_zero_point": ("dequantize", lambda q, s, z=0: np.asarray(q, np.float64) * s,
                                       test_quantization_example_from_the_pages),
     "load_over_tokens_not_slots": ("load_stats", _load_over_tokens, test_load_stats_closed_forms),
+    "fp8_truncating": ("fp8_e4m3_encode", _e4m3_truncating, test_fp8_e4m3_rounding_ties_and_saturation),
+    "fp8_exponent_bias_8": ("fp8_e4m3_decode", _e4m3_decode_bias8, test_fp8_e4m3_codes_by_hand),
+    "fp8_subnormals_as_normals": ("fp8_e4m3_decode", _e4m3_decode_no_subnormals, test_fp8_e4m3_codes_by_hand),
+    "fp8_scale_over_127": ("quantize_rows_fp8", _fp8_rows_scale_127,
+                           test_fp8_rows_map_each_row_maximum_to_448_and_stay_within_half_a_step),
     "topk_gap_one_place_too_far": ("topk_gap", _gap_one_past, test_topk_gap_by_hand),
     "topk_gap_one_place_too_high": ("topk_gap", _gap_one_short, test_topk_gap_by_hand),
     "topk_gap_never_rejects": ("topk_gap", _gap_always_inf, test_topk_gap_is_the_smallest_selected_minus_largest_unselected),
