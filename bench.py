@@ -17,7 +17,7 @@ the metric, against the bf16 MFMA peak). The same run then measures the same lay
 the decode sizes T = 8 and T = 256 (the HBM-bound half) and carries them under "decode".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode]
-                       [--no-cpu-baseline] [--layout frag16|rowmajor|int8] [--expert swiglu|gelu]
+                       [--no-cpu-baseline] [--layout frag16|rowmajor|int8|fp8] [--expert swiglu|gelu]
 """
 
 from __future__ import annotations
@@ -57,9 +57,9 @@ def parse():
     p.add_argument("--expert", choices=["swiglu", "gelu"], default="swiglu",
                    help="expert form: SwiGLU (with the shared expert), or the two-layer GELU expert with "
                         "biased linears (moe_grouped_ffn_gelu; no shared expert)")
-    p.add_argument("--layout", choices=["frag16", "rowmajor", "int8"], default="frag16",
-                   help="expert weight layout (frag16: packed once at load time, before timing; int8: "
-                        "per-row INT8 codes made once from the bf16 weights, before timing)")
+    p.add_argument("--layout", choices=["frag16", "rowmajor", "int8", "fp8"], default="frag16",
+                   help="expert weight layout (frag16: packed once at load time, before timing; int8, fp8: "
+                        "per-row INT8 or E4M3 codes made once from the bf16 weights, before timing)")
     return p.parse_args()
 
 
@@ -103,21 +103,21 @@ class HipEvents:
 
 
 # ------------------------------------------------------------------------------- work accounting
-def alg_bytes_and_flops(cfg, counts_list, es, int8=False):
+def alg_bytes_and_flops(cfg, counts_list, es, one_byte=False):
     """Per-stage algorithmic bytes and flops of one step, averaged over the cycled batches.
 
     Bytes are what the method must move once: each active expert's weights (one byte per weight
-    plus a float32 scale per row for INT8 weights), the shared expert's, the router, x in, out out
+    plus a float32 scale per row for INT8 or FP8 weights), the shared expert's, the router, x in, out out
     (plus, per kernel, its own inputs and outputs). Flops are 2*T*d*E (router) + 6*rows*d*H (gated
     MLP) + 6*T*d*Hs."""
     T, d, E, k, H, Hs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.H, cfg.Hs
     rows = T * k
-    wb = 1 if int8 else es
+    wb = 1 if one_byte else es
     res = []
     for counts in counts_list:
         n_act = int((counts > 0).sum())
-        sc_gu = 4 * (n_act * 2 * H + 2 * Hs) if int8 else 0
-        sc_dn = 4 * (n_act * d + (d if Hs else 0)) if int8 else 0
+        sc_gu = 4 * (n_act * 2 * H + 2 * Hs) if one_byte else 0
+        sc_dn = 4 * (n_act * d + (d if Hs else 0)) if one_byte else 0
         gate_up_w = wb * (n_act * 2 * H * d + 2 * Hs * d) + sc_gu
         down_w = wb * (n_act * d * H + d * Hs) + sc_dn
         gate_up = gate_up_w + es * T * d + es * (rows * H + T * Hs)              # weights + x + hidden out
@@ -160,7 +160,7 @@ def traffic_for(workload, kernel):
 
 
 # ----------------------------------------------------------------------------------- CPU oracle
-def cpu_baseline(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8, int8=False):
+def cpu_baseline(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8, quant=None):
     """The fp64 oracle on a bounded sample of the same workload (input generation excluded).
 
     The sample's oracle pass (routing, conversion of the selected experts' stored weights to fp64, SwiGLU,
@@ -181,13 +181,15 @@ def cpu_baseline(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8, int8=Fals
                              host.router_bias, cfg.routing)
     raw = {int(e): synth.expert_weights_host(cfg, 0, int(e)) for e in np.unique(idx)}   # untimed
     shared_raw = synth.expert_weights_host(cfg, 0, 0, shared=True) if cfg.Hs else None
-    # stored form of each weight (untimed): the bf16 bits, or per-row INT8 codes and scales
-    store = (lambda a: oracle.quantize_rows_int8(oracle.widen(a, cfg.dtype))) if int8 else (lambda a: a)
+    # stored form of each weight (untimed): the bf16 bits, or per-row INT8 / FP8 codes and scales
+    qz, dq = {"int8": (oracle.quantize_rows_int8, oracle.dequantize_rows_int8),
+              "fp8": (oracle.quantize_rows_fp8, oracle.dequantize_rows_fp8)}.get(quant, (None, None))
+    store = (lambda a: qz(oracle.widen(a, cfg.dtype))) if quant else (lambda a: a)
     stored = {e: tuple(store(a) for a in m) for e, m in raw.items()}
     shared_stored = tuple(store(a) for a in shared_raw) if shared_raw else None
 
     def weight(a):   # stored form -> the float64 weight the layer uses (timed, like the GPU's loads)
-        return oracle.dequantize_rows_int8(*a) if int8 else oracle.widen(a, cfg.dtype)
+        return dq(*a) if quant else oracle.widen(a, cfg.dtype)
     expert_fn = lambda e: tuple(weight(a) for a in stored[e])  # noqa: E731
     shared_fn = (lambda: tuple(weight(a) for a in shared_stored)) if shared_stored else None
     reps, total = 0, 0.0
@@ -201,9 +203,9 @@ def cpu_baseline(cfg, host, n_tokens, min_seconds=10.0, max_repeats=8, int8=Fals
     return {"value": round(len(tokens) * reps / total, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sampled": True, "sample_tokens": int(len(tokens)), "workload_tokens": cfg.T,
             "sample": f"{len(tokens)} of {cfg.T} tokens of {cfg.name}, {reps} passes in {total:.1f} s (routing, "
-                      f"{'INT8' if int8 else cfg.dtype}->fp64 conversion of the {len(raw)} selected experts"
+                      f"{quant.upper() if quant else cfg.dtype}->fp64 conversion of the {len(raw)} selected experts"
                       f"{' + shared' if shared_raw else ''}, SwiGLU, combine; expert weight generation"
-                      f"{' and quantization' if int8 else ''} excluded)"}
+                      f"{' and quantization' if quant else ''} excluded)"}
 
 
 # ------------------------------------------------------------------------ GELU expert variant
@@ -268,7 +270,7 @@ def main_gelu(args, cfg, K, W):
     import synth
     import sparse_moe_layer_router_amd as moe
 
-    if cfg.dtype != "bf16" or args.layout == "int8":
+    if cfg.dtype != "bf16" or args.layout in ("int8", "fp8"):
         print("--expert gelu runs bf16 layers with row-major or fragment-tiled weights", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
@@ -443,7 +445,7 @@ DECODE_SUBRECORDS = ("dsv3_decode_t8", "dsv3_decode_t256")   # same layer and we
 
 def make_weights(args, cfg, dev):
     """Expert weights of ``cfg`` drawn in device memory and, before any timing, put in the layout the
-    bench runs (fragment-tiled or per-row INT8): one-time preparation, like a model load."""
+    bench runs (fragment-tiled, or per-row INT8 or FP8): one-time preparation, like a model load."""
     import torch
     import synth
     import sparse_moe_layer_router_amd as moe
@@ -458,16 +460,16 @@ def make_weights(args, cfg, dev):
                   torch.empty(d, cfg.Hs, dtype=dt, device=dev))
     synth.fill_expert_weights_device(cfg, 0, wgt, wup, wdn, shared)
     layout = moe.MOE_LAYOUT_ROWMAJOR
-    if args.layout == "int8":
+    if args.layout in ("int8", "fp8"):
         if cfg.dtype != "bf16" or cfg.d % 64 or cfg.H % 64 or cfg.Hs % 64:
-            print(f"--layout int8 needs a bf16 layer with d, H, Hs multiples of 64 ({cfg.name} is not)",
+            print(f"--layout {args.layout} needs a bf16 layer with d, H, Hs multiples of 64 ({cfg.name} is not)",
                   file=sys.stderr)
             sys.exit(2)
-        quant = moe.quantize_expert_weights(wgt, wup, wdn, shared)
+        quant = moe.quantize_expert_weights(wgt, wup, wdn, shared, fp8=args.layout == "fp8")
         torch.cuda.synchronize()
         wgt, wup, wdn = quant[:3]
         shared = tuple(quant[3:]) if shared else None
-        layout = moe.MOE_LAYOUT_INT8_FRAG
+        layout = moe.MOE_LAYOUT_FP8_FRAG if args.layout == "fp8" else moe.MOE_LAYOUT_INT8_FRAG
         del quant
         torch.cuda.empty_cache()
     elif args.layout == "frag16" and cfg.dtype == "bf16" and cfg.d % 32 == 0 and cfg.H % 32 == 0 and cfg.Hs % 32 == 0:
@@ -589,7 +591,7 @@ def run_layer_bench(cfg, K, W, weights, layout, dev):
     ev.close()
 
     counts_np = [c.cpu().numpy() for c in counts]
-    work = alg_bytes_and_flops(cfg, counts_np, es, int8=layout == moe.MOE_LAYOUT_INT8_FRAG)
+    work = alg_bytes_and_flops(cfg, counts_np, es, one_byte=layout in (moe.MOE_LAYOUT_INT8_FRAG, moe.MOE_LAYOUT_FP8_FRAG))
     ms_per_step = elapsed * 1e3 / K
     kname = moe.moe_stage_kernel_name(shape, dom)
     if prefill:
@@ -626,6 +628,7 @@ def run_layer_bench(cfg, K, W, weights, layout, dev):
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
                    "d_hidden": cfg.H, "d_shared_hidden": cfg.Hs, "zipf_bias": cfg.zipf_s, "routing": cfg.routing,
                    "weight_layout": {moe.MOE_LAYOUT_FRAG16: "frag16", moe.MOE_LAYOUT_INT8_FRAG: "int8 per-row",
+                                     moe.MOE_LAYOUT_FP8_FRAG: "fp8 e4m3 per-row",
                                      moe.MOE_LAYOUT_ROWMAJOR: "rowmajor"}[layout],
                    "parallelism": "single GPU"},
         "roofline": roof,
@@ -712,7 +715,7 @@ def main():
             sub["frac_of_measured_read"] = round(sub["achieved"] / ceil["read_nontemporal_GBps"], 4)
     if not args.no_cpu_baseline:
         n_tok = args.cpu_sample_tokens or (8 if cfg.E > 8 else 16)
-        line["cpu_baseline"] = cpu_baseline(cfg, host, n_tok, int8=args.layout == "int8")
+        line["cpu_baseline"] = cpu_baseline(cfg, host, n_tok, quant=args.layout if args.layout in ("int8", "fp8") else None)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -64,9 +64,11 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum {
   MOE_LAYOUT_ROWMAJOR = 0, /* [out, in] row-major, like a linear layer's weight */
   MOE_LAYOUT_FRAG16 = 1,   /* fragment-tiled, see moe_pack_weights */
-  MOE_LAYOUT_INT8_FRAG = 2 /* INT8 codes with one float32 scale per output row, see
-                              moe_quantize_weights (bf16 layers; experts always run as the
-                              weight-streaming decode kernels) */
+  MOE_LAYOUT_INT8_FRAG = 2, /* INT8 codes with one float32 scale per output row, see
+                               moe_quantize_weights (bf16 layers; experts always run as the
+                               weight-streaming decode kernels) */
+  MOE_LAYOUT_FP8_FRAG = 3   /* FP8 E4M3 codes with one float32 scale per output row, in the same
+                               byte order, see moe_quantize_weights_fp8 (as INT8 otherwise) */
 } moe_weight_layout;
 
 /* How the router turns logits into the k experts and their weights. */
@@ -122,7 +124,37 @@ moe_status moe_pack_weights(const void* src, void* dst, int64_t n_mats, int32_t 
 moe_status moe_quantize_weights(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols,
                                 void* stream);
 
-/* Bytes of an MOE_LAYOUT_INT8_FRAG buffer of n_mats [rows, cols] matrices: codes plus scales. */
+/*
+ * moe_quantize_weights_fp8 -- the same as moe_quantize_weights with FP8 codes, for
+ * MOE_LAYOUT_FP8_FRAG (the same "1-byte weights" route of the inference-optimisation chapter; the
+ * pages fix no FP8 format, the format here is the OCP 8-bit float E4M3 "fn": 1 sign bit, 4 exponent
+ * bits with bias 7, 3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN, largest finite
+ * 448). For every row r of every matrix m:
+ *     s[m][r] = max_c |w[m][r][c]| / 448            (float32; 0 for an all-zero row)
+ *     q[m][r][c] = E4M3(w[m][r][c] / s[m][r])      (float32 division; the nearest E4M3 value, ties
+ *                                                    to the even code, 464 and above saturate to 448;
+ *                                                    never the NaN pattern)
+ * and the layer uses w ~ value(q) * s. Byte layout, buffer size (moe_quantized_weight_bytes) and
+ * argument rules as for moe_quantize_weights.
+ */
+moe_status moe_quantize_weights_fp8(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols,
+                                    void* stream);
+
+/*
+ * moe_dequantize_weights -- the float32 weights an MOE_LAYOUT_INT8_FRAG or MOE_LAYOUT_FP8_FRAG buffer
+ * (src, as written by moe_quantize_weights / moe_quantize_weights_fp8) stands for, row-major
+ * [n_mats, rows, cols]: dst[m][r][c] = value(q[m][r][c]) * s[m][r], one float32 multiplication,
+ * where value() is the code's integer (INT8) or E4M3 value (the NaN codes 0x7F / 0xFF, which the
+ * quantizers never write, give NaN). The code -> value step is the one the weight-streaming kernels
+ * run before their multiplications, so this shows exactly which weights the layer uses (inspection,
+ * export, checks). weight_layout other than those two: MOE_ERR_UNSUPPORTED. rows % 16 == 0,
+ * cols % 64 == 0; src and dst 16-byte aligned and not overlapping. Not part of the layer forward.
+ */
+moe_status moe_dequantize_weights(const void* src, int32_t weight_layout, float* dst, int64_t n_mats, int32_t rows,
+                                  int32_t cols, void* stream);
+
+/* Bytes of an MOE_LAYOUT_INT8_FRAG or MOE_LAYOUT_FP8_FRAG buffer of n_mats [rows, cols] matrices:
+ * codes plus scales. */
 size_t moe_quantized_weight_bytes(int64_t n_mats, int32_t rows, int32_t cols);
 
 /* Bytes of workspace that every entry point below accepts for shape `s` (0 if `s` is invalid). */

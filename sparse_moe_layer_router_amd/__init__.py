@@ -26,7 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20   # fixed device scratch of moe_layer_forward_noalloc
 MOE_CALIB_READ_BLOCKS, MOE_CALIB_MFMA_BLOCKS = 2048, 256   # workgroups (sink entries) of the probes
 MOE_F32, MOE_BF16 = 0, 1
-MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_FRAG16, MOE_LAYOUT_INT8_FRAG = 0, 1, 2
+MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_FRAG16, MOE_LAYOUT_INT8_FRAG, MOE_LAYOUT_FP8_FRAG = 0, 1, 2, 3
 MOE_ROUTING_SOFTMAX, MOE_ROUTING_SIGMOID = 0, 1
 STAGES = ["route_logits", "route_topk", "permute_count", "permute_scan", "permute_scatter", "ffn_schedule",
           "ffn_gate_up", "ffn_down", "combine"]
@@ -73,6 +73,9 @@ _sigs = {
     "moe_stage_kernel_name": (ctypes.c_char_p, [_S, ctypes.c_int]),
     "moe_pack_weights": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
     "moe_quantize_weights": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
+    "moe_quantize_weights_fp8": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
+    "moe_dequantize_weights": (ctypes.c_int, [_P, ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                              _P]),
     "moe_load_stats": (ctypes.c_int, [_S, _P, ctypes.c_float, _P, _P, _P]),
     "moe_quantized_weight_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
     # measurement probes (include/moe_calib.h)
@@ -252,13 +255,28 @@ def moe_quantized_weight_bytes(n_mats, rows, cols) -> int:
     return int(_lib.moe_quantized_weight_bytes(n_mats, rows, cols))
 
 
-def quantize_expert_weights(w_gate, w_up, w_down, shared=None, stream=None):
-    """INT8 buffers (uint8 tensors) of [E,H,d], [E,H,d], [E,d,H] (and an optional shared triple)."""
+def moe_quantize_weights_fp8(src, dst, n_mats, rows, cols, stream=None):
+    """FP8 E4M3 codes (fragment order) + per-row float32 scales of n_mats bf16 [rows, cols] matrices
+    (MOE_LAYOUT_FP8_FRAG)."""
+    _check("moe_quantize_weights_fp8", _lib.moe_quantize_weights_fp8(_ptr(src), _ptr(dst), n_mats, rows, cols,
+                                                                     _stream(stream)))
+
+
+def moe_dequantize_weights(src, weight_layout, dst, n_mats, rows, cols, stream=None):
+    """The float32 [n_mats, rows, cols] weights value(q) * s an INT8 or FP8 buffer stands for."""
+    _check("moe_dequantize_weights", _lib.moe_dequantize_weights(_ptr(src), weight_layout, _ptr(dst), n_mats, rows,
+                                                                 cols, _stream(stream)))
+
+
+def quantize_expert_weights(w_gate, w_up, w_down, shared=None, stream=None, fp8=False):
+    """INT8 (or, with fp8=True, FP8 E4M3) buffers (uint8 tensors) of [E,H,d], [E,H,d], [E,d,H] (and an
+    optional shared triple)."""
+    fn = moe_quantize_weights_fp8 if fp8 else moe_quantize_weights
     out = []
     for w in (w_gate, w_up, w_down) + (tuple(shared) if shared is not None else ()):
         n = 1 if w.dim() == 2 else w.shape[0]
         q = torch.empty(moe_quantized_weight_bytes(n, w.shape[-2], w.shape[-1]), dtype=torch.uint8, device=w.device)
-        moe_quantize_weights(w, q, n, w.shape[-2], w.shape[-1], stream)
+        fn(w, q, n, w.shape[-2], w.shape[-1], stream)
         out.append(q)
     return out
 

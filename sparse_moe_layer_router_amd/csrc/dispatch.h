@@ -73,10 +73,12 @@ hipError_t launch_gelu_up(const GeluGroups& g, hipStream_t stream);
 hipError_t launch_gelu_down(const GeluGroups& g, hipStream_t stream);
 const char* gelu_kernel_name(const GeluGroups& g, bool up);
 
-// ---- weight packing (MOE_LAYOUT_FRAG16) and INT8 quantization (MOE_LAYOUT_INT8_FRAG) --------------
+// ---- weight packing (MOE_LAYOUT_FRAG16) and INT8 / FP8 quantization (MOE_LAYOUT_INT8_FRAG / FP8_FRAG) ----
 hipError_t launch_pack_weights(const void* src, void* dst, long long n_mats, int rows, int cols, hipStream_t stream);
 size_t quantized_weight_bytes(long long n_mats, int rows, int cols);
-hipError_t launch_quantize_weights(const void* src, void* dst, long long n_mats, int rows, int cols,
+hipError_t launch_quantize_weights(const void* src, void* dst, long long n_mats, int rows, int cols, bool fp8,
                                    hipStream_t stream);
+hipError_t launch_dequantize_weights(const void* src, int layout, float* dst, long long n_mats, int rows, int cols,
+                                     hipStream_t stream);
 
 }  // namespace moe

@@ -13,6 +13,7 @@
 // the MFMA; gate and up share one B-fragment and their accumulators have identical layouts, so
 // SiLU(g) * u is formed in registers and stored as bf16. The down projection is the same loop
 // with W_down rows against the stored hidden rows.
+#include "codes.h"
 #include "kernels.h"
 #include "moe_device.h"
 
@@ -33,10 +34,10 @@ struct GroupView {
   long long r0;        // first row of the group in the (routed or shared) row space
   int n;               // rows in the group
   int Hg;              // hidden size of the group's expert
-  const void* wg;      // [Hg, d] (bf16, or INT8 codes in the fragment order)
+  const void* wg;      // [Hg, d] (bf16, or one-byte INT8 / E4M3 codes in the fragment order)
   const void* wu;      // [Hg, d]
   const void* wd;      // [d, Hg]
-  const float* sg;     // INT8 weights: per-row scales of wg [Hg], wu [Hg], wd [d]
+  const float* sg;     // one-byte weights: per-row scales of wg [Hg], wu [Hg], wd [d]
   const float* su;
   const float* sd;
   uint16_t* hid;       // hidden rows of this row space, row stride Hg
@@ -44,7 +45,7 @@ struct GroupView {
   bool routed;
 };
 
-// INT8 expert weights (MOE_LAYOUT_INT8_FRAG): a buffer of n matrices holds n * rows * cols one-byte
+// One-byte expert weights (MOE_LAYOUT_INT8_FRAG, MOE_LAYOUT_FP8_FRAG): a buffer of n matrices holds n * rows * cols one-byte
 // codes followed by n * rows float32 row scales.
 __device__ __forceinline__ const float* row_scales(const void* codes, long long n_codes) {
   return (const float*)((const int8_t*)codes + n_codes);
@@ -55,7 +56,7 @@ __device__ __forceinline__ const float* row_scales(const void* codes, long long 
 // the chunks run side by side instead of one group re-streaming the weights for every token tile.
 __device__ __forceinline__ GroupView group_view(const FfnGroups& p, int g, int chunk) {
   GroupView v;
-  const bool q8 = p.layout == kInt8Frag;
+  const bool q8 = byte_codes(p.layout);
   const size_t eb = q8 ? 1 : 2;  // bytes per weight element
   v.sg = v.su = v.sd = nullptr;
   if (g < p.E) {
@@ -124,24 +125,10 @@ __device__ __forceinline__ const uint16_t* frag_base(const void* wv, int r0, int
   return w + (size_t)r * K + (lane >> 4) * 8;
 }
 
-// INT8 fragment order: 1 KB block (r0/16, s2) covers 64 columns, lane's 16 bytes = its A-operand
+// One-byte fragment order: 1 KB block (r0/16, s2) covers 64 columns, lane's 16 bytes = its A-operand
 // chunk of k-steps 2*s2 and 2*s2+1; base + s2 * 1024 bytes.
 __device__ __forceinline__ const int8_t* q8_base(const void* wv, int r0, int K, int lane) {
   return (const int8_t*)wv + (size_t)(r0 / 16) * (K / 64) * 1024 + lane * 16;
-}
-
-// Eight int8 codes (two little-endian words) -> the eight bf16 values (exact: |q| <= 127).
-__device__ __forceinline__ u32x4_t i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  u32x4_t r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = i < 2 ? lo : hi;
-    const int b = (i & 1) * 2;  // byte index of the pair's first code
-    const float f0 = (float)((int32_t)(w << (24 - 8 * b)) >> 24);
-    const float f1 = (float)((int32_t)(w << (16 - 8 * b)) >> 24);
-    r[i] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-  }
-  return r;
 }
 
 template <int NTT, int LAYOUT>
@@ -159,7 +146,7 @@ ffn_gate_up_stream(const FfnGroups p) {
   const uint16_t* au = nullptr;
   const int8_t* qg = nullptr;
   const int8_t* qu = nullptr;
-  if (LAYOUT == kInt8Frag) {
+  if (byte_codes(LAYOUT)) {
     qg = q8_base(v.wg, h0, d, lane);
     qu = q8_base(v.wu, h0, d, lane);
   } else {
@@ -183,7 +170,7 @@ ffn_gate_up_stream(const FfnGroups p) {
     for (int j = 0; j < NTT; ++j) { accg[j] = f32x4_t{0, 0, 0, 0}; accu[j] = f32x4_t{0, 0, 0, 0}; }
     const u32x4_t zero = {0, 0, 0, 0};
     int k0 = 0;
-    if (LAYOUT == kInt8Frag) {
+    if (byte_codes(LAYOUT)) {
       // d is a multiple of 64: every load covers two whole k-steps
       for (; k0 + 32 * kUnroll <= d; k0 += 32 * kUnroll) {
         u32x4_t r_g[kUnroll / 2], r_u[kUnroll / 2], b[kUnroll][NTT];
@@ -198,8 +185,8 @@ ffn_gate_up_stream(const FfnGroups p) {
           for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bx[j] + k0 + 32 * s) : zero;
 #pragma unroll
         for (int s2 = 0; s2 < kUnroll / 2; ++s2) {
-          const u32x4_t g0 = i8x8_to_bf16x8(r_g[s2][0], r_g[s2][1]), g1 = i8x8_to_bf16x8(r_g[s2][2], r_g[s2][3]);
-          const u32x4_t u0 = i8x8_to_bf16x8(r_u[s2][0], r_u[s2][1]), u1 = i8x8_to_bf16x8(r_u[s2][2], r_u[s2][3]);
+          const u32x4_t g0 = codes_to_bf16x8<LAYOUT>(r_g[s2][0], r_g[s2][1]), g1 = codes_to_bf16x8<LAYOUT>(r_g[s2][2], r_g[s2][3]);
+          const u32x4_t u0 = codes_to_bf16x8<LAYOUT>(r_u[s2][0], r_u[s2][1]), u1 = codes_to_bf16x8<LAYOUT>(r_u[s2][2], r_u[s2][3]);
 #pragma unroll
           for (int j = 0; j < NTT; ++j) {
             accg[j] = mfma16x16x32(g0, b[2 * s2][j], accg[j]);
@@ -212,8 +199,8 @@ ffn_gate_up_stream(const FfnGroups p) {
       for (; k0 < d; k0 += 64) {
         const u32x4_t r_g = ld16_stream(qg + (size_t)(k0 / 64) * 1024);
         const u32x4_t r_u = ld16_stream(qu + (size_t)(k0 / 64) * 1024);
-        const u32x4_t g0 = i8x8_to_bf16x8(r_g[0], r_g[1]), g1 = i8x8_to_bf16x8(r_g[2], r_g[3]);
-        const u32x4_t u0 = i8x8_to_bf16x8(r_u[0], r_u[1]), u1 = i8x8_to_bf16x8(r_u[2], r_u[3]);
+        const u32x4_t g0 = codes_to_bf16x8<LAYOUT>(r_g[0], r_g[1]), g1 = codes_to_bf16x8<LAYOUT>(r_g[2], r_g[3]);
+        const u32x4_t u0 = codes_to_bf16x8<LAYOUT>(r_u[0], r_u[1]), u1 = codes_to_bf16x8<LAYOUT>(r_u[2], r_u[3]);
 #pragma unroll
         for (int j = 0; j < NTT; ++j) {
           const u32x4_t b0 = bok[j] ? ld16(bx[j] + k0) : zero;
@@ -256,10 +243,10 @@ ffn_gate_up_stream(const FfnGroups p) {
         }
       }
     }
-    // lane holds rows h0 + kq*4 + {0..3} of token column (lane & 15); INT8 rows carry their scale
+    // lane holds rows h0 + kq*4 + {0..3} of token column (lane & 15); one-byte rows carry their scale
     const int h = h0 + kq * 4;
     f32x4_t sg = {1.f, 1.f, 1.f, 1.f}, su = {1.f, 1.f, 1.f, 1.f};
-    if (LAYOUT == kInt8Frag && h < v.Hg) {
+    if (byte_codes(LAYOUT) && h < v.Hg) {
       sg = *(const f32x4_t*)(v.sg + h);
       su = *(const f32x4_t*)(v.su + h);
     }
@@ -268,7 +255,7 @@ ffn_gate_up_stream(const FfnGroups p) {
       const int rr = tt + j * 16 + ar;
       if (rr < v.n && h < v.Hg) {
         f32x4_t g = accg[j], u = accu[j];
-        if (LAYOUT == kInt8Frag) {
+        if (byte_codes(LAYOUT)) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) { g[e] *= sg[e]; u[e] *= su[e]; }
         }
@@ -294,7 +281,7 @@ ffn_down_stream(const FfnGroups p) {
   int ws = 0;
   const uint16_t* aw = nullptr;
   const int8_t* qw = nullptr;
-  if (LAYOUT == kInt8Frag)
+  if (byte_codes(LAYOUT))
     qw = q8_base(v.wd, i0, K, lane);
   else
     aw = frag_base<LAYOUT>(v.wd, i0, d, K, lane, &ws);
@@ -313,7 +300,7 @@ ffn_down_stream(const FfnGroups p) {
     for (int j = 0; j < NTT; ++j) acc[j] = f32x4_t{0, 0, 0, 0};
     const u32x4_t zero = {0, 0, 0, 0};
     int k0 = 0;
-    if (LAYOUT == kInt8Frag) {
+    if (byte_codes(LAYOUT)) {
       for (; k0 + 32 * kUnroll <= K; k0 += 32 * kUnroll) {
         u32x4_t r[kUnroll / 2], b[kUnroll][NTT];
 #pragma unroll
@@ -324,7 +311,7 @@ ffn_down_stream(const FfnGroups p) {
           for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bh[j] + k0 + 32 * s) : zero;
 #pragma unroll
         for (int s2 = 0; s2 < kUnroll / 2; ++s2) {
-          const u32x4_t a0 = i8x8_to_bf16x8(r[s2][0], r[s2][1]), a1 = i8x8_to_bf16x8(r[s2][2], r[s2][3]);
+          const u32x4_t a0 = codes_to_bf16x8<LAYOUT>(r[s2][0], r[s2][1]), a1 = codes_to_bf16x8<LAYOUT>(r[s2][2], r[s2][3]);
 #pragma unroll
           for (int j = 0; j < NTT; ++j) {
             acc[j] = mfma16x16x32(a0, b[2 * s2][j], acc[j]);
@@ -334,7 +321,7 @@ ffn_down_stream(const FfnGroups p) {
       }
       for (; k0 < K; k0 += 64) {  // K (the hidden size) is a multiple of 64
         const u32x4_t r = ld16_stream(qw + (size_t)(k0 / 64) * 1024);
-        const u32x4_t a0 = i8x8_to_bf16x8(r[0], r[1]), a1 = i8x8_to_bf16x8(r[2], r[3]);
+        const u32x4_t a0 = codes_to_bf16x8<LAYOUT>(r[0], r[1]), a1 = codes_to_bf16x8<LAYOUT>(r[2], r[3]);
 #pragma unroll
         for (int j = 0; j < NTT; ++j) {
           acc[j] = mfma16x16x32(a0, bok[j] ? ld16(bh[j] + k0) : zero, acc[j]);
@@ -367,13 +354,13 @@ ffn_down_stream(const FfnGroups p) {
     }
     const int i = i0 + kq * 4;
     f32x4_t sc = {1.f, 1.f, 1.f, 1.f};
-    if (LAYOUT == kInt8Frag && i < d) sc = *(const f32x4_t*)(v.sd + i);
+    if (byte_codes(LAYOUT) && i < d) sc = *(const f32x4_t*)(v.sd + i);
 #pragma unroll
     for (int j = 0; j < NTT; ++j) {
       const int rr = tt + j * 16 + ar;
       if (rr < v.n && i < d) {
         f32x4_t y = acc[j];
-        if (LAYOUT == kInt8Frag) {
+        if (byte_codes(LAYOUT)) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[e] *= sc[e];
         }
@@ -460,7 +447,7 @@ ffn_down_f32(const FfnGroups p) {
 
 // --------------------------------------------------------------------------------- launchers
 namespace {
-int stream_ntt(const FfnGroups& g) { return g.layout != kInt8Frag && g.T > 16 ? 2 : 1; }
+int stream_ntt(const FfnGroups& g) { return !byte_codes(g.layout) && g.T > 16 ? 2 : 1; }
 // routed groups + one group per 16 NTT-row chunk of the shared expert
 int groups_of(const FfnGroups& g) {
   const int c = 16 * stream_ntt(g);
@@ -472,7 +459,7 @@ long long all_rows(const FfnGroups& g) { return g.rows + (g.Hs > 0 ? g.T : 0); }
 
 FfnPath ffn_path(const FfnGroups& g) {
   if (g.dtype == kF32) return kPathF32;
-  if (g.layout == kInt8Frag) return kPathStream;  // INT8 weights are a decode (weight-streaming) format
+  if (byte_codes(g.layout)) return kPathStream;  // one-byte weights are a decode (weight-streaming) format
   return g.mean_rows_per_group >= kGemmMinRowsPerExpert ? kPathGemm : kPathStream;
 }
 
@@ -481,6 +468,8 @@ hipError_t launch_ffn_gate_up_stream(const FfnGroups& g, hipStream_t stream) {
   const bool two = stream_ntt(g) == 2;
   if (g.layout == kInt8Frag)
     hipLaunchKernelGGL((ffn_gate_up_stream<1, kInt8Frag>), grid, dim3(256), 0, stream, g);
+  else if (g.layout == kFp8Frag)
+    hipLaunchKernelGGL((ffn_gate_up_stream<1, kFp8Frag>), grid, dim3(256), 0, stream, g);
   else if (g.layout == kFrag16 && two)
     hipLaunchKernelGGL((ffn_gate_up_stream<2, kFrag16>), grid, dim3(256), 0, stream, g);
   else if (g.layout == kFrag16)
@@ -497,6 +486,8 @@ hipError_t launch_ffn_down_stream(const FfnGroups& g, hipStream_t stream) {
   const bool two = stream_ntt(g) == 2;
   if (g.layout == kInt8Frag)
     hipLaunchKernelGGL((ffn_down_stream<1, kInt8Frag>), grid, dim3(256), 0, stream, g);
+  else if (g.layout == kFp8Frag)
+    hipLaunchKernelGGL((ffn_down_stream<1, kFp8Frag>), grid, dim3(256), 0, stream, g);
   else if (g.layout == kFrag16 && two)
     hipLaunchKernelGGL((ffn_down_stream<2, kFrag16>), grid, dim3(256), 0, stream, g);
   else if (g.layout == kFrag16)
@@ -528,6 +519,7 @@ const char* ffn_gate_up_kernel_name(const FfnGroups& g) {
     case kPathF32: return "ffn_gate_up_f32";
     case kPathStream:
       if (g.layout == kInt8Frag) return "ffn_gate_up_stream<1, 2>";
+      if (g.layout == kFp8Frag) return "ffn_gate_up_stream<1, 3>";
       if (stream_ntt(g) == 2) return g.layout == kFrag16 ? "ffn_gate_up_stream<2, 1>" : "ffn_gate_up_stream<2, 0>";
       return g.layout == kFrag16 ? "ffn_gate_up_stream<1, 1>" : "ffn_gate_up_stream<1, 0>";
     default:
@@ -540,6 +532,7 @@ const char* ffn_down_kernel_name(const FfnGroups& g) {
     case kPathF32: return "ffn_down_f32";
     case kPathStream:
       if (g.layout == kInt8Frag) return "ffn_down_stream<1, 2>";
+      if (g.layout == kFp8Frag) return "ffn_down_stream<1, 3>";
       if (stream_ntt(g) == 2) return g.layout == kFrag16 ? "ffn_down_stream<2, 1>" : "ffn_down_stream<2, 0>";
       return g.layout == kFrag16 ? "ffn_down_stream<1, 1>" : "ffn_down_stream<1, 0>";
     default:

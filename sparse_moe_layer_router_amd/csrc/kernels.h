@@ -19,7 +19,9 @@ enum Dtype { kF32 = 0, kBF16 = 1 };
 // A set of expert groups: routed groups 0..E-1 take rows [offsets[g], offsets[g+1]) of the
 // dispatched order (source token perm_src[r] / k, or r when perm_src is NULL); the optional
 // shared group (index E) takes rows [shared_row0, shared_row0 + T) with source token r - row0.
-enum WeightLayout { kRowMajor = 0, kFrag16 = 1, kInt8Frag = 2 };
+enum WeightLayout { kRowMajor = 0, kFrag16 = 1, kInt8Frag = 2, kFp8Frag = 3 };
+// One-byte weight codes (INT8 or FP8 E4M3) in the same fragment order, with float32 row scales.
+__host__ __device__ constexpr bool byte_codes(int layout) { return layout == kInt8Frag || layout == kFp8Frag; }
 
 // Offset (elements) of element (r, c) of a [rows, cols] matrix in the fragment-tiled layout:
 // 16 x 32 blocks along each 16-row band; inside a block, 64 lanes x 8 consecutive columns in the

@@ -65,7 +65,7 @@ moe_status check_shape(const moe_shape* s) {
   if ((long long)s->T * s->top_k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (s->d_model % 8 || s->d_hidden % 8 || s->d_shared_hidden % 8) return MOE_ERR_ALIGNMENT;
   if (s->weight_layout != MOE_LAYOUT_ROWMAJOR && s->weight_layout != MOE_LAYOUT_FRAG16 &&
-      s->weight_layout != MOE_LAYOUT_INT8_FRAG)
+      s->weight_layout != MOE_LAYOUT_INT8_FRAG && s->weight_layout != MOE_LAYOUT_FP8_FRAG)
     return MOE_ERR_UNSUPPORTED;
   if (s->routing != MOE_ROUTING_SOFTMAX && s->routing != MOE_ROUTING_SIGMOID) return MOE_ERR_UNSUPPORTED;
   if (s->weight_layout == MOE_LAYOUT_FRAG16) {
@@ -73,7 +73,7 @@ moe_status check_shape(const moe_shape* s) {
     if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (s->d_model % 32 || s->d_hidden % 32 || s->d_shared_hidden % 32) return MOE_ERR_ALIGNMENT;
   }
-  if (s->weight_layout == MOE_LAYOUT_INT8_FRAG) {
+  if (s->weight_layout == MOE_LAYOUT_INT8_FRAG || s->weight_layout == MOE_LAYOUT_FP8_FRAG) {
     // every expert matrix tiles into 16 x 64 blocks of codes
     if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (s->d_model % 64 || s->d_hidden % 64 || s->d_shared_hidden % 64) return MOE_ERR_ALIGNMENT;
@@ -360,8 +360,9 @@ moe_status moe_load_stats(const moe_shape* s, const int32_t* expert_counts, floa
   return MOE_OK;
 }
 
-moe_status moe_quantize_weights(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols,
-                                void* stream) {
+namespace {
+moe_status quantize_impl(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols, bool fp8,
+                         void* stream) {
   if (n_mats < 0 || rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
   if (rows % 16 || cols % 64) return MOE_ERR_ALIGNMENT;
   if (n_mats == 0 || rows == 0 || cols == 0) return MOE_OK;
@@ -371,7 +372,34 @@ moe_status moe_quantize_weights(const void* src, void* dst, int64_t n_mats, int3
   const uintptr_t out = moe::quantized_weight_bytes(n_mats, rows, cols);
   const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
   if (a < b + out && b < a + in) return MOE_ERR_INVALID_ARG;  // overlapping buffers
-  MOE_LAUNCH(moe::launch_quantize_weights(src, dst, n_mats, rows, cols, (hipStream_t)stream));
+  MOE_LAUNCH(moe::launch_quantize_weights(src, dst, n_mats, rows, cols, fp8, (hipStream_t)stream));
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_quantize_weights(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols,
+                                void* stream) {
+  return quantize_impl(src, dst, n_mats, rows, cols, false, stream);
+}
+
+moe_status moe_quantize_weights_fp8(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols,
+                                    void* stream) {
+  return quantize_impl(src, dst, n_mats, rows, cols, true, stream);
+}
+
+moe_status moe_dequantize_weights(const void* src, int32_t weight_layout, float* dst, int64_t n_mats, int32_t rows,
+                                  int32_t cols, void* stream) {
+  if (weight_layout != MOE_LAYOUT_INT8_FRAG && weight_layout != MOE_LAYOUT_FP8_FRAG) return MOE_ERR_UNSUPPORTED;
+  if (n_mats < 0 || rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
+  if (rows % 16 || cols % 64) return MOE_ERR_ALIGNMENT;
+  if (n_mats == 0 || rows == 0 || cols == 0) return MOE_OK;
+  MOE_TRY(need(src, 16));
+  MOE_TRY(need(dst, 16));
+  const uintptr_t in = moe::quantized_weight_bytes(n_mats, rows, cols);
+  const uintptr_t out = (uintptr_t)n_mats * (uintptr_t)rows * (uintptr_t)cols * 4;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + out && b < a + in) return MOE_ERR_INVALID_ARG;  // overlapping buffers
+  MOE_LAUNCH(moe::launch_dequantize_weights(src, weight_layout, dst, n_mats, rows, cols, (hipStream_t)stream));
   return MOE_OK;
 }
 

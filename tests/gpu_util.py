@@ -50,14 +50,15 @@ class DeviceLayer:
         return moe.make_shape(c.T, c.d, c.E, c.k, c.H, c.Hs, c.dtype, self.layout, c.routing)
 
     @property
-    def int8(self) -> bool:
-        return self.layout == moe.MOE_LAYOUT_INT8_FRAG
+    def quant(self):
+        """One-byte weight format of the layout ("int8", "fp8"), or None for bf16 / fp32 weights."""
+        return {moe.MOE_LAYOUT_INT8_FRAG: "int8", moe.MOE_LAYOUT_FP8_FRAG: "fp8"}.get(self.layout)
 
     def expert_fn(self, cache=True):
-        return helpers.expert_fn_host(self.cfg, self.seed, self.stacked_host, cache=cache, int8=self.int8)
+        return helpers.expert_fn_host(self.cfg, self.seed, self.stacked_host, cache=cache, quant=self.quant)
 
     def shared_fn(self):
-        return helpers.shared_fn_host(self.cfg, self.seed, int8=self.int8)
+        return helpers.shared_fn_host(self.cfg, self.seed, quant=self.quant)
 
 
 def make_weights(cfg: synth.LayerConfig, seed: int, host_copy: bool):
@@ -91,11 +92,12 @@ def packed_weights(weights):
     return (tuple(out[:3]), tuple(out[3:]) if sh else (None, None, None), stacked)
 
 
-def int8_weights(weights):
-    """Per-row INT8 copies of the same bf16 weights (MOE_LAYOUT_INT8_FRAG buffers)."""
+def int8_weights(weights, fp8=False):
+    """Per-row INT8 (or FP8 E4M3) copies of the same bf16 weights (MOE_LAYOUT_INT8_FRAG or
+    MOE_LAYOUT_FP8_FRAG buffers)."""
     (g, u, dn), shared, stacked = weights
     sh = tuple(shared) if shared[0] is not None else None
-    out = moe.quantize_expert_weights(g, u, dn, sh)
+    out = moe.quantize_expert_weights(g, u, dn, sh, fp8=fp8)
     torch.cuda.synchronize()
     return (tuple(out[:3]), tuple(out[3:]) if sh else (None, None, None), stacked)
 
@@ -112,6 +114,8 @@ def make_layer(cfg: synth.LayerConfig, seed: int = 0, screen: bool = True, weigh
             weights = packed_weights(weights)
         elif layout == moe.MOE_LAYOUT_INT8_FRAG:
             weights = int8_weights(weights)
+        elif layout == moe.MOE_LAYOUT_FP8_FRAG:
+            weights = int8_weights(weights, fp8=True)
     (g, u, dn), (sg, su, sd), stacked = weights
     bias = torch.from_numpy(host.router_bias).cuda() if host.router_bias is not None else None
     return DeviceLayer(cfg, seed, host, to_dev(host.x, cfg.dtype), to_dev(host.w_router, cfg.dtype), bias,

@@ -33,15 +33,21 @@ def screen_gaps(inp: synth.HostInputs, min_gap: float = MIN_GAP, max_rounds: int
     raise RuntimeError("gap screening did not converge")
 
 
-def as_oracle_weight(a, dtype: str, int8: bool):
-    """float64 weight the oracle uses: the stored value, or the dequantized INT8 per-row code."""
+def as_oracle_weight(a, dtype: str, quant=None):
+    """float64 weight the oracle uses: the stored value, or the dequantized per-row one-byte code
+    (quant "int8" or "fp8")."""
     w = oracle.widen(a, dtype)
-    return oracle.dequantize_rows_int8(*oracle.quantize_rows_int8(w)) if int8 else w
+    if quant == "int8":
+        return oracle.dequantize_rows_int8(*oracle.quantize_rows_int8(w))
+    if quant == "fp8":
+        return oracle.dequantize_rows_fp8(*oracle.quantize_rows_fp8(w))
+    assert quant is None, quant
+    return w
 
 
-def expert_fn_host(cfg: synth.LayerConfig, seed: int, stacked=None, cache: bool = True, int8: bool = False):
+def expert_fn_host(cfg: synth.LayerConfig, seed: int, stacked=None, cache: bool = True, quant=None):
     """float64 expert weights for the oracle, regenerated on the host from the generator streams
-    (dequantized from their per-row INT8 codes when ``int8``).
+    (dequantized from their per-row one-byte codes when ``quant`` is "int8" or "fp8").
 
     ``cache=False`` regenerates on every call (large layers: one expert in memory at a time)."""
     store = {}
@@ -51,7 +57,7 @@ def expert_fn_host(cfg: synth.LayerConfig, seed: int, stacked=None, cache: bool 
             g, u, dn = (s[e] for s in stacked)
         else:
             g, u, dn = synth.expert_weights_host(cfg, seed, e)
-        return tuple(as_oracle_weight(a, cfg.dtype, int8) for a in (g, u, dn))
+        return tuple(as_oracle_weight(a, cfg.dtype, quant) for a in (g, u, dn))
 
     def fn(e):
         if not cache:
@@ -63,14 +69,14 @@ def expert_fn_host(cfg: synth.LayerConfig, seed: int, stacked=None, cache: bool 
     return fn
 
 
-def shared_fn_host(cfg: synth.LayerConfig, seed: int, int8: bool = False):
+def shared_fn_host(cfg: synth.LayerConfig, seed: int, quant=None):
     if cfg.Hs == 0:
         return None
     box = {}
 
     def fn():
         if "w" not in box:
-            box["w"] = tuple(as_oracle_weight(a, cfg.dtype, int8)
+            box["w"] = tuple(as_oracle_weight(a, cfg.dtype, quant)
                              for a in synth.expert_weights_host(cfg, seed, 0, shared=True))
         return box["w"]
 

@@ -22,7 +22,7 @@ def header_functions():
     inc = os.path.join(ROOT, "include")
     src = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -164,7 +164,11 @@ def test_status_strings_and_stage_names():
     (dict(weight_layout=moe.MOE_LAYOUT_INT8_FRAG, d_model=7200), moe.MOE_ERR_ALIGNMENT),
     (dict(weight_layout=moe.MOE_LAYOUT_INT8_FRAG, d_hidden=2080), moe.MOE_ERR_ALIGNMENT),
     (dict(weight_layout=moe.MOE_LAYOUT_INT8_FRAG, d_shared_hidden=2080), moe.MOE_ERR_ALIGNMENT),
-    (dict(weight_layout=3), moe.MOE_ERR_UNSUPPORTED),
+    (dict(weight_layout=moe.MOE_LAYOUT_FP8_FRAG), moe.MOE_OK),
+    (dict(weight_layout=moe.MOE_LAYOUT_FP8_FRAG, dtype=moe.MOE_F32), moe.MOE_ERR_UNSUPPORTED),
+    (dict(weight_layout=moe.MOE_LAYOUT_FP8_FRAG, d_model=7200), moe.MOE_ERR_ALIGNMENT),
+    (dict(weight_layout=moe.MOE_LAYOUT_FP8_FRAG, d_hidden=2080), moe.MOE_ERR_ALIGNMENT),
+    (dict(weight_layout=4), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_int8_layout_validation(shape, status):
     s = dsv3(**shape)
@@ -173,12 +177,12 @@ def test_int8_layout_validation(shape, status):
         assert status_of(moe.moe_layer_forward, s, **layer(s)) == status
 
 
-def test_int8_stage_names_always_stream():
-    q8 = moe.MOE_LAYOUT_INT8_FRAG
-    assert moe.moe_stage_kernel_name(dsv3(weight_layout=q8), 6) == "ffn_gate_up_stream<1, 2>"
-    assert moe.moe_stage_kernel_name(dsv3(weight_layout=q8), 7) == "ffn_down_stream<1, 2>"
-    big = dsv3(T=8192, weight_layout=q8)     # would be the grouped GEMM with bf16 weights
-    assert moe.moe_stage_kernel_name(big, 5) == "" and moe.moe_stage_kernel_name(big, 6) == "ffn_gate_up_stream<1, 2>"
+@pytest.mark.parametrize("layout,code", [(moe.MOE_LAYOUT_INT8_FRAG, 2), (moe.MOE_LAYOUT_FP8_FRAG, 3)])
+def test_one_byte_stage_names_always_stream(layout, code):
+    assert moe.moe_stage_kernel_name(dsv3(weight_layout=layout), 6) == f"ffn_gate_up_stream<1, {code}>"
+    assert moe.moe_stage_kernel_name(dsv3(weight_layout=layout), 7) == f"ffn_down_stream<1, {code}>"
+    big = dsv3(T=8192, weight_layout=layout)     # would be the grouped GEMM with bf16 weights
+    assert moe.moe_stage_kernel_name(big, 5) == "" and moe.moe_stage_kernel_name(big, 6) == f"ffn_gate_up_stream<1, {code}>"
 
 
 def test_load_stats_validation():
@@ -190,8 +194,8 @@ def test_load_stats_validation():
     assert status_of(moe.moe_load_stats, dsv3(top_k=0), A, 0.01, A, A) == moe.MOE_ERR_INVALID_ARG
 
 
-def test_quantize_weights_validation():
-    q = moe.moe_quantize_weights
+@pytest.mark.parametrize("q", [moe.moe_quantize_weights, moe.moe_quantize_weights_fp8])
+def test_quantize_weights_validation(q):
     assert moe.moe_quantized_weight_bytes(2, 16, 64) == 2 * 16 * 64 + 2 * 16 * 4
     assert moe.moe_quantized_weight_bytes(-1, 16, 64) == 0
     assert status_of(q, A, B, 1, 8, 64) == moe.MOE_ERR_ALIGNMENT      # rows % 16
@@ -201,6 +205,20 @@ def test_quantize_weights_validation():
     assert status_of(q, A + 8, B, 1, 16, 64) == moe.MOE_ERR_ALIGNMENT
     assert status_of(q, A, A + 1024, 1, 16, 64) == moe.MOE_ERR_INVALID_ARG   # overlapping
     assert status_of(q, None, None, 0, 16, 64) == moe.MOE_OK                 # nothing to do
+
+
+@pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_INT8_FRAG, moe.MOE_LAYOUT_FP8_FRAG])
+def test_dequantize_weights_validation(layout):
+    dq = moe.moe_dequantize_weights
+    for other in (moe.MOE_LAYOUT_ROWMAJOR, moe.MOE_LAYOUT_FRAG16, 4):
+        assert status_of(dq, A, other, B, 1, 16, 64) == moe.MOE_ERR_UNSUPPORTED
+    assert status_of(dq, A, layout, B, 1, 8, 64) == moe.MOE_ERR_ALIGNMENT       # rows % 16
+    assert status_of(dq, A, layout, B, 1, 16, 32) == moe.MOE_ERR_ALIGNMENT      # cols % 64
+    assert status_of(dq, A, layout, B, -1, 16, 64) == moe.MOE_ERR_INVALID_ARG
+    assert status_of(dq, A, layout, None, 1, 16, 64) == moe.MOE_ERR_INVALID_ARG
+    assert status_of(dq, A, layout, B + 4, 1, 16, 64) == moe.MOE_ERR_ALIGNMENT
+    assert status_of(dq, A, layout, A + 1024, 1, 16, 64) == moe.MOE_ERR_INVALID_ARG   # overlapping
+    assert status_of(dq, None, layout, None, 0, 16, 64) == moe.MOE_OK                 # nothing to do
 
 
 def test_empty_batch_accepts_null_tensors():

@@ -58,7 +58,7 @@ def test_int8_weights_count_one_byte_per_weight_plus_row_scales():
     cfg = synth.CONFIG_BY_NAME["dsv3_decode_t8"]
     counts = np.ones(cfg.E, dtype=np.int64)
     w16 = bench.alg_bytes_and_flops(cfg, [counts], 2)
-    w8 = bench.alg_bytes_and_flops(cfg, [counts], 2, int8=True)
+    w8 = bench.alg_bytes_and_flops(cfg, [counts], 2, one_byte=True)
     weights = cfg.E * 3 * cfg.d * cfg.H + 3 * cfg.d * cfg.Hs
     rows = cfg.E * (2 * cfg.H + cfg.d) + 2 * cfg.Hs + cfg.d     # one float scale per weight row
     assert w16["layer"] - w8["layer"] == weights - 4 * rows

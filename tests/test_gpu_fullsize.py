@@ -100,7 +100,7 @@ DSV3_IDS = [f"{c.name}-{lay}" for c, lay in DSV3_CASES]
 @pytest.fixture(scope="module")
 def dsv3_weights():
     w = G.make_weights(DSV3, 0, host_copy=False)
-    yield {"rowmajor": w, "frag16": G.packed_weights(w), "int8": G.int8_weights(w)}
+    yield {"rowmajor": w, "frag16": G.packed_weights(w), "int8": G.int8_weights(w), "fp8": G.int8_weights(w, fp8=True)}
     del w
     torch.cuda.empty_cache()
 
@@ -134,12 +134,15 @@ def test_dsv3_layer(case, dsv3_runs):
     check_run(dsv3_runs[case])
 
 
+@pytest.mark.parametrize("quant", ["int8", "fp8"])
 @pytest.mark.parametrize("name,n_sample", [("dsv3_decode_t8", None), ("dsv3_decode_t256", 12)])
-def test_dsv3_layer_int8_weights(name, n_sample, dsv3_weights):
-    """Per-row INT8 expert weights at the decode sizes, against the oracle on the dequantized weights."""
+def test_dsv3_layer_one_byte_weights(name, n_sample, quant, dsv3_weights):
+    """Per-row INT8 or FP8 expert weights at the decode sizes, against the oracle on the dequantized
+    weights."""
     cfg = synth.CONFIG_BY_NAME[name]
-    print(f"[{name}-int8] moe_layer_forward", flush=True)
-    L = G.make_layer(cfg, weights=dsv3_weights["int8"], layout=moe.MOE_LAYOUT_INT8_FRAG)
+    print(f"[{name}-{quant}] moe_layer_forward", flush=True)
+    layout = {"int8": moe.MOE_LAYOUT_INT8_FRAG, "fp8": moe.MOE_LAYOUT_FP8_FRAG}[quant]
+    L = G.make_layer(cfg, weights=dsv3_weights[quant], layout=layout)
     r = G.run_layer(L)
     check_logits_close(L, r)
     check_routing_on_gpu_logits(L, r)
