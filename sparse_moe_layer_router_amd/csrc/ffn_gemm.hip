@@ -32,11 +32,15 @@
 // last MFMA that needs the register it overwrites. A 16-byte-chunk XOR swizzle (activations) and
 // the fragment-tiled weight layout keep fragment reads bank-conflict free.
 //
-// Tile order: tiles are numbered expert by expert, N-tile by N-tile, with the M-tiles of one
-// (expert, N-tile) adjacent, and each XCD takes a contiguous range of that order, the ranges cut
-// by the schedule kernel so that they hold equal work. Workgroups are dealt round-robin to the 8
-// XCDs, so block L runs the (L / 8)-th tile of XCD L % 8's range: the N-tiles of one expert run at
-// the same time on the same XCD and share its activation rows in that XCD's L2.
+// Tile order: tiles are numbered expert by expert; within an expert, its M-tiles are taken in blocks
+// of up to eight, and a block's tiles run N-tile by N-tile with the block's M-tiles adjacent. Each
+// XCD takes a contiguous range of that order, the ranges cut by the schedule kernel so that they
+// hold equal work. Workgroups are dealt round-robin to the 8 XCDs, so block L runs the (L / 8)-th
+// tile of XCD L % 8's range, and an XCD's 32 CUs run 32 consecutive tiles at a time: the N-tiles of
+// a one-M-tile expert (every routed bucket of a prefill batch) share its activation rows in the
+// XCD's L2; for an expert of many M-tiles (the shared expert over all tokens, a heavily loaded
+// expert) they form an 8 x 4 patch that shares 4 weight tiles and 8 activation blocks, where one
+// N-tile over all its M-tiles would re-read every activation row once per N-tile.
 #include "kernels.h"
 #include "moe_device.h"
 
@@ -52,6 +56,7 @@ constexpr int kXcds = 8;
 constexpr int kCusPerXcd = 32;
 constexpr int kStages = 4;         // LDS ring depth: two slices in flight while one is consumed
 constexpr int kRowBytes = BK * 2;  // one tile row in LDS: 64 bytes = 4 chunks of 16
+constexpr int kMBlock = 8;         // M-tiles per super-tile block of a group (tile order below)
 
 enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2, kGeluUp = 3, kGeluDown = 4 };
 
@@ -198,9 +203,10 @@ __device__ __forceinline__ long long group_rows(const FfnGroups& p, int g, long 
 // full tiles would get the most work and every other XCD would wait for it. The work of an M-tile
 // with b 32-row blocks is modelled, in units of about 128 cycles, as 2 ceil(b / 2) + 3 per K slice
 // (the busiest wave runs ceil(b / 2) blocks; the loads, barriers and reads of a slice cost about
-// three units whatever b is) plus 192 for its set-up and epilogue. A bound falls between two M-tiles
-// of the group that holds it. With fewer than four tiles per CU the ranges stay equal in count:
-// there a range's time is set by how many rounds of tiles its CUs run, not by the sum of its work.
+// three units whatever b is) plus 192 for its set-up and epilogue. A bound inside a group goes to
+// the tile at the same fraction of the group's tiles as the target is of its work. With fewer than
+// four tiles per CU the ranges stay equal in count: there a range's time is set by how many rounds
+// of tiles its CUs run, not by the sum of its work.
 // With more than 1024 groups a first pass over them finds the totals; the last pass writes
 // everything.
 __device__ __forceinline__ long long tile_work(long long blocks, long long nk) {
@@ -271,21 +277,18 @@ gemm_schedule_kernel(const FfnGroups p, int32_t* __restrict__ sched_gu, int32_t*
           sched_dn[ngroups] = (int32_t)(ex[1] + v[1]);
           pband[ngroups] = (int32_t)(ex[2] + v[2]);
         }
-        // XCD bounds inside this group: target work x * total / kXcds in [ex, ex + v), placed after
-        // N-tile k and, within it, after the nearest M-tile
+        // XCD bounds inside this group: target work x * total / kXcds in [ex, ex + v), placed at
+        // the tile whose share of the group's tiles equals the target's share of its work (all
+        // tiles of a group but its last M-tile's cost the same)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const long long w0 = ex[3 + q], wg = v[3 + q], nt = q == 0 ? ntg : ntd;
-          const long long per_nt = wg / (nt > 0 ? nt : 1);  // work of one N-tile (all its M-tiles)
-          const long long per_m = tile_work(BM / 32, q == 0 ? nkg : nkd);
+          const long long w0 = ex[3 + q], wg = v[3 + q];
           if (total[q] < kXcds * kCusPerXcd * 4) continue;  // equal counts (below)
           for (int x = 1; x < kXcds; ++x) {
             const long long target = total[3 + q] * x / kXcds;
             if (wg > 0 && target >= w0 && target < w0 + wg) {
-              const long long k = (target - w0) / per_nt;   // < nt
-              long long m = (target - w0 - k * per_nt + per_m / 2) / per_m;
-              m = m < mt ? m : mt;
-              (q == 0 ? xb_gu : xb_dn)[x] = (int32_t)(ex[q] + k * mt + m);
+              const long long i = ((target - w0) * v[q] + wg / 2) / wg;   // <= v[q]
+              (q == 0 ? xb_gu : xb_dn)[x] = (int32_t)(ex[q] + i);
             }
           }
         }
@@ -627,10 +630,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
       nrows = p.T;
       Hg = p.Hs;
     }
-    const int mtiles = (nrows + G::BM - 1) / G::BM;
-    const int local = t - ga.sched[c.g];
-    nt = local / mtiles;
-    mt = local % mtiles;
     const size_t wsz = (size_t)p.H * p.d;
     if (first_pass(MODE)) {  // gate/up, or the GELU expert's W1 (held in w_gate)
       c.N = Hg;
@@ -643,6 +642,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
       c.K = Hg;
       Bp[0] = c.g < p.E ? (const uint16_t*)p.w_down + (size_t)c.g * wsz : (const uint16_t*)p.ws_down;
     }
+    // super-tile order within the group: blocks of kMBlock M-tiles, N-tile by N-tile inside a block
+    const int mtiles = (nrows + G::BM - 1) / G::BM;
+    const int ntiles = (c.N + G::BN - 1) / G::BN;
+    const int local = t - ga.sched[c.g];
+    const int mb0 = local / (kMBlock * ntiles) * kMBlock;
+    const int mb = mtiles - mb0 < kMBlock ? mtiles - mb0 : kMBlock;
+    const int within = local - mb0 * ntiles;
+    nt = within / mb;
+    mt = mb0 + within % mb;
   }
   const int m0 = mt * G::BM;
   c.rows = nrows - m0 < G::BM ? nrows - m0 : G::BM;
@@ -730,9 +738,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
     tile_body_na<MODE, LAYOUT, G::L_LO>(ga, c, smem, wv, na);
 }
 
-// Tiles are numbered expert by expert, N-tile by N-tile, with the M-tiles of one (expert, N-tile)
-// adjacent; XCD x takes the contiguous range [xb[x], xb[x + 1]) that the schedule balanced by work
-// (the router: equal ranges). Workgroup L runs on XCD L % 8 and takes the (L / 8)-th tile of its
+// Tiles are numbered expert by expert, in blocks of up to kMBlock M-tiles, N-tile by N-tile within
+// a block, with the block's M-tiles of one N-tile adjacent; XCD x takes the contiguous range
+// [xb[x], xb[x + 1]) that the schedule balanced by work (the router: equal ranges). Workgroup L runs on XCD L % 8 and takes the (L / 8)-th tile of its
 // XCD's range, then every (gridDim / 8)-th after it: with at least as many workgroups per XCD as
 // tiles in its range that is one tile, and the surplus workgroups exit at once.
 template <int MODE, int LAYOUT>
