@@ -34,9 +34,10 @@
 //
 // Tile order: tiles are numbered expert by expert; within an expert, its M-tiles are taken in blocks
 // of up to eight, and a block's tiles run N-tile by N-tile with the block's M-tiles adjacent. Each
-// XCD takes a contiguous range of that order, the ranges cut by the schedule kernel so that they
-// hold equal work. Workgroups are dealt round-robin to the 8 XCDs, so block L runs the (L / 8)-th
-// tile of XCD L % 8's range, and an XCD's 32 CUs run 32 consecutive tiles at a time: the N-tiles of
+// XCD owns a contiguous range of that order, the ranges cut by the schedule kernel so that they
+// hold equal modelled work. One persistent workgroup per CU takes the tiles of its XCD's range in
+// order from a counter, then helps the XCDs behind (see the kernel), so an XCD's 32 CUs run 32
+// consecutive tiles at a time: the N-tiles of
 // a one-M-tile expert (every routed bucket of a prefill batch) share its activation rows in the
 // XCD's L2; for an expert of many M-tiles (the shared expert over all tokens, a heavily loaded
 // expert) they form an 8 x 4 patch that shares 4 weight tiles and 8 activation blocks, where one
@@ -57,6 +58,7 @@ constexpr int kCusPerXcd = 32;
 constexpr int kStages = 4;         // LDS ring depth: two slices in flight while one is consumed
 constexpr int kRowBytes = BK * 2;  // one tile row in LDS: 64 bytes = 4 chunks of 16
 constexpr int kMBlock = 8;         // M-tiles per super-tile block of a group (tile order below)
+constexpr int kCtrStride = 16;     // ints between two XCDs' tile counters (one 64-byte line each)
 
 enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2, kGeluUp = 3, kGeluDown = 4 };
 
@@ -201,9 +203,11 @@ __device__ __forceinline__ long long group_rows(const FfnGroups& p, int g, long 
 // It also cuts each pass's tile sequence into kXcds contiguous ranges of about equal work (xb_gu,
 // xb_dn: kXcds + 1 bounds), one per XCD: with equal tile counts the XCD holding the shared expert's
 // full tiles would get the most work and every other XCD would wait for it. The work of an M-tile
-// with b 32-row blocks is modelled, in units of about 128 cycles, as 2 ceil(b / 2) + 3 per K slice
-// (the busiest wave runs ceil(b / 2) blocks; the loads, barriers and reads of a slice cost about
-// three units whatever b is) plus 192 for its set-up and epilogue. A bound inside a group goes to
+// with b 32-row blocks is modelled in units of about 128 cycles, from per-tile timings of both
+// passes. Gate/up: 2 ceil(b / 2) + 3 per K slice (the slice time barely moves with b: the operand
+// stream sets it) plus 192 for set-up and epilogue. Down: 5 b / 4 per K slice (each SIMD runs the
+// MFMAs of all b blocks, two waves of it; about 156 cycles per block and slice) plus 112 for
+// set-up, pipeline fill and the staged epilogue. A bound inside a group goes to
 // the tile at the same fraction of the group's tiles as the target is of its work. With fewer than
 // four tiles per CU the ranges stay equal in count: there a range's time is set by how many rounds
 // of tiles its CUs run, not by the sum of its work.
@@ -212,10 +216,14 @@ __device__ __forceinline__ long long group_rows(const FfnGroups& p, int g, long 
 __device__ __forceinline__ long long tile_work(long long blocks, long long nk) {
   return (2 * ((blocks + 1) / 2) + 3) * nk + 192;
 }
+__device__ __forceinline__ long long tile_work_down(long long blocks, long long nk) {
+  return 5 * blocks * nk / 4 + 112;
+}
 
 __global__ void __launch_bounds__(1024)
 gemm_schedule_kernel(const FfnGroups p, int32_t* __restrict__ sched_gu, int32_t* __restrict__ sched_dn,
-                     int32_t* __restrict__ pband, int32_t* __restrict__ xb_gu, int32_t* __restrict__ xb_dn) {
+                     int32_t* __restrict__ pband, int32_t* __restrict__ xb_gu, int32_t* __restrict__ xb_dn,
+                     int32_t* __restrict__ ctr) {
   constexpr int kQ = 5;  // per group: gate/up tiles, down tiles, bands, gate/up work, down work
   constexpr int BM = Geo<kGateUp>::BM;
   static_assert(Geo<kDown>::BM == BM, "one M-tiling for both passes");
@@ -244,7 +252,7 @@ gemm_schedule_kernel(const FfnGroups p, int32_t* __restrict__ sched_gu, int32_t*
         v[1] = mt * ntd;
         v[2] = g < p.E ? (n + 15) / 16 : 0;
         v[3] = mt > 0 ? ntg * ((mt - 1) * tile_work(BM / 32, nkg) + tile_work(b_last, nkg)) : 0;
-        v[4] = mt > 0 ? ntd * ((mt - 1) * tile_work(BM / 32, nkd) + tile_work(b_last, nkd)) : 0;
+        v[4] = mt > 0 ? ntd * ((mt - 1) * tile_work_down(BM / 32, nkd) + tile_work_down(b_last, nkd)) : 0;
       }
       long long inc[kQ];
 #pragma unroll
@@ -300,6 +308,7 @@ gemm_schedule_kernel(const FfnGroups p, int32_t* __restrict__ sched_gu, int32_t*
 #pragma unroll
     for (int q = 0; q < kQ; ++q) total[q] = carry[q];  // the same in every thread
   }
+  if (threadIdx.x < 2 * kXcds) ctr[threadIdx.x * kCtrStride] = 0;  // tile counters of both passes
   if (threadIdx.x == 0) {
     xb_gu[0] = 0;
     xb_dn[0] = 0;
@@ -319,6 +328,7 @@ struct GemmArgs {
   const int32_t* sched;   // [ngroups + 1] (kGateUp / kDown); unused for the router
   const int32_t* pband;   // [E + 1] first packed band of every routed group (kGateUp / kDown)
   const int32_t* xb;      // [kXcds + 1] tile ranges of the XCDs (kGateUp / kDown)
+  int32_t* ctr;           // [kXcds * kCtrStride] tile counters of the XCDs' ranges, zeroed by the schedule
   // router mode
   const void* x;          // [T, d]
   const void* w;          // [E, d]
@@ -739,29 +749,76 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
 }
 
 // Tiles are numbered expert by expert, in blocks of up to kMBlock M-tiles, N-tile by N-tile within
-// a block, with the block's M-tiles of one N-tile adjacent; XCD x takes the contiguous range
-// [xb[x], xb[x + 1]) that the schedule balanced by work (the router: equal ranges). Workgroup L runs on XCD L % 8 and takes the (L / 8)-th tile of its
-// XCD's range, then every (gridDim / 8)-th after it: with at least as many workgroups per XCD as
-// tiles in its range that is one tile, and the surplus workgroups exit at once.
+// a block, with the block's M-tiles of one N-tile adjacent; XCD x owns the contiguous range
+// [xb[x], xb[x + 1]) that the schedule balanced by modelled work (the router: equal ranges).
+// Router: one workgroup per tile; workgroup L runs on XCD L % 8 and takes the (L / 8)-th tile of
+// its XCD's range (then every (gridDim / 8)-th after it).
+// Expert passes: one persistent workgroup per compute unit (kXcds x kCusPerXcd, workgroup L on XCD
+// L % 8). A workgroup takes the next tile of its XCD's range from the range's counter (so the 32
+// CUs of an XCD work on consecutive tiles, in order, as the hardware would dispatch them, without
+// a launch between two tiles), and once its range is handed out, the next tile of another XCD's
+// range: XCDs run at clocks several percent apart under load, and the ones ahead finish the ones
+// behind. Lane y < 8 of wave 0 watches the range of XCD (xcd + y) % 8 (its first tile, its size and
+// its counter). Each round the lowest watching lane whose counter still reads below the range size
+// takes a number with one atomic add; a number past the range leaves that counter past it for good
+// (and the lane's next load sees its own add), so every failed round retires one range and the
+// loop ends within kXcds + 1 rounds; a workgroup leaves only once every range is handed out. The
+// tile number reaches the other waves through the first word of the LDS ring, free between tiles:
+// the workgroup's LDS stays at exactly 144 KiB (one more 4-byte shared variable made both expert
+// passes about 1.5x slower on this part).
 template <int MODE, int LAYOUT>
 __global__ void __launch_bounds__(kThreads, 1)
 grouped_gemm_kernel(const GemmArgs ga) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages][Geo<MODE>::STAGE];
   const int total = gemm_total_tiles<MODE>(ga);
-  const int xcd = (int)blockIdx.x % kXcds, stride = (int)gridDim.x / kXcds;
-  int lo, hi;
+  const int xcd = (int)blockIdx.x % kXcds;
   if (MODE == kRouter) {
+    const int stride = (int)gridDim.x / kXcds;
     const int per = (total + kXcds - 1) / kXcds;
-    lo = xcd * per;
-    hi = lo + per;
-  } else {
-    lo = ga.xb[xcd];
-    hi = ga.xb[xcd + 1];
+    const int lo = xcd * per < total ? xcd * per : total;
+    const int hi = lo + per < total ? lo + per : total;
+    for (int t = lo + (int)blockIdx.x / kXcds; t < hi; t += stride) {
+      if (t >= lo + stride) __syncthreads();  // the previous tile's LDS reads are over
+      gemm_tile<MODE, LAYOUT>(ga, t, smem);
+    }
+    return;
   }
-  lo = lo < 0 ? 0 : (lo > total ? total : lo);   // whatever the bounds hold, only tiles in [0, total)
-  hi = hi < lo ? lo : (hi > total ? total : hi);
-  for (int t = lo + (int)blockIdx.x / kXcds; t < hi; t += stride) {
-    if (t >= lo + stride) __syncthreads();  // the previous tile's LDS reads are over
+  const int lane0 = (int)threadIdx.x;
+  int d0 = 0, n = 0;
+  int32_t* cx = ga.ctr;
+  if (lane0 < kXcds) {
+    const int x = (xcd + lane0) % kXcds;
+    int xl = ga.xb[x], xh = ga.xb[x + 1];
+    xl = xl < 0 ? 0 : (xl > total ? total : xl);   // whatever the bounds hold, only tiles in [0, total)
+    xh = xh < xl ? xl : (xh > total ? total : xh);
+    d0 = xl;
+    n = xh - xl;
+    cx = ga.ctr + x * kCtrStride;
+  }
+  int* slot = (int*)&smem[0][0];
+  for (bool busy = false;; busy = true) {
+    if (busy) __syncthreads();  // the previous tile's LDS reads are over: the ring is free
+    if (lane0 < 64) {
+      int got_t = -1;
+      for (int round = 0; round <= kXcds && got_t < 0; ++round) {
+        const bool avail =
+            lane0 < kXcds && n > 0 && __hip_atomic_load(cx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n;
+        const unsigned long long m = __ballot(avail);
+        if (m == 0) break;
+        const int src = __ffsll(m) - 1;
+        int got = -1;
+        if (lane0 == src) {
+          const int d = atomicAdd(cx, 1);
+          got = d < n ? d0 + d : -1;
+        }
+        got_t = __shfl(got, src, 64);
+      }
+      if (lane0 == 0) *slot = got_t;
+    }
+    __syncthreads();
+    const int t = *slot;
+    __syncthreads();  // every wave has its copy before the tile's loads refill the ring
+    if (t < 0) break;
     gemm_tile<MODE, LAYOUT>(ga, t, smem);
   }
 }
@@ -770,32 +827,26 @@ grouped_gemm_kernel(const GemmArgs ga) {
 namespace {
 int round8(long long v) { return (int)((v + kXcds - 1) / kXcds * kXcds); }
 
-// Workgroups of a launch: one per tile (rounded to whole XCD sets). The hardware then starts the
-// tiles of each XCD in order as CUs free up, so the tiles that share activation rows start
-// together and stream them through L2 once.
+// Router workgroups: one per tile (rounded to whole XCD sets). Expert passes: one persistent
+// workgroup per compute unit.
 int gemm_grid(long long tiles_upper) { return round8(tiles_upper); }
+constexpr int kPersistentGrid = kXcds * kCusPerXcd;
 }  // namespace
 
-long long gemm_tiles_upper(const FfnGroups& p, int mode) {
-  constexpr int bm = Geo<kGateUp>::BM;
-  static_assert(Geo<kGateUp>::BM == Geo<kDown>::BM, "one M-tiling for both passes");
-  const long long mt_routed = p.rows / bm + p.E;  // each group adds at most one partial tile
-  const long long mt_shared = p.Hs > 0 ? (p.T + bm - 1) / bm : 0;
-  if (mode == kGateUp) {
-    const int bn = p.gelu ? Geo<kGeluUp>::BN : Geo<kGateUp>::BN;
-    return mt_routed * ((p.H + bn - 1) / bn) + mt_shared * ((p.Hs + bn - 1) / bn);
-  }
-  const int bn = Geo<kDown>::BN;
-  return (mt_routed + mt_shared) * ((p.d + bn - 1) / bn);
-}
+// [sched_gu | sched_dn | pband] (E + 2 ints each), [xb_gu | xb_dn] (kXcds + 1 each), then the tile
+// counters of both passes (kXcds each, one 64-byte line apart)
+size_t gemm_schedule_ints(int E) { return 3 * (size_t)(E + 2) + 2 * (kXcds + 1) + 2 * kXcds * kCtrStride + kCtrStride; }
 
-// [sched_gu | sched_dn | pband] (E + 2 ints each), then [xb_gu | xb_dn] (kXcds + 1 each)
-size_t gemm_schedule_ints(int E) { return 3 * (size_t)(E + 2) + 2 * (kXcds + 1); }
+// The tile counters: after the ranges, rounded up to a 64-byte boundary of the schedule buffer.
+int32_t* gemm_counters(int32_t* sched, int E) {
+  const size_t off = 3 * (size_t)(E + 2) + 2 * (kXcds + 1);
+  return sched + (off + kCtrStride - 1) / kCtrStride * kCtrStride;
+}
 
 hipError_t launch_gemm_schedule(const FfnGroups& p, int32_t* sched, hipStream_t stream) {
   int32_t* xb = sched + 3 * (p.E + 2);
   hipLaunchKernelGGL(gemm_schedule_kernel, dim3(1), dim3(1024), 0, stream, p, sched, sched + p.E + 2,
-                     sched + 2 * (p.E + 2), xb, xb + kXcds + 1);
+                     sched + 2 * (p.E + 2), xb, xb + kXcds + 1, gemm_counters(sched, p.E));
   return hipGetLastError();
 }
 
@@ -806,7 +857,8 @@ hipError_t launch_gemm_gate_up(const FfnGroups& p, const int32_t* sched, hipStre
   a.sched = sched;
   a.pband = sched + 2 * (p.E + 2);
   a.xb = sched + 3 * (p.E + 2);
-  const dim3 grid(gemm_grid(gemm_tiles_upper(p, kGateUp)));
+  a.ctr = gemm_counters(const_cast<int32_t*>(sched), p.E);
+  const dim3 grid(kPersistentGrid);
   if (p.gelu && p.layout == kFrag16)
     hipLaunchKernelGGL((grouped_gemm_kernel<kGeluUp, kFrag16>), grid, dim3(kThreads), 0, stream, a);
   else if (p.gelu)
@@ -824,7 +876,8 @@ hipError_t launch_gemm_down(const FfnGroups& p, const int32_t* sched, hipStream_
   a.sched = sched + p.E + 2;
   a.pband = sched + 2 * (p.E + 2);
   a.xb = sched + 3 * (p.E + 2) + kXcds + 1;
-  const dim3 grid(gemm_grid(gemm_tiles_upper(p, kDown)));
+  a.ctr = gemm_counters(const_cast<int32_t*>(sched), p.E) + kXcds * kCtrStride;
+  const dim3 grid(kPersistentGrid);
   if (p.gelu && p.layout == kFrag16)
     hipLaunchKernelGGL((grouped_gemm_kernel<kGeluDown, kFrag16>), grid, dim3(kThreads), 0, stream, a);
   else if (p.gelu)
