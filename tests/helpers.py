@@ -2,6 +2,8 @@
 
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 import oracle
@@ -124,3 +126,41 @@ def assert_tile_edges_covered(idx, counts, tokens, T, Hs):
         (T + M_TILE_ROWS - 1) // M_TILE_ROWS if Hs else 0)
     print(f"  checked tokens {len(chosen)} cover both edges of all {n_tiles} M-tiles "
           f"({int((counts > 0).sum())} experts{' + shared' if Hs else ''})", flush=True)
+
+
+def prefetching_expert_fn(expert_fn, cases, workers: int = 8, label: str = "oracle"):
+    """``expert_fn`` for an oracle pass over ``cases`` ((x_rows, w_router, k, bias, routing) each):
+    the experts the pass will ask for (every expert the oracle's routing selects, in ascending
+    order, as ``oracle.layer_forward_tokens`` and ``layer_forward_tokens_many`` visit them) are
+    prepared ``workers`` ahead on a thread pool (numpy releases the GIL), so regenerating and
+    dequantizing them on the host overlaps. Results are the same as ``expert_fn``'s; at most
+    ``workers`` + 1 experts are held at once. Prints a progress line every 32 experts."""
+    sel = set()
+    for x_rows, w_router, k, bias, routing in cases:
+        _, idx, _ = oracle.route(np.asarray(x_rows, np.float64), w_router, k, bias, routing)
+        sel.update(np.unique(idx).tolist())
+    order = iter(sorted(int(e) for e in sel))
+    pool = ThreadPoolExecutor(workers)
+    futs = {}
+    seen = []
+
+    def submit_next():
+        e = next(order, None)
+        if e is not None:
+            futs[e] = pool.submit(expert_fn, e)
+
+    for _ in range(workers):
+        submit_next()
+
+    def fn(e):
+        e = int(e)
+        seen.append(e)
+        if len(seen) % 32 == 0:
+            print(f"  {label}: {len(seen)} experts", flush=True)
+        f = futs.pop(e, None)
+        if f is None:
+            return expert_fn(e)
+        submit_next()
+        return f.result()
+
+    return fn

@@ -24,7 +24,7 @@ import torch
 import oracle
 import synth
 from tests import gpu_util as G
-from tests.helpers import M_TILE_ROWS, assert_tile_edges_covered, structural_tokens
+from tests.helpers import M_TILE_ROWS, assert_tile_edges_covered, prefetching_expert_fn, structural_tokens
 from tests.test_gpu_parity import check_logits_close, check_routing_on_gpu_logits
 
 import sparse_moe_layer_router_amd as moe
@@ -72,15 +72,8 @@ def attach_oracle(runs, expert_fn, shared_fn):
         L = runs[by_name[n][0]]["L"]
         x, wg, b = G.oracle_inputs(L)
         cases.append((x[toks[n]], wg, L.cfg.k, b, L.cfg.routing))
-    seen = []
-
-    def expert_fn_progress(e):   # a line every 32 experts: the weights are regenerated on the host
-        seen.append(e)
-        if len(seen) % 32 == 0:
-            print(f"  oracle: {len(seen)} experts", flush=True)
-        return expert_fn(e)
-
-    refs = oracle.layer_forward_tokens_many(cases, expert_fn_progress, shared_fn)
+    # the weights are regenerated on the host, several experts ahead, with a line every 32 experts
+    refs = oracle.layer_forward_tokens_many(cases, prefetching_expert_fn(expert_fn, cases), shared_fn)
     for n, ref in zip(names, refs):
         for key in by_name[n]:
             pos = np.searchsorted(toks[n], runs[key]["tokens"])
@@ -152,8 +145,8 @@ def test_dsv3_layer_one_byte_weights(name, n_sample, quant, dsv3_weights):
         rng = np.random.default_rng(0)
         tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, size=n_sample - 2, replace=False)]))
     x, wg, b = G.oracle_inputs(L)
-    ref = oracle.layer_forward_tokens(x[tokens], wg, cfg.k, L.expert_fn(cache=False), L.shared_fn(), b,
-                                      cfg.routing)
+    efn = prefetching_expert_fn(L.expert_fn(cache=False), [(x[tokens], wg, cfg.k, b, cfg.routing)])
+    ref = oracle.layer_forward_tokens(x[tokens], wg, cfg.k, efn, L.shared_fn(), b, cfg.routing)
     np.testing.assert_array_equal(np.sort(r.idx.cpu().numpy()[tokens], 1), np.sort(ref["idx"], 1))
     ok, err, bound = G.tolerance_ok(G.to_f64(r.out)[tokens], ref["out"])
     assert ok, (err, bound)

@@ -39,3 +39,30 @@ def test_coverage_check_names_a_missing_edge():
         assert_tile_edges_covered(idx, counts + np.eye(8, dtype=counts.dtype)[e], tokens, 3000, 0)
     with pytest.raises(AssertionError):   # a shared-expert M-tile edge left out
         assert_tile_edges_covered(idx, counts, tokens, 3000, 16)
+
+
+def test_prefetching_expert_fn_returns_what_expert_fn_returns():
+    """The prefetching wrapper hands the oracle the same arrays, for every expert its routing
+    selects, in any order it asks for them (and for an expert it did not predict)."""
+    import numpy as np
+
+    import oracle
+    from tests.helpers import prefetching_expert_fn
+
+    rng = np.random.default_rng(3)
+    T, d, E, k, H = 12, 16, 10, 3, 8
+    x, wg = rng.standard_normal((T, d)), rng.standard_normal((E, d))
+    weights = {e: tuple(rng.standard_normal(s) for s in ((H, d), (H, d), (d, H))) for e in range(E)}
+    calls = []
+
+    def expert_fn(e):
+        calls.append(e)
+        return weights[e]
+
+    cases = [(x, wg, k, None, "softmax"), (x[:4], wg, 2, None, "sigmoid")]
+    fn = prefetching_expert_fn(expert_fn, cases, workers=2)
+    ref = oracle.layer_forward_tokens_many(cases, expert_fn)
+    got = oracle.layer_forward_tokens_many(cases, fn)
+    for a, b in zip(ref, got):
+        np.testing.assert_array_equal(a["out"], b["out"])
+    assert fn(E - 1) is weights[E - 1]   # asked for again (or never selected): computed on the spot
