@@ -65,8 +65,9 @@ typedef enum {
   MOE_LAYOUT_ROWMAJOR = 0, /* [out, in] row-major, like a linear layer's weight */
   MOE_LAYOUT_FRAG16 = 1,   /* fragment-tiled, see moe_pack_weights */
   MOE_LAYOUT_INT8_FRAG = 2, /* INT8 codes with one float32 scale per output row, see
-                               moe_quantize_weights (bf16 layers; experts always run as the
-                               weight-streaming decode kernels) */
+                               moe_quantize_weights (bf16 layers; the codes become bf16 in
+                               registers, in the weight-streaming kernels below 32 rows per
+                               expert and in the grouped GEMM above, as for bf16 weights) */
   MOE_LAYOUT_FP8_FRAG = 3   /* FP8 E4M3 codes with one float32 scale per output row, in the same
                                byte order, see moe_quantize_weights_fp8 (as INT8 otherwise) */
 } moe_weight_layout;

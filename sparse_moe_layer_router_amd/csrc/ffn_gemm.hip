@@ -42,6 +42,7 @@
 // XCD's L2; for an expert of many M-tiles (the shared expert over all tokens, a heavily loaded
 // expert) they form an 8 x 4 patch that shares 4 weight tiles and 8 activation blocks, where one
 // N-tile over all its M-tiles would re-read every activation row once per N-tile.
+#include "codes.h"
 #include "kernels.h"
 #include "moe_device.h"
 
@@ -88,6 +89,29 @@ template <int MODE> struct Geo {
   static_assert(N_HI >= 1 && N_HI <= kWaves, "load split");
 };
 
+// Load slots of a slice and the LDS of a workgroup for a weight layout. bf16 weights as in Geo:
+// every ring stage holds the slice's A rows and its B blocks. One-byte weights (INT8 / E4M3 codes)
+// come in 1 KB blocks of 16 rows x 64 K, i.e. two slices: a pair of slices shares its blocks, held
+// in a ring of kBPairs pair buffers after the A ring. Slice kt loads half a pair: the second half
+// of pair kt / 2 (blocks BLK/2 ..) when kt is even, the first half of pair kt / 2 + 1 (blocks
+// 0 .. BLK/2 - 1) when kt is odd, so every slice issues the same loads per wave (waves N_HI..7 two
+// blocks each) and a pair is complete when the slice that opens it has landed.
+constexpr int kBPairs = 3;
+template <int MODE, int LAYOUT> struct Slots {
+  using G = Geo<MODE>;
+  static constexpr bool Q = byte_codes(LAYOUT);
+  static constexpr int B_INSTR = Q ? G::BROWS / 32 : G::B_INSTR;  // 1 KB weight loads per slice
+  static constexpr int L_HI = Q ? G::A_INSTR / 4 : G::L_HI;        // loads per slice, waves < N_HI
+  static constexpr int N_HI = Q ? 4 : G::N_HI;
+  static constexpr int L_LO = Q ? B_INSTR / 4 : G::L_LO;           // loads per slice, other waves
+  static constexpr int SPLIT = (L_HI + 1) / 2;
+  static constexpr int STAGE = Q ? G::A_BYTES : G::STAGE;           // one ring stage
+  static constexpr int PAIR = G::BROWS / 16 * 1024;                 // one-byte: the blocks of a pair
+  static constexpr int LDS = kStages * STAGE + (Q ? kBPairs * PAIR : 0);
+  static_assert(!Q || (N_HI * L_HI == G::A_INSTR && (kWaves - N_HI) * L_LO == B_INSTR), "one-byte load split");
+  static_assert(LDS <= 144 * 1024, "the workgroup's LDS stays within 144 KiB");
+};
+
 // LDS byte offset of 16-byte chunk `chunk` (0..3) of tile row `row`. The XOR key takes four
 // distinct values over any four rows of equal parity among 8 consecutive rows and over any four
 // rows of equal residue mod 4 among 16 consecutive rows, so a fragment read (16 or 8 consecutive
@@ -113,6 +137,12 @@ __device__ __forceinline__ u32x4_t read_a(const uint8_t* sa, int i, int wm, int 
 template <int MODE, int LAYOUT>
 __device__ __forceinline__ u32x4_t read_b(const uint8_t* sb, int j, int wn, int fr, int ch) {
   const int n = b_row<MODE>(j, wn, fr);
+  if constexpr (byte_codes(LAYOUT)) {
+    // one-byte codes: block n/16 of the pair, lane slot (n%16) + 16*chunk holds the 8 codes of the
+    // chunk for the pair's first slice, then the same for its second (sb points at the slice's half)
+    const u32x2_t v = *(const u32x2_t*)(sb + (n / 16) * 1024 + ((n & 15) + 16 * ch) * 16);
+    return codes_to_bf16x8<LAYOUT>(v[0], v[1]);
+  }
   if (LAYOUT == kFrag16)  // block n/16 of the stacked tile; lane position (n%16) + 16*chunk
     return *(const u32x4_t*)(sb + (n / 16) * 1024 + ((n & 15) + 16 * ch) * 16);
   return *(const u32x4_t*)(sb + swz(n, ch));
@@ -163,6 +193,11 @@ __device__ __forceinline__ void read_all(u32x4_t (&fa)[NA > 0 ? NA : 1], u32x4_t
 #pragma unroll
   for (int i = 0; i < NA; ++i) fa[i] = read_a<MODE>(sa, i, wm, fr, ch);
   fb[1] = read_b<MODE, LAYOUT>(sb, 1, wn, fr, ch);
+}
+
+// The float32 row scales of a one-byte weight buffer: they follow its `ncodes` codes.
+__device__ __forceinline__ const float* code_scales(const void* w, size_t ncodes) {
+  return (const float*)((const int8_t*)w + ncodes);
 }
 
 // One zero kilobyte: the source of packed A blocks past the end of a group.
@@ -349,6 +384,11 @@ struct TileCtx {
   const uint16_t* src[Geo<MODE>::L_HI];  // per load: lane's source at K slice 0
   int kc[Geo<MODE>::L_HI];               // per load: element offset of the lane's chunk in a slice
   int stride[Geo<MODE>::L_HI];           // per load: elements to advance per K slice (wave-uniform)
+  // one-byte weights, the weight-loading waves: lane's source of its two blocks in the first half
+  // of a pair (qodd: loaded by odd slices) and the second half (qeven), at pair 0; pairs in K
+  const int8_t* qodd[2];
+  const int8_t* qeven[2];
+  int npairs;
 };
 
 // Tile count of a launch: from the router's sizes, or the schedule's running total.
@@ -362,7 +402,7 @@ __device__ __forceinline__ int gemm_total_tiles(const GemmArgs& ga) {
 // per slice.
 template <int MODE, int LAYOUT, int NA, int L>
 __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE>& c,
-                                          uint8_t (*smem)[Geo<MODE>::STAGE], int wv) {
+                                          uint8_t (*smem)[Slots<MODE, LAYOUT>::STAGE], int wv) {
   using G = Geo<MODE>;
   constexpr int NAF = NA > 0 ? NA : 1;
   const int lane = lane_id();
@@ -376,13 +416,29 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   // weight blocks, which (a bucket being one M-tile) no other workgroup reads again: they load with
   // the non-temporal hint (policy bit NT = 2), leaving L2 to the activation rows that every N-tile
   // of the expert shares.
-  constexpr int kAux = (MODE != kRouter && L == G::L_LO && G::L_LO != G::L_HI) ? 2 : 0;
-  static_assert(MODE == kRouter || G::N_HI * G::L_HI == G::A_INSTR, "the L_LO waves load weights only");
+  using Sl = Slots<MODE, LAYOUT>;
+  constexpr bool kQB = Sl::Q && L == Sl::L_LO && Sl::L_LO != Sl::L_HI;   // this wave loads one-byte weight blocks
+  constexpr int kAux = (MODE != kRouter && L == Sl::L_LO && Sl::L_LO != Sl::L_HI) ? 2 : 0;
+  static_assert(MODE == kRouter || Sl::N_HI * Sl::L_HI == G::A_INSTR, "the L_LO waves load weights only");
+  uint8_t* const bring = &smem[0][0] + kStages * Sl::STAGE;   // one-byte weights: the pair ring
   auto issue = [&](int kt, int buf, int j0, int j1) {
     const int kcl = kt < nk ? kt : nk - 1;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       if (i < j0 || i >= j1) continue;
+      if constexpr (kQB) {
+        // half a pair (see Slots): pair (kt + 1) / 2, first half for odd kt (kt = -1: pair 0),
+        // second half for even kt. A pair past the end re-reads the last one into the pair buffer
+        // that no slice still to be read uses.
+        const int pair = (kt + 1) >> 1;
+        const int ps = pair < c.npairs ? pair : c.npairs - 1;
+        const int pd = pair < c.npairs ? pair : c.npairs;
+        const int blk = c.first + i - G::A_INSTR + ((kt & 1) ? 0 : Sl::B_INSTR);
+        const int8_t* s = ((kt & 1) ? c.qodd[i] : c.qeven[i]) + (size_t)ps * 1024;
+        __builtin_amdgcn_global_load_lds((const void*)s, (lds_t*)(bring + (pd % kBPairs) * Sl::PAIR + blk * 1024), 16,
+                                         0, kAux);
+        continue;
+      }
       const int k = kcl * BK + c.kc[i];
       const uint16_t* s = c.src[i] + (LAYOUT == kFrag16 || k < K ? (size_t)kcl * c.stride[i] + c.kc[i] : 0);  // past K: zeroed later
       __builtin_amdgcn_global_load_lds((const void*)s, (lds_t*)(smem[buf] + (c.first + i) * 1024), 16, 0, kAux);
@@ -419,7 +475,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   // and no barrier follows.
   constexpr int S = kStages;
   static_assert(S >= 3, "the issue schedule below needs a ring of at least 3 slices");
-  constexpr int P1 = G::SPLIT < L ? G::SPLIT : L;
+  constexpr int P1 = Sl::SPLIT < L ? Sl::SPLIT : L;
   constexpr int kAhead = (S - 2) * L;   // loads allowed in flight when slice kt+1 must land
   static_assert(kAhead + P1 < 64, "vmcnt holds 6 bits");
   auto arrive = [&](int kt) {
@@ -430,7 +486,13 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   };
 
   static_assert(BK / 16 == 2, "the loop below is written for two K steps per slice");
+  // the B fragments of slice kt: in its stage (bf16), or its half of its pair (one-byte codes)
+  auto bslice = [&](int kt) -> const uint8_t* {
+    if constexpr (Sl::Q) return bring + ((kt >> 1) % kBPairs) * Sl::PAIR + (kt & 1) * 8;
+    else return smem[kt % S] + G::A_BYTES;
+  };
   u32x4_t fa[NAF], fb[2];
+  if constexpr (kQB) issue(-1, 0, 0, L);   // the first half of pair 0 (the loads of slice -1)
 #pragma unroll
   for (int i = 0; i < S - 1; ++i) issue(i, i, 0, L);
   issue(S - 1, S - 1, 0, P1);
@@ -438,7 +500,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   if (LAYOUT != kFrag16 && nk == 1 && (K % BK)) zero_tail(0, 0);
   wait_lgkmcnt0();
   lds_barrier();
-  read_all<MODE, LAYOUT, NA>(fa, fb, smem[0], smem[0] + G::A_BYTES, wm, wn, fr, fh);
+  read_all<MODE, LAYOUT, NA>(fa, fb, smem[0], bslice(0), wm, wn, fr, fh);
   // Step 0 of slice kt (S0) multiplies while reading step 1 (chunks 2, 3 of the same slice) and
   // issuing part 2 of slice kt+S-1; step 1 (S1) multiplies while reading step 0 of slice kt+1 and
   // issuing part 1 of slice kt+S into slice kt's buffer. The loop runs S1(kt) S0(kt+1) arrive(kt+2),
@@ -447,25 +509,25 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   // current buffer (the values are never used) and sends its loads to the next buffer, since waves
   // that are behind may still read the current one and no barrier follows.
   auto s0 = [&](int kt) {
-    mma_and_read<MODE, LAYOUT, NA, L - P1>(acc, fa, fb, smem[kt % S], smem[kt % S] + G::A_BYTES, wm, wn, fr,
+    mma_and_read<MODE, LAYOUT, NA, L - P1>(acc, fa, fb, smem[kt % S], bslice(kt), wm, wn, fr,
                                            2 + fh, [&](int j) { issue(kt + S - 1, (kt + S - 1) % S, P1 + j, P1 + j + 1); });
   };
-  auto s1 = [&](int kt, int rbuf, int lbuf) {
-    mma_and_read<MODE, LAYOUT, NA, P1>(acc, fa, fb, smem[rbuf], smem[rbuf] + G::A_BYTES, wm, wn, fr, fh,
+  auto s1 = [&](int kt, int rslice, int lbuf) {
+    mma_and_read<MODE, LAYOUT, NA, P1>(acc, fa, fb, smem[rslice % S], bslice(rslice), wm, wn, fr, fh,
                                        [&](int j) { issue(kt + S, lbuf, j, j + 1); });
   };
   s0(0);
   if (nk > 1) arrive(1);
   for (int kt = 0; kt + 2 < nk; ++kt) {
-    s1(kt, (kt + 1) % S, kt % S);
+    s1(kt, kt + 1, kt % S);
     s0(kt + 1);
     arrive(kt + 2);
   }
   if (nk > 1) {
-    s1(nk - 2, (nk - 1) % S, (nk - 2) % S);
+    s1(nk - 2, nk - 1, (nk - 2) % S);
     s0(nk - 1);
   }
-  s1(nk - 1, (nk - 1) % S, nk % S);
+  s1(nk - 1, nk - 1, nk % S);
   wait_vmcnt<0>();  // no load may still write LDS when the tile ends
 
   // ---- epilogue ----------------------------------------------------------------------------------
@@ -490,7 +552,12 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
     // accumulators touches fall in distinct banks. The GELU expert's second linear adds its bias
     // (fp32) before the rounding.
     const float* b2 = MODE == kGeluDown && p.b2 ? p.b2 + (size_t)c.g * p.d : nullptr;
-    static_assert(G::MBW == 5 && G::BN == 256 && 160 * 512 <= kStages * G::STAGE, "staging layout");
+    // one-byte weights: the row scales of W_down multiply the fp32 sums before the rounding
+    const float* qs = nullptr;
+    if constexpr (Sl::Q)
+      qs = c.g < p.E ? code_scales(p.w_down, (size_t)p.E * p.d * p.H) + (size_t)c.g * p.d
+                     : code_scales(p.ws_down, (size_t)p.d * p.Hs);
+    static_assert(G::MBW == 5 && G::BN == 256 && 160 * 512 <= kStages * Sl::STAGE, "staging layout");
     uint8_t* lt = &smem[0][0];
     int tid = (int)threadIdx.x;
     asm volatile("" : "+v"(tid));  // (as for the lane index above)
@@ -508,6 +575,13 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
           for (int q = 0; q < 4; ++q) {
             const int nl = wn * 64 + j * 32 + q * 8 + efh * 4;
             float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            if constexpr (Sl::Q) {
+              if (c.n0 + nl < c.N) {  // N is a multiple of 64 here
+                const f32x4_t sc = *(const f32x4_t*)(qs + c.n0 + nl);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] *= sc[e];
+              }
+            }
             if (MODE == kGeluDown && b2 && c.n0 + nl < c.N) {  // N is a multiple of 8: 4 columns all in or all out
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] += b2[c.n0 + nl + e];
@@ -529,6 +603,15 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
     }
     return;
   }
+  // one-byte weights: the row scales of W_gate and W_up multiply the fp32 sums before SiLU(g) * u
+  const float* qsg = nullptr;
+  const float* qsu = nullptr;
+  if constexpr (Sl::Q && MODE == kGateUp) {
+    qsg = c.g < p.E ? code_scales(p.w_gate, (size_t)p.E * p.H * p.d) + (size_t)c.g * p.H
+                    : code_scales(p.ws_gate, (size_t)p.Hs * p.d);
+    qsu = c.g < p.E ? code_scales(p.w_up, (size_t)p.E * p.H * p.d) + (size_t)c.g * p.H
+                    : code_scales(p.ws_up, (size_t)p.Hs * p.d);
+  }
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int row = (wm + 2 * i) * 32 + efr;
@@ -541,11 +624,24 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
         if (MODE == kGateUp) {
           if (n >= np) continue;  // N, np and n are multiples of 4: the four columns are all in or all out
           u32x2_t v = {0u, 0u};
-          if (n < c.N)
-            v = u32x2_t{pack_bf16x2(silu(acc[i][0][4 * q]) * acc[i][1][4 * q],
-                                    silu(acc[i][0][4 * q + 1]) * acc[i][1][4 * q + 1]),
-                        pack_bf16x2(silu(acc[i][0][4 * q + 2]) * acc[i][1][4 * q + 2],
-                                    silu(acc[i][0][4 * q + 3]) * acc[i][1][4 * q + 3])};
+          if (n < c.N) {
+            float g4[4], u4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              g4[e] = acc[i][0][4 * q + e];
+              u4[e] = acc[i][1][4 * q + e];
+            }
+            if constexpr (Sl::Q) {
+              const f32x4_t a = *(const f32x4_t*)(qsg + n), b = *(const f32x4_t*)(qsu + n);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                g4[e] *= a[e];
+                u4[e] *= b[e];
+              }
+            }
+            v = u32x2_t{pack_bf16x2(silu(g4[0]) * u4[0], silu(g4[1]) * u4[1]),
+                        pack_bf16x2(silu(g4[2]) * u4[2], silu(g4[3]) * u4[3])};
+          }
           *(u32x2_t*)(hid + frag16_offset((size_t)(c.pr0 + row), (size_t)n, (size_t)np)) = v;
         } else if (MODE == kGeluUp) {
           if (n >= np) continue;  // (as for gate/up)
@@ -577,7 +673,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
 // The body specialised on the wave's active row-block count.
 template <int MODE, int LAYOUT, int L>
 __device__ __forceinline__ void tile_body_na(const GemmArgs& ga, const TileCtx<MODE>& c,
-                                             uint8_t (*smem)[Geo<MODE>::STAGE], int wv, int na) {
+                                             uint8_t (*smem)[Slots<MODE, LAYOUT>::STAGE], int wv, int na) {
   switch (na) {
     case 0: tile_body<MODE, LAYOUT, 0, L>(ga, c, smem, wv); break;
     case 1: tile_body<MODE, LAYOUT, 1, L>(ga, c, smem, wv); break;
@@ -590,7 +686,7 @@ __device__ __forceinline__ void tile_body_na(const GemmArgs& ga, const TileCtx<M
 
 // One output tile t (0 <= t < gemm_total_tiles) through the LDS ring `smem`.
 template <int MODE, int LAYOUT>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8_t (*smem)[Geo<MODE>::STAGE]) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8_t (*smem)[Slots<MODE, LAYOUT>::STAGE]) {
   using G = Geo<MODE>;
   const FfnGroups& p = ga.p;
   const int lane = lane_id();
@@ -602,6 +698,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
   long long gr0 = 0;     // first row of the group in its row space
   int nrows = 0;         // rows in the group
   const uint16_t* Bp[2] = {nullptr, nullptr};
+  const int8_t* QB[2] = {nullptr, nullptr};   // one-byte codes of the group's matrices
   c.g = 0;
   if (MODE == kRouter) {
     const int mtiles = (ga.T + G::BM - 1) / G::BM;
@@ -647,10 +744,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
       Bp[0] = c.g < p.E ? (const uint16_t*)p.w_gate + (size_t)c.g * wsz : (const uint16_t*)p.ws_gate;
       if (MODE == kGateUp)
         Bp[1] = c.g < p.E ? (const uint16_t*)p.w_up + (size_t)c.g * wsz : (const uint16_t*)p.ws_up;
+      if constexpr (byte_codes(LAYOUT)) {
+        QB[0] = c.g < p.E ? (const int8_t*)p.w_gate + (size_t)c.g * wsz : (const int8_t*)p.ws_gate;
+        QB[1] = c.g < p.E ? (const int8_t*)p.w_up + (size_t)c.g * wsz : (const int8_t*)p.ws_up;
+      }
     } else {
       c.N = p.d;
       c.K = Hg;
       Bp[0] = c.g < p.E ? (const uint16_t*)p.w_down + (size_t)c.g * wsz : (const uint16_t*)p.ws_down;
+      if constexpr (byte_codes(LAYOUT))
+        QB[0] = c.g < p.E ? (const int8_t*)p.w_down + (size_t)c.g * wsz : (const int8_t*)p.ws_down;
     }
     // super-tile order within the group: blocks of kMBlock M-tiles, N-tile by N-tile inside a block
     const int mtiles = (nrows + G::BM - 1) / G::BM;
@@ -681,12 +784,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
   // fragment-tiled: one contiguous 16 x 32 block of weight band n0/16 + q % (BN/16) of matrix
   // q / (BN/16); row-major: stacked B rows [16 q, 16 q + 16) like A. Slot s lands at LDS byte s * 1024
   // of the slice (A rows first, then the stacked B tiles).
-  const bool hi_wave = wv < G::N_HI;
-  c.first = hi_wave ? wv * G::L_HI : G::N_HI * G::L_HI + (wv - G::N_HI) * G::L_LO;
-  const int nload = hi_wave ? G::L_HI : G::L_LO;
+  using Sl = Slots<MODE, LAYOUT>;
+  const bool hi_wave = wv < Sl::N_HI;
+  c.first = hi_wave ? wv * Sl::L_HI : Sl::N_HI * Sl::L_HI + (wv - Sl::N_HI) * Sl::L_LO;
+  const int nload = hi_wave ? Sl::L_HI : Sl::L_LO;
+  c.npairs = c.K / 64;
   const int phys = lane & 3;
 #pragma unroll
-  for (int i = 0; i < G::L_HI; ++i) {
+  for (int i = 0; i < Sl::L_HI; ++i) {
     const int s = c.first + (i < nload ? i : 0);
     if (s < G::A_INSTR && !packed_a(MODE)) {
       const int row = s * 16 + (lane >> 2);
@@ -716,6 +821,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
         c.stride[i] = 0;
         c.src[i] = (const uint16_t*)g_zero_block + lane * 8;
       }
+    } else if constexpr (byte_codes(LAYOUT)) {
+      // one-byte weight blocks q (first half of a pair) and q + B_INSTR (second half): 16 rows x 64 K
+      // of codes each, stacked as in the bf16 tile (gate/up: 8 gate bands, then 8 up bands)
+      const int q = s - G::A_INSTR;
+      auto src_of = [&](int b) {
+        int band = c.n0 / 16 + b % (G::BN / 16);
+        band = band < c.N / 16 ? band : c.N / 16 - 1;   // bands past N: any valid band, never stored
+        return QB[b / (G::BN / 16)] + (size_t)band * c.npairs * 1024 + lane * 16;
+      };
+      if (i < 2) {
+        c.qodd[i] = src_of(q);
+        c.qeven[i] = src_of(q + Sl::B_INSTR);
+      }
+      c.kc[i] = 0;
+      c.stride[i] = 0;
+      c.src[i] = nullptr;
     } else {
       const int q = s - G::A_INSTR;
       if (LAYOUT == kFrag16) {
@@ -743,9 +864,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
   int na = nbt > wm ? (nbt - wm + 1) / 2 : 0;
   na = na < G::MBW ? na : G::MBW;
   if (hi_wave)
-    tile_body_na<MODE, LAYOUT, G::L_HI>(ga, c, smem, wv, na);
-  else if constexpr (G::L_LO != G::L_HI && G::N_HI < kWaves)
-    tile_body_na<MODE, LAYOUT, G::L_LO>(ga, c, smem, wv, na);
+    tile_body_na<MODE, LAYOUT, Sl::L_HI>(ga, c, smem, wv, na);
+  else if constexpr (Sl::L_LO != Sl::L_HI && Sl::N_HI < kWaves)
+    tile_body_na<MODE, LAYOUT, Sl::L_LO>(ga, c, smem, wv, na);
 }
 
 // Tiles are numbered expert by expert, in blocks of up to kMBlock M-tiles, N-tile by N-tile within
@@ -769,7 +890,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
 template <int MODE, int LAYOUT>
 __global__ void __launch_bounds__(kThreads, 1)
 grouped_gemm_kernel(const GemmArgs ga) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages][Geo<MODE>::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Slots<MODE, LAYOUT>::LDS];
+  auto smem = reinterpret_cast<uint8_t (*)[Slots<MODE, LAYOUT>::STAGE]>(lds);
   const int total = gemm_total_tiles<MODE>(ga);
   const int xcd = (int)blockIdx.x % kXcds;
   if (MODE == kRouter) {
@@ -865,6 +987,10 @@ hipError_t launch_gemm_gate_up(const FfnGroups& p, const int32_t* sched, hipStre
     hipLaunchKernelGGL((grouped_gemm_kernel<kGeluUp, kRowMajor>), grid, dim3(kThreads), 0, stream, a);
   else if (p.layout == kFrag16)
     hipLaunchKernelGGL((grouped_gemm_kernel<kGateUp, kFrag16>), grid, dim3(kThreads), 0, stream, a);
+  else if (p.layout == kInt8Frag)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kGateUp, kInt8Frag>), grid, dim3(kThreads), 0, stream, a);
+  else if (p.layout == kFp8Frag)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kGateUp, kFp8Frag>), grid, dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((grouped_gemm_kernel<kGateUp, kRowMajor>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
@@ -884,6 +1010,10 @@ hipError_t launch_gemm_down(const FfnGroups& p, const int32_t* sched, hipStream_
     hipLaunchKernelGGL((grouped_gemm_kernel<kGeluDown, kRowMajor>), grid, dim3(kThreads), 0, stream, a);
   else if (p.layout == kFrag16)
     hipLaunchKernelGGL((grouped_gemm_kernel<kDown, kFrag16>), grid, dim3(kThreads), 0, stream, a);
+  else if (p.layout == kInt8Frag)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kDown, kInt8Frag>), grid, dim3(kThreads), 0, stream, a);
+  else if (p.layout == kFp8Frag)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kDown, kFp8Frag>), grid, dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((grouped_gemm_kernel<kDown, kRowMajor>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();

@@ -459,7 +459,6 @@ long long all_rows(const FfnGroups& g) { return g.rows + (g.Hs > 0 ? g.T : 0); }
 
 FfnPath ffn_path(const FfnGroups& g) {
   if (g.dtype == kF32) return kPathF32;
-  if (byte_codes(g.layout)) return kPathStream;  // one-byte weights are a decode (weight-streaming) format
   return g.mean_rows_per_group >= kGemmMinRowsPerExpert ? kPathGemm : kPathStream;
 }
 
@@ -524,6 +523,8 @@ const char* ffn_gate_up_kernel_name(const FfnGroups& g) {
       return g.layout == kFrag16 ? "ffn_gate_up_stream<1, 1>" : "ffn_gate_up_stream<1, 0>";
     default:
       if (g.gelu) return g.layout == kFrag16 ? "grouped_gemm_kernel<3, 1>" : "grouped_gemm_kernel<3, 0>";
+      if (g.layout == kInt8Frag) return "grouped_gemm_kernel<0, 2>";
+      if (g.layout == kFp8Frag) return "grouped_gemm_kernel<0, 3>";
       return g.layout == kFrag16 ? "grouped_gemm_kernel<0, 1>" : "grouped_gemm_kernel<0, 0>";
   }
 }
@@ -537,6 +538,8 @@ const char* ffn_down_kernel_name(const FfnGroups& g) {
       return g.layout == kFrag16 ? "ffn_down_stream<1, 1>" : "ffn_down_stream<1, 0>";
     default:
       if (g.gelu) return g.layout == kFrag16 ? "grouped_gemm_kernel<4, 1>" : "grouped_gemm_kernel<4, 0>";
+      if (g.layout == kInt8Frag) return "grouped_gemm_kernel<1, 2>";
+      if (g.layout == kFp8Frag) return "grouped_gemm_kernel<1, 3>";
       return g.layout == kFrag16 ? "grouped_gemm_kernel<1, 1>" : "grouped_gemm_kernel<1, 0>";
   }
 }

@@ -178,11 +178,14 @@ def test_int8_layout_validation(shape, status):
 
 
 @pytest.mark.parametrize("layout,code", [(moe.MOE_LAYOUT_INT8_FRAG, 2), (moe.MOE_LAYOUT_FP8_FRAG, 3)])
-def test_one_byte_stage_names_always_stream(layout, code):
+def test_one_byte_stage_names_follow_the_rows_per_expert(layout, code):
+    """One-byte weights stream at decode sizes and take the grouped GEMM at prefill sizes, as bf16."""
     assert moe.moe_stage_kernel_name(dsv3(weight_layout=layout), 6) == f"ffn_gate_up_stream<1, {code}>"
     assert moe.moe_stage_kernel_name(dsv3(weight_layout=layout), 7) == f"ffn_down_stream<1, {code}>"
-    big = dsv3(T=8192, weight_layout=layout)     # would be the grouped GEMM with bf16 weights
-    assert moe.moe_stage_kernel_name(big, 5) == "" and moe.moe_stage_kernel_name(big, 6) == f"ffn_gate_up_stream<1, {code}>"
+    big = dsv3(T=8192, weight_layout=layout)
+    assert moe.moe_stage_kernel_name(big, 5) == "gemm_schedule_kernel"
+    assert moe.moe_stage_kernel_name(big, 6) == f"grouped_gemm_kernel<0, {code}>"
+    assert moe.moe_stage_kernel_name(big, 7) == f"grouped_gemm_kernel<1, {code}>"
 
 
 def test_load_stats_validation():

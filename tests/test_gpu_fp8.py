@@ -14,7 +14,7 @@ import torch
 import oracle
 from synth import LayerConfig
 from tests import gpu_util as G
-from tests.test_gpu_int8 import packed_reference
+from tests.test_gpu_int8 import expected_stage_names, packed_reference
 from tests.test_gpu_parity import check_logits_close, check_routing_on_gpu_logits
 
 import sparse_moe_layer_router_amd as moe
@@ -78,14 +78,20 @@ FP8 = [
     LayerConfig("fp8_mid_shared", 40, 256, 16, 4, 128, 64, "bf16"),
     LayerConfig("fp8_zipf", 64, 512, 64, 6, 256, 0, "bf16", zipf_s=1.2),
     LayerConfig("fp8_sigmoid_fused", 12, 128, 64, 6, 64, 64, "bf16", routing="sigmoid", score_bias_std=0.05),
-    LayerConfig("fp8_many_rows", 600, 256, 8, 2, 192, 128, "bf16"),  # one-byte weights keep the streaming kernels
+    # grouped GEMM cases, as for INT8: a partial N-tile and three K pairs; two M-tiles and one K
+    # pair; a shared expert of four M-tiles and two K pairs
+    LayerConfig("fp8_many_rows", 600, 256, 8, 2, 192, 128, "bf16"),
+    LayerConfig("fp8_gemm_two_mtiles", 1200, 64, 4, 2, 256, 0, "bf16", zipf_s=0.8),
+    LayerConfig("fp8_gemm_shared", 1000, 128, 16, 2, 128, 192, "bf16"),
 ]
 
 
 @pytest.mark.parametrize("cfg", FP8, ids=lambda c: c.name)
 def test_layer_fp8_weights_match_oracle(cfg):
     L = G.make_layer(cfg, layout=moe.MOE_LAYOUT_FP8_FRAG)
-    assert moe.moe_stage_kernel_name(L.shape, moe.STAGES.index("ffn_gate_up")) == "ffn_gate_up_stream<1, 3>"
+    gu, dn = expected_stage_names(cfg, 3)
+    assert moe.moe_stage_kernel_name(L.shape, moe.STAGES.index("ffn_gate_up")) == gu
+    assert moe.moe_stage_kernel_name(L.shape, moe.STAGES.index("ffn_down")) == dn
     r = G.run_layer(L)
     check_logits_close(L, r)
     check_routing_on_gpu_logits(L, r)

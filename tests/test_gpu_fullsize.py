@@ -128,10 +128,12 @@ def test_dsv3_layer(case, dsv3_runs):
 
 
 @pytest.mark.parametrize("quant", ["int8", "fp8"])
-@pytest.mark.parametrize("name,n_sample", [("dsv3_decode_t8", None), ("dsv3_decode_t256", 12)])
+@pytest.mark.parametrize("name,n_sample", [("dsv3_decode_t8", None), ("dsv3_decode_t256", 12),
+                                           ("dsv3_prefill_t8192", "structural")])
 def test_dsv3_layer_one_byte_weights(name, n_sample, quant, dsv3_weights):
-    """Per-row INT8 or FP8 expert weights at the decode sizes, against the oracle on the dequantized
-    weights."""
+    """Per-row INT8 or FP8 expert weights at the decode sizes (weight streaming) and at the prefill
+    size (grouped GEMM, every M-tile's first and last row checked), against the oracle on the
+    dequantized weights."""
     cfg = synth.CONFIG_BY_NAME[name]
     print(f"[{name}-{quant}] moe_layer_forward", flush=True)
     layout = {"int8": moe.MOE_LAYOUT_INT8_FRAG, "fp8": moe.MOE_LAYOUT_FP8_FRAG}[quant]
@@ -141,6 +143,11 @@ def test_dsv3_layer_one_byte_weights(name, n_sample, quant, dsv3_weights):
     check_routing_on_gpu_logits(L, r)
     if n_sample is None:
         tokens = np.arange(cfg.T)
+    elif n_sample == "structural":
+        idx = r.idx.cpu().numpy()
+        tokens = structural_tokens(idx, cfg.T, cfg.Hs)
+        assert_tile_edges_covered(idx, r.counts.cpu().numpy(), tokens, cfg.T, cfg.Hs)
+        assert moe.moe_stage_kernel_name(L.shape, moe.STAGES.index("ffn_gate_up")).startswith("grouped_gemm_kernel<0")
     else:
         rng = np.random.default_rng(0)
         tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, size=n_sample - 2, replace=False)]))

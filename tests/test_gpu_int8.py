@@ -56,15 +56,29 @@ INT8 = [
     LayerConfig("int8_mid_shared", 40, 256, 16, 4, 128, 64, "bf16"),
     LayerConfig("int8_zipf", 64, 512, 64, 6, 256, 0, "bf16", zipf_s=1.2),
     LayerConfig("int8_sigmoid_fused", 12, 128, 64, 6, 64, 64, "bf16", routing="sigmoid", score_bias_std=0.05),
-    # 150 rows per expert: the INT8 layout keeps the weight-streaming kernels (many token tiles)
+    # grouped GEMM (>= 32 rows per expert): 150 rows per expert, a partial N-tile (H = 192 = 128 + 64)
+    # and a down pass over three K pairs (K = 192)
     LayerConfig("int8_many_rows", 600, 256, 8, 2, 192, 128, "bf16"),
+    # grouped GEMM: ~600 rows per expert (two M-tiles), one K pair in gate/up (d = 64), skew
+    LayerConfig("int8_gemm_two_mtiles", 1200, 64, 4, 2, 256, 0, "bf16", zipf_s=0.8),
+    # grouped GEMM: shared expert of four M-tiles over 1000 tokens, two K pairs (d = 128)
+    LayerConfig("int8_gemm_shared", 1000, 128, 16, 2, 128, 192, "bf16"),
 ]
+
+
+def expected_stage_names(cfg, code):
+    """The expert kernels the layer runs: the grouped GEMM from 32 rows per expert, else streaming."""
+    if cfg.T * cfg.k / cfg.E >= 32:
+        return f"grouped_gemm_kernel<0, {code}>", f"grouped_gemm_kernel<1, {code}>"
+    return f"ffn_gate_up_stream<1, {code}>", f"ffn_down_stream<1, {code}>"
 
 
 @pytest.mark.parametrize("cfg", INT8, ids=lambda c: c.name)
 def test_layer_int8_weights_match_oracle(cfg):
     L = G.make_layer(cfg, layout=moe.MOE_LAYOUT_INT8_FRAG)
-    assert moe.moe_stage_kernel_name(L.shape, moe.STAGES.index("ffn_gate_up")) == "ffn_gate_up_stream<1, 2>"
+    gu, dn = expected_stage_names(cfg, 2)
+    assert moe.moe_stage_kernel_name(L.shape, moe.STAGES.index("ffn_gate_up")) == gu
+    assert moe.moe_stage_kernel_name(L.shape, moe.STAGES.index("ffn_down")) == dn
     r = G.run_layer(L)
     check_logits_close(L, r)
     check_routing_on_gpu_logits(L, r)
