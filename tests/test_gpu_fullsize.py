@@ -127,9 +127,14 @@ def test_dsv3_layer(case, dsv3_runs):
     check_run(dsv3_runs[case])
 
 
-@pytest.mark.parametrize("quant", ["int8", "fp8"])
-@pytest.mark.parametrize("name,n_sample", [("dsv3_decode_t8", None), ("dsv3_decode_t256", 12),
-                                           ("dsv3_prefill_t8192", "structural")])
+ONE_BYTE_CASES = [(n, k, q) for n, k in (("dsv3_decode_t8", None), ("dsv3_decode_t256", 12)) for q in ("int8", "fp8")]
+# the prefill size for INT8 only: the two code formats share every line of the grouped GEMM but the
+# code -> bf16 step (checked for all 256 codes of both), and the oracle's host-side E4M3 encoding
+# of all 256 experts would double the module's time
+ONE_BYTE_CASES.append(("dsv3_prefill_t8192", "structural", "int8"))
+
+
+@pytest.mark.parametrize("name,n_sample,quant", ONE_BYTE_CASES, ids=lambda v: str(v))
 def test_dsv3_layer_one_byte_weights(name, n_sample, quant, dsv3_weights):
     """Per-row INT8 or FP8 expert weights at the decode sizes (weight streaming) and at the prefill
     size (grouped GEMM, every M-tile's first and last row checked), against the oracle on the
