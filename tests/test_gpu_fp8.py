@@ -83,6 +83,9 @@ FP8 = [
     LayerConfig("fp8_many_rows", 600, 256, 8, 2, 192, 128, "bf16"),
     LayerConfig("fp8_gemm_two_mtiles", 1200, 64, 4, 2, 256, 0, "bf16", zipf_s=0.8),
     LayerConfig("fp8_gemm_shared", 1000, 128, 16, 2, 128, 192, "bf16"),
+    # grouped GEMM: d = 320, a partial 256-wide N-tile in the down pass (bands and scales past d
+    # never used) and five K pairs in gate/up (the pair ring wraps)
+    LayerConfig("fp8_gemm_ragged_d", 600, 320, 8, 2, 128, 64, "bf16"),
 ]
 
 
