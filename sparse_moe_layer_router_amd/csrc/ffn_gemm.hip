@@ -530,6 +530,41 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
   s1(nk - 1, nk - 1, nk % S);
   wait_vmcnt<0>();  // no load may still write LDS when the tile ends
 
+  if constexpr (Sl::Q && MODE != kRouter) {
+    // One-byte weights: each weight row's scale multiplies its fp32 sums (output column n of the
+    // tile), once, before either epilogue. The lane's 4 columns of each (column block, chunk):
+    // gate/up blocks 0 and 1 are the gate and up rows of the same hidden columns.
+    const FfnGroups& qp = ga.p;
+    const float* s0;
+    const float* s1;
+    if (first_pass(MODE)) {
+      s0 = c.g < qp.E ? code_scales(qp.w_gate, (size_t)qp.E * qp.H * qp.d) + (size_t)c.g * qp.H
+                      : code_scales(qp.ws_gate, (size_t)qp.Hs * qp.d);
+      s1 = c.g < qp.E ? code_scales(qp.w_up, (size_t)qp.E * qp.H * qp.d) + (size_t)c.g * qp.H
+                      : code_scales(qp.ws_up, (size_t)qp.Hs * qp.d);
+    } else {
+      s0 = s1 = c.g < qp.E ? code_scales(qp.w_down, (size_t)qp.E * qp.d * qp.H) + (size_t)c.g * qp.d
+                           : code_scales(qp.ws_down, (size_t)qp.d * qp.Hs);
+    }
+    f32x4_t sc[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int n = (MODE == kGateUp ? c.n0 + wn * 32 : c.n0 + wn * 64 + j * 32) + q * 8 + fh * 4;
+        n = n + 4 <= c.N ? n : c.N - 4;   // columns past N (N a multiple of 64) are never stored
+        sc[j][q] = *(const f32x4_t*)((j ? s1 : s0) + n);
+      }
+#pragma unroll
+    for (int i = 0; i < NAF; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] *= sc[j][q][e];
+  }
+
   // ---- epilogue ----------------------------------------------------------------------------------
   // The MFMAs take the weights as their first operand, so each 32x32 block holds the transposed
   // product: lane l has output row fr = l % 32 of the block and, for q = 0..3, the four
@@ -552,11 +587,6 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
     // accumulators touches fall in distinct banks. The GELU expert's second linear adds its bias
     // (fp32) before the rounding.
     const float* b2 = MODE == kGeluDown && p.b2 ? p.b2 + (size_t)c.g * p.d : nullptr;
-    // one-byte weights: the row scales of W_down multiply the fp32 sums before the rounding
-    const float* qs = nullptr;
-    if constexpr (Sl::Q)
-      qs = c.g < p.E ? code_scales(p.w_down, (size_t)p.E * p.d * p.H) + (size_t)c.g * p.d
-                     : code_scales(p.ws_down, (size_t)p.d * p.Hs);
     static_assert(G::MBW == 5 && G::BN == 256 && 160 * 512 <= kStages * Sl::STAGE, "staging layout");
     uint8_t* lt = &smem[0][0];
     int tid = (int)threadIdx.x;
@@ -575,13 +605,6 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
           for (int q = 0; q < 4; ++q) {
             const int nl = wn * 64 + j * 32 + q * 8 + efh * 4;
             float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            if constexpr (Sl::Q) {
-              if (c.n0 + nl < c.N) {  // N is a multiple of 64 here
-                const f32x4_t sc = *(const f32x4_t*)(qs + c.n0 + nl);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] *= sc[e];
-              }
-            }
             if (MODE == kGeluDown && b2 && c.n0 + nl < c.N) {  // N is a multiple of 8: 4 columns all in or all out
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] += b2[c.n0 + nl + e];
@@ -603,15 +626,6 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
     }
     return;
   }
-  // one-byte weights: the row scales of W_gate and W_up multiply the fp32 sums before SiLU(g) * u
-  const float* qsg = nullptr;
-  const float* qsu = nullptr;
-  if constexpr (Sl::Q && MODE == kGateUp) {
-    qsg = c.g < p.E ? code_scales(p.w_gate, (size_t)p.E * p.H * p.d) + (size_t)c.g * p.H
-                    : code_scales(p.ws_gate, (size_t)p.Hs * p.d);
-    qsu = c.g < p.E ? code_scales(p.w_up, (size_t)p.E * p.H * p.d) + (size_t)c.g * p.H
-                    : code_scales(p.ws_up, (size_t)p.Hs * p.d);
-  }
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int row = (wm + 2 * i) * 32 + efr;
@@ -630,14 +644,6 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
             for (int e = 0; e < 4; ++e) {
               g4[e] = acc[i][0][4 * q + e];
               u4[e] = acc[i][1][4 * q + e];
-            }
-            if constexpr (Sl::Q) {
-              const f32x4_t a = *(const f32x4_t*)(qsg + n), b = *(const f32x4_t*)(qsu + n);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                g4[e] *= a[e];
-                u4[e] *= b[e];
-              }
             }
             v = u32x2_t{pack_bf16x2(silu(g4[0]) * u4[0], silu(g4[1]) * u4[1]),
                         pack_bf16x2(silu(g4[2]) * u4[2], silu(g4[3]) * u4[3])};
