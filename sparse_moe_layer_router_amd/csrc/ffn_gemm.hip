@@ -134,18 +134,35 @@ __device__ __forceinline__ u32x4_t read_a(const uint8_t* sa, int i, int wm, int 
   if (packed_a(MODE)) return *(const u32x4_t*)(sa + (r / 16) * 1024 + ((r & 15) + 16 * ch) * 16);
   return *(const u32x4_t*)(sa + swz(r, ch));
 }
+// E4M3 codes become bf16 in four instructions, late (cvt_b, below); INT8 codes take about twenty
+// integer instructions, which measured better right at the read, overlapping the MFMAs in flight.
+constexpr bool late_cvt(int layout) { return layout == kFp8Frag; }
+
 template <int MODE, int LAYOUT>
 __device__ __forceinline__ u32x4_t read_b(const uint8_t* sb, int j, int wn, int fr, int ch) {
   const int n = b_row<MODE>(j, wn, fr);
   if constexpr (byte_codes(LAYOUT)) {
     // one-byte codes: block n/16 of the pair, lane slot (n%16) + 16*chunk holds the 8 codes of the
-    // chunk for the pair's first slice, then the same for its second (sb points at the slice's half)
+    // chunk for the pair's first slice, then the same for its second (sb points at the slice's
+    // half). With late_cvt the raw codes go to the low half of the fragment and cvt_b makes them
+    // bf16 later.
     const u32x2_t v = *(const u32x2_t*)(sb + (n / 16) * 1024 + ((n & 15) + 16 * ch) * 16);
+    if constexpr (late_cvt(LAYOUT)) return u32x4_t{v[0], v[1], 0u, 0u};
     return codes_to_bf16x8<LAYOUT>(v[0], v[1]);
   }
   if (LAYOUT == kFrag16)  // block n/16 of the stacked tile; lane position (n%16) + 16*chunk
     return *(const u32x4_t*)(sb + (n / 16) * 1024 + ((n & 15) + 16 * ch) * 16);
   return *(const u32x4_t*)(sb + swz(n, ch));
+}
+
+// A B fragment as the MFMA takes it: E4M3 codes (read raw by read_b) become bf16 here, right
+// before the MFMAs that use them, so that the LDS read they come from is waited for a step after
+// it was issued, and not at once together with every read in flight (FP8 down pass: 1,553 ->
+// 1,482 cycles per slice).
+template <int LAYOUT>
+__device__ __forceinline__ u32x4_t cvt_b(u32x4_t f) {
+  if constexpr (late_cvt(LAYOUT)) return codes_to_bf16x8<LAYOUT>(f[0], f[1]);
+  return f;
 }
 
 // The MFMAs of one 16-wide K step on the fragments in fa / fb, and the LDS reads of the next step
@@ -159,6 +176,10 @@ template <int MODE, int LAYOUT, int NA, int NV, class Load>
 __device__ __forceinline__ void mma_and_read(f32x16_t (&acc)[NA > 0 ? NA : 1][2], u32x4_t (&fa)[NA > 0 ? NA : 1],
                                              u32x4_t (&fb)[2], const uint8_t* sa, const uint8_t* sb, int wm,
                                              int wn, int fr, int ch, Load&& load) {
+  if constexpr (late_cvt(LAYOUT)) {
+    if (NA > 0) fb[0] = cvt_b<LAYOUT>(fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     acc[i][0] = mfma32x32x16(fb[0], fa[i], acc[i][0]);
@@ -172,6 +193,10 @@ __device__ __forceinline__ void mma_and_read(f32x16_t (&acc)[NA > 0 ? NA : 1][2]
   for (int j = NA; j < NV; ++j) load(j);
   __builtin_amdgcn_sched_barrier(0);
   if (NA > 0) fb[0] = read_b<MODE, LAYOUT>(sb, 0, wn, fr, ch);
+  if constexpr (late_cvt(LAYOUT)) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (NA > 0) fb[1] = cvt_b<LAYOUT>(fb[1]);
+  }
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     __builtin_amdgcn_sched_barrier(0);
