@@ -11,7 +11,8 @@
 namespace moe {
 
 // Eight int8 codes (two little-endian words) -> the eight bf16 values, byte i of lo in the low half
-// of word i / 2 (exact: |q| <= 127 has at most 7 significant bits).
+// of word i / 2. Exact: |q| <= 127 has at most 7 significant bits, so the float's low 16 bits are
+// zero and its high half is the bf16 value; one byte permute packs the high halves of a pair.
 __device__ __forceinline__ u32x4_t i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   u32x4_t r;
 #pragma unroll
@@ -20,7 +21,7 @@ __device__ __forceinline__ u32x4_t i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
     const int b = (i & 1) * 2;  // byte index of the pair's first code
     const float f0 = (float)((int32_t)(w << (24 - 8 * b)) >> 24);
     const float f1 = (float)((int32_t)(w << (16 - 8 * b)) >> 24);
-    r[i] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+    r[i] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
   }
   return r;
 }
