@@ -386,12 +386,14 @@ def main_gelu(args, cfg, K, W):
 
 
 # ------------------------------------------------------------------------------- measured roofs
-def measure_ceilings(dev, read_gib=4, mfma_iters=40000, reps=7):
+def measure_ceilings(dev, read_gib=4, mfma_iters=40000, reps=7, expert_cfg=None):
     """What this GPU sustains, from the library's probes (include/moe_calib.h), timed with HIP
     events on the launch stream (medians over ``reps``): a streaming read of a ``read_gib`` GiB
     buffer with and without the non-temporal hint, a device copy (read + write), and a register-only
     bf16 MFMA loop, two waves per SIMD, on random and on constant operands, with the shader clock
-    each ran at (from the counters each wave reads at its start and end)."""
+    each ran at (from the counters each wave reads at its start and end). With ``expert_cfg`` (a
+    layer of many rows per expert) also the vendor GEMM on that layer's expert work: see
+    ``library_expert_gemm``."""
     import torch
     import sparse_moe_layer_router_amd as moe
 
@@ -436,7 +438,45 @@ def measure_ceilings(dev, read_gib=4, mfma_iters=40000, reps=7):
     out["note"] = (f"read/copy: {read_gib} GiB; MFMA: {moe.MOE_CALIB_MFMA_BLOCKS} workgroups x 8 waves, "
                    f"{mfma_iters} x 8 32x32x16 bf16 MFMAs per wave; medians of {reps} event-timed runs")
     torch.cuda.empty_cache()
+    if expert_cfg is not None:
+        out["library_expert_gemm"] = library_expert_gemm(expert_cfg, dev, reps)
     return out
+
+
+def library_expert_gemm(cfg, dev, reps=7):
+    """The vendor GEMM (torch.bmm, which dispatches to hipBLASLt) on the expert work of ``cfg`` made
+    as easy as it gets: every routed expert holding exactly T*k/E rows, already gathered into
+    contiguous [E, M, d] blocks, no shared expert, no activation epilogue. Two batched products per
+    layer, each expert with its own weights streamed from HBM: gate and up as one [M, d] x [d, 2H]
+    product per expert, and down as [M, H] x [H, d]. Right operands are contiguous (never a
+    transposed view). Timed like the probes: one untimed call, then ``reps`` calls between HIP
+    events on the current stream, median."""
+    import torch
+
+    E, d, H = cfg.E, cfg.d, cfg.H
+    M = round(cfg.T * cfg.k / E)
+    stream = torch.cuda.current_stream(dev)
+    ev = HipEvents(2 * reps)
+    gen = torch.Generator(device=dev).manual_seed(1)
+    res = {"shape": f"{E} experts x {M} rows, d={d}, H={H} (uniform buckets, contiguous rows)"}
+    for name, (m, kk, n) in (("gate_up", (M, d, 2 * H)), ("down", (M, H, d))):
+        a = torch.randn(E, m, kk, generator=gen, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(E, kk, n, generator=gen, device=dev, dtype=torch.bfloat16)
+        c = torch.empty(E, m, n, device=dev, dtype=torch.bfloat16)
+        torch.bmm(a, b, out=c)
+        torch.cuda.synchronize()
+        for i in range(reps):
+            ev.record(2 * i, stream.cuda_stream)
+            torch.bmm(a, b, out=c)
+            ev.record(2 * i + 1, stream.cuda_stream)
+        torch.cuda.synchronize()
+        ms = statistics.median(ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps))
+        tflops = 2.0 * E * m * kk * n / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "TFLOPs": round(tflops, 1), "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+        del a, b, c
+        torch.cuda.empty_cache()
+    ev.close()
+    return res
 
 
 # ----------------------------------------------------------------------------------------- main
@@ -652,7 +692,7 @@ def sub_record(rec):
             "ms_per_step": rec["ms_per_step"], "tokens_per_s": rec["value"], "kernel": r["kernel"],
             "kernel_ms": r["kernel_ms"], "bound": r["bound"], "achieved": r["achieved"], "unit": r["unit"],
             "frac": r["frac"], "traffic": r["traffic"], "layer_hbm_GBps": rec["layer"]["hbm_GBps"],
-            "step_ms_events": rec["step_ms_events"]}
+            "stage_ms": rec["stage_ms"], "step_ms_events": rec["step_ms_events"]}
 
 
 def main():
@@ -669,7 +709,9 @@ def main():
     if args.ceilings:
         dev = torch.device("cuda:0")
         torch.cuda.set_device(dev)
-        print(json.dumps({"ceilings": measure_ceilings(dev)}), flush=True)
+        c = synth.CONFIG_BY_NAME[args.workload]
+        many_rows = c.dtype == "bf16" and c.T * c.k / c.E > 32
+        print(json.dumps({"ceilings": measure_ceilings(dev, expert_cfg=c if many_rows else None)}), flush=True)
         return
     cfg = synth.CONFIG_BY_NAME[args.workload]
     prefill = cfg.T * cfg.k / cfg.E > 32
@@ -702,12 +744,16 @@ def main():
         if subs:
             line["decode"] = subs
     if not args.no_ceilings:   # measured after the layer runs, so they do not disturb them
-        ceil = measure_ceilings(dev)
+        ceil = measure_ceilings(dev, expert_cfg=cfg if prefill and cfg.dtype == "bf16" else None)
         line["ceilings"] = ceil
         rf = line["roofline"]
         if rf["bound"] == "mfma":
             rf["measured_mfma_random_TFLOPs"] = ceil["mfma_bf16_random_TFLOPs"]
             rf["frac_of_measured_mfma"] = round(rf["achieved"] / ceil["mfma_bf16_random_TFLOPs"], 4)
+            lib = ceil.get("library_expert_gemm")
+            if lib and args.expert == "swiglu":   # the dominant kernel is the gate/up pass
+                rf["library_gate_up_TFLOPs"] = lib["gate_up"]["TFLOPs"]
+                rf["frac_of_library"] = round(rf["achieved"] / lib["gate_up"]["TFLOPs"], 4)
         else:
             rf["measured_read_GBps"] = ceil["read_nontemporal_GBps"]
             rf["frac_of_measured_read"] = round(rf["achieved"] / ceil["read_nontemporal_GBps"], 4)

@@ -8,10 +8,10 @@
 // One block per token, a thread per 8 consecutive features (one 16-byte bf16 load per row); a
 // block has up to 1024 threads for a few tokens and 256 for many, looping over the features. The
 // token's k slots (inv_perm, weight) are read once into registers; for k <= 8 (kernels for k <= 2,
-// 4 and 8) all k expert rows of a feature chunk are loaded before the first is used, so their
-// latencies overlap. Accumulation is fp32 in fixed slot order starting from the shared-expert row,
-// rounded once. Expert rows are loaded and bf16 outputs stored with the non-temporal hint: each is
-// touched once here (prefill: 0.26 -> 0.22 ms).
+// 4 and 8) all k expert rows of a feature chunk (and the shared-expert row) are loaded before the
+// first is used, so their latencies overlap. Accumulation is fp32 in fixed slot order starting from
+// the shared-expert row, rounded once. Expert rows are loaded and bf16 outputs stored with the
+// non-temporal hint: each is touched once here.
 #include "dispatch.h"
 #include "moe_device.h"
 
@@ -59,37 +59,47 @@ combine_kernel(const void* __restrict__ y, const int32_t* __restrict__ inv_perm,
   constexpr int KR = KMAX > 0 ? KMAX : 1;
   long long rr[KR];
   float wr[KR];
+  // The slots come in with one vector load (lane j reads slot j) and are then broadcast from their
+  // lanes. Slots past k repeat slot k - 1 (the same row, never added), so every row load below is
+  // unconditional and the compiler issues them back to back: behind a branch per slot it waited for
+  // each load before issuing the next.
+  if (KMAX > 0) {
+    const int lane = lane_id();
+    const int js = lane < k ? lane : k - 1;
+    int32_t rl = inv_perm[(size_t)t * k + js];
+    rl = rl < 0 ? 0 : (rl >= rows ? (int32_t)(rows - 1) : rl);  // never read outside y, whatever the indices hold
+    const float wl = w[(size_t)t * k + js];
 #pragma unroll
-  for (int j = 0; j < KR; ++j) {
-    long long r = 0;
-    float wj = 0.f;
-    if (KMAX > 0 && j < k) {
-      r = inv_perm[(size_t)t * k + j];
-      r = r < 0 ? 0 : (r >= rows ? rows - 1 : r);  // never read outside y, whatever the indices hold
-      wj = w[(size_t)t * k + j];
+    for (int j = 0; j < KR; ++j) {
+      const int src = j < k ? j : k - 1;
+      rr[j] = __shfl(rl, src, 64);
+      wr[j] = __shfl(wl, src, 64);
     }
-    rr[j] = r;
-    wr[j] = wj;
   }
   for (int i = threadIdx.x * 8; i < d; i += blockDim.x * 8) {
     float acc[8];
-    if (shared) {
-      load_row8<DT>(shared, (size_t)t * d + i, acc);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-    }
     if (KMAX > 0) {
       float v[KR][8];
 #pragma unroll
-      for (int j = 0; j < KR; ++j)
-        if (j < k) load_row8<DT, true>(y, (size_t)rr[j] * d + i, v[j]);
+      for (int j = 0; j < KR; ++j) load_row8<DT, true>(y, (size_t)rr[j] * d + i, v[j]);
+      if (shared) {
+        load_row8<DT>(shared, (size_t)t * d + i, acc);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+      }
 #pragma unroll
       for (int j = 0; j < KR; ++j)
         if (j < k)
 #pragma unroll
           for (int q = 0; q < 8; ++q) acc[q] += wr[j] * v[j][q];
     } else {
+      if (shared) {
+        load_row8<DT>(shared, (size_t)t * d + i, acc);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+      }
       for (int j = 0; j < k; ++j) {
         long long r = inv_perm[(size_t)t * k + j];
         r = r < 0 ? 0 : (r >= rows ? rows - 1 : r);

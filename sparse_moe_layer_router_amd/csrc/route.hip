@@ -10,7 +10,9 @@ namespace moe {
 
 // ------------------------------------------------------------------------------------- logits
 // One wave per (token, expert): lanes stride the d axis 8 elements at a time, fp32 accumulate,
-// deterministic butterfly reduction. Four experts per 256-thread block.
+// deterministic butterfly reduction. Four experts per 256-thread block. The bf16 loads of kChunks
+// consecutive strides are issued together before any of them is used, so a row of d = 7168 costs
+// two memory round trips instead of fourteen (the sums keep the same order).
 template <int DT>
 __global__ void __launch_bounds__(256)
 route_logits_valu(const void* __restrict__ x, const void* __restrict__ w, const float* __restrict__ bias,
@@ -21,14 +23,26 @@ route_logits_valu(const void* __restrict__ x, const void* __restrict__ w, const 
   if (e >= E) return;
   float acc = 0.f;
   if (DT == kBF16) {
+    constexpr int kChunks = 8;
     const uint16_t* xr = (const uint16_t*)x + (size_t)t * d;
     const uint16_t* wr = (const uint16_t*)w + (size_t)e * d;
-    for (int i = lane * 8; i < d; i += 64 * 8) {
-      u32x4_t a = ld16(xr + i), b = ld16(wr + i);
+    const u32x4_t zero = {0, 0, 0, 0};
+    for (int i0 = lane * 8; i0 < d; i0 += 64 * 8 * kChunks) {
+      u32x4_t a[kChunks], b[kChunks];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc += bf16_to_f32(a[q] & 0xFFFFu) * bf16_to_f32(b[q] & 0xFFFFu);
-        acc += bf16_to_f32(a[q] >> 16) * bf16_to_f32(b[q] >> 16);
+      for (int c = 0; c < kChunks; ++c) {
+        const int i = i0 + 64 * 8 * c;  // d is a multiple of 8: a lane's chunk is all in or all out
+        a[c] = i < d ? ld16(xr + i) : zero;
+        b[c] = i < d ? ld16(wr + i) : zero;
+      }
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        if (i0 + 64 * 8 * c >= d) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc += bf16_to_f32(a[c][q] & 0xFFFFu) * bf16_to_f32(b[c][q] & 0xFFFFu);
+          acc += bf16_to_f32(a[c][q] >> 16) * bf16_to_f32(b[c][q] >> 16);
+        }
       }
     }
   } else {
@@ -138,15 +152,24 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
   float v[NPER];  // the score that decides the selection
   float a[NPER];  // sigmoid routing: the unbiased affinity that enters the weights
   uint32_t taken = 0;
+  // every lane's scores (and biases) are loaded before any is used: from a clamped index, so the
+  // loads need no branch and share one memory round trip
+  float raw[NPER], rb[NPER];
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const int e = lane + 64 * j;
+    raw[j] = row[e < E ? e : E - 1];
+    rb[j] = (SIG && bias) ? bias[e < E ? e : E - 1] : 0.f;
+  }
 #pragma unroll
   for (int j = 0; j < NPER; ++j) {
     const int e = lane + 64 * j;
     const bool ok = e < E;
-    const float val = ok ? row[e] : 0.f;
+    const float val = ok ? raw[j] : 0.f;
     const bool nan = val != val;
     if (SIG) {
       a[j] = nan ? 0.f : 1.0f / (1.0f + expf(-val));
-      v[j] = nan ? -__builtin_inff() : a[j] + ((bias && ok) ? bias[e] : 0.f);
+      v[j] = nan ? -__builtin_inff() : a[j] + (ok ? rb[j] : 0.f);
     } else {
       v[j] = nan ? -__builtin_inff() : val;  // NaN orders like -inf so k ids are always chosen
     }
