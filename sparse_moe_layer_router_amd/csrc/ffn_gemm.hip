@@ -225,9 +225,6 @@ __device__ __forceinline__ const float* code_scales(const void* w, size_t ncodes
   return (const float*)((const int8_t*)w + ncodes);
 }
 
-// One zero kilobyte: the source of packed A blocks past the end of a group.
-__device__ __attribute__((aligned(16))) const uint32_t g_zero_block[256] = {0};
-
 // s_waitcnt through the builtin, so that the compiler's own wait insertion knows what has landed
 // (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; a field at its maximum waits
 // for nothing).
@@ -842,16 +839,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& ga, const int t, uint8
       }
       c.src[i] = (const uint16_t*)(MODE == kRouter ? ga.x : p.x) + (size_t)src * c.K;
     } else if (s < G::A_INSTR) {
-      // packed A: one contiguous 1 KB block per slice; bands past the group read zeros
-      const int bl = m0 / 16 + s;
+      // packed A: one contiguous 1 KB block per slice. Bands past the group (rows never stored) repeat
+      // its last band, which the tile loads anyway: a single zero kilobyte shared by every workgroup
+      // drew all of them to one L2 channel and measured slower
+      int bl = m0 / 16 + s;
+      bl = bl < gbands ? bl : gbands - 1;   // gbands >= 1: a group without rows has no tiles
       c.kc[i] = 0;
-      if (bl < gbands) {
-        c.stride[i] = 512;
-        c.src[i] = abase + (size_t)(band0 + bl) * (c.nk * 512) + lane * 8;
-      } else {
-        c.stride[i] = 0;
-        c.src[i] = (const uint16_t*)g_zero_block + lane * 8;
-      }
+      c.stride[i] = 512;
+      c.src[i] = abase + (size_t)(band0 + bl) * (c.nk * 512) + lane * 8;
     } else if constexpr (byte_codes(LAYOUT)) {
       // one-byte weight blocks q (first half of a pair) and q + B_INSTR (second half): 16 rows x 64 K
       // of codes each, stacked as in the bf16 tile (gate/up: 8 gate bands, then 8 up bands)
