@@ -267,6 +267,137 @@ ffn_gate_up_stream(const FfnGroups p) {
   }
 }
 
+// One matrix, 16 weight rows, against NTT 16-token tiles: the streaming loop of the down kernel
+// below with any B rows (x rows for the first layer). aw / qw: the lane's fragment source (bf16 with
+// ws elements between k-steps, or one-byte codes), bsrc: the lane's B row per tile (8 elements at
+// its k-chunk), K: reduction length.
+template <int NTT, int LAYOUT>
+__device__ __forceinline__ void stream_rows(const uint16_t* aw, const int8_t* qw, int ws, const uint16_t* const (&bsrc)[NTT],
+                                            const bool (&bok)[NTT], int K, int kq, f32x4_t (&acc)[NTT]) {
+  const u32x4_t zero = {0, 0, 0, 0};
+  int k0 = 0;
+  if (byte_codes(LAYOUT)) {
+    for (; k0 + 32 * kUnroll <= K; k0 += 32 * kUnroll) {
+      u32x4_t r[kUnroll / 2], b[kUnroll][NTT];
+#pragma unroll
+      for (int s2 = 0; s2 < kUnroll / 2; ++s2) r[s2] = ld16_stream(qw + (size_t)(k0 / 64 + s2) * 1024);
+#pragma unroll
+      for (int s = 0; s < kUnroll; ++s)
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bsrc[j] + k0 + 32 * s) : zero;
+#pragma unroll
+      for (int s2 = 0; s2 < kUnroll / 2; ++s2) {
+        const u32x4_t a0 = codes_to_bf16x8<LAYOUT>(r[s2][0], r[s2][1]), a1 = codes_to_bf16x8<LAYOUT>(r[s2][2], r[s2][3]);
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) {
+          acc[j] = mfma16x16x32(a0, b[2 * s2][j], acc[j]);
+          acc[j] = mfma16x16x32(a1, b[2 * s2 + 1][j], acc[j]);
+        }
+      }
+    }
+    for (; k0 < K; k0 += 64) {  // one-byte layouts: K is a multiple of 64
+      const u32x4_t r = ld16_stream(qw + (size_t)(k0 / 64) * 1024);
+      const u32x4_t a0 = codes_to_bf16x8<LAYOUT>(r[0], r[1]), a1 = codes_to_bf16x8<LAYOUT>(r[2], r[3]);
+#pragma unroll
+      for (int j = 0; j < NTT; ++j) {
+        acc[j] = mfma16x16x32(a0, bok[j] ? ld16(bsrc[j] + k0) : zero, acc[j]);
+        acc[j] = mfma16x16x32(a1, bok[j] ? ld16(bsrc[j] + k0 + 32) : zero, acc[j]);
+      }
+    }
+  } else {
+    for (; k0 + 32 * kUnroll <= K; k0 += 32 * kUnroll) {
+      u32x4_t a[kUnroll], b[kUnroll][NTT];
+#pragma unroll
+      for (int s = 0; s < kUnroll; ++s) a[s] = ld16_stream(aw + (size_t)(k0 / 32 + s) * ws);
+#pragma unroll
+      for (int s = 0; s < kUnroll; ++s)
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bsrc[j] + k0 + 32 * s) : zero;
+#pragma unroll
+      for (int s = 0; s < kUnroll; ++s)
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) acc[j] = mfma16x16x32(a[s], b[s][j], acc[j]);
+    }
+    for (; k0 < K; k0 += 32) {  // tail: K is a multiple of 8, so a lane's 8-chunk is all in or all out
+      const bool kok = k0 + kq * 8 < K;
+      const u32x4_t a = kok ? ld16_stream(aw + (size_t)(k0 / 32) * ws) : zero;
+#pragma unroll
+      for (int j = 0; j < NTT; ++j) acc[j] = mfma16x16x32(a, (kok && bok[j]) ? ld16(bsrc[j] + k0) : zero, acc[j]);
+    }
+  }
+}
+
+// The first layer with gate and up in separate waves: block (hb, g) owns 32 hidden rows of group g,
+// waves 2r (gate) and 2r + 1 (up) stream the 16 rows h0 = 32 hb + 16 r of one matrix each, and the up
+// wave hands its fp32 sums to the gate wave through LDS for SiLU(g) * u. One weight stream per wave
+// (as in the down kernel) at about two thirds of the registers of the two-stream kernel above, so
+// more waves fit on a SIMD, and half the bytes per wave. The sums are the same, bit for bit.
+template <int NTT, int LAYOUT>
+__global__ void __launch_bounds__(256)
+ffn_gate_up_stream_pair(const FfnGroups p) {
+  __shared__ f32x4_t up_sum[2][NTT][64];
+  const GroupView v = group_view(p, blockIdx.y, 16 * NTT);
+  if (v.n <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int is_up = wave & 1, rg = wave >> 1;
+  const int h0 = blockIdx.x * 32 + rg * 16;
+  const bool active = h0 < v.Hg;  // every wave stays to the barriers below
+  const int d = p.d;
+  const int ar = lane & 15, kq = lane >> 4;
+  const void* wmat = is_up ? v.wu : v.wg;
+  int ws = 0;
+  const uint16_t* aw = nullptr;
+  const int8_t* qw = nullptr;
+  if (active) {
+    if (byte_codes(LAYOUT)) qw = q8_base(wmat, h0, d, lane);
+    else aw = frag_base<LAYOUT>(wmat, h0, v.Hg, d, lane, &ws);
+  }
+  const uint16_t* xb = (const uint16_t*)p.x;
+  const int h = h0 + kq * 4;  // lane's four rows
+  f32x4_t sc = {1.f, 1.f, 1.f, 1.f};
+  if (byte_codes(LAYOUT) && active && h < v.Hg) sc = *(const f32x4_t*)((is_up ? v.su : v.sg) + h);
+
+  for (int tt = 0; tt < v.n; tt += 16 * NTT) {
+    const uint16_t* bx[NTT];
+    bool bok[NTT];
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) {
+      const int rr = tt + j * 16 + ar;
+      bok[j] = rr < v.n;
+      const long long src = bok[j] ? source_row(p, v, v.r0 + rr) : 0;
+      bx[j] = xb + (size_t)src * d + kq * 8;
+    }
+    f32x4_t acc[NTT];
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) acc[j] = f32x4_t{0, 0, 0, 0};
+    if (active) stream_rows<NTT, LAYOUT>(aw, qw, ws, bx, bok, d, kq, acc);
+    if (byte_codes(LAYOUT)) {
+#pragma unroll
+      for (int j = 0; j < NTT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[j][e] *= sc[e];
+    }
+    if (is_up) {
+#pragma unroll
+      for (int j = 0; j < NTT; ++j) up_sum[rg][j][lane] = acc[j];
+    }
+    __syncthreads();
+    if (!is_up && active) {
+#pragma unroll
+      for (int j = 0; j < NTT; ++j) {
+        const int rr = tt + j * 16 + ar;
+        if (rr < v.n && h < v.Hg) {
+          const f32x4_t g = acc[j], u = up_sum[rg][j][lane];
+          const uint32_t lo = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+          const uint32_t hi = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
+          *(u32x2_t*)(v.hid + (size_t)(v.r0 + rr) * v.Hg + h) = u32x2_t{lo, hi};
+        }
+      }
+    }
+    __syncthreads();  // the next token tile rewrites up_sum
+  }
+}
+
 template <int NTT, int LAYOUT>
 __global__ void __launch_bounds__(256)
 ffn_down_stream(const FfnGroups p) {
@@ -448,6 +579,12 @@ ffn_down_f32(const FfnGroups p) {
 // --------------------------------------------------------------------------------- launchers
 namespace {
 int stream_ntt(const FfnGroups& g) { return !byte_codes(g.layout) && g.T > 16 ? 2 : 1; }
+// Gate and up in separate waves (ffn_gate_up_stream_pair) for batches of at most 16 tokens, where an
+// expert holds one or two rows and the weight stream is all there is: decode T = 8 gate/up 0.540 ->
+// 0.527 ms (bf16), 0.295 -> 0.284 ms (FP8), 0.293 -> 0.287 ms (INT8). With more rows per expert both
+// waves of a pair read the same activation rows, and it loses (T = 256: bf16 2.33 -> 2.46 ms, INT8
+// 1.27 -> 1.58 ms).
+bool pair_waves(const FfnGroups& g) { return g.T <= 16; }
 // routed groups + one group per 16 NTT-row chunk of the shared expert
 int groups_of(const FfnGroups& g) {
   const int c = 16 * stream_ntt(g);
@@ -465,6 +602,18 @@ FfnPath ffn_path(const FfnGroups& g) {
 hipError_t launch_ffn_gate_up_stream(const FfnGroups& g, hipStream_t stream) {
   dim3 grid((hmax(g) + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
   const bool two = stream_ntt(g) == 2;
+  if (pair_waves(g)) {  // gate and up in separate waves, 32 hidden rows per block
+    const dim3 pgrid((hmax(g) + 31) / 32, groups_of(g));
+    if (g.layout == kInt8Frag)
+      hipLaunchKernelGGL((ffn_gate_up_stream_pair<1, kInt8Frag>), pgrid, dim3(256), 0, stream, g);
+    else if (g.layout == kFp8Frag)
+      hipLaunchKernelGGL((ffn_gate_up_stream_pair<1, kFp8Frag>), pgrid, dim3(256), 0, stream, g);
+    else if (g.layout == kFrag16)
+      hipLaunchKernelGGL((ffn_gate_up_stream_pair<1, kFrag16>), pgrid, dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((ffn_gate_up_stream_pair<1, kRowMajor>), pgrid, dim3(256), 0, stream, g);
+    return hipGetLastError();
+  }
   if (g.layout == kInt8Frag)
     hipLaunchKernelGGL((ffn_gate_up_stream<1, kInt8Frag>), grid, dim3(256), 0, stream, g);
   else if (g.layout == kFp8Frag)
@@ -517,6 +666,11 @@ const char* ffn_gate_up_kernel_name(const FfnGroups& g) {
   switch (ffn_path(g)) {
     case kPathF32: return "ffn_gate_up_f32";
     case kPathStream:
+      if (pair_waves(g)) {
+        if (g.layout == kInt8Frag) return "ffn_gate_up_stream_pair<1, 2>";
+        if (g.layout == kFp8Frag) return "ffn_gate_up_stream_pair<1, 3>";
+        return g.layout == kFrag16 ? "ffn_gate_up_stream_pair<1, 1>" : "ffn_gate_up_stream_pair<1, 0>";
+      }
       if (g.layout == kInt8Frag) return "ffn_gate_up_stream<1, 2>";
       if (g.layout == kFp8Frag) return "ffn_gate_up_stream<1, 3>";
       if (stream_ntt(g) == 2) return g.layout == kFrag16 ? "ffn_gate_up_stream<2, 1>" : "ffn_gate_up_stream<2, 0>";

@@ -147,7 +147,7 @@ def test_status_strings_and_stage_names():
     assert moe.moe_stage_kernel_name(dsv3(T=4096, n_experts=8, top_k=2, routing=sig), 1) == "route_topk_kernel<1, 1>"
     assert names[6] == "grouped_gemm_kernel<0, 0>" and names[7] == "grouped_gemm_kernel<1, 0>"
     packed = dsv3(T=8, weight_layout=moe.MOE_LAYOUT_FRAG16)
-    assert moe.moe_stage_kernel_name(packed, 6) == "ffn_gate_up_stream<1, 1>"
+    assert moe.moe_stage_kernel_name(packed, 6) == "ffn_gate_up_stream_pair<1, 1>"
     # router logits: one wave per (token, expert) up to 16 tokens, MFMA tiles up to 2047, the GEMM after
     assert moe.moe_stage_kernel_name(dsv3(T=16), 0) == "route_logits_valu<1>"
     assert moe.moe_stage_kernel_name(dsv3(T=256), 0) == "route_logits_mfma"
@@ -180,7 +180,7 @@ def test_int8_layout_validation(shape, status):
 @pytest.mark.parametrize("layout,code", [(moe.MOE_LAYOUT_INT8_FRAG, 2), (moe.MOE_LAYOUT_FP8_FRAG, 3)])
 def test_one_byte_stage_names_follow_the_rows_per_expert(layout, code):
     """One-byte weights stream at decode sizes and take the grouped GEMM at prefill sizes, as bf16."""
-    assert moe.moe_stage_kernel_name(dsv3(weight_layout=layout), 6) == f"ffn_gate_up_stream<1, {code}>"
+    assert moe.moe_stage_kernel_name(dsv3(weight_layout=layout), 6) == f"ffn_gate_up_stream_pair<1, {code}>"
     assert moe.moe_stage_kernel_name(dsv3(weight_layout=layout), 7) == f"ffn_down_stream<1, {code}>"
     big = dsv3(T=8192, weight_layout=layout)
     assert moe.moe_stage_kernel_name(big, 5) == "gemm_schedule_kernel"
