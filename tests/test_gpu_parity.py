@@ -31,6 +31,9 @@ MID = [
     LayerConfig("k_equals_E", 20, 128, 4, 4, 64, 32, "bf16"),
     LayerConfig("k12_wide_topk", 40, 128, 32, 12, 64, 32, "bf16"),  # combine with more than 8 slots
     LayerConfig("one_token", 1, 256, 32, 8, 128, 64, "bf16"),
+    # a decode batch (gate and up in separate waves) whose hidden sizes end inside a 16-row group and
+    # whose d ends inside a 32-wide k-step
+    LayerConfig("decode_ragged_shared", 12, 264, 16, 4, 200, 136, "bf16"),
     LayerConfig("wide_E1024", 40, 64, 1024, 2, 16, 0, "bf16"),
     synth.CONFIGS[0],
     # many rows per expert: tiled MFMA grouped GEMM (K tails of 8, partial N and M tiles)
