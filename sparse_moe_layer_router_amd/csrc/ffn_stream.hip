@@ -503,6 +503,75 @@ ffn_down_stream(const FfnGroups p) {
   }
 }
 
+// The down projection of one-byte weights for batches of more than 16 tokens: each wave streams 32
+// weight rows (two 16-row fragments) against one set of hidden-row fragments. With one byte per
+// weight the hidden rows (bf16, read from L2 by every wave of the expert) outweigh the codes, and a
+// 16-row wave read twice as many of them per weight byte. Block = 4 waves x 32 rows. Same sums, in
+// the same order, as ffn_down_stream<1, LAYOUT>.
+template <int LAYOUT>
+__global__ void __launch_bounds__(256)
+ffn_down_stream_wide(const FfnGroups p) {
+  static_assert(byte_codes(LAYOUT), "one-byte weights only");
+  const GroupView v = group_view(p, blockIdx.y, 16);
+  if (v.n <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int d = p.d;
+  const int i0 = blockIdx.x * 128 + wave * 32;   // rows i0 .. i0 + 15 and i0 + 16 .. i0 + 31
+  if (i0 >= d) return;
+  const bool two = i0 + 16 < d;                  // d is a multiple of 64: both groups or only the first
+  const int K = v.Hg;
+  const int ar = lane & 15, kq = lane >> 4;
+  const int8_t* qw0 = q8_base(v.wd, i0, K, lane);
+  const int8_t* qw1 = two ? q8_base(v.wd, i0 + 16, K, lane) : qw0;
+  const u32x4_t zero = {0, 0, 0, 0};
+  for (int tt = 0; tt < v.n; tt += 16) {
+    const int rr = tt + ar;
+    const bool bok = rr < v.n;
+    const uint16_t* bh = v.hid + (size_t)(v.r0 + (bok ? rr : 0)) * K + kq * 8;
+    f32x4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    int k0 = 0;
+    for (; k0 + 32 * kUnroll <= K; k0 += 32 * kUnroll) {
+      u32x4_t r0[kUnroll / 2], r1[kUnroll / 2], b[kUnroll];
+#pragma unroll
+      for (int s2 = 0; s2 < kUnroll / 2; ++s2) {
+        r0[s2] = ld16_stream(qw0 + (size_t)(k0 / 64 + s2) * 1024);
+        r1[s2] = ld16_stream(qw1 + (size_t)(k0 / 64 + s2) * 1024);
+      }
+#pragma unroll
+      for (int s = 0; s < kUnroll; ++s) b[s] = bok ? ld16(bh + k0 + 32 * s) : zero;
+#pragma unroll
+      for (int s2 = 0; s2 < kUnroll / 2; ++s2) {
+        const u32x4_t a0 = codes_to_bf16x8<LAYOUT>(r0[s2][0], r0[s2][1]), a1 = codes_to_bf16x8<LAYOUT>(r0[s2][2], r0[s2][3]);
+        const u32x4_t c0 = codes_to_bf16x8<LAYOUT>(r1[s2][0], r1[s2][1]), c1 = codes_to_bf16x8<LAYOUT>(r1[s2][2], r1[s2][3]);
+        acc0 = mfma16x16x32(a0, b[2 * s2], acc0);
+        acc0 = mfma16x16x32(a1, b[2 * s2 + 1], acc0);
+        acc1 = mfma16x16x32(c0, b[2 * s2], acc1);
+        acc1 = mfma16x16x32(c1, b[2 * s2 + 1], acc1);
+      }
+    }
+    for (; k0 < K; k0 += 64) {  // K (the hidden size) is a multiple of 64
+      const u32x4_t r0 = ld16_stream(qw0 + (size_t)(k0 / 64) * 1024);
+      const u32x4_t r1 = ld16_stream(qw1 + (size_t)(k0 / 64) * 1024);
+      const u32x4_t b0 = bok ? ld16(bh + k0) : zero, b1 = bok ? ld16(bh + k0 + 32) : zero;
+      acc0 = mfma16x16x32(codes_to_bf16x8<LAYOUT>(r0[0], r0[1]), b0, acc0);
+      acc0 = mfma16x16x32(codes_to_bf16x8<LAYOUT>(r0[2], r0[3]), b1, acc0);
+      acc1 = mfma16x16x32(codes_to_bf16x8<LAYOUT>(r1[0], r1[1]), b0, acc1);
+      acc1 = mfma16x16x32(codes_to_bf16x8<LAYOUT>(r1[2], r1[3]), b1, acc1);
+    }
+    if (!bok) continue;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      if (g == 1 && !two) break;
+      const int i = i0 + 16 * g + kq * 4;
+      const f32x4_t sc = *(const f32x4_t*)(v.sd + i);
+      const f32x4_t a = g ? acc1 : acc0;
+      const uint32_t lo = pack_bf16x2(a[0] * sc[0], a[1] * sc[1]);
+      const uint32_t hi = pack_bf16x2(a[2] * sc[2], a[3] * sc[3]);
+      *(u32x2_t*)(v.y + (size_t)(v.r0 + rr) * d + i) = u32x2_t{lo, hi};
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------ fp32 (VALU)
 // Plain per-element form for float32 layers: one thread per (row, output column).
 
@@ -585,6 +654,7 @@ int stream_ntt(const FfnGroups& g) { return !byte_codes(g.layout) && g.T > 16 ? 
 // waves of a pair read the same activation rows, and it loses (T = 256: bf16 2.33 -> 2.46 ms, INT8
 // 1.27 -> 1.58 ms).
 bool pair_waves(const FfnGroups& g) { return g.T <= 16; }
+bool wide_down(const FfnGroups& g) { return byte_codes(g.layout) && g.T > 16; }
 // routed groups + one group per 16 NTT-row chunk of the shared expert
 int groups_of(const FfnGroups& g) {
   const int c = 16 * stream_ntt(g);
@@ -632,6 +702,14 @@ hipError_t launch_ffn_gate_up_stream(const FfnGroups& g, hipStream_t stream) {
 hipError_t launch_ffn_down_stream(const FfnGroups& g, hipStream_t stream) {
   dim3 grid((g.d + kRowsPerBlock - 1) / kRowsPerBlock, groups_of(g));
   const bool two = stream_ntt(g) == 2;
+  if (wide_down(g)) {  // one-byte weights above 16 tokens: 32 weight rows per wave
+    const dim3 wgrid((g.d + 127) / 128, groups_of(g));
+    if (g.layout == kInt8Frag)
+      hipLaunchKernelGGL((ffn_down_stream_wide<kInt8Frag>), wgrid, dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((ffn_down_stream_wide<kFp8Frag>), wgrid, dim3(256), 0, stream, g);
+    return hipGetLastError();
+  }
   if (g.layout == kInt8Frag)
     hipLaunchKernelGGL((ffn_down_stream<1, kInt8Frag>), grid, dim3(256), 0, stream, g);
   else if (g.layout == kFp8Frag)
@@ -686,8 +764,8 @@ const char* ffn_down_kernel_name(const FfnGroups& g) {
   switch (ffn_path(g)) {
     case kPathF32: return "ffn_down_f32";
     case kPathStream:
-      if (g.layout == kInt8Frag) return "ffn_down_stream<1, 2>";
-      if (g.layout == kFp8Frag) return "ffn_down_stream<1, 3>";
+      if (g.layout == kInt8Frag) return wide_down(g) ? "ffn_down_stream_wide<2>" : "ffn_down_stream<1, 2>";
+      if (g.layout == kFp8Frag) return wide_down(g) ? "ffn_down_stream_wide<3>" : "ffn_down_stream<1, 3>";
       if (stream_ntt(g) == 2) return g.layout == kFrag16 ? "ffn_down_stream<2, 1>" : "ffn_down_stream<2, 0>";
       return g.layout == kFrag16 ? "ffn_down_stream<1, 1>" : "ffn_down_stream<1, 0>";
     default:

@@ -73,8 +73,9 @@ def expected_stage_names(cfg, code):
     """The expert kernels the layer runs: the grouped GEMM from 32 rows per expert, else streaming."""
     if cfg.T * cfg.k / cfg.E >= 32:
         return f"grouped_gemm_kernel<0, {code}>", f"grouped_gemm_kernel<1, {code}>"
-    gu = "ffn_gate_up_stream_pair" if cfg.T <= 16 else "ffn_gate_up_stream"   # gate and up in separate waves
-    return f"{gu}<1, {code}>", f"ffn_down_stream<1, {code}>"
+    if cfg.T <= 16:   # gate and up in separate waves
+        return f"ffn_gate_up_stream_pair<1, {code}>", f"ffn_down_stream<1, {code}>"
+    return f"ffn_gate_up_stream<1, {code}>", f"ffn_down_stream_wide<{code}>"   # 32 down rows per wave
 
 
 @pytest.mark.parametrize("cfg", INT8, ids=lambda c: c.name)
