@@ -503,6 +503,83 @@ ffn_down_stream(const FfnGroups p) {
   }
 }
 
+// The first layer of one-byte weights for batches of more than 16 tokens: each wave streams 32 gate
+// and 32 up rows (two 16-row fragments of each) against one set of x fragments, for the reason
+// given at ffn_down_stream_wide. Block = 4 waves x 32 hidden rows. Same sums, in the same order, as
+// ffn_gate_up_stream<1, LAYOUT>.
+template <int LAYOUT>
+__global__ void __launch_bounds__(256)
+ffn_gate_up_stream_wide(const FfnGroups p) {
+  static_assert(byte_codes(LAYOUT), "one-byte weights only");
+  constexpr int kU = 8;  // k-steps per block of loads (kU / 2 loads per fragment stream)
+  const GroupView v = group_view(p, blockIdx.y, 16);
+  if (v.n <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int h0 = blockIdx.x * 128 + wave * 32;   // hidden rows h0 .. h0 + 31
+  if (h0 >= v.Hg) return;                        // Hg is a multiple of 64: both halves or none
+  const int d = p.d;
+  const int ar = lane & 15, kq = lane >> 4;
+  const int8_t* qg[2] = {q8_base(v.wg, h0, d, lane), q8_base(v.wg, h0 + 16, d, lane)};
+  const int8_t* qu[2] = {q8_base(v.wu, h0, d, lane), q8_base(v.wu, h0 + 16, d, lane)};
+  const uint16_t* xb = (const uint16_t*)p.x;
+  const u32x4_t zero = {0, 0, 0, 0};
+  for (int tt = 0; tt < v.n; tt += 16) {
+    const int rr = tt + ar;
+    const bool bok = rr < v.n;
+    const long long src = bok ? source_row(p, v, v.r0 + rr) : 0;
+    const uint16_t* bx = xb + (size_t)src * d + kq * 8;
+    f32x4_t accg[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, accu[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    int k0 = 0;
+    for (; k0 + 32 * kU <= d; k0 += 32 * kU) {
+      u32x4_t rg[2][kU / 2], ru[2][kU / 2], b[kU];
+#pragma unroll
+      for (int s2 = 0; s2 < kU / 2; ++s2)
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          rg[f][s2] = ld16_stream(qg[f] + (size_t)(k0 / 64 + s2) * 1024);
+          ru[f][s2] = ld16_stream(qu[f] + (size_t)(k0 / 64 + s2) * 1024);
+        }
+#pragma unroll
+      for (int s = 0; s < kU; ++s) b[s] = bok ? ld16(bx + k0 + 32 * s) : zero;
+#pragma unroll
+      for (int s2 = 0; s2 < kU / 2; ++s2)
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const u32x4_t g0 = codes_to_bf16x8<LAYOUT>(rg[f][s2][0], rg[f][s2][1]), g1 = codes_to_bf16x8<LAYOUT>(rg[f][s2][2], rg[f][s2][3]);
+          const u32x4_t u0 = codes_to_bf16x8<LAYOUT>(ru[f][s2][0], ru[f][s2][1]), u1 = codes_to_bf16x8<LAYOUT>(ru[f][s2][2], ru[f][s2][3]);
+          accg[f] = mfma16x16x32(g0, b[2 * s2], accg[f]);
+          accu[f] = mfma16x16x32(u0, b[2 * s2], accu[f]);
+          accg[f] = mfma16x16x32(g1, b[2 * s2 + 1], accg[f]);
+          accu[f] = mfma16x16x32(u1, b[2 * s2 + 1], accu[f]);
+        }
+    }
+    for (; k0 < d; k0 += 64) {  // one-byte layouts: d is a multiple of 64
+      const u32x4_t b0 = bok ? ld16(bx + k0) : zero, b1 = bok ? ld16(bx + k0 + 32) : zero;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const u32x4_t r_g = ld16_stream(qg[f] + (size_t)(k0 / 64) * 1024);
+        const u32x4_t r_u = ld16_stream(qu[f] + (size_t)(k0 / 64) * 1024);
+        accg[f] = mfma16x16x32(codes_to_bf16x8<LAYOUT>(r_g[0], r_g[1]), b0, accg[f]);
+        accu[f] = mfma16x16x32(codes_to_bf16x8<LAYOUT>(r_u[0], r_u[1]), b0, accu[f]);
+        accg[f] = mfma16x16x32(codes_to_bf16x8<LAYOUT>(r_g[2], r_g[3]), b1, accg[f]);
+        accu[f] = mfma16x16x32(codes_to_bf16x8<LAYOUT>(r_u[2], r_u[3]), b1, accu[f]);
+      }
+    }
+    if (!bok) continue;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int h = h0 + 16 * f + kq * 4;
+      const f32x4_t sg = *(const f32x4_t*)(v.sg + h), su = *(const f32x4_t*)(v.su + h);
+      f32x4_t g = accg[f], u = accu[f];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { g[e] *= sg[e]; u[e] *= su[e]; }
+      const uint32_t lo = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+      const uint32_t hi = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
+      *(u32x2_t*)(v.hid + (size_t)(v.r0 + rr) * v.Hg + h) = u32x2_t{lo, hi};
+    }
+  }
+}
+
 // The down projection of one-byte weights for batches of more than 16 tokens: each wave streams 32
 // weight rows (two 16-row fragments) against one set of hidden-row fragments. With one byte per
 // weight the hidden rows (bf16, read from L2 by every wave of the expert) outweigh the codes, and a
@@ -684,6 +761,14 @@ hipError_t launch_ffn_gate_up_stream(const FfnGroups& g, hipStream_t stream) {
       hipLaunchKernelGGL((ffn_gate_up_stream_pair<1, kRowMajor>), pgrid, dim3(256), 0, stream, g);
     return hipGetLastError();
   }
+  if (wide_down(g)) {  // one-byte weights above 16 tokens: 32 gate and 32 up rows per wave
+    const dim3 wgrid((hmax(g) + 127) / 128, groups_of(g));
+    if (g.layout == kInt8Frag)
+      hipLaunchKernelGGL((ffn_gate_up_stream_wide<kInt8Frag>), wgrid, dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((ffn_gate_up_stream_wide<kFp8Frag>), wgrid, dim3(256), 0, stream, g);
+    return hipGetLastError();
+  }
   if (g.layout == kInt8Frag)
     hipLaunchKernelGGL((ffn_gate_up_stream<1, kInt8Frag>), grid, dim3(256), 0, stream, g);
   else if (g.layout == kFp8Frag)
@@ -749,8 +834,8 @@ const char* ffn_gate_up_kernel_name(const FfnGroups& g) {
         if (g.layout == kFp8Frag) return "ffn_gate_up_stream_pair<1, 3>";
         return g.layout == kFrag16 ? "ffn_gate_up_stream_pair<1, 1>" : "ffn_gate_up_stream_pair<1, 0>";
       }
-      if (g.layout == kInt8Frag) return "ffn_gate_up_stream<1, 2>";
-      if (g.layout == kFp8Frag) return "ffn_gate_up_stream<1, 3>";
+      if (g.layout == kInt8Frag) return wide_down(g) ? "ffn_gate_up_stream_wide<2>" : "ffn_gate_up_stream<1, 2>";
+      if (g.layout == kFp8Frag) return wide_down(g) ? "ffn_gate_up_stream_wide<3>" : "ffn_gate_up_stream<1, 3>";
       if (stream_ntt(g) == 2) return g.layout == kFrag16 ? "ffn_gate_up_stream<2, 1>" : "ffn_gate_up_stream<2, 0>";
       return g.layout == kFrag16 ? "ffn_gate_up_stream<1, 1>" : "ffn_gate_up_stream<1, 0>";
     default:

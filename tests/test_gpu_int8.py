@@ -75,7 +75,7 @@ def expected_stage_names(cfg, code):
         return f"grouped_gemm_kernel<0, {code}>", f"grouped_gemm_kernel<1, {code}>"
     if cfg.T <= 16:   # gate and up in separate waves
         return f"ffn_gate_up_stream_pair<1, {code}>", f"ffn_down_stream<1, {code}>"
-    return f"ffn_gate_up_stream<1, {code}>", f"ffn_down_stream_wide<{code}>"   # 32 down rows per wave
+    return f"ffn_gate_up_stream_wide<{code}>", f"ffn_down_stream_wide<{code}>"   # 32 weight rows per wave
 
 
 @pytest.mark.parametrize("cfg", INT8, ids=lambda c: c.name)
