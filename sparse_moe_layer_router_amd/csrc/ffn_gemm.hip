@@ -75,7 +75,8 @@ template <int MODE> struct Geo {
   static constexpr int MBW = MODE == kRouter ? 1 : 5;              // 32-row blocks per wave
   static constexpr int BM = MBW * kWavesM * 32;                    // tile rows: 320 (router 64)
   static constexpr int NB = MODE == kGateUp ? 2 : 1;               // B matrices per tile
-  static constexpr int BN = MODE == kGateUp ? 128 : 256;           // rows of each B tile
+  static constexpr int NBJ = MODE == kRouter ? 1 : 2;              // 32-column blocks per wave
+  static constexpr int BN = MODE == kGateUp ? 128 : NBJ * kWavesN * 32;  // rows of each B tile (router 128)
   static constexpr int BROWS = NB * BN;                            // stacked B rows (256)
   static constexpr int A_INSTR = BM / 16;                          // 1 KB loads of A per slice
   static constexpr int B_INSTR = BROWS / 16;                       // 1 KB loads of B per slice
@@ -122,7 +123,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes 
 // Stacked B row (inside the slice's B region) of the wave's B fragment j for fragment row fr.
 template <int MODE>
 __device__ __forceinline__ int b_row(int j, int wn, int fr) {
-  return MODE == kGateUp ? j * Geo<MODE>::BN + wn * 32 + fr : wn * 64 + j * 32 + fr;
+  return MODE == kGateUp ? j * Geo<MODE>::BN + wn * 32 + fr : wn * 32 * Geo<MODE>::NBJ + j * 32 + fr;
 }
 
 // A fragment i (rows (wm + 2 i) * 32 + fr) and B fragment j of one 16-wide K step, chunk column ch.
@@ -176,6 +177,25 @@ template <int MODE, int LAYOUT, int NA, int NV, class Load>
 __device__ __forceinline__ void mma_and_read(f32x16_t (&acc)[NA > 0 ? NA : 1][2], u32x4_t (&fa)[NA > 0 ? NA : 1],
                                              u32x4_t (&fb)[2], const uint8_t* sa, const uint8_t* sb, int wm,
                                              int wn, int fr, int ch, Load&& load) {
+  if constexpr (Geo<MODE>::NBJ == 1) {  // the router: one column block, the reads after its MFMAs
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      acc[i][0] = mfma32x32x16(fb[0], fa[i], acc[i][0]);
+      if (i < NV) {
+        __builtin_amdgcn_sched_barrier(0);
+        load(i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int j = NA; j < NV; ++j) load(j);
+    __builtin_amdgcn_sched_barrier(0);
+    if (NA > 0) fb[0] = read_b<MODE, LAYOUT>(sb, 0, wn, fr, ch);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) fa[i] = read_a<MODE>(sa, i, wm, fr, ch);
+    __builtin_amdgcn_sched_barrier(0);
+    return;
+  }
   if constexpr (late_cvt(LAYOUT)) {
     if (NA > 0) fb[0] = cvt_b<LAYOUT>(fb[0]);
     __builtin_amdgcn_sched_barrier(0);
@@ -217,7 +237,7 @@ __device__ __forceinline__ void read_all(u32x4_t (&fa)[NA > 0 ? NA : 1], u32x4_t
   fb[0] = read_b<MODE, LAYOUT>(sb, 0, wn, fr, ch);
 #pragma unroll
   for (int i = 0; i < NA; ++i) fa[i] = read_a<MODE>(sa, i, wm, fr, ch);
-  fb[1] = read_b<MODE, LAYOUT>(sb, 1, wn, fr, ch);
+  if constexpr (Geo<MODE>::NBJ == 2) fb[1] = read_b<MODE, LAYOUT>(sb, 1, wn, fr, ch);
 }
 
 // The float32 row scales of a one-byte weight buffer: they follow its `ncodes` codes.
@@ -653,10 +673,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs& ga, const TileCtx<MODE
     const int row = (wm + 2 * i) * 32 + efr;
     if (row >= c.rows) continue;
 #pragma unroll
-    for (int j = 0; j < (MODE == kGateUp ? 1 : 2); ++j) {
+    for (int j = 0; j < (MODE == kGateUp ? 1 : G::NBJ); ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = c.n0 + (MODE == kGateUp ? wn * 32 : wn * 64 + j * 32) + q * 8 + efh * 4;  // 4 columns
+        const int n = c.n0 + (MODE == kGateUp ? wn * 32 : wn * 32 * G::NBJ + j * 32) + q * 8 + efh * 4;  // 4 columns
         if (MODE == kGateUp) {
           if (n >= np) continue;  // N, np and n are multiples of 4: the four columns are all in or all out
           u32x2_t v = {0u, 0u};
