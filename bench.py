@@ -60,6 +60,10 @@ def parse():
     p.add_argument("--layout", choices=["frag16", "rowmajor", "int8", "fp8"], default="frag16",
                    help="expert weight layout (frag16: packed once at load time, before timing; int8, fp8: "
                         "per-row INT8 or E4M3 codes made once from the bf16 weights, before timing)")
+    p.add_argument("--ep-share", type=int, default=0, metavar="G",
+                   help="instead of the layer, time the expert stage of one GPU of G in expert parallel: "
+                        "its E/G experts over the rows routed to them from G batches of T tokens, and the "
+                        "shared expert over its own T tokens (bf16 weights)")
     return p.parse_args()
 
 
@@ -686,6 +690,136 @@ def run_layer_bench(cfg, K, W, weights, layout, dev):
     return rec, host
 
 
+def ep_share_rows(cfg, G, weights_dtype, dev):
+    """The rows one GPU of G receives in an expert-parallel layer: G batches of T tokens (one per GPU)
+    are routed and permuted by the layer's own kernels; GPU 0 holds experts [0, E/G) and receives
+    every row routed to them, which the dispatch places in local-expert order (each source's rows of
+    an expert contiguous, the sources in rank order). Returns the received rows [R, d], the local
+    bucket offsets [E/G + 1] and the per-expert counts (host)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import sparse_moe_layer_router_amd as moe
+
+    El = cfg.E // G
+    host = synth.host_small_inputs(cfg, 0)
+    dt = weights_dtype
+    w_router = torch.from_numpy(np.ascontiguousarray(host.w_router).view(np.int16)).view(torch.bfloat16).to(dev)
+    bias = torch.from_numpy(host.router_bias).to(dev) if host.router_bias is not None else None
+    shape = moe.make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.H, cfg.Hs, cfg.dtype, moe.MOE_LAYOUT_ROWMAJOR, cfg.routing)
+    ws = moe.allocate_workspace(shape)
+    logits = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=dev)
+    idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
+    tw = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=dev)
+    cnt = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    offs = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev)
+    inv = torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev)
+    chunks = [[] for _ in range(El)]
+    for g in range(G):
+        x = torch.empty(cfg.T, cfg.d, dtype=dt, device=dev)
+        synth.normal_device(x, 300 + g, synth.stream_id(synth.K_X), 1.0)
+        moe.moe_route(shape, x, w_router, bias, logits, idx, tw, ws)
+        moe.moe_permute(shape, idx, cnt, offs, perm, inv, ws)
+        o = offs.cpu().numpy()
+        for e in range(El):
+            src = (perm[int(o[e]):int(o[e + 1])] // cfg.k).long()
+            chunks[e].append(x.index_select(0, src))
+        del x
+    rows = [torch.cat(c) for c in chunks]
+    counts = np.array([r.shape[0] for r in rows], dtype=np.int64)
+    xr = torch.cat(rows).contiguous()
+    del rows, chunks, ws
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return xr, offsets, counts
+
+
+def main_ep_share(args, cfg, K, W):
+    """Expert stage of one GPU of ``args.ep_share`` in expert parallel, at the prefill size per GPU:
+    moe_grouped_ffn over the GPU's E/G experts and the rows routed to them from all G batches, then
+    the shared expert over the GPU's own T tokens (a second moe_grouped_ffn; in a full layer it can
+    run while the dispatch exchange is in flight). The exchange itself is not part of this build.
+    One JSON line: the expert stage's tokens/s (the GPU's own T tokens per stage time) and the routed
+    call (schedule, gate/up and down launches) against the bf16 MFMA peak."""
+    import torch
+
+    import synth
+    import sparse_moe_layer_router_amd as moe
+
+    G = args.ep_share
+    if cfg.dtype != "bf16" or args.layout not in ("frag16", "rowmajor") or cfg.E % G or args.expert != "swiglu":
+        print("--ep-share needs a bf16 SwiGLU layer, --layout frag16 or rowmajor, and G dividing E", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    El = cfg.E // G
+    (wgt, wup, wdn, shared), layout = make_weights(args, cfg, dev)
+    wgt, wup, wdn = wgt[:El], wup[:El], wdn[:El]   # experts [0, E/G): contiguous prefixes
+    xr, offs, counts = ep_share_rows(cfg, G, wgt.dtype, dev)
+    R = int(counts.sum())
+    s_r = moe.make_shape(R, cfg.d, El, 1, cfg.H, 0, cfg.dtype, layout, cfg.routing)
+    ws_r = moe.allocate_workspace(s_r)
+    y_r = torch.empty(R, cfg.d, dtype=wgt.dtype, device=dev)
+    x_own = torch.empty(cfg.T, cfg.d, dtype=wgt.dtype, device=dev)
+    synth.normal_device(x_own, 300, synth.stream_id(synth.K_X), 1.0)
+    s_s = moe.make_shape(cfg.T, cfg.d, 1, 1, cfg.Hs, 0, cfg.dtype, layout, cfg.routing)
+    ws_s = moe.allocate_workspace(s_s)
+    offs_s = torch.tensor([0, cfg.T], dtype=torch.int32, device=dev)
+    y_s = torch.empty(cfg.T, cfg.d, dtype=wgt.dtype, device=dev)
+    sg, su, sd = shared
+    stream = torch.cuda.current_stream(dev)
+
+    def routed():
+        moe.moe_grouped_ffn(s_r, xr, None, offs, wgt, wup, wdn, y_r, ws_r, stream)
+
+    def shared_ffn():
+        moe.moe_grouped_ffn(s_s, x_own, None, offs_s, sg, su, sd, y_s, ws_s, stream)
+
+    for _ in range(W):
+        routed()
+        shared_ffn()
+    torch.cuda.synchronize()
+    ev = HipEvents(4 * K)
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev.record(4 * i, stream.cuda_stream)
+        routed()
+        ev.record(4 * i + 1, stream.cuda_stream)
+        ev.record(4 * i + 2, stream.cuda_stream)
+        shared_ffn()
+        ev.record(4 * i + 3, stream.cuda_stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    r_ms = statistics.median(ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(K))
+    s_ms = statistics.median(ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(K))
+    ev.close()
+    flops_r = 6.0 * R * cfg.d * cfg.H
+    flops_s = 6.0 * cfg.T * cfg.d * cfg.Hs
+    ach = flops_r / (r_ms * 1e-3) / 1e12
+    kname = " + ".join(moe.moe_stage_kernel_name(s_r, moe.STAGES.index(st)) for st in ("ffn_gate_up", "ffn_down"))
+    line = {"metric": "expert-stage tokens/s of one GPU's expert-parallel share", "value": round(cfg.T * K / elapsed, 2),
+            "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(elapsed * 1e3 / K, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+            "data": "synthetic (seeded Philox normal draws; random-init weights of the named layer shape)",
+            "config": {"workload": f"{cfg.name}_ep{G}_share", "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E,
+                       "top_k": cfg.k, "d_hidden": cfg.H, "d_shared_hidden": cfg.Hs, "ep_degree": G,
+                       "local_experts": El, "received_rows": R,
+                       "rows_per_expert": {"min": int(counts.min()), "mean": round(float(counts.mean()), 1),
+                                           "max": int(counts.max())},
+                       "weight_layout": "frag16" if layout == moe.MOE_LAYOUT_FRAG16 else "rowmajor",
+                       "parallelism": f"one GPU's share of ep{G} (the exchange not included)"},
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ach / BF16_PEAK_TFLOPS, 4), "kernel": kname, "kernel_ms": round(r_ms, 4),
+                         "kernel_scope": "the routed moe_grouped_ffn call (schedule, gate/up and down launches)",
+                         "traffic": None},
+            "shared_expert": {"ms": round(s_ms, 4), "TFLOPs": round(flops_s / (s_ms * 1e-3) / 1e12, 2)},
+            "cpu_baseline": None}
+    print(json.dumps(line), flush=True)
+
+
 def sub_record(rec):
     """The decode figures carried next to the headline: step time, tokens/s and the dominant
     kernel against the HBM roofline (with its counter traffic when the summary is current)."""
@@ -719,6 +853,8 @@ def main():
     prefill = cfg.T * cfg.k / cfg.E > 32
     K = args.steps if args.steps is not None else (30 if prefill else 50)
     W = args.warmup if args.warmup is not None else 5
+    if args.ep_share:
+        return main_ep_share(args, cfg, K, W)
     if args.expert == "gelu":
         return main_gelu(args, cfg, K, W)
     dev = torch.device("cuda:0")

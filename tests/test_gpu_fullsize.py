@@ -24,6 +24,7 @@ import torch
 import oracle
 import synth
 from tests import gpu_util as G
+from tests import helpers
 from tests.helpers import M_TILE_ROWS, assert_tile_edges_covered, prefetching_expert_fn, structural_tokens
 from tests.test_gpu_parity import check_logits_close, check_routing_on_gpu_logits
 
@@ -162,6 +163,70 @@ def test_dsv3_layer_one_byte_weights(name, n_sample, quant, dsv3_weights):
     np.testing.assert_array_equal(np.sort(r.idx.cpu().numpy()[tokens], 1), np.sort(ref["idx"], 1))
     ok, err, bound = G.tolerance_ok(G.to_f64(r.out)[tokens], ref["out"])
     assert ok, (err, bound)
+
+
+EP_EXPERTS = 32   # one GPU's experts when the 256 are split over 8 GPUs in expert parallel
+
+
+def ep_share_counts(seed=0):
+    """Bucket sizes around the 2,048 rows per expert that one GPU of eight receives when each GPU
+    routes 8,192 tokens, with the ragged cases of the 320-row M-tiling: an empty expert, a single
+    row, an exact multiple of the tile and one row past it."""
+    rng = np.random.default_rng(seed)
+    c = rng.integers(1800, 2300, size=EP_EXPERTS)
+    c[3], c[7], c[11], c[19] = 0, 1, 6 * M_TILE_ROWS, 6 * M_TILE_ROWS + 1
+    return c
+
+
+@pytest.mark.timeout(900)
+def test_dsv3_ep8_share_grouped_ffn(dsv3_weights):
+    """moe_grouped_ffn at one expert-parallel GPU's share of the DeepSeek-V3-shaped layer (the
+    shape bench.py --ep-share 8 times): the first 32 experts over ~2,048 contiguous received rows
+    each (perm_src NULL, k = 1), both bf16 weight layouts. Checked rows: the first and last row of
+    every 320-row M-tile of every bucket plus a seeded sample, against the oracle's SwiGLU of each
+    expert on those rows."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    cfg = DSV3
+    counts = ep_share_counts()
+    R = int(counts.sum())
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    x = torch.empty(R, cfg.d, dtype=torch.bfloat16, device="cuda")
+    synth.normal_device(x, 7, synth.stream_id(synth.K_X), 1.0)
+    rows = set()
+    for e in range(EP_EXPERTS):
+        for m0 in range(int(offs[e]), int(offs[e + 1]), M_TILE_ROWS):
+            rows.update((m0, min(m0 + M_TILE_ROWS, int(offs[e + 1])) - 1))
+    rows.update(np.random.default_rng(1).choice(R, size=16, replace=False).tolist())
+    rows = np.array(sorted(rows), dtype=np.int64)
+    owner = np.searchsorted(offs, rows, side="right") - 1
+    outs = {}
+    for lname in ("frag16", "rowmajor"):
+        print(f"[ep8-share-{lname}] moe_grouped_ffn E={EP_EXPERTS} rows={R} d={cfg.d} H={cfg.H}", flush=True)
+        (g, u, dn), _, _ = dsv3_weights[lname]
+        s = moe.make_shape(R, cfg.d, EP_EXPERTS, 1, cfg.H, 0, "bf16", LAYOUTS[lname])
+        y = torch.empty_like(x)
+        moe.moe_grouped_ffn(s, x, None, torch.from_numpy(offs.astype(np.int32)).cuda(), g[:EP_EXPERTS],
+                            u[:EP_EXPERTS], dn[:EP_EXPERTS], y, moe.allocate_workspace(s))
+        torch.cuda.synchronize()
+        outs[lname] = G.to_f64(y[torch.from_numpy(rows).cuda()])
+        del y
+    x_rows = G.to_f64(x[torch.from_numpy(rows).cuda()])
+    del x
+    print(f"[ep8-share] oracle SwiGLU of {len(rows)} rows over {int((counts > 0).sum())} experts", flush=True)
+    efn = helpers.expert_fn_host(cfg, 0, cache=False)
+
+    def expert_rows(e):
+        sel = owner == e
+        return sel, oracle.swiglu(x_rows[sel], *efn(e))
+
+    ref = np.zeros_like(x_rows)
+    with ThreadPoolExecutor(8) as pool:
+        for sel, r in pool.map(expert_rows, sorted(set(owner.tolist()))):
+            ref[sel] = r
+    for lname, out in outs.items():
+        ok, err, bound = G.tolerance_ok(out, ref)
+        assert ok, (lname, err, bound)
 
 
 SKEWED = synth.CONFIG_BY_NAME["skewed_mixtral_t4096"]
