@@ -28,6 +28,9 @@ CONFIGS = [
     # grouped-GEMM path with many groups: ~256 rows per expert (one M-tile, some spilling into a
     # second), partial N-tiles of both passes (H = 192 < 256)
     synth.LayerConfig("gelu_gemm_groups", 4096, 256, 64, 4, 192, 0, "bf16"),
+    # the shapes of the overview article's layer example (section 4.1): model width 768, 8 experts
+    # of width 3072, top-2, a batch of 2 sequences of 10 tokens (20 rows)
+    synth.LayerConfig("gelu_overview_example", 20, 768, 8, 2, 3072, 0, "bf16"),
 ]
 CASES = [(c, moe.MOE_LAYOUT_ROWMAJOR) for c in CONFIGS] + \
         [(c, moe.MOE_LAYOUT_FRAG16) for c in CONFIGS if c.d % 32 == 0 and c.H % 32 == 0]
