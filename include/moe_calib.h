@@ -24,13 +24,14 @@ extern "C" {
 #endif
 
 /* Workgroups each probe launches: the entries of its `sink`. */
-#define MOE_CALIB_READ_BLOCKS 2048
+#define MOE_CALIB_READ_BLOCKS 512
 #define MOE_CALIB_MFMA_BLOCKS 256
 
 /*
- * moe_calib_read_stream -- read `bytes` of `buf` once, 16 bytes per lane per load: every wave of
- * MOE_CALIB_READ_BLOCKS x 256 threads streams its own contiguous share of the buffer, 1 KB per load
- * instruction and eight loads in flight, the access pattern of the weight-streaming kernels.
+ * moe_calib_read_stream -- read `bytes` of `buf` once, 16 bytes per lane per load: each of
+ * MOE_CALIB_READ_BLOCKS workgroups of 256 threads reads its own contiguous share of the buffer,
+ * 1 KB per load instruction, its four waves taking alternate kilobytes with eight loads each in
+ * flight: a few long streams per compute unit, the fastest read pattern measured on the part.
  * nontemporal != 0 gives every load the non-temporal hint, as the weight-streaming kernels use.
  * Each workgroup folds what it read into one word of sink[MOE_CALIB_READ_BLOCKS] (uint32), so no load
  * can be dropped. bytes must be a non-zero multiple of 16; buf 16-byte aligned.

@@ -24,7 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 (MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
  MOE_ERR_TOO_LARGE) = range(7)
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20   # fixed device scratch of moe_layer_forward_noalloc
-MOE_CALIB_READ_BLOCKS, MOE_CALIB_MFMA_BLOCKS = 2048, 256   # workgroups (sink entries) of the probes
+MOE_CALIB_READ_BLOCKS, MOE_CALIB_MFMA_BLOCKS = 512, 256   # workgroups (sink entries) of the probes
 MOE_F32, MOE_BF16 = 0, 1
 MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_FRAG16, MOE_LAYOUT_INT8_FRAG, MOE_LAYOUT_FP8_FRAG = 0, 1, 2, 3
 MOE_ROUTING_SOFTMAX, MOE_ROUTING_SIGMOID = 0, 1
