@@ -98,3 +98,13 @@ def test_gelu_bench_refuses_int8_weights_before_touching_a_device():
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 2
     assert "--expert gelu" in r.stderr
+
+
+@pytest.mark.parametrize("extra", [["--layout", "int8"], ["--workload", "tiny_fp32"], ["--ep-share", "3"]])
+def test_ep_share_refuses_what_it_cannot_split_before_touching_a_device(extra):
+    """The expert-parallel share needs bf16 weights of a SwiGLU layer and a degree that divides E."""
+    args = ["--ep-share", "8"] + extra if extra[0] != "--ep-share" else extra
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args,
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    assert "--ep-share" in r.stderr
