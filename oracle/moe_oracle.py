@@ -31,7 +31,7 @@ Sources (the pages this follows):
                   and the router listing of §4.3 (sigmoid of the raw logits plus the bias, top-k on
                   that, weights from the unbiased sigmoid of the selected).
 
-Readings where the pages are silent or garbled (each is also listed in the design doc):
+Readings where the pages are silent or garbled:
   * combine: out = Shared(x) + sum_j w_j * Expert_{e_j}(x); the shared expert has weight 1, no
     residual and no norm inside the layer (the [MoE kernels] §1.1 formula is lost in extraction).
   * no learned router bias; an optional per-expert logit bias is an explicit input, added to the
