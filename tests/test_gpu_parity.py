@@ -412,3 +412,28 @@ def test_layer_matches_oracle_packed_weights(cfg):
     Lr = G.make_layer(cfg)
     rr = G.run_layer(Lr)
     assert torch.equal(r.out.view(torch.int16), rr.out.view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [12, 200, 3000])   # decode tail, one wave per token, grouped GEMM
+@pytest.mark.parametrize("layout", ["rowmajor", "frag16"])
+def test_every_token_on_the_same_experts(T, layout):
+    """A logit bias that sends every token to experts 5 and 9 (k = 2): one or two buckets hold all the
+    rows, the other 14 are empty (at T = 3000 the GEMM runs 10 M-tiles of one group while the tile
+    schedule hands out nothing for the rest). Routing bit-exact, output within the layer tolerance."""
+    cfg = LayerConfig(f"all_on_two_T{T}", T, 256, 16, 2, 192, 64, "bf16")
+    L = G.make_layer(cfg, screen=False, layout={"rowmajor": moe.MOE_LAYOUT_ROWMAJOR,
+                                                "frag16": moe.MOE_LAYOUT_FRAG16}[layout])
+    bias = np.zeros(cfg.E, dtype=np.float32)
+    bias[5], bias[9] = 100.0, 50.0
+    L.host.logit_bias = bias
+    L.bias = torch.from_numpy(bias).cuda()
+    r = G.run_layer(L)
+    counts = r.counts.cpu().numpy()
+    assert counts[5] == T and counts[9] == T and counts.sum() == 2 * T
+    check_logits_close(L, r)
+    check_routing_on_gpu_logits(L, r)
+    x, wg, b = G.oracle_inputs(L)
+    ref = oracle.layer_forward(x, wg, cfg.k, L.expert_fn(), L.shared_fn(), b, cfg.routing)
+    np.testing.assert_array_equal(r.idx.cpu().numpy(), ref["idx"])
+    ok, err, bound = G.tolerance_ok(G.to_f64(r.out), ref["out"])
+    assert ok, (err, bound)
