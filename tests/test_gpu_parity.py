@@ -35,6 +35,11 @@ MID = [
     # whose d ends inside a 32-wide k-step
     LayerConfig("decode_ragged_shared", 12, 264, 16, 4, 200, 136, "bf16"),
     LayerConfig("wide_E1024", 40, 64, 1024, 2, 16, 0, "bf16"),
+    # the smallest sizes the ABI takes (d, H, Hs = 8: a single K chunk shorter than a k-step or a
+    # GEMM slice) on the decode tail, the grouped GEMM and the router GEMM
+    LayerConfig("tiny_dims_decode", 5, 8, 4, 2, 8, 8, "bf16"),
+    LayerConfig("tiny_dims_gemm", 600, 8, 2, 1, 8, 8, "bf16"),
+    LayerConfig("tiny_dims_router_gemm", 2048, 8, 4, 2, 16, 0, "bf16"),
     synth.CONFIGS[0],
     # many rows per expert: tiled MFMA grouped GEMM (K tails of 8, partial N and M tiles)
     LayerConfig("gemm_ragged_shared", 600, 264, 16, 2, 200, 136, "bf16"),
