@@ -270,7 +270,10 @@ ffn_gate_up_stream(const FfnGroups p) {
 // One matrix, 16 weight rows, against NTT 16-token tiles: the streaming loop of the down kernel
 // below with any B rows (x rows for the first layer). aw / qw: the lane's fragment source (bf16 with
 // ws elements between k-steps, or one-byte codes), bsrc: the lane's B row per tile (8 elements at
-// its k-chunk), K: reduction length.
+// its k-chunk; an in-bounds row also for lanes past the group), K: reduction length. With one
+// token tile (bf16) the B loads are issued for every lane and the rows past the group zeroed at
+// the MFMA, so no load waits behind a per-lane branch (decode T=8: -0.6%); with two tiles the
+// second is mostly past the group and its loads stay masked (unmasked, T=256 down took 8% longer).
 template <int NTT, int LAYOUT>
 __device__ __forceinline__ void stream_rows(const uint16_t* aw, const int8_t* qw, int ws, const uint16_t* const (&bsrc)[NTT],
                                             const bool (&bok)[NTT], int K, int kq, f32x4_t (&acc)[NTT]) {
@@ -312,11 +315,11 @@ __device__ __forceinline__ void stream_rows(const uint16_t* aw, const int8_t* qw
 #pragma unroll
       for (int s = 0; s < kUnroll; ++s)
 #pragma unroll
-        for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bsrc[j] + k0 + 32 * s) : zero;
+        for (int j = 0; j < NTT; ++j) b[s][j] = NTT == 1 || bok[j] ? ld16(bsrc[j] + k0 + 32 * s) : zero;
 #pragma unroll
       for (int s = 0; s < kUnroll; ++s)
 #pragma unroll
-        for (int j = 0; j < NTT; ++j) acc[j] = mfma16x16x32(a[s], b[s][j], acc[j]);
+        for (int j = 0; j < NTT; ++j) acc[j] = mfma16x16x32(a[s], bok[j] ? b[s][j] : zero, acc[j]);
     }
     for (; k0 < K; k0 += 32) {  // tail: K is a multiple of 8, so a lane's 8-chunk is all in or all out
       const bool kok = k0 + kq * 8 < K;
@@ -467,11 +470,11 @@ ffn_down_stream(const FfnGroups p) {
 #pragma unroll
         for (int s = 0; s < kUnroll; ++s)
 #pragma unroll
-          for (int j = 0; j < NTT; ++j) b[s][j] = bok[j] ? ld16(bh[j] + k0 + 32 * s) : zero;
+          for (int j = 0; j < NTT; ++j) b[s][j] = NTT == 1 || bok[j] ? ld16(bh[j] + k0 + 32 * s) : zero;
 #pragma unroll
         for (int s = 0; s < kUnroll; ++s)
 #pragma unroll
-          for (int j = 0; j < NTT; ++j) acc[j] = mfma16x16x32(a[s], b[s][j], acc[j]);
+          for (int j = 0; j < NTT; ++j) acc[j] = mfma16x16x32(a[s], bok[j] ? b[s][j] : zero, acc[j]);
       }
       for (; k0 < K; k0 += 32) {
         const bool kok = k0 + kq * 8 < K;
