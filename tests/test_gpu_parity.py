@@ -442,3 +442,33 @@ def test_every_token_on_the_same_experts(T, layout):
     np.testing.assert_array_equal(r.idx.cpu().numpy(), ref["idx"])
     ok, err, bound = G.tolerance_ok(G.to_f64(r.out), ref["out"])
     assert ok, (err, bound)
+
+
+@pytest.mark.parametrize("name", ["decode_ragged_shared", "gemm_ragged_shared"])
+def test_timed_layer_matches_the_layer_and_times_every_stage(name):
+    """moe_layer_forward_timed (the entry point the benchmark times stages with) gives the same bits
+    as moe_layer_forward, and every event pair it records closes: a positive duration for each stage
+    that launches a kernel (moe_stage_kernel_name non-empty), the events of a stage that launches
+    nothing recorded back to back."""
+    import ctypes
+    import bench
+
+    cfg = MID_BY_NAME[name]
+    L = G.make_layer(cfg)
+    ref = G.run_layer(L)
+    n_st = moe.MOE_NUM_STAGES
+    ev = bench.HipEvents(2 * n_st)
+    try:
+        out = torch.empty_like(ref.out)
+        stream = torch.cuda.current_stream()
+        moe.moe_layer_forward_timed(L.shape, L.x, L.w_router, L.bias, L.w_gate, L.w_up, L.w_down, L.ws_gate,
+                                    L.ws_up, L.ws_down, out, workspace=moe.allocate_workspace(L.shape),
+                                    stream=stream, events=ev.array(0, 2 * n_st))
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.out.view(torch.int16))
+        for st in range(n_st):
+            ms = ev.elapsed_ms(2 * st, 2 * st + 1)
+            launches = moe.moe_stage_kernel_name(L.shape, st) != ""
+            assert (ms > 0) if launches else (0 <= ms < 0.05), (moe.STAGES[st], ms)
+    finally:
+        ev.close()
