@@ -1,5 +1,5 @@
 """The measurement probes on the GPU: the read stream touches every 16-byte unit of the buffer exactly
-once (needs an MI355X)."""
+once, and the MFMA loop executes every instruction it counts (needs an MI355X)."""
 
 import numpy as np
 import pytest
@@ -23,3 +23,20 @@ def test_read_probe_reads_every_unit_once(nbytes, nontemporal):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy())
     assert got == np.bitwise_xor.reduce(host)
+
+
+@pytest.mark.parametrize("iters", [1, 4])
+def test_mfma_probe_accumulates_every_instruction(iters):
+    """With every operand 1.0 each 32x32x16 MFMA adds 16 to each of a wave's 1,024 outputs, so a
+    workgroup's sum is 8 waves x 8 accumulators x 1,024 outputs x 16 x iters (exact in float32 for
+    these counts): an instruction dropped or an accumulator left out changes it. The clock counters
+    of every wave advance."""
+    n = moe.MOE_CALIB_MFMA_BLOCKS * 512 * 16
+    ops = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(moe.MOE_CALIB_MFMA_BLOCKS, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(moe.MOE_CALIB_MFMA_BLOCKS * 8 * 4, dtype=torch.int64, device="cuda")
+    moe.moe_calib_mfma(ops, iters, sink, clocks)
+    torch.cuda.synchronize()
+    assert (sink.cpu().numpy() == 8 * 8 * 1024 * 16 * iters).all()
+    c = clocks.view(-1, 4).cpu().numpy()
+    assert (c[:, 2] > c[:, 0]).all() and (c[:, 3] >= c[:, 1]).all()
