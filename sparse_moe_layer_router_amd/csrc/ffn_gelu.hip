@@ -13,7 +13,9 @@
 // fp32 inside the MFMA; the bias is added in fp32 before the activation and the single rounding.
 // A bucket of n rows streams its expert's weights ceil(n / 16 NTT) times, so this is the decode-regime
 // form; layers with many rows per expert run the tiled grouped GEMM instead (ffn_gemm.hip, GELU
-// modes).
+// modes). With one token tile the B loads are issued for every lane (rows past the bucket read its
+// first row) and zeroed at the MFMA, so no load waits behind a per-lane branch; with two tiles the
+// second is mostly past the bucket and its loads stay masked.
 #include "dispatch.h"
 #include "moe_device.h"
 
@@ -91,11 +93,11 @@ ffn_gelu_stream(const GeluGroups p) {
 #pragma unroll
       for (int s = 0; s < kGeluUnroll; ++s)
 #pragma unroll
-        for (int j = 0; j < NTT; ++j) x[s][j] = bok[j] ? ld16(bx[j] + k0 + 32 * s) : zero;
+        for (int j = 0; j < NTT; ++j) x[s][j] = NTT == 1 || bok[j] ? ld16(bx[j] + k0 + 32 * s) : zero;
 #pragma unroll
       for (int s = 0; s < kGeluUnroll; ++s)
 #pragma unroll
-        for (int j = 0; j < NTT; ++j) acc[j] = mfma16x16x32(w[s], x[s][j], acc[j]);
+        for (int j = 0; j < NTT; ++j) acc[j] = mfma16x16x32(w[s], bok[j] ? x[s][j] : zero, acc[j]);
     }
     for (; k0 < K; k0 += 32) {  // tail: K is a multiple of 8, so a lane's 8 columns are all in or all out
       const bool kok = k0 + kq * 8 < K;
