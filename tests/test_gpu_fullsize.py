@@ -229,6 +229,64 @@ def test_dsv3_ep8_share_grouped_ffn(dsv3_weights):
         assert ok, (lname, err, bound)
 
 
+FP8_GEMM_COUNTS = [256, 0, 1, 320, 321, 300, 250, 200, 640, 33, 32, 31, 257, 100, 500, 288]
+
+
+@pytest.mark.timeout(900)
+def test_dsv3_fp8_grouped_gemm_at_full_width():
+    """The one-byte grouped GEMM with E4M3 codes at the DeepSeek-V3 widths (d = 7168, H = 2048):
+    moe_grouped_ffn over the first 16 experts (quantized on their own) and buckets of 0 to 640
+    contiguous rows (mean 221, so the grouped GEMM runs; an empty and a one-row bucket, buckets of
+    exactly one M-tile and one row more, two M-tiles). The layer test at T = 8192 runs the INT8
+    form of the same GEMM; this one checks the E4M3 decode inside it at that size. Checked rows:
+    the first and last row of every 320-row M-tile plus a seeded sample, against the oracle's SwiGLU
+    on the dequantized E4M3 weights."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    cfg = DSV3
+    E = len(FP8_GEMM_COUNTS)
+    counts = np.array(FP8_GEMM_COUNTS)
+    R = int(counts.sum())
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    (g, u, dn), _, _ = G.make_weights(dataclasses.replace(cfg, E=E), 0, host_copy=False)
+    q = moe.quantize_expert_weights(g, u, dn, fp8=True)
+    torch.cuda.synchronize()
+    del g, u, dn
+    x = torch.empty(R, cfg.d, dtype=torch.bfloat16, device="cuda")
+    synth.normal_device(x, 11, synth.stream_id(synth.K_X), 1.0)
+    s = moe.make_shape(R, cfg.d, E, 1, cfg.H, 0, "bf16", moe.MOE_LAYOUT_FP8_FRAG)
+    assert moe.moe_stage_kernel_name(s, moe.STAGES.index("ffn_gate_up")) == "grouped_gemm_kernel<0, 3>"
+    print(f"[fp8-gemm] moe_grouped_ffn E={E} rows={R} d={cfg.d} H={cfg.H}", flush=True)
+    y = torch.empty_like(x)
+    moe.moe_grouped_ffn(s, x, None, torch.from_numpy(offs.astype(np.int32)).cuda(), q[0], q[1], q[2], y,
+                        moe.allocate_workspace(s))
+    torch.cuda.synchronize()
+    rows = set()
+    for e in range(E):
+        for m0 in range(int(offs[e]), int(offs[e + 1]), M_TILE_ROWS):
+            rows.update((m0, min(m0 + M_TILE_ROWS, int(offs[e + 1])) - 1))
+    rows.update(np.random.default_rng(2).choice(R, size=16, replace=False).tolist())
+    rows = np.array(sorted(rows), dtype=np.int64)
+    owner = np.searchsorted(offs, rows, side="right") - 1
+    out = G.to_f64(y[torch.from_numpy(rows).cuda()])
+    x_rows = G.to_f64(x[torch.from_numpy(rows).cuda()])
+    del x, y, q
+    print(f"[fp8-gemm] oracle SwiGLU of {len(rows)} rows over {len(set(owner.tolist()))} experts (E4M3 weights)",
+          flush=True)
+    efn = helpers.expert_fn_host(dataclasses.replace(cfg, E=E), 0, cache=False, quant="fp8")
+
+    def expert_rows(e):
+        sel = owner == e
+        return sel, oracle.swiglu(x_rows[sel], *efn(e))
+
+    ref = np.zeros_like(x_rows)
+    with ThreadPoolExecutor(8) as pool:
+        for sel, r in pool.map(expert_rows, sorted(set(owner.tolist()))):
+            ref[sel] = r
+    ok, err, bound = G.tolerance_ok(out, ref)
+    assert ok, (err, bound)
+
+
 SKEWED = synth.CONFIG_BY_NAME["skewed_mixtral_t4096"]
 
 
